@@ -1,0 +1,29 @@
+"""Plain fp64 CPU oracle for permuted block-sparse attention prefill.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import or call anything in this package.  The GPU library never does, and
+nothing here imports the GPU library: the two share no code.
+
+``pbsa_oracle`` follows the pages' definitions step by step in NumPy fp64 (library matmul,
+sort and exp as primitives).  ``brute`` re-derives every stage with pure-Python loops and
+``math.fsum`` for tiny shapes.  Every function is pinned by the CPU tests (closed forms,
+invariants, the brute force and a hand-derived example); none is marked "parity unpinned".
+"""
+from .pbsa_oracle import (  # noqa: F401
+    block_mask,
+    block_range,
+    block_sparse_attention,
+    calibrate_thresholds,
+    dense_attention,
+    default_scale,
+    kept_bitmap,
+    key_importance,
+    key_rows_of_block,
+    num_blocks,
+    pool_blocks,
+    pool_permuted_blocks,
+    segment_of_block,
+    segment_permutation,
+    tile_max,
+    tri_offset,
+)

@@ -1,0 +1,161 @@
+"""Pure-Python brute force of every stage, for tiny shapes (test infrastructure only).
+
+Written independently of ``pbsa_oracle``: per-(h, i, j) predicates, explicit loops, ``math.fsum``
+for every sum, and an exhaustive search over block subsets for the mask instead of a sort.  It is
+the check that pins the NumPy oracle on shapes with N <= 64, d <= 8 and at most 13 blocks.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from typing import Dict, List, Optional, Tuple
+
+
+def _dot(a, b) -> float:
+    return math.fsum(float(x) * float(y) for x, y in zip(a, b))
+
+
+def _seg(pos_block_start: int, S: Optional[int]) -> int:
+    return 0 if S is None else pos_block_start // S
+
+
+def importance(q, k, B: int, scale: float) -> List[List[float]]:
+    """imp[g][j] = (1 / (G * R)) * sum over the last-block rows of the causal softmax weight of j."""
+    Hq, N = len(q), len(q[0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    rows = list(range(max(0, N - B), N))
+    imp = []
+    for g in range(Hkv):
+        parts: List[List[float]] = [[] for _ in range(N)]
+        for h in range(g * G, (g + 1) * G):
+            for i in rows:
+                s = [scale * _dot(q[h][i], k[g][j]) for j in range(i + 1)]
+                m = max(s)
+                z = math.fsum(math.exp(x - m) for x in s)
+                lse = m + math.log(z)
+                for j in range(i + 1):
+                    parts[j].append(math.exp(s[j] - lse))
+        imp.append([math.fsum(parts[j]) / (G * len(rows)) for j in range(N)])
+    return imp
+
+
+def check_permutation(perm, imp, S: int, tol: float = 1e-12) -> None:
+    """perm must map each segment onto itself and list it by importance desc, position asc."""
+    Hkv, N = len(perm), len(perm[0])
+    for g in range(Hkv):
+        for a in range(0, N, S):
+            b = min(a + S, N)
+            seg = [int(x) for x in perm[g][a:b]]
+            assert sorted(seg) == list(range(a, b)), "not a bijection on its segment"
+            for r in range(len(seg) - 1):
+                x, y = seg[r], seg[r + 1]
+                ix, iy = imp[g][x], imp[g][y]
+                if abs(ix - iy) <= tol * max(abs(ix), abs(iy), 1e-300):
+                    assert x < y, "equal importance not in position order"
+                else:
+                    assert ix > iy, "importance not descending"
+
+
+def _key_rows(J: int, I: int, perm_g, B: int, S: Optional[int], N: int) -> List[int]:
+    out = []
+    for t in range(B):
+        p = J * B + t
+        if p >= N:
+            break
+        if perm_g is not None and _seg(J * B, S) < _seg(I * B, S):
+            out.append(int(perm_g[p]))
+        else:
+            out.append(p)
+    return out
+
+
+def mask(q, k, perm, B: int, S: Optional[int], tau: float, force_diag: bool, force_first: bool,
+         scale: float) -> Tuple[Dict[Tuple[int, int], List[int]], Dict[Tuple[int, int], List[float]]]:
+    """Selected blocks per (h, I) by exhaustive subset search (I <= 12).
+
+    Among all subsets of {0..I} whose pooled probability mass reaches tau, take the smallest
+    cardinality, then the largest mass, then the lexicographically smallest index tuple.
+    """
+    Hq, N, d = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    NB = -(-N // B)
+    sel, probs = {}, {}
+    for h in range(Hq):
+        g = h // G
+        pg = None if perm is None else perm[g]
+        for I in range(NB):
+            qrows = list(range(I * B, min((I + 1) * B, N)))
+            qbar = [math.fsum(float(q[h][i][t]) for i in qrows) / len(qrows) for t in range(d)]
+            z = []
+            for J in range(I + 1):
+                kr = _key_rows(J, I, pg, B, S, N)
+                kbar = [math.fsum(float(k[g][j][t]) for j in kr) / len(kr) for t in range(d)]
+                z.append(scale * _dot(qbar, kbar))
+            m = max(z)
+            tot = math.fsum(math.exp(x - m) for x in z)
+            p = [math.exp(x - m) / tot for x in z]
+            probs[(h, I)] = p
+            best = None
+            if tau >= 1.0:
+                best = tuple(range(I + 1))
+            else:
+                for size in range(1, I + 2):
+                    cands = []
+                    for sub in itertools.combinations(range(I + 1), size):
+                        mass = math.fsum(p[J] for J in sub)
+                        if mass >= tau:
+                            cands.append((-mass, sub))
+                    if cands:
+                        best = min(cands)[1]
+                        break
+                if best is None:
+                    best = tuple(range(I + 1))
+            chosen = set(best)
+            if force_diag:
+                chosen.add(I)
+            if force_first:
+                chosen.add(0)
+            sel[(h, I)] = sorted(chosen)
+    return sel, probs
+
+
+def attention(q, k, v, perm, sel: Dict[Tuple[int, int], List[int]], B: int, S: Optional[int],
+              scale: float, theta=None):
+    """o[h][i] and lse[h][i] over the union of (kept) selected blocks, per-element predicates."""
+    Hq, N, d = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    NB = -(-N // B)
+    out = [[None] * N for _ in range(Hq)]
+    lse = [[None] * N for _ in range(Hq)]
+    kept = {}
+    for h in range(Hq):
+        g = h // G
+        pg = None if perm is None else perm[g]
+        for I in range(NB):
+            qrows = list(range(I * B, min((I + 1) * B, N)))
+            blocks = []
+            for J in sel[(h, I)]:
+                kr = _key_rows(J, I, pg, B, S, N)
+                if theta is not None and J != I:
+                    mx = max(scale * _dot(q[h][i], k[g][j]) for i in qrows for j in kr if j <= i)
+                    if mx < theta[h][I]:
+                        continue
+                blocks.append((J, kr))
+            kept[(h, I)] = [J for J, _ in blocks]
+            for i in qrows:
+                keys = [j for _, kr in blocks for j in kr if j <= i]
+                if not keys:
+                    out[h][i] = [0.0] * d
+                    lse[h][i] = -math.inf
+                    continue
+                s = [scale * _dot(q[h][i], k[g][j]) for j in keys]
+                m = max(s)
+                w = [math.exp(x - m) for x in s]
+                z = math.fsum(w)
+                out[h][i] = [math.fsum(w[n] * float(v[g][j][t]) for n, j in enumerate(keys)) / z
+                             for t in range(d)]
+                lse[h][i] = m + math.log(z)
+    return out, lse, kept

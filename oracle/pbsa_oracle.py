@@ -1,0 +1,371 @@
+"""fp64 NumPy oracle for permuted block-sparse attention prefill (test infrastructure only).
+
+Notation (batch 1): N tokens, Hq query heads, Hkv KV heads, G = Hq / Hkv, g(h) = h // G,
+head dim d, block size B (query block = key block), segment size S (a multiple of B),
+NB = ceil(N / B) blocks, block J = tokens [J*B, min((J+1)*B, N)), segment of block J
+sigma(J) = (J*B) // S, logit scale c = 1/sqrt(d) unless given.
+
+Inputs are fp64 arrays laid out [heads][tokens][d]; the GPU path receives the same values as
+bf16, so callers pass the bf16-rounded values widened to fp64.
+
+Readings taken where the pages leave a step open (each is listed with its reason in the
+design notes of the repository):
+  * importance rows are the last B query positions [max(0, N-B), N) of every query head of the
+    KV group; masked (j > i) entries count as zero; the mean divides by G * (number of rows);
+  * one permutation per KV head, sorting by importance descending, ties by position ascending;
+  * a query block reads its own segment in natural order; only strictly earlier segments are
+    read through the permutation;
+  * pooled block score = c * (mean query of the block) . (mean key of the key block), softmax
+    over J <= I, no intra-block causal mask on the diagonal block's score;
+  * the mask keeps the shortest prefix of the (p desc, J asc) order whose cumulative mass
+    reaches tau (>=), plus the forced blocks; tau >= 1 keeps every J <= I;
+  * the early-stop gate is decided per whole tile on the exact max of the scaled causal
+    logits; a skipped tile contributes nothing to the softmax state.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- geometry
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+def num_blocks(n: int, b: int) -> int:
+    return -(-n // b)
+
+
+def block_range(J: int, B: int, N: int) -> np.ndarray:
+    """Token positions of natural block J."""
+    return np.arange(J * B, min((J + 1) * B, N))
+
+
+def segment_of_block(J: int, B: int, S: Optional[int]) -> int:
+    """Segment index of block J (Sparser Block-Sparse Attention via Token Permutation, §2)."""
+    if S is None:
+        return 0
+    return (J * B) // S
+
+
+def tri_offset(I: int) -> int:
+    """Start of row I in the row-major packed lower triangle of an NB x NB block matrix."""
+    return I * (I + 1) // 2
+
+
+def key_rows_of_block(J: int, I: int, perm_g: Optional[np.ndarray], B: int, S: Optional[int],
+                      N: int) -> np.ndarray:
+    """Physical key positions that block J stands for when read by query block I.
+
+    S2O (§1, "Online Permutation via Index-Driven Loading"): tensors keep their HBM layout and an
+    index array says which tokens a tile loads.  Permutation stays inside segments and never
+    crosses segment causality (Sparser Block-Sparse Attention via Token Permutation, §2), so a
+    block in a segment strictly before I's segment is read through the permutation, and a block
+    in I's own segment is read in natural order.
+    """
+    if perm_g is not None and segment_of_block(J, B, S) < segment_of_block(I, B, S):
+        return np.asarray(perm_g[J * B:min((J + 1) * B, N)], dtype=np.int64)
+    return block_range(J, B, N)
+
+
+# ----------------------------------------------------------------------------- stage 1: permutation
+
+def key_importance(q: np.ndarray, k: np.ndarray, block_size: int,
+                   scale: Optional[float] = None) -> np.ndarray:
+    """Global key-importance vector imp [Hkv][N] from the last block of queries.
+
+    Sparser Block-Sparse Attention via Token Permutation, §3 ("Proxy Scoring"): the importance of
+    every key is the mean, over the last block of queries, of the attention probability that key
+    receives.  For KV head g the rows are (h, i) with g(h) = g and i in [max(0, N-B), N); each
+    row's probabilities are the causal softmax over keys j <= i.
+    """
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    c = default_scale(d) if scale is None else scale
+    rows = np.arange(max(0, N - block_size), N)
+    keys = np.arange(N)
+    allowed = keys[None, :] <= rows[:, None]
+    imp = np.zeros((Hkv, N))
+    for g in range(Hkv):
+        acc = np.zeros(N)
+        for h in range(g * G, (g + 1) * G):
+            s = c * (q[h, rows] @ k[g].T)                      # [rows][N]
+            s = np.where(allowed, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            lse = m + np.log(np.exp(s - m).sum(axis=1, keepdims=True))
+            acc += np.exp(s - lse).sum(axis=0)                 # masked entries are exp(-inf) = 0
+        imp[g] = acc / (G * len(rows))
+    return imp
+
+
+def segment_permutation(imp: np.ndarray, segment_size: int) -> np.ndarray:
+    """Per-KV-head index list perm [Hkv][N]: each segment's positions by importance, descending.
+
+    Sparser Block-Sparse Attention via Token Permutation, §2 (segments of S tokens, permutation
+    only inside a segment) and §3 ("Sorting": keys of a segment in descending order of global
+    importance).  Equal importance keeps the original order (stable).  perm[g, a + r] is the
+    position of the r-th most important key of segment [a, a + S).
+    """
+    Hkv, N = imp.shape
+    perm = np.empty((Hkv, N), dtype=np.int64)
+    for g in range(Hkv):
+        for a in range(0, N, segment_size):
+            b = min(a + segment_size, N)
+            pos = np.arange(a, b)
+            order = np.lexsort((pos, -imp[g, a:b]))            # primary: -imp asc; then pos asc
+            perm[g, a:b] = pos[order]
+    return perm
+
+
+# ----------------------------------------------------------------------------- stage 2: block mask
+
+def pool_blocks(x: np.ndarray, block_size: int) -> np.ndarray:
+    """Mean of each natural block's rows: [H][N][d] -> [H][NB][d]."""
+    H, N, d = x.shape
+    NB = num_blocks(N, block_size)
+    out = np.empty((H, NB, d))
+    for J in range(NB):
+        out[:, J] = x[:, J * block_size:min((J + 1) * block_size, N)].mean(axis=1)
+    return out
+
+
+def pool_permuted_blocks(k: np.ndarray, perm: np.ndarray, block_size: int) -> np.ndarray:
+    """Mean key of each block of the permuted order: rows perm[g, J*B ...]."""
+    Hkv, N, d = k.shape
+    NB = num_blocks(N, block_size)
+    out = np.empty((Hkv, NB, d))
+    for g in range(Hkv):
+        for J in range(NB):
+            out[g, J] = k[g, perm[g, J * block_size:min((J + 1) * block_size, N)]].mean(axis=0)
+    return out
+
+
+def block_mask(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_size: int,
+               segment_size: Optional[int], mass_tau: float, force_diag: bool = True,
+               force_first: bool = True, scale: Optional[float] = None):
+    """Per (query head, query block) list of selected key blocks.
+
+    Sparser Block-Sparse Attention via Token Permutation, §4 ("Block Selection"): block
+    importance is estimated by mean pooling, on the permuted keys.  The keep rule is a
+    cumulative-mass target: SampleAttention (Technical Deep Dive) controls sparsity by the
+    attention mass that must be preserved per query.
+
+    Row (h, I): z_J = c * Qbar_{h,I} . Kbar_J for J <= I, with Kbar_J pooled over the rows block J
+    stands for when read by I (``key_rows_of_block``); p = softmax(z); order J by (p desc, J asc);
+    keep the shortest prefix whose running sum reaches mass_tau (all J <= I when mass_tau >= 1 or
+    when rounding keeps the sum below it); add I (force_diag) and 0 (force_first).
+
+    Returns (count [Hq][NB] int64, idx [Hq][NB(NB+1)/2] int64 ascending per row, -1 padded,
+    prob [Hq][NB(NB+1)/2] fp64 = p per row).
+    """
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    qbar = pool_blocks(q, B)
+    knat = pool_blocks(k, B)
+    kperm = pool_permuted_blocks(k, perm, B) if perm is not None else knat
+    ntri = NB * (NB + 1) // 2
+    count = np.zeros((Hq, NB), dtype=np.int64)
+    idx = np.full((Hq, ntri), -1, dtype=np.int64)
+    prob = np.full((Hq, ntri), np.nan)
+    for h in range(Hq):
+        g = h // G
+        for I in range(NB):
+            sI = segment_of_block(I, B, S)
+            kbar = np.stack([kperm[g, J] if segment_of_block(J, B, S) < sI else knat[g, J]
+                             for J in range(I + 1)])
+            z = c * (kbar @ qbar[h, I])
+            e = np.exp(z - z.max())
+            p = e / e.sum()
+            order = np.lexsort((np.arange(I + 1), -p))
+            kstar = I + 1
+            if mass_tau < 1.0:
+                hit = np.nonzero(np.cumsum(p[order]) >= mass_tau)[0]
+                if hit.size:
+                    kstar = int(hit[0]) + 1
+            chosen = set(int(J) for J in order[:kstar])
+            if force_diag:
+                chosen.add(I)
+            if force_first:
+                chosen.add(0)
+            lst = sorted(chosen)
+            o = tri_offset(I)
+            count[h, I] = len(lst)
+            idx[h, o:o + len(lst)] = lst
+            prob[h, o:o + I + 1] = p
+    return count, idx, prob
+
+
+# ----------------------------------------------------------------------------- stage 3: attention
+
+def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: Optional[np.ndarray],
+                           count: Optional[np.ndarray], idx: Optional[np.ndarray], block_size: int,
+                           segment_size: Optional[int], scale: Optional[float] = None,
+                           theta: Optional[np.ndarray] = None,
+                           rows: Optional[Iterable[Tuple[int, int]]] = None,
+                           return_weights: bool = False):
+    """Causal block-sparse attention over the selected (permuted) key blocks.
+
+    Sparser Block-Sparse Attention via Token Permutation, Problem Statement: blocks outside the
+    mask are skipped; S2O §1: selected tiles are gathered by index; S2O §3: the result is the
+    online-softmax state (m, l, acc) over the visited blocks, i.e. exact softmax attention over
+    their union.  For query i of block I of head h the keys are
+        K_hi = { j in key_rows_of_block(J, I) : J in sel(h, I), j <= i }.
+    count/idx None means every J <= I.
+
+    Early stop (Block Sparse Flash Attention, Approach): with theta [Hq][NB], a selected J != I
+    whose exact tile max  max_{i in I, j in rows(J), j <= i} c q_i.k_j  is below theta[h, I] is
+    dropped before the softmax (no V load, no PV, no change to m or l).
+
+    rows: optional iterable of (h, I) to evaluate (others stay NaN).
+    A query left with no key (possible only when the diagonal block is not selected and the gate
+    drops every other tile) gets out = 0 and lse = -inf.
+    Returns (out [Hq][N][d], lse [Hq][N], kept {(h, I): [J ...]}, weights or None).
+    weights (only with return_weights) maps (h, i) -> (key positions, probabilities).
+    """
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    out = np.full((Hq, N, d), np.nan)
+    lse = np.full((Hq, N), np.nan)
+    kept: Dict[Tuple[int, int], List[int]] = {}
+    weights = {} if return_weights else None
+    todo = [(h, I) for h in range(Hq) for I in range(NB)] if rows is None else list(rows)
+    for h, I in todo:
+        g = h // G
+        perm_g = None if perm is None else perm[g]
+        qi = block_range(I, B, N)
+        if count is None:
+            sel = list(range(I + 1))
+        else:
+            o = tri_offset(I)
+            sel = [int(J) for J in idx[h, o:o + int(count[h, I])]]
+        keep_lists = []
+        kept_J = []
+        for J in sel:
+            kj = key_rows_of_block(J, I, perm_g, B, S, N)
+            if theta is not None and J != I:
+                st = c * (q[h, qi] @ k[g, kj].T)
+                st = np.where(kj[None, :] <= qi[:, None], st, -np.inf)
+                if st.max() < theta[h, I]:
+                    continue
+            keep_lists.append(kj)
+            kept_J.append(J)
+        kept[(h, I)] = kept_J
+        keys = np.concatenate(keep_lists) if keep_lists else np.zeros(0, dtype=np.int64)
+        s = c * (q[h, qi] @ k[g, keys].T)                      # [rows of I][keys]
+        s = np.where(keys[None, :] <= qi[:, None], s, -np.inf)
+        for r, i in enumerate(qi):
+            ok = keys <= i
+            if not ok.any():                                   # no key left: output 0, lse -inf
+                out[h, i] = 0.0
+                lse[h, i] = -np.inf
+                if return_weights:
+                    weights[(h, int(i))] = (keys[:0], np.zeros(0))
+                continue
+            m = s[r].max()
+            e = np.exp(s[r] - m)
+            l = e.sum()
+            out[h, i] = (e @ v[g, keys]) / l
+            lse[h, i] = m + np.log(l)
+            if return_weights:
+                weights[(h, int(i))] = (keys, e / l)
+    return out, lse, kept, weights
+
+
+def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optional[float] = None,
+                    causal: bool = True, allowed: Optional[np.ndarray] = None):
+    """Direct softmax(c Q K^T + mask) V per head (GQA: query head h reads KV head h // G).
+
+    allowed: optional [N][N] boolean matrix of (i, j) pairs that may attend (combined with the
+    causal rule when causal is True).  Returns (out [Hq][N][d], lse [Hq][N]).
+    """
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    c = default_scale(d) if scale is None else scale
+    ok = np.ones((N, N), dtype=bool)
+    if causal:
+        ok &= np.tri(N, dtype=bool)
+    if allowed is not None:
+        ok &= allowed
+    out = np.empty((Hq, N, d))
+    lse = np.empty((Hq, N))
+    for h in range(Hq):
+        g = h // G
+        s = np.where(ok, c * (q[h] @ k[g].T), -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        l = e.sum(axis=1, keepdims=True)
+        out[h] = (e / l) @ v[g]
+        lse[h] = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- early-stop support
+
+def tile_max(q: np.ndarray, k: np.ndarray, block_size: int, scale: Optional[float] = None,
+             rows: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+    """Exact per-tile max of the scaled causal logits, natural order, packed lower triangle.
+
+    Block Sparse Flash Attention, Approach: the gate looks at the exact QK^T scores of a tile.
+    Entry (h, I, J), J <= I, is max over i in block I, j in block J, j <= i of c q_i.k_j.
+    Returns [Hq][NB(NB+1)/2] (rows not requested stay NaN).
+    """
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    B = block_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    out = np.full((Hq, NB * (NB + 1) // 2), np.nan)
+    todo = [(h, I) for h in range(Hq) for I in range(NB)] if rows is None else list(rows)
+    for h, I in todo:
+        g = h // G
+        qi = block_range(I, B, N)
+        for J in range(I + 1):
+            kj = block_range(J, B, N)
+            st = c * (q[h, qi] @ k[g, kj].T)
+            st = np.where(kj[None, :] <= qi[:, None], st, -np.inf)
+            out[h, tri_offset(I) + J] = st.max()
+    return out
+
+
+def calibrate_thresholds(tmax: np.ndarray, num_blocks_: int, keep: int) -> np.ndarray:
+    """Per (head, query block) threshold that keeps the `keep` largest tile maxima of the row.
+
+    Block Sparse Flash Attention, Approach: thresholds are calibrated offline so that roughly the
+    top-k blocks per query survive.  theta[h, I] is the keep-th largest tile max over J <= I, and
+    -inf when the row has no more than `keep` tiles.
+    """
+    Hq = tmax.shape[0]
+    theta = np.full((Hq, num_blocks_), -np.inf)
+    for h in range(Hq):
+        for I in range(num_blocks_):
+            if I + 1 > keep:
+                row = tmax[h, tri_offset(I):tri_offset(I) + I + 1]
+                theta[h, I] = np.sort(row)[::-1][keep - 1]
+    return theta
+
+
+def kept_bitmap(kept: Dict[Tuple[int, int], Sequence[int]], num_q_heads: int, nb: int) -> np.ndarray:
+    """Bitmap [Hq][ceil(NB(NB+1)/2 / 32)] uint32 with bit (tri_offset(I) + J) set for each kept tile."""
+    ntri = nb * (nb + 1) // 2
+    words = -(-ntri // 32)
+    bm = np.zeros((num_q_heads, words), dtype=np.uint32)
+    for (h, I), lst in kept.items():
+        for J in lst:
+            t = tri_offset(I) + J
+            bm[h, t // 32] |= np.uint32(1) << np.uint32(t % 32)
+    return bm

@@ -1,0 +1,73 @@
+"""check 4: the NumPy oracle agrees with the pure-Python brute force on tiny shapes."""
+import math
+
+import numpy as np
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+from oracle import brute
+from conftest import small_inputs
+
+
+@st.composite
+def tiny_case(draw):
+    B = draw(st.sampled_from([2, 4, 8]))
+    S = B * draw(st.sampled_from([1, 2, 4]))
+    nb = draw(st.integers(1, 10))
+    N = draw(st.integers(max(1, (nb - 1) * B + 1), nb * B))      # ragged last block allowed
+    Hkv = draw(st.sampled_from([1, 2]))
+    G = draw(st.sampled_from([1, 2]))
+    d = draw(st.integers(1, 8))
+    tau = draw(st.sampled_from([0.3, 0.5, 0.8, 0.95, 1.0]))
+    diag = draw(st.booleans())
+    first = draw(st.booleans())
+    perm_on = draw(st.booleans())
+    seed = draw(st.integers(0, 2 ** 20))
+    stripes = draw(st.integers(0, 3))
+    return dict(B=B, S=S, N=N, Hkv=Hkv, Hq=Hkv * G, d=d, tau=tau, diag=diag, first=first,
+                perm_on=perm_on, seed=seed, stripes=stripes)
+
+
+@settings(max_examples=40, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case())
+def test_oracle_matches_brute_force(c):
+    N, Hq, Hkv, d, B, S = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"], c["S"]
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+
+    imp = oracle.key_importance(q, k, B)
+    imp_b = brute.importance(q, k, B, scale)
+    np.testing.assert_allclose(imp, np.array(imp_b), rtol=1e-12, atol=1e-300)
+
+    perm = oracle.segment_permutation(imp, S)
+    brute.check_permutation(perm, imp_b, S)
+    use_perm = perm if c["perm_on"] else None
+
+    count, idx, prob = oracle.block_mask(q, k, use_perm, B, S, c["tau"], c["diag"], c["first"])
+    sel_b, prob_b = brute.mask(q, k, use_perm, B, S, c["tau"], c["diag"], c["first"], scale)
+    NB = oracle.num_blocks(N, B)
+    for h in range(Hq):
+        for I in range(NB):
+            o = oracle.tri_offset(I)
+            np.testing.assert_allclose(prob[h, o:o + I + 1], prob_b[(h, I)], rtol=1e-12, atol=1e-300)
+            assert idx[h, o:o + count[h, I]].tolist() == sel_b[(h, I)], (h, I)
+
+    out, lse, _, _ = oracle.block_sparse_attention(q, k, v, use_perm, count, idx, B, S)
+    out_b, lse_b, _ = brute.attention(q, k, v, use_perm, sel_b, B, S, scale)
+    np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)
+
+    # early stop with a threshold between the row's tile maxima, so some tiles drop
+    rng = np.random.default_rng(c["seed"])
+    tm = oracle.tile_max(q, k, B)
+    theta = np.empty((Hq, NB))
+    for h in range(Hq):
+        for I in range(NB):
+            row = tm[h, oracle.tri_offset(I):oracle.tri_offset(I) + I + 1]
+            theta[h, I] = rng.uniform(row.min() - 0.1, row.max() + 0.1)
+    out, lse, kept, _ = oracle.block_sparse_attention(q, k, v, use_perm, count, idx, B, S, theta=theta)
+    out_b, lse_b, kept_b = brute.attention(q, k, v, use_perm, sel_b, B, S, scale, theta=theta)
+    assert kept == kept_b
+    np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)

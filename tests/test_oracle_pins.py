@@ -1,0 +1,292 @@
+"""Pins of the fp64 oracle: invariants, closed forms and special cases fixed by the pages.
+
+The four required self-checks: (1) a full mask reproduces dense causal attention, (2) moving K/V
+physically or jointly permuting them leaves outputs unchanged, (3) softmax rows sum to one,
+(4) tiny cases match the brute force (test_oracle_brute.py).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import small_inputs
+
+SHAPES = [
+    # N, Hq, Hkv, d, B, S  (100 and 72 leave a ragged last block and a ragged last segment)
+    (96, 4, 2, 8, 8, 32),
+    (100, 2, 1, 8, 8, 32),
+    (72, 2, 2, 4, 8, 16),
+]
+
+
+def _pipeline(q, k, v, B, S, tau, perm_on=True, diag=True, first=True):
+    imp = oracle.key_importance(q, k, B)
+    perm = oracle.segment_permutation(imp, S) if perm_on else None
+    count, idx, prob = oracle.block_mask(q, k, perm, B, S, tau, diag, first)
+    return imp, perm, count, idx, prob
+
+
+def _sdpa(q, k, v):
+    G = q.shape[0] // k.shape[0]
+    kt = torch.from_numpy(np.repeat(k, G, axis=0))
+    vt = torch.from_numpy(np.repeat(v, G, axis=0))
+    o = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), kt, vt, is_causal=True)
+    return o.numpy()
+
+
+# ---------------------------------------------------------------- check 1: full mask == dense causal
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("perm_on", [True, False])
+def test_full_mask_is_dense_causal(shape, perm_on):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=11)
+    _, perm, count, idx, _ = _pipeline(q, k, v, B, S, 1.0, perm_on)
+    NB = oracle.num_blocks(N, B)
+    assert (count == np.arange(1, NB + 1)[None, :]).all()
+    out, lse, _, _ = oracle.block_sparse_attention(q, k, v, perm, count, idx, B, S)
+    ref, ref_lse = oracle.dense_attention(q, k, v)
+    assert np.abs(out - ref).max() <= 1e-12
+    assert np.abs(lse - ref_lse).max() <= 1e-12
+    assert np.abs(out - _sdpa(q, k, v)).max() <= 1e-12
+
+
+def test_dense_attention_matches_library_sdpa():
+    q, k, v = small_inputs(64, 2, 1, 16, n_stripes=2, seed=3)
+    ref, _ = oracle.dense_attention(q, k, v)
+    assert np.abs(ref - _sdpa(q, k, v)).max() <= 1e-12
+
+
+# ---------------------------------------------------------------- check 2: permutation semantics
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_index_list_equals_physical_gather(shape):
+    """Reading past segments through perm == physically moving those rows first (S2O §1)."""
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=5)
+    _, perm, count, idx, prob = _pipeline(q, k, v, B, S, 0.6)
+    out, lse, _, _ = oracle.block_sparse_attention(q, k, v, perm, count, idx, B, S)
+    NB = oracle.num_blocks(N, B)
+    for sigma in range(1, -(-N // S)):
+        kp, vp = k.copy(), v.copy()
+        kp[:, :sigma * S] = np.take_along_axis(k, perm[:, :sigma * S, None], axis=1)
+        vp[:, :sigma * S] = np.take_along_axis(v, perm[:, :sigma * S, None], axis=1)
+        rows_I = [I for I in range(NB) if oracle.segment_of_block(I, B, S) == sigma]
+        c2, i2, p2 = oracle.block_mask(q, kp, None, B, S, 0.6)
+        for I in rows_I:
+            o = oracle.tri_offset(I)
+            assert (c2[:, I] == count[:, I]).all()
+            assert (i2[:, o:o + I + 1] == idx[:, o:o + I + 1]).all()
+            assert np.abs(p2[:, o:o + I + 1] - prob[:, o:o + I + 1]).max() <= 1e-13
+        rows = [(h, I) for h in range(Hq) for I in rows_I]
+        o2, l2, _, _ = oracle.block_sparse_attention(q, kp, vp, None, count, idx, B, S, rows=rows)
+        t0 = rows_I[0] * B
+        assert np.array_equal(o2[:, t0:min(N, (rows_I[-1] + 1) * B)], out[:, t0:min(N, (rows_I[-1] + 1) * B)])
+
+
+def test_joint_kv_permutation_invariance_and_query_equivariance():
+    """Non-causal attention ignores the order of (k, v) pairs; permuting queries permutes the output
+    (Sparser Block-Sparse Attention via Token Permutation, §1)."""
+    q, k, v = small_inputs(80, 2, 1, 8, n_stripes=3, seed=9)
+    rng = np.random.default_rng(0)
+    P = rng.permutation(80)
+    ref, _ = oracle.dense_attention(q, k, v, causal=False)
+    o1, _ = oracle.dense_attention(q, k[:, P], v[:, P], causal=False)
+    assert np.abs(o1 - ref).max() <= 1e-12
+    o2, _ = oracle.dense_attention(q[:, P], k, v, causal=False)
+    assert np.abs(o2 - ref[:, P]).max() <= 1e-12
+    inv = np.argsort(P)
+    o3, _ = oracle.dense_attention(q[:, P], k[:, P], v[:, P], causal=False)
+    assert np.abs(o3[:, inv] - ref).max() <= 1e-12
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_past_segment_permutation_leaves_later_queries_unchanged(shape):
+    """Jointly permuting K, V inside a strictly earlier segment does not change causal outputs of
+    later queries (segment causality, Sparser Block-Sparse Attention via Token Permutation, §2)."""
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, seed=21)
+    rng = np.random.default_rng(1)
+    P = np.arange(N)
+    P[:S] = rng.permutation(S)
+    out, lse, _, _ = oracle.block_sparse_attention(q, k, v, None, None, None, B, S)
+    o2, l2, _, _ = oracle.block_sparse_attention(q, k[:, P], v[:, P], None, None, None, B, S)
+    assert np.abs(o2[:, S:] - out[:, S:]).max() <= 1e-12
+    assert np.abs(l2[:, S:] - lse[:, S:]).max() <= 1e-12
+    # the importance proxy moves with the keys, so the permutation lists the same keys
+    imp = oracle.key_importance(q, k, B)
+    imp2 = oracle.key_importance(q, k[:, P], B)
+    assert np.abs(imp2 - imp[:, P]).max() <= 1e-15 + 1e-12 * np.abs(imp).max()
+
+
+# ---------------------------------------------------------------- check 3: normalisation
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_softmax_rows_sum_to_one(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=13)
+    imp, perm, count, idx, prob = _pipeline(q, k, v, B, S, 0.7)
+    assert np.abs(imp.sum(axis=1) - 1.0).max() <= 1e-12
+    NB = oracle.num_blocks(N, B)
+    for I in range(NB):
+        o = oracle.tri_offset(I)
+        assert np.abs(prob[:, o:o + I + 1].sum(axis=1) - 1.0).max() <= 1e-12
+    _, _, _, w = oracle.block_sparse_attention(q, k, v, perm, count, idx, B, S, return_weights=True)
+    assert len(w) == Hq * N
+    for (h, i), (keys, p) in w.items():
+        assert abs(p.sum() - 1.0) <= 1e-12
+        assert (keys <= i).all() or (p[keys > i] == 0).all()
+
+
+# ---------------------------------------------------------------- closed forms: mask
+
+@pytest.mark.parametrize("perm_on", [True, False])
+def test_zero_queries_give_uniform_mass(perm_on):
+    """Q = 0 makes every pooled logit 0: p is uniform, ties go to lower J, so a row keeps blocks
+    0 .. ceil(tau (I+1)) - 1 plus the forced diagonal."""
+    N, Hq, Hkv, d, B, S = 96, 2, 1, 8, 8, 32
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, seed=4)
+    q[:] = 0.0
+    tau = 0.61
+    _, perm, count, idx, prob = _pipeline(q, k, v, B, S, tau, perm_on, diag=True, first=False)
+    NB = oracle.num_blocks(N, B)
+    for I in range(NB):
+        want = sorted(set(range(math.ceil(tau * (I + 1)))) | {I})
+        o = oracle.tri_offset(I)
+        for h in range(Hq):
+            assert idx[h, o:o + count[h, I]].tolist() == want
+            assert np.allclose(prob[h, o:o + I + 1], 1.0 / (I + 1), rtol=1e-15, atol=0)
+
+
+def test_mass_boundary_is_inclusive():
+    """Cumulative mass exactly equal to tau stops the prefix (C_k >= tau): with 4 or 8 equal
+    blocks and tau = 0.5 the sums 0.25+0.25 and 4 * 0.125 are exact."""
+    N, B, S = 64, 8, 64
+    q, k, v = small_inputs(N, 1, 1, 4, seed=2)
+    q[:] = 0.0
+    count, idx, _ = oracle.block_mask(q, k, None, B, S, 0.5, force_diag=False, force_first=False)
+    assert idx[0, oracle.tri_offset(3):oracle.tri_offset(3) + count[0, 3]].tolist() == [0, 1]
+    assert idx[0, oracle.tri_offset(7):oracle.tri_offset(7) + count[0, 7]].tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.5])
+def test_tau_at_least_one_selects_all(tau):
+    q, k, v = small_inputs(100, 2, 1, 8, n_stripes=4, seed=8)
+    _, _, count, idx, _ = _pipeline(q, k, v, 8, 32, tau, diag=False, first=False)
+    NB = oracle.num_blocks(100, 8)
+    for I in range(NB):
+        o = oracle.tri_offset(I)
+        assert idx[:, o:o + I + 1].tolist() == [list(range(I + 1))] * 2
+
+
+def test_one_block_segments_make_permutation_irrelevant_to_mask():
+    """S = B: a permuted block holds the same keys as the natural block, so the mask is the same."""
+    q, k, v = small_inputs(96, 4, 2, 8, n_stripes=4, band=16, seed=6)
+    _, _, c1, i1, p1 = _pipeline(q, k, v, 8, 8, 0.8, perm_on=True)
+    _, _, c2, i2, p2 = _pipeline(q, k, v, 8, 8, 0.8, perm_on=False)
+    assert np.array_equal(c1, c2) and np.array_equal(i1, i2)
+    assert np.abs(np.nan_to_num(p1) - np.nan_to_num(p2)).max() <= 1e-15
+
+
+def test_forced_blocks_are_kept():
+    q, k, v = small_inputs(100, 2, 1, 8, n_stripes=4, seed=12)
+    _, _, count, idx, _ = _pipeline(q, k, v, 8, 32, 0.05, diag=True, first=True)
+    for I in range(oracle.num_blocks(100, 8)):
+        o = oracle.tri_offset(I)
+        for h in range(2):
+            row = idx[h, o:o + count[h, I]].tolist()
+            assert row == sorted(row) and 0 in row and I in row and len(row) <= 3
+
+
+# ---------------------------------------------------------------- closed forms: permutation
+
+def test_zero_keys_give_identity_permutation():
+    q, k, v = small_inputs(96, 2, 1, 8, seed=1)
+    k[:] = 0.0
+    imp = oracle.key_importance(q, k, 8)
+    perm = oracle.segment_permutation(imp, 32)
+    assert np.array_equal(perm, np.tile(np.arange(96), (1, 1)))
+    # uniform causal weights: key j gets (1/R) sum_{i >= max(j, N-B)} 1/(i+1)
+    rows = np.arange(88, 96)
+    want = np.array([sum(1.0 / (i + 1) for i in rows if i >= j) for j in range(96)]) / (2 * len(rows)) * 2
+    assert np.abs(imp[0] - want).max() <= 1e-15
+
+
+def test_queries_outside_last_block_do_not_change_permutation():
+    q, k, v = small_inputs(96, 4, 2, 8, n_stripes=4, band=16, seed=7)
+    imp = oracle.key_importance(q, k, 8)
+    q2 = q.copy()
+    q2[:, :88] = np.random.default_rng(3).standard_normal(q2[:, :88].shape)
+    imp2 = oracle.key_importance(q2, k, 8)
+    assert np.array_equal(imp, imp2)
+    assert np.array_equal(oracle.segment_permutation(imp, 32), oracle.segment_permutation(imp2, 32))
+
+
+def test_permutation_maps_each_segment_onto_itself():
+    q, k, v = small_inputs(100, 4, 2, 8, n_stripes=6, band=16, seed=17)
+    imp = oracle.key_importance(q, k, 8)
+    perm = oracle.segment_permutation(imp, 32)
+    for g in range(2):
+        for a in range(0, 100, 32):
+            seg = perm[g, a:min(a + 32, 100)]
+            assert sorted(seg.tolist()) == list(range(a, min(a + 32, 100)))
+            assert (np.diff(imp[g, seg]) <= 0).all()
+
+
+# ---------------------------------------------------------------- closed forms: attention / early stop
+
+def test_constant_values_give_constant_output():
+    q, k, v = small_inputs(100, 4, 2, 8, n_stripes=4, band=16, seed=10)
+    v[:] = np.array([0.5, -1.25, 3.0, 0.0, 1.0, -2.0, 0.75, 4.0])
+    _, perm, count, idx, _ = _pipeline(q, k, v, 8, 32, 0.5)
+    theta = np.random.default_rng(0).normal(0.0, 1.0, (4, oracle.num_blocks(100, 8)))
+    out, _, _, _ = oracle.block_sparse_attention(q, k, v, perm, count, idx, 8, 32, theta=theta)
+    assert np.abs(out - v[0, 0]).max() <= 1e-12
+
+
+def test_threshold_limits():
+    N, B, S = 100, 8, 32
+    q, k, v = small_inputs(N, 2, 1, 8, n_stripes=4, band=16, seed=14)
+    NB = oracle.num_blocks(N, B)
+    ref, ref_lse = oracle.dense_attention(q, k, v)
+    lo = np.full((2, NB), -np.inf)
+    out, lse, kept, _ = oracle.block_sparse_attention(q, k, v, None, None, None, B, S, theta=lo)
+    assert np.abs(out - ref).max() <= 1e-12
+    hi = np.full((2, NB), np.inf)
+    out, lse, kept, _ = oracle.block_sparse_attention(q, k, v, None, None, None, B, S, theta=hi)
+    assert all(lst == [I] for (h, I), lst in kept.items())
+    blk = np.arange(N) // B
+    diag_only, _ = oracle.dense_attention(q, k, v, allowed=blk[:, None] == blk[None, :])
+    assert np.abs(out - diag_only).max() <= 1e-12
+
+
+def test_calibration_on_same_inputs_keeps_exactly_k():
+    N, B, keep = 160, 8, 6
+    q, k, v = small_inputs(N, 2, 1, 8, n_stripes=4, band=16, seed=15)
+    NB = oracle.num_blocks(N, B)
+    tm = oracle.tile_max(q, k, B)
+    theta = oracle.calibrate_thresholds(tm, NB, keep)
+    _, _, kept, _ = oracle.block_sparse_attention(q, k, v, None, None, None, B, None, theta=theta)
+    for (h, I), lst in kept.items():
+        if I + 1 <= keep:
+            assert lst == list(range(I + 1))
+        else:
+            row = tm[h, oracle.tri_offset(I):oracle.tri_offset(I) + I + 1]
+            top = set(np.argsort(-row)[:keep].tolist())
+            assert set(lst) == top | {I}
+            assert len(lst) == (keep if I in top else keep + 1)
+
+
+def test_tile_max_matches_dense_logits():
+    N, B = 72, 8
+    q, k, v = small_inputs(N, 2, 1, 8, n_stripes=3, seed=16)
+    tm = oracle.tile_max(q, k, B)
+    c = 1.0 / math.sqrt(8)
+    for h in range(2):
+        s = c * q[h] @ k[0].T
+        for I in range(9):
+            for J in range(I + 1):
+                blockvals = [s[i, j] for i in range(I * B, (I + 1) * B) for j in range(J * B, (J + 1) * B) if j <= i]
+                assert abs(tm[h, oracle.tri_offset(I) + J] - max(blockvals)) <= 1e-13 * max(1.0, abs(max(blockvals)))
