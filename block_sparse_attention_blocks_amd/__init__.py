@@ -1,0 +1,191 @@
+"""Permuted block-sparse attention prefill for MI355X (gfx950): thin torch binding of libpbsa.
+
+Each function marshals torch device tensors into the C ABI of ``include/pbsa.h`` and enqueues the
+work on torch's current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; torch only provides device memory and the stream.  Layouts: q [Hq][N][d], k and v
+[Hkv][N][d] bf16 with a contiguous last dimension (any head/token strides that are multiples of
+8 elements); out fp32 [Hq][N][d].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import (PBSA_FORCE_DIAG, PBSA_FORCE_FIRST, PBSA_OP_ATTENTION, PBSA_OP_MASK,  # noqa: F401
+                   PBSA_OP_PERMUTATION, PbsaError, PbsaShape)
+
+__all__ = [
+    "build_segment_permutation",
+    "estimate_block_mask",
+    "block_sparse_attn_prefill",
+    "tile_max",
+    "workspace_size",
+    "make_shape",
+    "num_blocks",
+    "PbsaError",
+]
+
+
+def num_blocks(seq_len: int, block_size: int) -> int:
+    return -(-seq_len // block_size)
+
+
+def _check_bf16(name: str, t: torch.Tensor, heads: Optional[int] = None) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be bf16 [heads][tokens][d] with a contiguous last dimension")
+    if heads is not None and t.shape[0] != heads:
+        raise ValueError(f"{name} has {t.shape[0]} heads, expected {heads}")
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, block_size: int, segment_size: int,
+               scale: Optional[float] = None, out: Optional[torch.Tensor] = None) -> PbsaShape:
+    """pbsa_shape for q [Hq][N][d] and k (and v) [Hkv][N][d] with their strides."""
+    s = PbsaShape()
+    s.seq_len = q.shape[1]
+    s.num_q_heads = q.shape[0]
+    s.num_kv_heads = k.shape[0]
+    s.head_dim = q.shape[2]
+    s.block_size = block_size
+    s.segment_size = segment_size or 0
+    s.softmax_scale = float(scale) if scale else 0.0
+    s.q_stride_head, s.q_stride_token = q.stride(0), q.stride(1)
+    s.kv_stride_head, s.kv_stride_token = k.stride(0), k.stride(1)
+    if out is not None:
+        s.o_stride_head, s.o_stride_token = out.stride(0), out.stride(1)
+    else:
+        s.o_stride_head, s.o_stride_token = q.shape[1] * q.shape[2], q.shape[2]
+    return s
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_size(shape: PbsaShape, op: int) -> int:
+    n = _lib.lib().pbsa_workspace_size(ctypes.byref(shape), op)
+    if n == _lib.SIZE_MAX:
+        raise PbsaError(_lib.PBSA_ERR_INVALID_ARG, "pbsa_workspace_size")
+    return n
+
+
+def _workspace(shape: PbsaShape, op: int, device, ws: Optional[torch.Tensor]) -> Tuple[Optional[torch.Tensor], int]:
+    need = workspace_size(shape, op)
+    if need == 0:
+        return None, 0
+    if ws is None or ws.numel() * ws.element_size() < need:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    # 256-byte alignment of the start (torch allocations are, but views need not be)
+    off = (-ws.data_ptr()) % 256
+    ws = ws[off:]
+    return ws, ws.numel()
+
+
+def build_segment_permutation(q: torch.Tensor, k: torch.Tensor, block_size: int, segment_size: int,
+                              scale: Optional[float] = None, return_importance: bool = False,
+                              perm: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Stage 1: int32 index list perm [Hkv][N] (and fp64 importance [Hkv][N] if asked)."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, segment_size, scale)
+    Hkv, N = k.shape[0], k.shape[1]
+    if perm is None:
+        perm = torch.empty((Hkv, N), dtype=torch.int32, device=q.device)
+    imp = torch.empty((Hkv, N), dtype=torch.float64, device=q.device) if return_importance else None
+    ws, nbytes = _workspace(shape, PBSA_OP_PERMUTATION, q.device, workspace)
+    st = _lib.lib().pbsa_build_segment_permutation(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(perm), _ptr(imp),
+                                                   _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_build_segment_permutation")
+    return (perm, imp) if return_importance else perm
+
+
+def estimate_block_mask(q: torch.Tensor, k: torch.Tensor, perm: Optional[torch.Tensor], block_size: int,
+                        segment_size: int, mass_tau: float, force_diag: bool = True, force_first: bool = True,
+                        scale: Optional[float] = None, return_prob: bool = False,
+                        out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                        workspace: Optional[torch.Tensor] = None):
+    """Stage 2: (block_count int32 [Hq][NB], block_idx int32 [Hq][NB(NB+1)/2][, prob fp64])."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, segment_size, scale)
+    Hq, N = q.shape[0], q.shape[1]
+    NB = num_blocks(N, block_size)
+    if out is None:
+        count = torch.empty((Hq, NB), dtype=torch.int32, device=q.device)
+        idx = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device=q.device)
+    else:
+        count, idx = out
+    prob = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.float64, device=q.device) if return_prob else None
+    flags = (PBSA_FORCE_DIAG if force_diag else 0) | (PBSA_FORCE_FIRST if force_first else 0)
+    ws, nbytes = _workspace(shape, PBSA_OP_MASK, q.device, workspace)
+    st = _lib.lib().pbsa_estimate_block_mask(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(perm), float(mass_tau),
+                                             flags, _ptr(count), _ptr(idx), _ptr(prob), _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_estimate_block_mask")
+    return (count, idx, prob) if return_prob else (count, idx)
+
+
+def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              perm: Optional[torch.Tensor] = None, block_count: Optional[torch.Tensor] = None,
+                              block_idx: Optional[torch.Tensor] = None, block_size: int = 128,
+                              segment_size: int = 0, early_stop_theta: Optional[torch.Tensor] = None,
+                              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                              return_kept: bool = False, return_error: bool = False):
+    """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word)."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    _check_bf16("v", v, heads=k.shape[0])
+    if v.stride() != k.stride():
+        raise ValueError("k and v must share strides")
+    Hq, N, d = q.shape
+    if out is None:
+        out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.stride(2) != 1:
+        raise ValueError("out must be fp32 with a contiguous last dimension")
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    NB = num_blocks(N, block_size)
+    kept = None
+    if return_kept:
+        words = -(-(NB * (NB + 1) // 2) // 32)
+        kept = torch.zeros((Hq, words), dtype=torch.int32, device=q.device)
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if return_error else None
+    shape = make_shape(q, k, block_size, segment_size, scale, out=out)
+    ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, None)
+    st = _lib.lib().pbsa_block_sparse_attn_prefill(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
+        _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_block_sparse_attn_prefill")
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_kept:
+        res.append(kept)
+    if return_error:
+        res.append(err)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def tile_max(q: torch.Tensor, k: torch.Tensor, block_size: int, scale: Optional[float] = None) -> torch.Tensor:
+    """Calibration helper: fp32 [Hq][NB(NB+1)/2] exact per-tile max of the scaled causal logits."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, 0, scale)
+    NB = num_blocks(q.shape[1], block_size)
+    tm = torch.empty((q.shape[0], NB * (NB + 1) // 2), dtype=torch.float32, device=q.device)
+    st = _lib.lib().pbsa_tile_max(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(tm), _stream())
+    _lib.check(st, "pbsa_tile_max")
+    return tm
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,164 @@
+// C ABI of libpbsa: argument validation, workspace sizing and stream-ordered launches.
+// Every check runs before anything is enqueued, so a rejected call leaves all outputs untouched.
+#include "pbsa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "common.h"
+
+using pbsa::Geometry;
+
+namespace {
+
+constexpr int kMaxSegment = 8192;  // segment sort holds one segment in LDS
+constexpr int kMaxBlocks = 2048;   // block selection holds one row of block scores in LDS
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Fill g from the caller's shape.  Returns PBSA_OK or the reason the shape is rejected.
+pbsa_status make_geometry(const pbsa_shape* s, Geometry* g) {
+  if (!s) return PBSA_ERR_INVALID_ARG;
+  if (s->seq_len < 0 || s->num_q_heads <= 0 || s->num_kv_heads <= 0) return PBSA_ERR_INVALID_ARG;
+  if (s->num_q_heads % s->num_kv_heads != 0) return PBSA_ERR_INVALID_ARG;
+  if (s->block_size <= 0 || s->segment_size < 0 || s->head_dim <= 0) return PBSA_ERR_INVALID_ARG;
+  if (s->segment_size % s->block_size != 0) return PBSA_ERR_INVALID_ARG;
+  if (!(s->softmax_scale == s->softmax_scale) || isinf(s->softmax_scale)) return PBSA_ERR_INVALID_ARG;
+  if (s->head_dim != 64 && s->head_dim != 128) return PBSA_ERR_UNSUPPORTED;
+  if (s->block_size != 64 && s->block_size != 128) return PBSA_ERR_UNSUPPORTED;
+  if (s->segment_size > kMaxSegment) return PBSA_ERR_UNSUPPORTED;
+  const int64_t nb = ((int64_t)s->seq_len + s->block_size - 1) / s->block_size;
+  if (nb > kMaxBlocks) return PBSA_ERR_UNSUPPORTED;
+  const int d = s->head_dim;
+  // strides: (0, 0) means contiguous [heads][tokens][d]; otherwise token stride >= d, both
+  // non-negative and multiples of 8 elements (16-byte rows for bf16, 32-byte for fp32 out)
+  auto strides = [&](int64_t sh, int64_t st, int64_t* osh, int64_t* ost) -> bool {
+    if (sh == 0 && st == 0) {
+      *ost = d;
+      *osh = (int64_t)s->seq_len * d;
+      return true;
+    }
+    if (sh < 0 || st < d || (sh % 8) != 0 || (st % 8) != 0) return false;
+    *osh = sh;
+    *ost = st;
+    return true;
+  };
+  if (!strides(s->q_stride_head, s->q_stride_token, &g->qsh, &g->qst)) return PBSA_ERR_INVALID_ARG;
+  if (!strides(s->kv_stride_head, s->kv_stride_token, &g->kvsh, &g->kvst)) return PBSA_ERR_INVALID_ARG;
+  if (!strides(s->o_stride_head, s->o_stride_token, &g->osh, &g->ost)) return PBSA_ERR_INVALID_ARG;
+  // kernels address one head's rows with 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)s->seq_len * g->qst * 2 >= lim || (int64_t)s->seq_len * g->kvst * 2 >= lim) return PBSA_ERR_UNSUPPORTED;
+  g->N = s->seq_len;
+  g->Hq = s->num_q_heads;
+  g->Hkv = s->num_kv_heads;
+  g->G = s->num_q_heads / s->num_kv_heads;
+  g->d = d;
+  g->B = s->block_size;
+  g->S = s->segment_size;
+  g->NB = (int)nb;
+  g->scale64 = s->softmax_scale > 0.f ? (double)s->softmax_scale : 1.0 / sqrt((double)d);
+  g->scale = (float)g->scale64;
+  return PBSA_OK;
+}
+
+pbsa_status check_workspace(size_t need, const void* ws, size_t bytes) {
+  if (need == 0) return PBSA_OK;
+  if (!ws || bytes < need || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return PBSA_ERR_WORKSPACE;
+  return PBSA_OK;
+}
+
+pbsa_status from_hip(hipError_t e) { return e == hipSuccess ? PBSA_OK : PBSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t pbsa_workspace_size(const pbsa_shape* shape, int op) {
+  Geometry g;
+  if (make_geometry(shape, &g) != PBSA_OK) return SIZE_MAX;
+  switch (op) {
+    case PBSA_OP_PERMUTATION: return pbsa::importance_workspace_bytes(g);
+    case PBSA_OP_MASK: return pbsa::mask_workspace_bytes(g);
+    case PBSA_OP_ATTENTION: return 0;
+    default: return SIZE_MAX;
+  }
+}
+
+pbsa_status pbsa_build_segment_permutation(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                           int32_t* perm, double* importance, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (g.S <= 0) return PBSA_ERR_INVALID_ARG;
+  if (!q || !k || !perm || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
+  if (importance && (reinterpret_cast<uintptr_t>(importance) & 7u)) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(pbsa::importance_workspace_bytes(g), workspace, workspace_bytes)) != PBSA_OK)
+    return st;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_build_permutation(g, q, k, perm, importance, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+pbsa_status pbsa_estimate_block_mask(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                     const int32_t* perm, double mass_tau, uint32_t flags, int32_t* block_count,
+                                     int32_t* block_idx, double* block_prob, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (!q || !k || !block_count || !block_idx || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
+  if (perm && g.S <= 0) return PBSA_ERR_INVALID_ARG;
+  if (!(mass_tau > 0.0 && mass_tau <= 1.0)) return PBSA_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(PBSA_FORCE_DIAG | PBSA_FORCE_FIRST)) return PBSA_ERR_INVALID_ARG;
+  if (block_prob && (reinterpret_cast<uintptr_t>(block_prob) & 7u)) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(pbsa::mask_workspace_bytes(g), workspace, workspace_bytes)) != PBSA_OK) return st;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_block_mask(g, q, k, perm, mass_tau, flags, block_count, block_idx, block_prob,
+                                          workspace, static_cast<hipStream_t>(stream)));
+}
+
+pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, const int32_t* perm, const int32_t* block_count,
+                                           const int32_t* block_idx, const float* early_stop_theta, float* out,
+                                           float* lse, uint32_t* kept_bitmap, int32_t* device_error,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (!q || !k || !v || !out) return PBSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PBSA_ERR_INVALID_ARG;
+  if ((block_count == nullptr) != (block_idx == nullptr)) return PBSA_ERR_INVALID_ARG;
+  if (perm && g.S <= 0) return PBSA_ERR_INVALID_ARG;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out, lse,
+                                         kept_bitmap, device_error, static_cast<hipStream_t>(stream)));
+}
+
+pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, float* tile_max,
+                          void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (!q || !k || !tile_max || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_tile_max(g, q, k, tile_max, static_cast<hipStream_t>(stream)));
+}
+
+const char* pbsa_status_string(pbsa_status status) {
+  switch (status) {
+    case PBSA_OK: return "ok";
+    case PBSA_ERR_INVALID_ARG: return "invalid argument";
+    case PBSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case PBSA_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case PBSA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t pbsa_version(void) { return 100; }
+
+}  // extern "C"

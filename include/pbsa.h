@@ -1,0 +1,197 @@
+/*
+ * pbsa.h -- permuted block-sparse attention prefill on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpbsa.so.  Three calls make up one prefill of one attention layer (batch 1):
+ *
+ *   1. pbsa_build_segment_permutation  key importance from the last block of queries, then a
+ *                                      descending sort inside every segment -> index list perm
+ *   2. pbsa_estimate_block_mask        mean-pooled block scores, softmax per query block, and the
+ *                                      shortest set of key blocks reaching a cumulative mass
+ *   3. pbsa_block_sparse_attn_prefill  causal attention over the selected key blocks, keys
+ *                                      gathered through perm, online softmax, optional tile-max
+ *                                      early stop
+ *
+ * plus pbsa_tile_max (calibration of early-stop thresholds) and small helpers.
+ *
+ * Sources of each operation (page title, section):
+ *   - Sparser Block-Sparse Attention via Token Permutation: section 2 (segmented permutation),
+ *     section 3 (proxy scoring from the last query block, sorting inside segments), section 4
+ *     (block selection by mean pooling on the permuted keys), Problem Statement (block-sparse
+ *     attention skips blocks outside a mask).
+ *   - S2O: Early Stopping for Sparse Attention via Online Permutation: section 1 (the
+ *     permutation is an index array that steers which tokens a tile loads; tensors stay in place)
+ *     and section 3 (FlashAttention-style online softmax state m, l, acc).
+ *   - SampleAttention (Technical Deep Dive): sparsity chosen by the attention mass that must be
+ *     kept per query.
+ *   - Block Sparse Flash Attention, Approach: exact QK^T of a tile, V load and PV skipped when the
+ *     tile's max score is below a calibrated per-(head, position) threshold.
+ *
+ * Conventions shared by every call
+ *   - Tensors: q [Hq][N][d], k and v [Hkv][N][d], bf16 (passed as uint16_t bit patterns), with
+ *     element strides given in pbsa_shape (0 = contiguous [heads][tokens][d]); the d dimension must
+ *     be contiguous and token strides multiples of 8 elements, base pointers 16-byte aligned.
+ *     out is fp32 with its own strides; lse is fp32 [Hq][N] contiguous.
+ *   - Query head h reads KV head h / (Hq / Hkv).  Block J = tokens [J*B, min((J+1)*B, N));
+ *     NB = ceil(N / B).  Segment of block J = (J*B) / S.  N need not be a multiple of B or S.
+ *   - Ownership: every pointer is device memory owned by the caller (except pbsa_shape, which is
+ *     host memory read during the call).  The library allocates nothing and keeps no state;
+ *     scratch memory is the caller's workspace, sized by pbsa_workspace_size.
+ *   - Streams: stream is a hipStream_t (NULL = the default stream).  Every call only enqueues
+ *     work on it and returns; outputs are valid once the stream reaches that point.  Inputs,
+ *     outputs and workspace must stay alive until then.  Calls that share a workspace must be
+ *     ordered on one stream.
+ *   - Errors: the status is returned synchronously.  Arguments are validated before anything is
+ *     enqueued, so an error other than PBSA_ERR_HIP leaves every output untouched.  No exception
+ *     crosses the ABI.  Calls are reentrant.
+ *   - Supported: d in {64, 128}; B in {64, 128}; S a positive multiple of B up to 8192 (or 0 for
+ *     "no permutation"); Hq a positive multiple of Hkv; N >= 0 (N = 0 is a no-op); NB <= 2048.
+ */
+#ifndef PBSA_H
+#define PBSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PBSA_OK = 0,
+  PBSA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride, tau, flag combination */
+  PBSA_ERR_UNSUPPORTED = 2,  /* a valid shape this build does not handle (d, B, S, NB limits) */
+  PBSA_ERR_WORKSPACE = 3,    /* workspace null or smaller than pbsa_workspace_size */
+  PBSA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
+} pbsa_status;
+
+typedef struct {
+  int32_t seq_len;        /* N, tokens (>= 0) */
+  int32_t num_q_heads;    /* Hq */
+  int32_t num_kv_heads;   /* Hkv, divides Hq */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t block_size;     /* B: query block = key block, 64 or 128 */
+  int32_t segment_size;   /* S: multiple of B (<= 8192); 0 = no permutation */
+  float softmax_scale;    /* logit scale c; <= 0 selects 1/sqrt(d) */
+  int64_t q_stride_head, q_stride_token;    /* elements; 0,0 = contiguous [Hq][N][d] */
+  int64_t kv_stride_head, kv_stride_token;  /* elements, shared by k and v; 0,0 = contiguous */
+  int64_t o_stride_head, o_stride_token;    /* elements of out; 0,0 = contiguous */
+} pbsa_shape;
+
+/* Workspace selectors for pbsa_workspace_size. */
+enum {
+  PBSA_OP_PERMUTATION = 0,
+  PBSA_OP_MASK = 1,
+  PBSA_OP_ATTENTION = 2
+};
+
+/* Flags of pbsa_estimate_block_mask. */
+enum {
+  PBSA_FORCE_DIAG = 1u,   /* always keep the diagonal block J = I */
+  PBSA_FORCE_FIRST = 2u   /* always keep block J = 0 of the row's (permuted) order */
+};
+
+/*
+ * Bytes of workspace the given call needs for this shape (0 if none; SIZE_MAX if the shape is
+ * invalid).  Monotone non-decreasing in N.  Host-only; never touches the GPU.
+ */
+size_t pbsa_workspace_size(const pbsa_shape* shape, int op);
+
+/*
+ * Stage 1 -- segmented key permutation as an index list.
+ *
+ * Sparser Block-Sparse Attention via Token Permutation, sections 2 and 3.  For KV head g the proxy
+ * rows are the last B query positions [max(0, N-B), N) of each of its Hq/Hkv query heads.  Each row
+ * i takes the causal softmax of c * q_i . k_j over j <= i; importance[g][j] is the mean of these
+ * probabilities over all proxy rows (masked entries count 0), computed in fp64.  Inside every
+ * segment [s*S, min((s+1)*S, N)) the positions are sorted by importance descending, ties by
+ * position ascending: perm[g][s*S + r] = position of the r-th key.  perm is a bijection on each
+ * segment; K and V are never moved.
+ *
+ *   q, k        bf16 inputs (see conventions); v is not needed
+ *   perm        out, int32 [Hkv][N]
+ *   importance  out, fp64 [Hkv][N], or NULL
+ *   workspace   >= pbsa_workspace_size(shape, PBSA_OP_PERMUTATION) bytes, 256-byte aligned
+ * Requires segment_size > 0.
+ */
+pbsa_status pbsa_build_segment_permutation(const pbsa_shape* shape, const uint16_t* q,
+                                           const uint16_t* k, int32_t* perm, double* importance,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 2 -- block mask by mean pooling and cumulative mass.
+ *
+ * Sparser Block-Sparse Attention via Token Permutation, section 4, with the keep rule of
+ * SampleAttention's cumulative attention mass.  In fp64: Qbar[h][I] = mean of the query rows of
+ * block I; for J <= I, Kbar[J] = mean of the keys block J stands for when read by I -- rows
+ * perm[g][J*B ...] when J's segment is strictly before I's segment, natural rows J*B ... otherwise
+ * (perm == NULL: natural rows always).  z_J = c * Qbar . Kbar[J]; p = softmax over J <= I.  Order J
+ * by (p descending, J ascending) and keep the shortest prefix whose running sum is >= mass_tau
+ * (every J <= I if mass_tau >= 1 or the sum stays below it), then add J = I (PBSA_FORCE_DIAG) and
+ * J = 0 (PBSA_FORCE_FIRST).
+ *
+ *   perm         int32 [Hkv][N] from stage 1, or NULL (permutation off)
+ *   mass_tau     in (0, 1]
+ *   block_count  out, int32 [Hq][NB]: number of kept blocks of row (h, I)
+ *   block_idx    out, int32 [Hq][NB(NB+1)/2]: row (h, I) starts at I(I+1)/2 and lists its kept
+ *                J in ascending order; entries past block_count are left unspecified
+ *   block_prob   out, fp64 [Hq][NB(NB+1)/2] (p of row (h, I) at I(I+1)/2 + J), or NULL
+ *   workspace    >= pbsa_workspace_size(shape, PBSA_OP_MASK) bytes, 256-byte aligned
+ * Requires segment_size > 0 when perm is not NULL.
+ */
+pbsa_status pbsa_estimate_block_mask(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                     const int32_t* perm, double mass_tau, uint32_t flags,
+                                     int32_t* block_count, int32_t* block_idx, double* block_prob,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Stage 3 -- causal block-sparse attention prefill.
+ *
+ * Sparser Block-Sparse Attention via Token Permutation, Problem Statement; S2O section 1 (index-
+ * driven gather) and section 3 (online softmax).  For query i of block I of head h:
+ *   K_hi = { j : j in rows(J, I) for a kept J of row (h, I), j <= i }
+ *   out[h][i] = sum_{j in K_hi} softmax_j(c q_i . k_j) v_j,   lse[h][i] = log sum_j exp(c q_i . k_j)
+ * rows(J, I) as in stage 2.  A query with no key gets out = 0 and lse = -inf.  bf16 products are
+ * accumulated in fp32 on the matrix cores; probabilities are rounded to bf16 for the PV product.
+ *
+ *   perm              int32 [Hkv][N] or NULL (natural order)
+ *   block_count/idx   the mask of stage 2, or both NULL for dense causal attention (every J <= I)
+ *   early_stop_theta  fp32 [Hq][NB] or NULL.  Block Sparse Flash Attention, Approach: for a kept
+ *                     J != I the kernel computes the tile's exact scores; if their max over valid
+ *                     (i, j) pairs, c * max q_i . k_j, is below theta[h][I], the V load and the
+ *                     PV product are skipped and the tile leaves (m, l, acc) unchanged.
+ *   out               out, fp32, strides o_stride_*
+ *   lse               out, fp32 [Hq][N] natural-log LSE, or NULL
+ *   kept_bitmap       out, uint32 [Hq][ceil(NB(NB+1)/2 / 32)], or NULL: bit I(I+1)/2 + J set for
+ *                     every tile that was computed through PV; must be zeroed by the caller
+ *   device_error      out, int32, or NULL: set to a non-zero code if an index in perm or the mask
+ *                     is out of range (the offending entries are skipped); caller zeroes it
+ *   workspace         >= pbsa_workspace_size(shape, PBSA_OP_ATTENTION) bytes (may be 0)
+ */
+pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16_t* q,
+                                           const uint16_t* k, const uint16_t* v,
+                                           const int32_t* perm, const int32_t* block_count,
+                                           const int32_t* block_idx,
+                                           const float* early_stop_theta, float* out, float* lse,
+                                           uint32_t* kept_bitmap, int32_t* device_error,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Early-stop calibration helper (Block Sparse Flash Attention, Approach: offline thresholds).
+ * tile_max[h][I(I+1)/2 + J] = c * max over i in block I, j in block J, j <= i of q_i . k_j for
+ * every J <= I, natural order, computed like stage 3's gate (fp32 accumulation).
+ *   tile_max  out, fp32 [Hq][NB(NB+1)/2]
+ */
+pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                          float* tile_max, void* stream);
+
+/* Static description of a status code. */
+const char* pbsa_status_string(pbsa_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pbsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBSA_H */

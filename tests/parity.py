@@ -1,0 +1,106 @@
+"""Comparison helpers for GPU-vs-oracle parity (imported by the gpu tests, smoke and bench).
+
+Tie rules, used wherever a floating-point comparison decides an integer result:
+  * permutation: a rank where GPU and oracle list different keys is a recorded tie iff the two
+    keys' oracle importances differ by at most 1e-6 relative;
+  * block mask: a differing row is a recorded tie iff every differing block has
+    |p_J - p_(k*)| <= 1e-6, or the oracle's running mass C_{k*-1} or C_{k*} is within 1e-6 of tau;
+  * early stop: the GPU gate must equal the decision  fp32 tile max >= theta  taken on the GPU's
+    own fp32 tile maxima (same precision as the kernel); against the fp64 oracle, decisions must
+    agree wherever the oracle's tile max is further than the fp32 error bound from theta.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+TIE = 1e-6
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+
+
+def compare_perm(perm_gpu: np.ndarray, perm_o: np.ndarray, imp_o: np.ndarray, S: int) -> int:
+    """Assert the GPU permutation equals the oracle's up to recorded ties; return the tie count."""
+    Hkv, N = perm_o.shape
+    for g in range(Hkv):
+        for a in range(0, N, S):
+            seg = perm_gpu[g, a:min(a + S, N)]
+            assert sorted(seg.tolist()) == list(range(a, min(a + S, N))), f"perm head {g} segment {a // S} not a bijection"
+    ties = 0
+    for g, p in np.argwhere(perm_gpu != perm_o):
+        x, y = int(perm_gpu[g, p]), int(perm_o[g, p])
+        ix, iy = imp_o[g, x], imp_o[g, y]
+        rel = abs(ix - iy) / max(abs(ix), abs(iy), 1e-300)
+        assert rel <= TIE, f"perm head {g} rank {p}: gpu key {x} ({ix!r}) vs oracle key {y} ({iy!r})"
+        ties += 1
+    return ties
+
+
+def _row(idx, count, h, I):
+    o = oracle.tri_offset(I)
+    return [int(x) for x in idx[h, o:o + int(count[h, I])]]
+
+
+def compare_mask(count_g, idx_g, count_o, idx_o, prob_o, tau: float) -> int:
+    """Assert the GPU mask equals the oracle's up to recorded ties; return the number of tie rows."""
+    Hq, NB = count_o.shape
+    ties = 0
+    for h in range(Hq):
+        for I in range(NB):
+            rg, ro = _row(idx_g, count_g, h, I), _row(idx_o, count_o, h, I)
+            assert rg == sorted(set(rg)) and all(0 <= J <= I for J in rg), f"row ({h},{I}) malformed {rg}"
+            if rg == ro:
+                continue
+            o = oracle.tri_offset(I)
+            p = prob_o[h, o:o + I + 1]
+            order = np.lexsort((np.arange(I + 1), -p))
+            csum = np.cumsum(p[order])
+            hit = np.nonzero(csum >= tau)[0]
+            kstar = int(hit[0]) + 1 if (tau < 1.0 and hit.size) else I + 1
+            pk = p[order[kstar - 1]]
+            diff = set(rg) ^ set(ro)
+            near_p = all(abs(p[J] - pk) <= TIE for J in diff)
+            near_c = abs(csum[kstar - 1] - tau) <= TIE or (kstar >= 2 and abs(csum[kstar - 2] - tau) <= TIE)
+            assert near_p or near_c, f"mask row ({h},{I}): gpu {rg} vs oracle {ro}"
+            ties += 1
+    return ties
+
+
+def compare_out(out_g: np.ndarray, out_o: np.ndarray, what: str = "out"):
+    """Max and mean abs error over the rows the oracle computed (non-NaN)."""
+    ok = ~np.isnan(out_o)
+    err = np.abs(out_g[ok] - out_o[ok])
+    mx, mean = float(err.max()), float(err.mean())
+    assert mx <= O_MAX_ABS and mean <= O_MEAN_ABS, f"{what}: max abs {mx:.3e}, mean abs {mean:.3e}"
+    return mx, mean
+
+
+def compare_lse(lse_g: np.ndarray, lse_o: np.ndarray):
+    ok = ~np.isnan(lse_o)
+    a, b = lse_g[ok], lse_o[ok]
+    inf = np.isinf(b)
+    assert np.array_equal(np.isinf(a), inf), "lse: -inf pattern differs"
+    err = np.abs(a[~inf] - b[~inf])
+    assert err.size == 0 or err.max() <= O_MAX_ABS, f"lse: max abs {err.max():.3e}"
+
+
+def bitmap_to_kept(bm: np.ndarray, NB: int):
+    """{(h, I): [J ...]} from a [Hq][words] kept-tile bitmap."""
+    bm = bm.astype(np.uint32)
+    kept = {}
+    for h in range(bm.shape[0]):
+        for I in range(NB):
+            o = oracle.tri_offset(I)
+            kept[(h, I)] = [J for J in range(I + 1) if (bm[h, (o + J) // 32] >> np.uint32((o + J) % 32)) & 1]
+    return kept
+
+
+def kept_to_mask(kept, Hq: int, NB: int):
+    count = np.zeros((Hq, NB), dtype=np.int64)
+    idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    for (h, I), lst in kept.items():
+        o = oracle.tri_offset(I)
+        count[h, I] = len(lst)
+        idx[h, o:o + len(lst)] = lst
+    return count, idx

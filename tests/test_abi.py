@@ -1,0 +1,161 @@
+"""Host-side checks of the C ABI: exported symbols and argument validation (no GPU work).
+
+Every call here is rejected (or is an N = 0 no-op) before the library touches the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_blocks_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pbsa.h")
+
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pbsa_[a-z_]+)\s*\(", text)))
+
+
+def shape(N=1024, Hq=4, Hkv=2, d=128, B=128, S=512, scale=0.0):
+    s = _lib.PbsaShape()
+    s.seq_len, s.num_q_heads, s.num_kv_heads, s.head_dim = N, Hq, Hkv, d
+    s.block_size, s.segment_size, s.softmax_scale = B, S, scale
+    return s
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"pbsa_build_segment_permutation", "pbsa_estimate_block_mask",
+                          "pbsa_block_sparse_attn_prefill", "pbsa_tile_max", "pbsa_workspace_size",
+                          "pbsa_status_string", "pbsa_version"}
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pbsa_version() >= 100
+
+
+def test_status_strings():
+    for st in range(5):
+        assert _lib.status_string(st)
+    assert _lib.status_string(99) == "unknown status"
+
+
+def test_shape_struct_layout_matches_header():
+    # 6 int32 + float (28 bytes) padded to 32, then 6 int64
+    assert ctypes.sizeof(_lib.PbsaShape) == 32 + 6 * 8
+    assert _lib.PbsaShape.q_stride_head.offset == 32
+
+
+def ws_size(s, op):
+    return _lib.lib().pbsa_workspace_size(ctypes.byref(s), op)
+
+
+def test_workspace_sizes_monotone_in_n():
+    for op in (_lib.PBSA_OP_PERMUTATION, _lib.PBSA_OP_MASK, _lib.PBSA_OP_ATTENTION):
+        prev = 0
+        for N in (0, 1, 127, 128, 129, 1000, 4096, 32768, 131072):
+            n = ws_size(shape(N=N), op)
+            assert n != _lib.SIZE_MAX
+            assert n >= prev
+            prev = n
+    assert ws_size(shape(), 7) == _lib.SIZE_MAX
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=96), _lib.PBSA_ERR_UNSUPPORTED),
+    (dict(B=32), _lib.PBSA_ERR_UNSUPPORTED),
+    (dict(S=16384), _lib.PBSA_ERR_UNSUPPORTED),
+    (dict(N=128 * 2049), _lib.PBSA_ERR_UNSUPPORTED),
+    (dict(S=192), _lib.PBSA_ERR_INVALID_ARG),        # not a multiple of B
+    (dict(Hq=6, Hkv=4), _lib.PBSA_ERR_INVALID_ARG),  # Hq % Hkv
+    (dict(N=-1), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(Hkv=0), _lib.PBSA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.PBSA_ERR_INVALID_ARG),
+])
+def test_shape_validation(kw, expect):
+    s = shape(**kw)
+    l = _lib.lib()
+    assert ws_size(s, 0) == _lib.SIZE_MAX
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == expect
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 3, FAKE, FAKE, None, FAKE,
+                                      1 << 40, None) == expect
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                            None, None, None, None, 0, None) == expect
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == expect
+
+
+def test_null_shape_and_pointers():
+    l = _lib.lib()
+    E = _lib.PBSA_ERR_INVALID_ARG
+    assert l.pbsa_build_segment_permutation(None, FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == E
+    s = shape()
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), None, FAKE, FAKE, None, FAKE, 1 << 40, None) == E
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, 1 << 40, None) == E
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 3, None, FAKE, None, FAKE,
+                                      1 << 40, None) == E
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, None, None, None, None, None, FAKE,
+                                            None, None, None, None, 0, None) == E
+    # count without idx
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE,
+                                            None, None, None, None, 0, None) == E
+    # misaligned tensor
+    bad = ctypes.c_void_p(0x10002)
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), bad, FAKE, FAKE, None, None, None, None, FAKE,
+                                            None, None, None, None, 0, None) == E
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, None) == E
+
+
+def test_permutation_needs_segments_and_mask_needs_valid_tau_and_flags():
+    l = _lib.lib()
+    E = _lib.PBSA_ERR_INVALID_ARG
+    s0 = shape(S=0)
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s0), FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == E
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s0), FAKE, FAKE, FAKE, 0.9, 3, FAKE, FAKE, None, FAKE,
+                                      1 << 40, None) == E
+    s = shape()
+    for tau in (0.0, -0.5, 1.0000001, float("nan")):
+        assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, tau, 3, FAKE, FAKE, None, FAKE,
+                                          1 << 40, None) == E
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 4, FAKE, FAKE, None, FAKE,
+                                      1 << 40, None) == E
+
+
+def test_workspace_checks():
+    l = _lib.lib()
+    W = _lib.PBSA_ERR_WORKSPACE
+    s = shape()
+    need = ws_size(s, _lib.PBSA_OP_PERMUTATION)
+    assert need > 0
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, need, None) == W
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == W
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None,
+                                            ctypes.c_void_p(0x10010), need, None) == W  # not 256-aligned
+    needm = ws_size(s, _lib.PBSA_OP_MASK)
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 3, FAKE, FAKE, None, FAKE,
+                                      needm - 8, None) == W
+
+
+def test_stride_validation():
+    l = _lib.lib()
+    s = shape()
+    s.q_stride_head, s.q_stride_token = 1024 * 128, 100  # token stride < d
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == _lib.PBSA_ERR_INVALID_ARG
+    s.q_stride_token = 132  # not a multiple of 8
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == _lib.PBSA_ERR_INVALID_ARG
+
+
+def test_empty_sequence_is_a_no_op():
+    l = _lib.lib()
+    s = shape(N=0)
+    assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == 0
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 3, FAKE, FAKE, None, FAKE,
+                                      1 << 20, None) == 0
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                            None, None, None, None, 0, None) == 0
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == 0

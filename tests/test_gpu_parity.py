@@ -1,0 +1,259 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle on the same seeded inputs.
+
+Stage-wise: each stage gets the same upstream input on both sides (the GPU's own upstream output,
+checked first), so a recorded tie in one stage cannot cascade.  Tie rules: tests/parity.py.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, kept_to_mask)
+from workloads import bf16_bits_to_f32, generate
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_blocks_amd as pbsa  # noqa: F401 (raises if the library is missing)
+    return pbsa
+
+
+# (name, N, Hq, Hkv, d, B, S, stripes, band, tau, seed)
+CASES = [
+    ("single_head_1k", 1024, 1, 1, 64, 64, 256, 8, 0, 0.9, 1001),
+    ("gqa_ragged_2125", 2125, 4, 2, 128, 128, 512, 16, 256, 0.9, 7),
+    ("b64_d128_ragged_1500", 1500, 2, 1, 128, 64, 256, 8, 128, 0.8, 8),
+    ("b128_d64_ragged_1000", 1000, 4, 1, 64, 128, 256, 8, 128, 0.95, 9),
+    ("shorter_than_a_block_100", 100, 2, 2, 128, 128, 128, 2, 0, 0.9, 10),
+]
+
+
+def _inputs(N, Hq, Hkv, d, stripes, band, seed):
+    x = generate(N, Hq, Hkv, d, stripes, band, seed)
+    dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    host = {n: bf16_bits_to_f32(x[n]).astype(np.float64) for n in ("q", "k", "v")}
+    return dev, host
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pipeline_stagewise(case):
+    pbsa = _need_gpu()
+    name, N, Hq, Hkv, d, B, S, stripes, band, tau, seed = case
+    _log(f"[parity] {name}: N={N} Hq={Hq} Hkv={Hkv} d={d} B={B} S={S}")
+    dev, host = _inputs(N, Hq, Hkv, d, stripes, band, seed)
+    q, k, v = host["q"], host["k"], host["v"]
+    NB = oracle.num_blocks(N, B)
+
+    # stage 1
+    perm_t, imp_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
+    torch.cuda.synchronize()
+    imp_g, perm_g = imp_t.cpu().numpy(), perm_t.cpu().numpy()
+    imp_o = oracle.key_importance(q, k, B)
+    np.testing.assert_allclose(imp_g, imp_o, rtol=1e-12, atol=1e-300)
+    compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
+
+    # stage 2, on the GPU's permutation
+    for use_perm in (True, False):
+        count_t, idx_t, prob_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t if use_perm else None, B, S,
+                                                          tau, return_prob=True)
+        torch.cuda.synchronize()
+        count_o, idx_o, prob_o = oracle.block_mask(q, k, perm_g if use_perm else None, B, S, tau)
+        pg = prob_t.cpu().numpy()
+        for I in range(NB):
+            o = oracle.tri_offset(I)
+            np.testing.assert_allclose(pg[:, o:o + I + 1], prob_o[:, o:o + I + 1], rtol=1e-11, atol=1e-300)
+        compare_mask(count_t.cpu().numpy(), idx_t.cpu().numpy(), count_o, idx_o, prob_o, tau)
+
+    # stage 3, on the GPU's permutation and mask
+    count_t, idx_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, tau)
+    out_t, lse_t, kept_t, err_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t,
+                                                                 B, S, return_kept=True, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err_t.item()) == 0
+    cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+    out_o, lse_o, kept_o, _ = oracle.block_sparse_attention(q, k, v, perm_g, cg, ig, B, S)
+    mx, mean = compare_out(out_t.cpu().numpy(), out_o)
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    assert bitmap_to_kept(kept_t.cpu().numpy(), NB) == kept_o
+    _log(f"[parity] {name}: attention max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_dense_causal_mode(case):
+    pbsa = _need_gpu()
+    name, N, Hq, Hkv, d, B, S, stripes, band, tau, seed = case
+    dev, host = _inputs(N, Hq, Hkv, d, stripes, band, seed + 100)
+    out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.dense_attention(host["q"], host["k"], host["v"])
+    compare_out(out_t.cpu().numpy(), ref, "dense")
+    compare_lse(lse_t.cpu().numpy(), ref_lse)
+
+
+def test_full_mask_with_permutation_equals_dense():
+    """tau = 1 keeps every block; reading past segments through perm must not change the result."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 1536, 4, 2, 128, 128, 512
+    dev, host = _inputs(N, Hq, Hkv, d, 12, 256, 21)
+    perm = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    count, idx = pbsa.estimate_block_mask(dev["q"], dev["k"], perm, B, S, 1.0)
+    out = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count, idx, B, S, return_lse=False)
+    torch.cuda.synchronize()
+    assert (count.cpu().numpy() == np.arange(1, oracle.num_blocks(N, B) + 1)[None, :]).all()
+    ref, _ = oracle.dense_attention(host["q"], host["k"], host["v"])
+    compare_out(out.cpu().numpy(), ref, "full mask")
+
+
+def test_early_stop_gate():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, keep = 2048, 4, 2, 128, 128, 6
+    dev, host = _inputs(N, Hq, Hkv, d, 16, 256, 31)
+    cal, _ = _inputs(N, Hq, Hkv, d, 16, 256, 32)
+    NB = oracle.num_blocks(N, B)
+    q, k, v = host["q"], host["k"], host["v"]
+
+    # tile max of the calibration draw and of the evaluation draw
+    tm_cal = pbsa.tile_max(cal["q"], cal["k"], B).cpu().numpy()
+    tm_o = oracle.tile_max(q, k, B)
+    tm_g = pbsa.tile_max(dev["q"], dev["k"], B).cpu().numpy()
+    assert np.abs(tm_g - tm_o).max() <= 1e-3, np.abs(tm_g - tm_o).max()
+    theta = oracle.calibrate_thresholds(tm_cal.astype(np.float64), NB, keep).astype(np.float32)
+    theta_t = torch.from_numpy(theta).cuda()
+
+    for mode in ("dense", "masked"):
+        if mode == "dense":
+            count_t = idx_t = None
+            cnt_np = idx_np = None
+        else:
+            count_t, idx_t = pbsa.estimate_block_mask(dev["q"], dev["k"], None, B, 512, 0.95)
+            cnt_np, idx_np = count_t.cpu().numpy(), idx_t.cpu().numpy()
+        out_t, lse_t, kept_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], None, count_t, idx_t, B, 512,
+                                                              early_stop_theta=theta_t, return_kept=True)
+        torch.cuda.synchronize()
+        kept_g = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+        # the gate equals the fp32 decision on the kernel's own tile maxima
+        for h in range(Hq):
+            for I in range(NB):
+                o = oracle.tri_offset(I)
+                sel = list(range(I + 1)) if cnt_np is None else [int(x) for x in idx_np[h, o:o + cnt_np[h, I]]]
+                want = [J for J in sel if J == I or np.float32(tm_g[h, o + J]) >= theta[h, I]]
+                assert kept_g[(h, I)] == want, (h, I)
+                # and the fp64 oracle's decision wherever it is clear of the fp32 error band
+                for J in sel:
+                    if J != I and abs(tm_o[h, o + J] - float(theta[h, I])) > 1e-3:
+                        assert (J in kept_g[(h, I)]) == (tm_o[h, o + J] >= float(theta[h, I])), (h, I, J)
+        # outputs equal block-sparse attention on the realised kept set
+        kc, ki = kept_to_mask(kept_g, Hq, NB)
+        out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, kc, ki, B, 512)
+        compare_out(out_t.cpu().numpy(), out_o, f"early stop ({mode})")
+        compare_lse(lse_t.cpu().numpy(), lse_o)
+
+
+def test_threshold_limits():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B = 1000, 2, 1, 128, 128
+    dev, host = _inputs(N, Hq, Hkv, d, 8, 128, 41)
+    NB = oracle.num_blocks(N, B)
+    ref = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B, return_lse=False)
+    lo = torch.full((Hq, NB), -math.inf, device="cuda")
+    out_lo = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B, early_stop_theta=lo,
+                                            return_lse=False)
+    hi = torch.full((Hq, NB), math.inf, device="cuda")
+    out_hi = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B, early_stop_theta=hi,
+                                            return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out_lo, ref)
+    blk = np.arange(N) // B
+    diag_only, _ = oracle.dense_attention(host["q"], host["k"], host["v"], allowed=blk[:, None] == blk[None, :])
+    compare_out(out_hi.cpu().numpy(), diag_only, "theta=+inf")
+
+
+def test_deterministic():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 2048, 4, 2, 128, 128, 512
+    dev, _ = _inputs(N, Hq, Hkv, d, 16, 256, 51)
+    res = []
+    for _ in range(2):
+        perm, imp = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
+        count, idx, prob = pbsa.estimate_block_mask(dev["q"], dev["k"], perm, B, S, 0.9, return_prob=True)
+        out, lse = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count, idx, B, S)
+        torch.cuda.synchronize()
+        # only the first count entries of each idx / prob row are defined
+        valid = torch.zeros_like(idx, dtype=torch.bool)
+        cnt = count.cpu().numpy()
+        for h in range(Hq):
+            for I in range(cnt.shape[1]):
+                o = oracle.tri_offset(I)
+                valid[h, o:o + int(cnt[h, I])] = True
+        pvalid = torch.zeros_like(prob, dtype=torch.bool)
+        for I in range(cnt.shape[1]):
+            pvalid[:, oracle.tri_offset(I):oracle.tri_offset(I) + I + 1] = True
+        res.append([perm.clone(), imp.clone(), count.clone(), idx[valid].clone(), prob[pvalid].clone(),
+                    out.clone(), lse.clone()])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
+
+
+def test_bad_indices_are_flagged_not_read():
+    """Out-of-range mask entries and permutation entries are skipped by the kernel's own bounds
+    checks and reported through the device error word."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 1024, 2, 1, 128, 128, 256
+    dev, host = _inputs(N, Hq, Hkv, d, 8, 0, 61)
+    NB = oracle.num_blocks(N, B)
+    count = torch.full((Hq, NB), 1, dtype=torch.int32, device="cuda")
+    idx = torch.zeros((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device="cuda")
+    for I in range(NB):
+        idx[:, oracle.tri_offset(I)] = I
+    idx[0, oracle.tri_offset(5)] = 7          # J > I
+    count[1, 3] = 2
+    idx[1, oracle.tri_offset(3) + 1] = -4     # negative J
+    out, err = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], None, count, idx, B, S,
+                                              return_lse=False, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1
+    # a permutation entry outside [0, N): rows of segments >= 1 read block 0 through it
+    perm = torch.arange(N, dtype=torch.int32, device="cuda").repeat(Hkv, 1)
+    perm[0, 10] = N + 5
+    count2 = torch.full((Hq, NB), 2, dtype=torch.int32, device="cuda")
+    count2[:, 0] = 1
+    idx2 = torch.zeros((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device="cuda")
+    for I in range(1, NB):
+        idx2[:, oracle.tri_offset(I) + 1] = I
+    out, err = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count2, idx2, B, S,
+                                              return_lse=False, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
+    assert torch.isfinite(out).all()
+
+
+def test_strided_layout_matches_contiguous():
+    """[N][H][d] (token-major) tensors passed through strides give the same result."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 1024, 4, 2, 128, 128, 256
+    dev, _ = _inputs(N, Hq, Hkv, d, 8, 128, 71)
+    qs = dev["q"].transpose(0, 1).contiguous().transpose(0, 1)
+    ks = dev["k"].transpose(0, 1).contiguous().transpose(0, 1)
+    vs = dev["v"].transpose(0, 1).contiguous().transpose(0, 1)
+    assert qs.stride(1) == Hq * d
+    perm = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    perm_s = pbsa.build_segment_permutation(qs, ks, B, S)
+    c, i = pbsa.estimate_block_mask(dev["q"], dev["k"], perm, B, S, 0.9)
+    cs, is_ = pbsa.estimate_block_mask(qs, ks, perm_s, B, S, 0.9)
+    o = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm, c, i, B, S, return_lse=False)
+    os_ = pbsa.block_sparse_attn_prefill(qs, ks, vs, perm_s, cs, is_, B, S, return_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(perm, perm_s) and torch.equal(c, cs)
+    assert torch.equal(o, os_)
