@@ -35,18 +35,9 @@ struct AttnCfg {
   static constexpr int DB = D / 32;                    // 32-row d sub-blocks of O^T
   static constexpr int KLOADS = BLK * KCH / THREADS;   // K chunks per thread
   static constexpr int VBLOCKS = (BLK / 8) * (D / 8);  // 8 x 8 blocks of the V transpose
+  static constexpr int KT = 64;                        // keys per pipelined LDS stage
+  static constexpr int STAGES = BLK / KT;              // stages per key block
 };
-
-// LDS swizzles: XOR the 16-byte chunk index so that MFMA operand reads (32 consecutive rows, one
-// chunk) and tile writes hit distinct banks.
-template <int D>
-__device__ __forceinline__ int k_swz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int BLK>
-__device__ __forceinline__ int v_swz(int d) {
-  return BLK == 128 ? (((d >> 3) + 2 * (d & 7)) & 15) : ((d >> 1) & 7);
-}
 
 struct AttnArgs {
   const uint16_t* q;
@@ -69,70 +60,186 @@ struct AttnArgs {
   float sl2;    // c * log2(e)
 };
 
-enum { MODE_ATTN = 0, MODE_ATTN_GATED = 1, MODE_TILE_MAX = 2 };
+enum { MODE_ATTN = 0, MODE_ATTN_GATED = 1, MODE_TILE_MAX = 2, MODE_DENSE = 3 };
 
-__device__ __forceinline__ uint32_t half16(const u32x4& x, int dd) {
-  return (x[dd >> 1] >> ((dd & 1) * 16)) & 0xffffu;
+// ---------------------------------------------------------------------------------------------
+// Pipelined kernel.  K and V tiles are gathered straight from HBM into LDS by the buffer unit
+// (buffer_load_dwordx4 ... lds: lane i of a wave fills bytes [16 i, 16 i + 16) of a 1 KiB LDS
+// window, from any global address it chooses), so the gather needs no registers and no VALU.
+// Both tiles keep the natural [key][d] layout with a per-row XOR swizzle of the 16-byte chunks,
+// chosen through the per-lane source addresses.  K feeds S^T = K Q^T with 16-byte reads; V feeds
+// O^T = V^T P^T through ds_read_b64_tr_b16, which transposes 16-bit data across each 16-lane
+// group: lane i receives element e = M[4e + i/4][i%4] of the 4-element rows M[j] addressed by
+// lanes j.  Pointing lane j at V[k0 + j/4][d0 + 4 (j%4) ...] hands lane i the four keys
+// k0..k0+3 of column d0 + i.
+// ---------------------------------------------------------------------------------------------
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int D>
+__device__ __forceinline__ int kt_swz(int row) {  // K tile: 16 consecutive rows hit 16 chunks
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vt_swz(int key) {  // V tile: 4 consecutive keys hit disjoint banks
+  return D == 128 ? ((key & 3) << 2) : ((key & 3) << 1);
+}
+
+// One gathered tile: rows row(j) of the head's slab into LDS [BLK][D] with the chunk swizzle.
+template <int D, int BLK, bool IS_V, typename RowFn, int ROWS = AttnCfg<D, BLK>::KT>
+__device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, uint32_t row_bytes, RowFn row) {
+  using C = AttnCfg<D, BLK>;
+  constexpr int RPI = 512 / D;  // rows per 1 KiB wave instruction
+  constexpr int LPR = D / 8;    // lanes per row
+  constexpr int NI = ROWS / (RPI * C::WAVES);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row0 = (wave * NI + i) * RPI;
+    const int rw = row0 + lane / LPR;
+    const int c = (lane % LPR) ^ (IS_V ? vt_swz<D>(rw) : kt_swz<D>(rw));
+    const int rr = row(rw);
+    const uint32_t off = rr >= 0 ? (uint32_t)rr * row_bytes + c * 16 : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + row0 * D), 16, off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Online-softmax state of one lane's query column (S2O section 3: m, l, acc).  m is kept in log2
+// units and only moved when a block of scores exceeds it by more than kLazy: the probabilities
+// are then at most 2^kLazy, well inside fp32 and bf16 range, and most steps skip the rescale.
+constexpr float kLazy = 8.0f;
+
+template <int D, int BLK>
+struct SoftmaxState {
+  f32x16 o[AttnCfg<D, BLK>::DB];
+  float m;  // reference max, log2 units
+  float l;  // sum of the bf16-rounded probabilities relative to m (this lane's half of the keys)
+};
+
+// S^T block kb (32 keys of the LDS tile x this wave's 32 queries) = K[kb] Q^T, with the causal
+// mask on the diagonal tile.  rel = query row - first key of the block - 4*h2, so register r holds
+// key offset 8*(r/4) + r%4 relative to it.
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 block_scores(const uint16_t* Ks, const bf16x8* qf, int kb, bool diag, int rel) {
+  using C = AttnCfg<D, BLK>;
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  const int krow = kb * 32 + l32;
+  const uint16_t* kp = Ks + krow * D;
+  const int ksw = kt_swz<D>(krow);
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + (((kk * 2 + h2) ^ ksw) * 8));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s, 0, 0, 0);
+  }
+  if (diag) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) > rel) s[r] = -INFINITY;
+  }
+  return s;
+}
+
+// Row max of a score block over this lane's query (both half-waves), unscaled.
+__device__ __forceinline__ float block_row_max(const f32x16& s) {
+  float mx = s[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+// Online softmax of one 32-key score block and O^T += V[kb]^T P^T (V rows kb*32.. of the LDS tile).
+template <int D, int BLK>
+__device__ __forceinline__ void block_softmax_pv(SoftmaxState<D, BLK>& st, const f32x16& s, const uint16_t* Vs,
+                                                 int kb, float sl2) {
+  using C = AttnCfg<D, BLK>;
+  const int lane = threadIdx.x & 63;
+  const int h2 = lane >> 5;
+  const float mx = block_row_max(s) * sl2;
+  const bool need = mx > st.m + kLazy;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float m_new = need ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 pb[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_use));
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 pair = {pb[hf][2 * e], pb[hf][2 * e + 1]};
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
+    }
+  // V^T operand: keys kb*32 + 16 hf + 4 h2 + {0..3} then + 8 (the keys this lane's P holds)
+  const int i16 = lane & 15, dsub = (lane >> 4) & 1;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int key0 = kb * 32 + 16 * hf + 4 * h2 + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int dcol = db * 32 + dsub * 16 + 4 * (i16 & 3);
+      const uint16_t* p0 = Vs + key0 * D + (((dcol >> 3) ^ vt_swz<D>(key0)) * 8) + (dcol & 7);
+      const uint16_t* p1 = Vs + (key0 + 8) * D + (((dcol >> 3) ^ vt_swz<D>(key0 + 8)) * 8) + (dcol & 7);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[hf], st.o[db], 0, 0, 0);
+    }
+  }
 }
 
 template <int D, int BLK>
-__device__ __forceinline__ void load_k_tile(uint16_t* Ks, rsrc_t kr, uint32_t row_bytes, const int* rowid) {
+__device__ __forceinline__ void write_output(const AttnArgs& a, const SoftmaxState<D, BLK>& st, int h, int qpos,
+                                             bool qvalid, int h2) {
   using C = AttnCfg<D, BLK>;
-  const int t = threadIdx.x;
-  u32x4 val[C::KLOADS];
+  const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (!qvalid) return;
+  float* orow = a.out + (int64_t)h * a.osh + (int64_t)qpos * a.ost;
 #pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    const int ci = t + i * C::THREADS;
-    const int row = ci / C::KCH, c = ci % C::KCH;
-    const int r = rowid[row];
-    val[i] = buf_load16(kr, r >= 0 ? (uint32_t)r * row_bytes + c * 16 : kOutOfRange);
-  }
+  for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-  for (int i = 0; i < C::KLOADS; ++i) {
-    const int ci = t + i * C::THREADS;
-    const int row = ci / C::KCH, c = ci % C::KCH;
-    *reinterpret_cast<u32x4*>(Ks + row * D + ((c ^ k_swz<D>(row)) * 8)) = val[i];
-  }
+    for (int rq = 0; rq < 4; ++rq) {
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) val[e] = st.o[db][rq * 4 + e] * inv;
+      *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * rq + 4 * h2) = val;
+    }
+  if (a.lse && h2 == 0)
+    a.lse[(size_t)h * a.N + qpos] = l_tot > 0.f ? st.m * 0.69314718055994531f + logf(l_tot) : -INFINITY;
 }
 
-// V tile [BLK keys][D] -> LDS V^T [D][BLK] with the per-16-key position map
-// key k -> (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1), via an 8 x 8 register transpose per thread.
-template <int D, int BLK>
-__device__ __forceinline__ void load_v_tile(uint16_t* Vt, rsrc_t vr, uint32_t row_bytes, const int* rowid) {
-  using C = AttnCfg<D, BLK>;
-  const int t = threadIdx.x;
-  if (C::VBLOCKS < C::THREADS && t >= C::VBLOCKS) return;
-  const int dg = t % (D / 8), kg = t / (D / 8);
-  u32x4 rv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = rowid[kg * 8 + i];
-    rv[i] = buf_load16(vr, r >= 0 ? (uint32_t)r * row_bytes + dg * 16 : kOutOfRange);
-  }
-  const int c0 = (kg >> 1) * 2, sub = (kg & 1) * 4;
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int d = dg * 8 + dd;
-    const int sw = v_swz<BLK>(d);
-    u32x2 lo, hi;
-    lo[0] = half16(rv[0], dd) | (half16(rv[1], dd) << 16);
-    lo[1] = half16(rv[2], dd) | (half16(rv[3], dd) << 16);
-    hi[0] = half16(rv[4], dd) | (half16(rv[5], dd) << 16);
-    hi[1] = half16(rv[6], dd) | (half16(rv[7], dd) << 16);
-    *reinterpret_cast<u32x2*>(Vt + d * BLK + ((c0 ^ sw) * 8) + sub) = lo;
-    *reinterpret_cast<u32x2*>(Vt + d * BLK + (((c0 + 1) ^ sw) * 8) + sub) = hi;
-  }
-}
-
-template <int D, int BLK, int MODE>
+// Software-pipelined block-sparse (DENSE = false) or dense causal (DENSE = true) attention.
+// A key block of BLK keys is processed in stages of KT keys.  While stage s is computed from LDS
+// buffer s % 2, the buffer unit gathers stage s + 1 into the other buffer and the physical row ids
+// of stage s + 2 are fetched from perm.  Two workgroups share a CU (64 KiB LDS, <= 256 registers
+// per lane each), so each SIMD interleaves one wave's softmax with another wave's MFMAs.
+template <int D, int BLK, bool DENSE>
 __global__ __attribute__((amdgpu_flat_work_group_size(AttnCfg<D, BLK>::THREADS, AttnCfg<D, BLK>::THREADS),
-                          amdgpu_waves_per_eu(1)))
-void attn_kernel(AttnArgs a) {
+                          amdgpu_waves_per_eu(2)))
+void attn_pipe_kernel(AttnArgs a) {
   using C = AttnCfg<D, BLK>;
-  __shared__ __align__(16) uint16_t Ks[BLK * D];
-  __shared__ __align__(16) uint16_t Vt[(MODE == MODE_TILE_MAX) ? 8 : D * BLK];
-  __shared__ int rowid[BLK];
-  __shared__ float red[C::WAVES];
+  constexpr int KT = C::KT;
+  __shared__ __align__(16) uint16_t Ks[2][KT * D];
+  __shared__ __align__(16) uint16_t Vs[2][KT * D];
+  __shared__ int rowid[DENSE ? 1 : 3][KT];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
@@ -145,12 +252,21 @@ void attn_kernel(AttnArgs a) {
   const int qpos = I0 + qloc;
   const bool qvalid = qpos < a.N;
   const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
-
   const rsrc_t qr = make_rsrc(a.q + (int64_t)h * a.qsh, a.q_bytes);
   const rsrc_t kr = make_rsrc(a.k + (int64_t)g * a.kvsh, a.kv_bytes);
   const rsrc_t vr = make_rsrc(a.v + (int64_t)g * a.kvsh, a.kv_bytes);
 
-  // Q fragment of this lane: B operand (column = query qloc) for every k-step of S^T = K Q^T.
+  // rows past N are never written by the gather: start from finite (zero) tiles
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(&Ks[0][0]);
+    u32x4* zv = reinterpret_cast<u32x4*>(&Vs[0][0]);
+    constexpr int NZ = 2 * KT * D * 2 / 16;
+    for (int i = t; i < NZ; i += C::THREADS) {
+      z[i] = u32x4{0u, 0u, 0u, 0u};
+      zv[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
   bf16x8 qf[C::KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < C::KSTEPS; ++kk) {
@@ -158,6 +274,155 @@ void attn_kernel(AttnArgs a) {
     qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(qr, off));
   }
 
+  int cnt = I + 1;
+  const int32_t* list = nullptr;
+  if (!DENSE) {
+    cnt = a.count[(size_t)h * a.NB + I];
+    list = a.idx + (size_t)h * ntri + tri_offset(I);
+    if (cnt < 0 || cnt > I + 1) {
+      if (t == 0 && a.err) atomicOr(a.err, 4);
+      cnt = cnt < 0 ? 0 : I + 1;
+    }
+  }
+  const int nst = cnt * C::STAGES;
+  const int sI = a.S > 0 ? I0 / a.S : 0;
+  // key block of stage s (-1 if the list entry is out of range; such stages are skipped)
+  auto block_of = [&](int s) -> int {
+    const int it = s / C::STAGES;
+    if (DENSE) return it;
+    const int J = list[it];
+    return (J >= 0 && J <= I) ? J : -1;
+  };
+  // physical key row of row j of stage s (-1 when past N, J invalid or perm out of range)
+  auto phys_row = [&](int s, int j) -> int {
+    const int J = block_of(s);
+    if (J < 0) return -1;
+    const int p = J * BLK + (s % C::STAGES) * KT + j;
+    if (p >= a.N) return -1;
+    if (!DENSE && a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI) {
+      const int r = a.perm[(size_t)g * a.N + p];
+      if (r < 0 || r >= a.N) {
+        if (a.err) atomicOr(a.err, 2);
+        return -1;
+      }
+      return r;
+    }
+    return p;
+  };
+
+  SoftmaxState<D, BLK> st;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  if (nst > 0) {
+    if (!DENSE && t < KT) {
+      rowid[0][t] = phys_row(0, t);
+      if (nst > 1) rowid[1][t] = phys_row(1, t);
+    }
+    if (!DENSE && t == 0 && a.err)
+      for (int it = 0; it < cnt; ++it)
+        if (block_of(it * C::STAGES) < 0) atomicOr(a.err, 1);
+    __syncthreads();  // zero fill and row ids visible
+    if (DENSE) {
+      auto rf = [&](int j) { return phys_row(0, j); };
+      dma_tile<D, BLK, false>(Ks[0], kr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true>(Vs[0], vr, a.kv_row_bytes, rf);
+    } else {
+      auto rf = [&](int j) { return rowid[0][j]; };
+      dma_tile<D, BLK, false>(Ks[0], kr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true>(Vs[0], vr, a.kv_row_bytes, rf);
+    }
+    wait_dma();
+    __syncthreads();
+  }
+
+  for (int s = 0; s < nst; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nst) {
+      if (DENSE) {
+        auto rf = [&](int j) { return phys_row(s + 1, j); };
+        dma_tile<D, BLK, false>(Ks[cur ^ 1], kr, a.kv_row_bytes, rf);
+        dma_tile<D, BLK, true>(Vs[cur ^ 1], vr, a.kv_row_bytes, rf);
+      } else {
+        const int* ids = rowid[(s + 1) % 3];
+        auto rf = [&](int j) { return ids[j]; };
+        dma_tile<D, BLK, false>(Ks[cur ^ 1], kr, a.kv_row_bytes, rf);
+        dma_tile<D, BLK, true>(Vs[cur ^ 1], vr, a.kv_row_bytes, rf);
+      }
+    }
+    int pr = -1;
+    if (!DENSE && s + 2 < nst && t < KT) pr = phys_row(s + 2, t);
+
+    const int J = block_of(s);
+    if (J >= 0) {
+      const bool diag = (J == I);
+      const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
+      if (a.kept && t == 0 && (s % C::STAGES) == 0) {
+        const size_t bit = tri_offset(I) + J;
+        atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
+      }
+#pragma unroll
+      for (int kb = 0; kb < KT / 32; ++kb) {
+        int rel = qloc - koff - kb * 32 - 4 * h2;
+        asm volatile("" : "+v"(rel));  // keep the causal compares inside the loop
+        const f32x16 sc = block_scores<D, BLK>(Ks[cur], qf, kb, diag, rel);
+        block_softmax_pv<D, BLK>(st, sc, Vs[cur], kb, a.sl2);
+      }
+    }
+    if (!DENSE && s + 2 < nst && t < KT) rowid[(s + 2) % 3][t] = pr;
+    wait_dma();
+    __syncthreads();
+  }
+  write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
+}
+
+// Early-stop kernel (Block Sparse Flash Attention, Approach) and calibration tile maxima.  Per key
+// block: gather K, compute the whole tile's scores, reduce their exact max across the workgroup,
+// and only when the tile is kept gather V and run the same online-softmax / PV steps as the
+// pipelined kernel (so a threshold of -inf reproduces it bit for bit).  MODE_TILE_MAX only writes
+// the scaled tile maxima.
+template <int D, int BLK, int MODE>
+__global__ __attribute__((amdgpu_flat_work_group_size(AttnCfg<D, BLK>::THREADS, AttnCfg<D, BLK>::THREADS),
+                          amdgpu_waves_per_eu(1)))
+void attn_gated_kernel(AttnArgs a) {
+  using C = AttnCfg<D, BLK>;
+  __shared__ __align__(16) uint16_t Ks[BLK * D];
+  __shared__ __align__(16) uint16_t Vs[(MODE == MODE_TILE_MAX) ? 8 : BLK * D];
+  __shared__ int rowid[BLK];
+  __shared__ float red[C::WAVES];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int w = blockIdx.x;
+  const int I = a.NB - 1 - w / a.Hq;
+  const int h = w % a.Hq;
+  const int g = h / a.G;
+  const int I0 = I * BLK;
+  const int qloc = wave * 32 + l32;
+  const int qpos = I0 + qloc;
+  const bool qvalid = qpos < a.N;
+  const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
+  const rsrc_t qr = make_rsrc(a.q + (int64_t)h * a.qsh, a.q_bytes);
+  const rsrc_t kr = make_rsrc(a.k + (int64_t)g * a.kvsh, a.kv_bytes);
+  const rsrc_t vr = make_rsrc(a.v + (int64_t)g * a.kvsh, a.kv_bytes);
+  {
+    u32x4* z = reinterpret_cast<u32x4*>(Ks);
+    for (int i = t; i < BLK * D * 2 / 16; i += C::THREADS) z[i] = u32x4{0u, 0u, 0u, 0u};
+    if (MODE != MODE_TILE_MAX) {
+      u32x4* zv = reinterpret_cast<u32x4*>(Vs);
+      for (int i = t; i < BLK * D * 2 / 16; i += C::THREADS) zv[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  bf16x8 qf[C::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+    const uint32_t off = qvalid ? (uint32_t)qpos * a.q_row_bytes + kk * 32 + h2 * 16 : kOutOfRange;
+    qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(qr, off));
+  }
   int cnt = I + 1;
   const int32_t* list = nullptr;
   if (MODE != MODE_TILE_MAX && a.count != nullptr) {
@@ -169,13 +434,13 @@ void attn_kernel(AttnArgs a) {
     }
   }
   const int sI = a.S > 0 ? I0 / a.S : 0;
-
-  f32x16 o[C::DB];
+  SoftmaxState<D, BLK> st;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
 
   for (int it = 0; it < cnt; ++it) {
     const int J = list ? list[it] : it;
@@ -185,7 +450,7 @@ void attn_kernel(AttnArgs a) {
     }
     const bool diag = (J == I);
     const bool permuted = a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI;
-    __syncthreads();  // every wave is done with the previous tile's LDS
+    __syncthreads();  // previous tile's LDS reads are done
     if (t < BLK) {
       const int p = J * BLK + t;
       int r = -1;
@@ -199,37 +464,20 @@ void attn_kernel(AttnArgs a) {
       rowid[t] = r;
     }
     __syncthreads();
-    load_k_tile<D, BLK>(Ks, kr, a.kv_row_bytes, rowid);
-    if (MODE == MODE_ATTN) load_v_tile<D, BLK>(Vt, vr, a.kv_row_bytes, rowid);
+    auto rf = [&](int j) { return rowid[j]; };
+    dma_tile<D, BLK, false, decltype(rf), BLK>(Ks, kr, a.kv_row_bytes, rf);
+    wait_dma();
     __syncthreads();
-
-    f32x16 s[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < C::KSTEPS; ++kk) {
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const int row = kb * 32 + l32;
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + row * D + (((kk * 2 + h2) ^ k_swz<D>(row)) * 8));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s[kb], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // bound how far LDS operand reads are hoisted
-    }
+    f32x16 sc[C::KB];
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        if (diag && key > qloc) s[kb][r] = -INFINITY;
-        mx = fmaxf(mx, s[kb][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-
-    if (MODE == MODE_TILE_MAX || (MODE == MODE_ATTN_GATED && !diag)) {
+    for (int kb = 0; kb < C::KB; ++kb) {
+      int rel = qloc - kb * 32 - 4 * h2;
+      asm volatile("" : "+v"(rel));
+      sc[kb] = block_scores<D, BLK>(Ks, qf, kb, diag, rel);
+      mx = fmaxf(mx, block_row_max(sc[kb]));
+    }
+    if (MODE == MODE_TILE_MAX || !diag) {
       float tm = wave_max_f32(qvalid ? mx : -INFINITY);
       if (lane == 0) red[wave] = tm;
       __syncthreads();
@@ -242,71 +490,30 @@ void attn_kernel(AttnArgs a) {
       }
       if (tm * a.scale < a.theta[(size_t)h * a.NB + I]) continue;  // gate: no V load, no PV
     }
-    if (MODE == MODE_ATTN_GATED) {
-      load_v_tile<D, BLK>(Vt, vr, a.kv_row_bytes, rowid);
-      __syncthreads();
-    }
     if (MODE != MODE_TILE_MAX) {
+      dma_tile<D, BLK, true, decltype(rf), BLK>(Vs, vr, a.kv_row_bytes, rf);
       if (a.kept && t == 0) {
         const size_t bit = tri_offset(I) + J;
-        const size_t words = (ntri + 31) / 32;
-        atomicOr(&a.kept[(size_t)h * words + bit / 32], 1u << (bit % 32));
+        atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
       }
-      const float m_new = fmaxf(m_run, mx * a.sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      l_run *= alpha;
+      wait_dma();
+      __syncthreads();
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        bf16x8 pb[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], a.sl2, -m_use));
-          l_run += p;
-          pb[r >> 3][r & 7] = (__bf16)p;
-        }
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const int d = db * 32 + l32;
-            const int c = kb * 4 + hf * 2 + h2;
-            const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + d * BLK + ((c ^ v_swz<BLK>(d)) * 8));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[hf], o[db], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      for (int kb = 0; kb < C::KB; ++kb) block_softmax_pv<D, BLK>(st, sc[kb], Vs, kb, a.sl2);
     }
   }
-
-  if (MODE == MODE_TILE_MAX) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qvalid) {
-    float* orow = a.out + (int64_t)h * a.osh + (int64_t)qpos * a.ost;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        f32x4 val;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = o[db][rq * 4 + e] * inv;
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * rq + 4 * h2) = val;
-      }
-    if (a.lse && h2 == 0)
-      a.lse[(size_t)h * a.N + qpos] = l_tot > 0.f ? m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
-  }
+  if (MODE != MODE_TILE_MAX) write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
 }
 
 template <int D, int BLK, int MODE>
 static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st) {
-  attn_kernel<D, BLK, MODE><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
+  if constexpr (MODE == MODE_ATTN) {
+    attn_pipe_kernel<D, BLK, false><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
+  } else if constexpr (MODE == MODE_DENSE) {
+    attn_pipe_kernel<D, BLK, true><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
+  } else {
+    attn_gated_kernel<D, BLK, MODE><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
@@ -356,6 +563,7 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
   a.kept = kept;
   a.err = err;
   if (theta) return dispatch<MODE_ATTN_GATED>(g, a, st);
+  if (count == nullptr) return dispatch<MODE_DENSE>(g, a, st);
   return dispatch<MODE_ATTN>(g, a, st);
 }
 

@@ -174,6 +174,7 @@ def test_threshold_limits():
     out_hi = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B, early_stop_theta=hi,
                                             return_lse=False)
     torch.cuda.synchronize()
+    # the gated kernel runs the same per-block softmax steps: theta = -inf changes nothing
     assert torch.equal(out_lo, ref)
     blk = np.arange(N) // B
     diag_only, _ = oracle.dense_attention(host["q"], host["k"], host["v"], allowed=blk[:, None] == blk[None, :])
