@@ -119,25 +119,30 @@ struct SoftmaxState {
   float l;  // sum of the bf16-rounded probabilities relative to m (this lane's half of the keys)
 };
 
-// S^T block kb (32 keys of the LDS tile x this wave's 32 queries) = K[kb] Q^T, with the causal
-// mask on the diagonal tile.  rel = query row - first key of the block - 4*h2, so register r holds
-// key offset 8*(r/4) + r%4 relative to it.
+// K operands of score block kb: A operand (row = key kb*32 + l32) for every k-step of S^T = K Q^T.
 template <int D, int BLK>
-__device__ __forceinline__ f32x16 block_scores(const uint16_t* Ks, const bf16x8* qf, int kb, bool diag, int rel) {
+__device__ __forceinline__ void load_k_ops(bf16x8* kop, const uint16_t* Ks, int kb) {
   using C = AttnCfg<D, BLK>;
   const int lane = threadIdx.x & 63;
-  const int l32 = lane & 31, h2 = lane >> 5;
-  f32x16 s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
-  const int krow = kb * 32 + l32;
+  const int krow = kb * 32 + (lane & 31), h2 = lane >> 5;
   const uint16_t* kp = Ks + krow * D;
   const int ksw = kt_swz<D>(krow);
 #pragma unroll
-  for (int kk = 0; kk < C::KSTEPS; ++kk) {
-    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + (((kk * 2 + h2) ^ ksw) * 8));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s, 0, 0, 0);
-  }
+  for (int kk = 0; kk < C::KSTEPS; ++kk)
+    kop[kk] = *reinterpret_cast<const bf16x8*>(kp + (((kk * 2 + h2) ^ ksw) * 8));
+}
+
+// S^T block (32 keys x this wave's 32 queries) from preloaded K operands, with the causal mask on
+// the diagonal tile.  rel = query row - first key of the block - 4*h2, so register r holds key
+// offset 8*(r/4) + r%4 relative to it.
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 block_scores_ops(const bf16x8* kop, const bf16x8* qf, bool diag, int rel) {
+  using C = AttnCfg<D, BLK>;
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[kk], s, 0, 0, 0);
   if (diag) {
 #pragma unroll
     for (int r = 0; r < 16; ++r)
@@ -146,21 +151,59 @@ __device__ __forceinline__ f32x16 block_scores(const uint16_t* Ks, const bf16x8*
   return s;
 }
 
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 block_scores(const uint16_t* Ks, const bf16x8* qf, int kb, bool diag, int rel) {
+  bf16x8 kop[AttnCfg<D, BLK>::KSTEPS];
+  load_k_ops<D, BLK>(kop, Ks, kb);
+  return block_scores_ops<D, BLK>(kop, qf, diag, rel);
+}
+
+// V^T operands of block kb through the transposing LDS read: for half hf and d block db, keys
+// kb*32 + 16 hf + 4 h2 + {0..3} then + 8 -- the keys this lane's P operand holds.
+template <int D, int BLK>
+__device__ __forceinline__ void load_v_ops(bf16x8* vop, const uint16_t* Vs, int kb) {
+  using C = AttnCfg<D, BLK>;
+  const int lane = threadIdx.x & 63;
+  const int h2 = lane >> 5, i16 = lane & 15, dsub = (lane >> 4) & 1;
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int key0 = kb * 32 + 16 * hf + 4 * h2 + (i16 >> 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int dcol = db * 32 + dsub * 16 + 4 * (i16 & 3);
+      const uint16_t* p0 = Vs + key0 * D + (((dcol >> 3) ^ vt_swz<D>(key0)) * 8) + (dcol & 7);
+      const uint16_t* p1 = Vs + (key0 + 8) * D + (((dcol >> 3) ^ vt_swz<D>(key0 + 8)) * 8) + (dcol & 7);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      vop[hf * C::DB + db] = __builtin_bit_cast(bf16x8, both);
+    }
+  }
+}
+
+// Values of lanes l and l ^ 32 (the two halves of one query column) side by side.
+__device__ __forceinline__ void half_swap(float x, float* a, float* b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+
 // Row max of a score block over this lane's query (both half-waves), unscaled.
 __device__ __forceinline__ float block_row_max(const f32x16& s) {
   float mx = s[0];
 #pragma unroll
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float a, b;
+  half_swap(mx, &a, &b);
+  return fmaxf(a, b);
 }
 
-// Online softmax of one 32-key score block and O^T += V[kb]^T P^T (V rows kb*32.. of the LDS tile).
+// Online softmax of one 32-key score block and O^T += V^T P^T with preloaded V^T operands.
 template <int D, int BLK>
-__device__ __forceinline__ void block_softmax_pv(SoftmaxState<D, BLK>& st, const f32x16& s, const uint16_t* Vs,
-                                                 int kb, float sl2) {
+__device__ __forceinline__ void block_softmax_pv_ops(SoftmaxState<D, BLK>& st, const f32x16& s, const bf16x8* vop,
+                                                     float sl2) {
   using C = AttnCfg<D, BLK>;
-  const int lane = threadIdx.x & 63;
-  const int h2 = lane >> 5;
   const float mx = block_row_max(s) * sl2;
   const bool need = mx > st.m + kLazy;
   if (__builtin_amdgcn_ballot_w64(need)) {
@@ -186,22 +229,40 @@ __device__ __forceinline__ void block_softmax_pv(SoftmaxState<D, BLK>& st, const
       const bf16x2 pair = {pb[hf][2 * e], pb[hf][2 * e + 1]};
       st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
     }
-  // V^T operand: keys kb*32 + 16 hf + 4 h2 + {0..3} then + 8 (the keys this lane's P holds)
-  const int i16 = lane & 15, dsub = (lane >> 4) & 1;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int key0 = kb * 32 + 16 * hf + 4 * h2 + (i16 >> 2);
+  for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int dcol = db * 32 + dsub * 16 + 4 * (i16 & 3);
-      const uint16_t* p0 = Vs + key0 * D + (((dcol >> 3) ^ vt_swz<D>(key0)) * 8) + (dcol & 7);
-      const uint16_t* p1 = Vs + (key0 + 8) * D + (((dcol >> 3) ^ vt_swz<D>(key0 + 8)) * 8) + (dcol & 7);
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pb[hf], st.o[db], 0, 0, 0);
-    }
+    for (int db = 0; db < C::DB; ++db)
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[hf * C::DB + db], pb[hf], st.o[db], 0, 0, 0);
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ void block_softmax_pv(SoftmaxState<D, BLK>& st, const f32x16& s, const uint16_t* Vs,
+                                                 int kb, float sl2) {
+  bf16x8 vop[2 * AttnCfg<D, BLK>::DB];
+  load_v_ops<D, BLK>(vop, Vs, kb);
+  block_softmax_pv_ops<D, BLK>(st, s, vop, sl2);
+}
+
+// One KT-key stage from LDS: for each 32-key block, the V operands of this block and the K
+// operands of the next are read while the scores and softmax of this block are computed.
+template <int D, int BLK>
+__device__ __forceinline__ void stage_compute(SoftmaxState<D, BLK>& st, const uint16_t* Kc, const uint16_t* Vc,
+                                              const bf16x8* qf, bool diag, int rel0, float sl2) {
+  using C = AttnCfg<D, BLK>;
+  constexpr int NKB = C::KT / 32;
+  bf16x8 kop[C::KSTEPS];
+  load_k_ops<D, BLK>(kop, Kc, 0);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    bf16x8 vop[2 * C::DB];
+    load_v_ops<D, BLK>(vop, Vc, kb);
+    int rel = rel0 - kb * 32;
+    asm volatile("" : "+v"(rel));  // keep the causal compares inside the loop
+    const f32x16 sc = block_scores_ops<D, BLK>(kop, qf, diag, rel);
+    if (kb + 1 < NKB) load_k_ops<D, BLK>(kop, Kc, kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    block_softmax_pv_ops<D, BLK>(st, sc, vop, sl2);
   }
 }
 
@@ -209,7 +270,9 @@ template <int D, int BLK>
 __device__ __forceinline__ void write_output(const AttnArgs& a, const SoftmaxState<D, BLK>& st, int h, int qpos,
                                              bool qvalid, int h2) {
   using C = AttnCfg<D, BLK>;
-  const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
+  float la, lb;
+  half_swap(st.l, &la, &lb);
+  const float l_tot = la + lb;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!qvalid) return;
   float* orow = a.out + (int64_t)h * a.osh + (int64_t)qpos * a.ost;
@@ -226,6 +289,21 @@ __device__ __forceinline__ void write_output(const AttnArgs& a, const SoftmaxSta
     a.lse[(size_t)h * a.N + qpos] = l_tot > 0.f ? st.m * 0.69314718055994531f + logf(l_tot) : -INFINITY;
 }
 
+// Workgroup -> (query block I, query head h).  Rows with more key blocks (larger I) go first.  The
+// dispatcher deals workgroups to the 8 XCDs round-robin (w % 8), and each XCD has its own L2: when
+// Hq is a multiple of 8, XCD x gets the contiguous query heads [x Hq/8, (x+1) Hq/8), so the query
+// heads of a KV group run side by side on one XCD and share the gathered K/V tiles in its L2.
+__device__ __forceinline__ void work_item(const AttnArgs& a, int w, int* I, int* h) {
+  if ((a.Hq & 7) == 0) {
+    const int hp = a.Hq >> 3, r = w >> 3;
+    *I = a.NB - 1 - r / hp;
+    *h = (w & 7) * hp + r % hp;
+  } else {
+    *I = a.NB - 1 - w / a.Hq;
+    *h = w % a.Hq;
+  }
+}
+
 // Software-pipelined block-sparse (DENSE = false) or dense causal (DENSE = true) attention.
 // A key block of BLK keys is processed in stages of KT keys.  While stage s is computed from LDS
 // buffer s % 2, the buffer unit gathers stage s + 1 into the other buffer and the physical row ids
@@ -237,15 +315,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(AttnCfg<D, BLK>::THREADS, 
 void attn_pipe_kernel(AttnArgs a) {
   using C = AttnCfg<D, BLK>;
   constexpr int KT = C::KT;
-  __shared__ __align__(16) uint16_t Ks[2][KT * D];
-  __shared__ __align__(16) uint16_t Vs[2][KT * D];
+  // two stage buffers as distinct LDS objects, so reads of one are not ordered behind the
+  // gather still filling the other
+  __shared__ __align__(16) uint16_t Ks0[KT * D];
+  __shared__ __align__(16) uint16_t Ks1[KT * D];
+  __shared__ __align__(16) uint16_t Vs0[KT * D];
+  __shared__ __align__(16) uint16_t Vs1[KT * D];
   __shared__ int rowid[DENSE ? 1 : 3][KT];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
-  const int w = blockIdx.x;
-  const int I = a.NB - 1 - w / a.Hq;  // longest rows first
-  const int h = w % a.Hq;
+  int I, h;
+  work_item(a, blockIdx.x, &I, &h);
   const int g = h / a.G;
   const int I0 = I * BLK;
   const int qloc = wave * 32 + l32;
@@ -258,12 +339,12 @@ void attn_pipe_kernel(AttnArgs a) {
 
   // rows past N are never written by the gather: start from finite (zero) tiles
   {
-    u32x4* z = reinterpret_cast<u32x4*>(&Ks[0][0]);
-    u32x4* zv = reinterpret_cast<u32x4*>(&Vs[0][0]);
-    constexpr int NZ = 2 * KT * D * 2 / 16;
+    constexpr int NZ = KT * D * 2 / 16;
     for (int i = t; i < NZ; i += C::THREADS) {
-      z[i] = u32x4{0u, 0u, 0u, 0u};
-      zv[i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(Ks0)[i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(Ks1)[i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(Vs0)[i] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(Vs1)[i] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -329,53 +410,49 @@ void attn_pipe_kernel(AttnArgs a) {
     __syncthreads();  // zero fill and row ids visible
     if (DENSE) {
       auto rf = [&](int j) { return phys_row(0, j); };
-      dma_tile<D, BLK, false>(Ks[0], kr, a.kv_row_bytes, rf);
-      dma_tile<D, BLK, true>(Vs[0], vr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, false>(Ks0, kr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true>(Vs0, vr, a.kv_row_bytes, rf);
     } else {
       auto rf = [&](int j) { return rowid[0][j]; };
-      dma_tile<D, BLK, false>(Ks[0], kr, a.kv_row_bytes, rf);
-      dma_tile<D, BLK, true>(Vs[0], vr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, false>(Ks0, kr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true>(Vs0, vr, a.kv_row_bytes, rf);
     }
     wait_dma();
     __syncthreads();
   }
 
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
+  // one pipeline step: gather stage s + 1 into (Kn, Vn) while computing stage s from (Kc, Vc)
+  auto step = [&](int s, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
     if (s + 1 < nst) {
       if (DENSE) {
         auto rf = [&](int j) { return phys_row(s + 1, j); };
-        dma_tile<D, BLK, false>(Ks[cur ^ 1], kr, a.kv_row_bytes, rf);
-        dma_tile<D, BLK, true>(Vs[cur ^ 1], vr, a.kv_row_bytes, rf);
+        dma_tile<D, BLK, false>(Kn, kr, a.kv_row_bytes, rf);
+        dma_tile<D, BLK, true>(Vn, vr, a.kv_row_bytes, rf);
       } else {
         const int* ids = rowid[(s + 1) % 3];
         auto rf = [&](int j) { return ids[j]; };
-        dma_tile<D, BLK, false>(Ks[cur ^ 1], kr, a.kv_row_bytes, rf);
-        dma_tile<D, BLK, true>(Vs[cur ^ 1], vr, a.kv_row_bytes, rf);
+        dma_tile<D, BLK, false>(Kn, kr, a.kv_row_bytes, rf);
+        dma_tile<D, BLK, true>(Vn, vr, a.kv_row_bytes, rf);
       }
     }
     int pr = -1;
     if (!DENSE && s + 2 < nst && t < KT) pr = phys_row(s + 2, t);
-
     const int J = block_of(s);
     if (J >= 0) {
-      const bool diag = (J == I);
       const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
       if (a.kept && t == 0 && (s % C::STAGES) == 0) {
         const size_t bit = tri_offset(I) + J;
         atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
       }
-#pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb) {
-        int rel = qloc - koff - kb * 32 - 4 * h2;
-        asm volatile("" : "+v"(rel));  // keep the causal compares inside the loop
-        const f32x16 sc = block_scores<D, BLK>(Ks[cur], qf, kb, diag, rel);
-        block_softmax_pv<D, BLK>(st, sc, Vs[cur], kb, a.sl2);
-      }
+      stage_compute<D, BLK>(st, Kc, Vc, qf, J == I, qloc - koff - 4 * h2, a.sl2);
     }
     if (!DENSE && s + 2 < nst && t < KT) rowid[(s + 2) % 3][t] = pr;
     wait_dma();
     __syncthreads();
+  };
+  for (int s = 0; s < nst; s += 2) {
+    step(s, Ks0, Vs0, Ks1, Vs1);
+    if (s + 1 < nst) step(s + 1, Ks1, Vs1, Ks0, Vs0);
   }
   write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
 }
@@ -397,9 +474,8 @@ void attn_gated_kernel(AttnArgs a) {
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
-  const int w = blockIdx.x;
-  const int I = a.NB - 1 - w / a.Hq;
-  const int h = w % a.Hq;
+  int I, h;
+  work_item(a, blockIdx.x, &I, &h);
   const int g = h / a.G;
   const int I0 = I * BLK;
   const int qloc = wave * 32 + l32;
