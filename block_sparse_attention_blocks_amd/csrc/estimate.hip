@@ -14,18 +14,27 @@ namespace pbsa {
 // Stage 1a: key importance (Sparser Block-Sparse Attention via Token Permutation, section 3,
 // "Proxy Scoring").  The proxy rows of KV head g are (h, i) with h in g's query-head group and
 // i in [N - R1, N), R1 = min(B, N); there are R = G * R1 of them.  Row r maps to
-// h = g*G + r / R1, i = N - R1 + r % R1.  Three launches:
-//   imp_partial : per (key chunk, g) and row, the chunk's max logit and sum of exp(logit - max)
-//   imp_lse     : per (row, g), combine the chunk partials into the row's log-sum-exp
-//   imp_accum   : per (key chunk, g), sum over rows of exp(logit - lse), divided by R
-// The logits are recomputed in imp_accum rather than stored.
+// h = g*G + r / R1, i = N - R1 + r % R1.  imp_j = (1/R) sum_r exp(s_rj - lse_r), s_rj = c q_r.k_j
+// over causal j <= i.  Three launches:
+//   imp_scores : per (64-key chunk c, g), the fp64 logits of all R rows on the fp64 matrix cores
+//                (v_mfma_f64_16x16x4_f64); per row the chunk max m_cr and l_cr = sum exp(s - m_cr),
+//                and e_rj = exp(s_rj - m_cr) stored to the workspace
+//   imp_lse    : per (row, g), lse_r = M + log sum_c l_cr exp(m_cr - M)
+//   imp_colsum : per key, imp_j = (1/R) sum_r e_rj exp(m_c(j)r - lse_r) in row order
+// so every logit is computed once and exponentiated once.
 // =====================================================================================
 
-constexpr int IMP_CK = 64;       // keys per workgroup
-constexpr int IMP_RT = 64;       // proxy rows per inner tile
-constexpr int IMP_THREADS = 256;  // 16 row groups x 16 key groups, 4 x 4 logits per thread
+constexpr int IMP_CK = 64;        // keys per workgroup (4 MFMA tiles of 16)
+constexpr int IMP_RT = 64;        // proxy rows per inner tile (4 waves x 16 rows)
+constexpr int IMP_THREADS = 256;
+constexpr int IMP_PITCH = 132;    // fp32 LDS row pitch: 16 rows x 4 k hit 64 distinct banks
+constexpr int COL_KEYS = 256;     // keys per workgroup of imp_colsum
+constexpr int COL_ROWS = 256;     // rows staged per pass of imp_colsum
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 struct ImpWs {
+  double* e;       // [Hkv][R][N] chunk-normalised exponentials
   double* part_m;  // [Hkv][nchunk][R]
   double* part_l;  // [Hkv][nchunk][R]
   double* lse;     // [Hkv][R]
@@ -41,6 +50,8 @@ static ImpWs carve_imp_ws(const Geometry& g, void* ws) {
   const size_t R = imp_rows(g), C = imp_chunks(g);
   char* p = static_cast<char*>(ws);
   ImpWs w;
+  w.e = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * R * (size_t)g.N);
   w.part_m = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * C * R);
   w.part_l = reinterpret_cast<double*>(p);
@@ -53,47 +64,8 @@ static ImpWs carve_imp_ws(const Geometry& g, void* ws) {
 
 size_t importance_workspace_bytes(const Geometry& g) {
   const size_t R = imp_rows(g), C = imp_chunks(g);
-  return 2 * align256(sizeof(double) * g.Hkv * C * R) + align256(sizeof(double) * g.Hkv * R) +
-         align256(sizeof(double) * g.Hkv * (size_t)g.N);
-}
-
-// Load a [rows][d] bf16 tile into LDS transposed as fp32 [d][IMP_CK] (zeros for invalid rows).
-// Lane -> row mapping keeps LDS writes conflict-free; each lane reads 16 bytes of its row.
-__device__ __forceinline__ void imp_load_tile_T(float* dst, const uint16_t* base, int64_t row_stride,
-                                                const int* row_pos, int d) {
-  const int t = threadIdx.x;
-  const int row = t & (IMP_CK - 1);
-  const int pos = row_pos[row];
-  for (int dg = t >> 6; dg < d / 8; dg += IMP_THREADS / 64) {
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (pos >= 0) raw = *reinterpret_cast<const u32x4*>(base + (int64_t)pos * row_stride + dg * 8);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dst[(dg * 8 + 2 * e) * IMP_CK + row] = bf16_bits_to_f32(raw[e] & 0xffffu);
-      dst[(dg * 8 + 2 * e + 1) * IMP_CK + row] = bf16_bits_to_f32(raw[e] >> 16);
-    }
-  }
-}
-
-// 4 x 4 fp64 logits of this thread: rows rg*4.., keys kg*4.. of the tile (unscaled dot products).
-__device__ __forceinline__ void imp_tile_dots(const float* qT, const float* kT, int d, double acc[4][4]) {
-  const int t = threadIdx.x;
-  const int rg = t >> 4, kg = t & 15;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int dd = 0; dd < d; ++dd) {
-    const f32x4 qv = *reinterpret_cast<const f32x4*>(qT + dd * IMP_CK + rg * 4);
-    const f32x4 kv = *reinterpret_cast<const f32x4*>(kT + dd * IMP_CK + kg * 4);
-    double qd[4], kd[4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) { qd[a] = (double)qv[a]; kd[a] = (double)kv[a]; }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = fma(qd[a], kd[b], acc[a][b]);
-  }
+  return align256(sizeof(double) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
+         align256(sizeof(double) * g.Hkv * R) + align256(sizeof(double) * g.Hkv * (size_t)g.N);
 }
 
 struct ImpArgs {
@@ -110,81 +82,102 @@ __device__ __forceinline__ void imp_row(const ImpArgs& a, int g, int r, int* h, 
   *i = a.N - a.R1 + r % a.R1;
 }
 
-__global__ __launch_bounds__(IMP_THREADS) void imp_partial_kernel(ImpArgs a, double* part_m, double* part_l) {
-  __shared__ __align__(16) float qT[128 * IMP_CK];
-  __shared__ __align__(16) float kT[128 * IMP_CK];
-  __shared__ int kpos[IMP_CK];
-  __shared__ int qpos[IMP_RT];
-  __shared__ int qpos_i[IMP_RT];
+// One bf16 row (d values, 16-byte chunks) widened to fp32 into LDS; zeros when src is null.
+__device__ __forceinline__ void imp_row_to_lds(float* dst, const uint16_t* src, int cc) {
+  u32x4 raw = {0u, 0u, 0u, 0u};
+  if (src) raw = *reinterpret_cast<const u32x4*>(src + cc * 8);
+  f32x4 lo = {bf16_bits_to_f32(raw[0] & 0xffffu), bf16_bits_to_f32(raw[0] >> 16), bf16_bits_to_f32(raw[1] & 0xffffu),
+              bf16_bits_to_f32(raw[1] >> 16)};
+  f32x4 hi = {bf16_bits_to_f32(raw[2] & 0xffffu), bf16_bits_to_f32(raw[2] >> 16), bf16_bits_to_f32(raw[3] & 0xffffu),
+              bf16_bits_to_f32(raw[3] >> 16)};
+  *reinterpret_cast<f32x4*>(dst + cc * 8) = lo;
+  *reinterpret_cast<f32x4*>(dst + cc * 8 + 4) = hi;
+}
+
+// v_mfma_f64_16x16x4_f64 layouts (lane l): A holds row l%16, k = l/16; B holds column l%16,
+// k = l/16; D holds column l%16, rows l/16 + 4 r in its four doubles r = 0..3.
+__global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, double* E, double* part_m,
+                                                                 double* part_l) {
+  __shared__ __align__(16) float Kt[IMP_CK * IMP_PITCH];
+  __shared__ __align__(16) float Qt[IMP_RT * IMP_PITCH];
+  __shared__ int qi_s[IMP_RT];
   const int chunk = blockIdx.x, g = blockIdx.y, nchunk = gridDim.x;
-  const int t = threadIdx.x, rg = t >> 4, kg = t & 15;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
   const int j0 = chunk * IMP_CK;
-  if (t < IMP_CK) kpos[t] = (j0 + t < a.N) ? j0 + t : -1;
-  __syncthreads();
-  imp_load_tile_T(kT, a.k + (int64_t)g * a.kvsh, a.kvst, kpos, a.d);
+  const int cpr = a.d / 8;  // 16-byte chunks per row
+  for (int c = t; c < IMP_CK * cpr; c += IMP_THREADS) {
+    const int row = c / cpr, j = j0 + row;
+    imp_row_to_lds(Kt + row * IMP_PITCH, j < a.N ? a.k + (int64_t)g * a.kvsh + (int64_t)j * a.kvst : nullptr,
+                   c % cpr);
+  }
+  const int ksteps = a.d / 4;
   for (int r0 = 0; r0 < a.R; r0 += IMP_RT) {
-    __syncthreads();
-    if (t < IMP_RT) {
-      int h, i;
-      const int r = r0 + t;
+    __syncthreads();  // previous Q tile consumed (and K tile written, first time)
+    for (int c = t; c < IMP_RT * cpr; c += IMP_THREADS) {
+      const int row = c / cpr, r = r0 + row;
+      const uint16_t* src = nullptr;
       if (r < a.R) {
+        int h, i;
         imp_row(a, g, r, &h, &i);
-        qpos[t] = i;
-        qpos_i[t] = i;
-      } else {
-        qpos[t] = -1;
-        qpos_i[t] = -1;
+        src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst;
+        if (c % cpr == 0) qi_s[row] = i;
+      } else if (c % cpr == 0) {
+        qi_s[row] = -1;
       }
+      imp_row_to_lds(Qt + row * IMP_PITCH, src, c % cpr);
     }
     __syncthreads();
-    // rows of one tile may span two query heads: load each row from its own head
-    {
-      const int row = t & (IMP_RT - 1);
-      const int r = r0 + row;
-      const int pos = qpos[row];
-      int h = 0, i = 0;
-      if (r < a.R) imp_row(a, g, r, &h, &i);
-      const uint16_t* qrow = a.q + (int64_t)h * a.qsh + (int64_t)pos * a.qst;
-      for (int dg = t >> 6; dg < a.d / 8; dg += IMP_THREADS / 64) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (pos >= 0) raw = *reinterpret_cast<const u32x4*>(qrow + dg * 8);
+    f64x4 acc[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qT[(dg * 8 + 2 * e) * IMP_CK + row] = bf16_bits_to_f32(raw[e] & 0xffffu);
-          qT[(dg * 8 + 2 * e + 1) * IMP_CK + row] = bf16_bits_to_f32(raw[e] >> 16);
-        }
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const float* qa = Qt + (16 * w + l16) * IMP_PITCH + lg;
+    const float* kb = Kt + l16 * IMP_PITCH + lg;
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const double av = (double)qa[ks * 4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const double bv = (double)kb[tt * 16 * IMP_PITCH + ks * 4];
+        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[tt], 0, 0, 0);
       }
     }
-    __syncthreads();
-    double acc[4][4];
-    imp_tile_dots(qT, kT, a.d, acc);
 #pragma unroll
-    for (int ra = 0; ra < 4; ++ra) {
-      const int row = rg * 4 + ra;
-      const int i = qpos_i[row];
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 16 * w + lg + 4 * rr;
+      const int i = qi_s[row];
       double s[4];
       double m = -INFINITY;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int j = kpos[kg * 4 + b];
-        const bool ok = (i >= 0) && (j >= 0) && (j <= i);
-        s[b] = ok ? a.scale * acc[ra][b] : -INFINITY;
-        m = fmax(m, s[b]);
+      for (int tt = 0; tt < 4; ++tt) {
+        const int j = j0 + 16 * tt + l16;
+        const bool ok = (i >= 0) && (j < a.N) && (j <= i);
+        s[tt] = ok ? a.scale * acc[tt][rr] : -INFINITY;
+        m = fmax(m, s[tt]);
       }
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 16));
       double l = 0.0;
-      if (m > -INFINITY) {
+      double e[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) l += (s[b] > -INFINITY) ? exp(s[b] - m) : 0.0;
+      for (int tt = 0; tt < 4; ++tt) {
+        e[tt] = (s[tt] > -INFINITY) ? exp(s[tt] - m) : 0.0;
+        l += e[tt];
       }
 #pragma unroll
       for (int o = 8; o >= 1; o >>= 1) l += __shfl_xor(l, o, 16);
       const int r = r0 + row;
-      if (kg == 0 && r < a.R) {
-        const size_t o = ((size_t)g * nchunk + chunk) * a.R + r;
-        part_m[o] = m;
-        part_l[o] = l;
+      if (r < a.R) {
+        double* er = E + ((size_t)g * a.R + r) * a.N;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int j = j0 + 16 * tt + l16;
+          if (j < a.N) er[j] = e[tt];
+        }
+        if (l16 == 0) {
+          const size_t o = ((size_t)g * nchunk + chunk) * a.R + r;
+          part_m[o] = m;
+          part_l[o] = l;
+        }
       }
     }
   }
@@ -213,75 +206,36 @@ __global__ __launch_bounds__(256) void imp_lse_kernel(const double* part_m, cons
   if (t == 0) lse[(size_t)g * R + r] = m + log((sl[0] + sl[1]) + (sl[2] + sl[3]));
 }
 
-__global__ __launch_bounds__(IMP_THREADS) void imp_accum_kernel(ImpArgs a, const double* lse, double* imp) {
-  __shared__ __align__(16) float qT[128 * IMP_CK];
-  __shared__ __align__(16) float kT[128 * IMP_CK];
-  __shared__ int kpos[IMP_CK];
-  __shared__ int qpos[IMP_RT];
-  __shared__ double rlse[IMP_RT];
-  __shared__ double red[16][IMP_CK];
-  const int chunk = blockIdx.x, g = blockIdx.y;
-  const int t = threadIdx.x, rg = t >> 4, kg = t & 15;
-  const int j0 = chunk * IMP_CK;
-  if (t < IMP_CK) kpos[t] = (j0 + t < a.N) ? j0 + t : -1;
-  __syncthreads();
-  imp_load_tile_T(kT, a.k + (int64_t)g * a.kvsh, a.kvst, kpos, a.d);
-  double colsum[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int r0 = 0; r0 < a.R; r0 += IMP_RT) {
+// imp_j = (1/R) sum_r e_rj * exp(m_c(j)r - lse_r), rows summed in order.
+__global__ __launch_bounds__(COL_KEYS) void imp_colsum_kernel(const double* E, const double* part_m,
+                                                              const double* lse, int N, int R, int nchunk,
+                                                              double* imp) {
+  constexpr int CPB = COL_KEYS / IMP_CK;  // chunks per workgroup
+  __shared__ double wsh[CPB][COL_ROWS];
+  const int g = blockIdx.y, t = threadIdx.x;
+  const int j = blockIdx.x * COL_KEYS + t;
+  const int c0 = blockIdx.x * CPB;
+  double sum = 0.0;
+  for (int rb = 0; rb < R; rb += COL_ROWS) {
     __syncthreads();
-    if (t < IMP_RT) {
-      const int r = r0 + t;
-      if (r < a.R) {
-        int h, i;
-        imp_row(a, g, r, &h, &i);
-        qpos[t] = i;
-        rlse[t] = lse[(size_t)g * a.R + r];
-      } else {
-        qpos[t] = -1;
-        rlse[t] = 0.0;
+    for (int x = t; x < CPB * COL_ROWS; x += COL_KEYS) {
+      const int cl = x / COL_ROWS, rr = x % COL_ROWS, r = rb + rr, c = c0 + cl;
+      double wv = 0.0;
+      if (r < R && c < nchunk) {
+        const double mc = part_m[((size_t)g * nchunk + c) * R + r];
+        if (mc > -INFINITY) wv = exp(mc - lse[(size_t)g * R + r]);
       }
+      wsh[cl][rr] = wv;
     }
     __syncthreads();
-    {
-      const int row = t & (IMP_RT - 1);
-      const int r = r0 + row;
-      const int pos = qpos[row];
-      int h = 0, i = 0;
-      if (r < a.R) imp_row(a, g, r, &h, &i);
-      const uint16_t* qrow = a.q + (int64_t)h * a.qsh + (int64_t)pos * a.qst;
-      for (int dg = t >> 6; dg < a.d / 8; dg += IMP_THREADS / 64) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (pos >= 0) raw = *reinterpret_cast<const u32x4*>(qrow + dg * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qT[(dg * 8 + 2 * e) * IMP_CK + row] = bf16_bits_to_f32(raw[e] & 0xffffu);
-          qT[(dg * 8 + 2 * e + 1) * IMP_CK + row] = bf16_bits_to_f32(raw[e] >> 16);
-        }
-      }
-    }
-    __syncthreads();
-    double acc[4][4];
-    imp_tile_dots(qT, kT, a.d, acc);
-#pragma unroll
-    for (int ra = 0; ra < 4; ++ra) {
-      const int row = rg * 4 + ra;
-      const int i = qpos[row];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int j = kpos[kg * 4 + b];
-        if (i >= 0 && j >= 0 && j <= i) colsum[b] += exp(a.scale * acc[ra][b] - rlse[row]);
-      }
+    if (j < N) {
+      const double* col = E + ((size_t)g * R + rb) * N + j;
+      const int nr = min(COL_ROWS, R - rb);
+      const double* wc = wsh[t / IMP_CK];
+      for (int rr = 0; rr < nr; ++rr) sum = fma(col[(size_t)rr * N], wc[rr], sum);
     }
   }
-#pragma unroll
-  for (int b = 0; b < 4; ++b) red[rg][kg * 4 + b] = colsum[b];
-  __syncthreads();
-  if (t < IMP_CK) {
-    double s = 0.0;
-    for (int x = 0; x < 16; ++x) s += red[x][t];
-    const int j = j0 + t;
-    if (j < a.N) imp[(size_t)g * a.N + j] = s / (double)a.R;
-  }
+  if (j < N) imp[(size_t)g * N + j] = sum / (double)R;
 }
 
 static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, const uint16_t* k, double* out,
@@ -301,9 +255,10 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
   a.kvst = g.kvst;
   a.scale = g.scale64;
   const int nchunk = imp_chunks(g);
-  imp_partial_kernel<<<dim3(nchunk, g.Hkv), IMP_THREADS, 0, st>>>(a, w.part_m, w.part_l);
+  imp_scores_kernel<<<dim3(nchunk, g.Hkv), IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
   imp_lse_kernel<<<dim3(a.R, g.Hkv), 256, 0, st>>>(w.part_m, w.part_l, nchunk, a.R, w.lse);
-  imp_accum_kernel<<<dim3(nchunk, g.Hkv), IMP_THREADS, 0, st>>>(a, w.lse, out);
+  imp_colsum_kernel<<<dim3((g.N + COL_KEYS - 1) / COL_KEYS, g.Hkv), COL_KEYS, 0, st>>>(w.e, w.part_m, w.lse, g.N,
+                                                                                       a.R, nchunk, out);
   return hipGetLastError();
 }
 
