@@ -87,12 +87,13 @@ __device__ __forceinline__ int vt_swz(int key) {  // V tile: 4 consecutive keys 
 }
 
 // One gathered tile: rows row(j) of the head's slab into LDS [BLK][D] with the chunk swizzle.
-template <int D, int BLK, bool IS_V, typename RowFn, int ROWS = AttnCfg<D, BLK>::KT>
+template <int D, int BLK, bool IS_V, typename RowFn, int ROWS = AttnCfg<D, BLK>::KT,
+          int WAVES = AttnCfg<D, BLK>::WAVES>
 __device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, uint32_t row_bytes, RowFn row) {
-  using C = AttnCfg<D, BLK>;
   constexpr int RPI = 512 / D;  // rows per 1 KiB wave instruction
   constexpr int LPR = D / 8;    // lanes per row
-  constexpr int NI = ROWS / (RPI * C::WAVES);
+  constexpr int NI = ROWS / (RPI * WAVES);
+  static_assert(NI * RPI * WAVES == ROWS, "tile rows must split evenly over the waves");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -289,47 +290,83 @@ __device__ __forceinline__ void write_output(const AttnArgs& a, const SoftmaxSta
     a.lse[(size_t)h * a.N + qpos] = l_tot > 0.f ? st.m * 0.69314718055994531f + logf(l_tot) : -INFINITY;
 }
 
-// Workgroup -> (query block I, query head h).  Rows with more key blocks (larger I) go first.  The
-// dispatcher deals workgroups to the 8 XCDs round-robin (w % 8), and each XCD has its own L2: when
-// Hq is a multiple of 8, XCD x gets the contiguous query heads [x Hq/8, (x+1) Hq/8), so the query
-// heads of a KV group run side by side on one XCD and share the gathered K/V tiles in its L2.
-__device__ __forceinline__ void work_item(const AttnArgs& a, int w, int* I, int* h) {
-  if ((a.Hq & 7) == 0) {
-    const int hp = a.Hq >> 3, r = w >> 3;
-    *I = a.NB - 1 - r / hp;
-    *h = (w & 7) * hp + r % hp;
+// Pipelined kernel configuration: HPW query heads of one KV group per workgroup (WAVES_PER_HEAD
+// waves of 32 query rows each), KT-key LDS stages, NBUF stage buffers.
+template <int D, int BLK, int HPW>
+struct PipeCfg {
+  static constexpr int WAVES_PER_HEAD = BLK / 32;
+  static constexpr int WAVES = HPW * WAVES_PER_HEAD;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int KT = AttnCfg<D, BLK>::KT;
+  static constexpr int STAGES = BLK / KT;
+  static constexpr int NBUF = HPW == 1 ? 2 : 3;  // one workgroup per CU has room for three
+  static constexpr int RING = NBUF + 1;          // row-id slots
+  static constexpr int NDMA = 2 * KT / ((512 / D) * WAVES);  // gather instructions per wave per stage
+  static constexpr int MAXNB = 2048;
+};
+
+// Workgroup -> (query block I, first query head h).  Rows with more key blocks (larger I) go first.
+// The dispatcher deals workgroups to the 8 XCDs round-robin (w % 8) and each XCD has its own L2;
+// when the head units divide by 8, XCD x gets a contiguous range of query heads, so the heads of a
+// KV group run side by side on one XCD and reuse the gathered K/V tiles in its L2.
+__device__ __forceinline__ void work_item(int NB, int units, int hpw, int w, int* I, int* h) {
+  int u;
+  if ((units & 7) == 0) {
+    const int up = units >> 3, r = w >> 3;
+    *I = NB - 1 - r / up;
+    u = (w & 7) * up + r % up;
   } else {
-    *I = a.NB - 1 - w / a.Hq;
-    *h = w % a.Hq;
+    *I = NB - 1 - w / units;
+    u = w % units;
   }
+  *h = u * hpw;
 }
 
-// Software-pipelined block-sparse (DENSE = false) or dense causal (DENSE = true) attention.
-// A key block of BLK keys is processed in stages of KT keys.  While stage s is computed from LDS
-// buffer s % 2, the buffer unit gathers stage s + 1 into the other buffer and the physical row ids
-// of stage s + 2 are fetched from perm.  Two workgroups share a CU (64 KiB LDS, <= 256 registers
-// per lane each), so each SIMD interleaves one wave's softmax with another wave's MFMAs.
-template <int D, int BLK, bool DENSE>
-__global__ __attribute__((amdgpu_flat_work_group_size(AttnCfg<D, BLK>::THREADS, AttnCfg<D, BLK>::THREADS),
+__device__ __forceinline__ void work_item(const AttnArgs& a, int w, int* I, int* h) {
+  work_item(a.NB, a.Hq, 1, w, I, h);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Software-pipelined block-sparse (DENSE = false) or dense causal (DENSE = true) attention for
+// HPW query heads h0 .. h0+HPW-1 of one KV group and one query block I.  The workgroup walks the
+// union of the heads' kept key blocks in ascending order; each KT-key stage of a block is gathered
+// once into LDS and used by the waves of every head that kept the block (the query heads of a
+// group usually keep nearly the same blocks).  While stage s is computed, stages s+1 .. s+NBUF-1
+// are in flight, and the physical row ids of stage s+NBUF are fetched from perm.
+template <int D, int BLK, bool DENSE, int HPW>
+__global__ __attribute__((amdgpu_flat_work_group_size(PipeCfg<D, BLK, HPW>::THREADS, PipeCfg<D, BLK, HPW>::THREADS),
                           amdgpu_waves_per_eu(2)))
 void attn_pipe_kernel(AttnArgs a) {
-  using C = AttnCfg<D, BLK>;
+  using C = PipeCfg<D, BLK, HPW>;
   constexpr int KT = C::KT;
-  // two stage buffers as distinct LDS objects, so reads of one are not ordered behind the
-  // gather still filling the other
-  __shared__ __align__(16) uint16_t Ks0[KT * D];
-  __shared__ __align__(16) uint16_t Ks1[KT * D];
-  __shared__ __align__(16) uint16_t Vs0[KT * D];
-  __shared__ __align__(16) uint16_t Vs1[KT * D];
-  __shared__ int rowid[DENSE ? 1 : 3][KT];
+  constexpr int NBUF = C::NBUF;
+  // stage buffers as distinct LDS objects, so reads of one are not ordered behind the gathers still
+  // filling the others
+  __shared__ __align__(16) uint16_t K0[KT * D];
+  __shared__ __align__(16) uint16_t K1[KT * D];
+  __shared__ __align__(16) uint16_t K2[NBUF > 2 ? KT * D : 8];
+  __shared__ __align__(16) uint16_t V0[KT * D];
+  __shared__ __align__(16) uint16_t V1[KT * D];
+  __shared__ __align__(16) uint16_t V2[NBUF > 2 ? KT * D : 8];
+  __shared__ int rowid[DENSE ? 1 : C::RING][KT];
+  __shared__ uint32_t mlist[DENSE ? 1 : C::MAXNB];  // J | kept-by-head bits << 16
+  __shared__ uint8_t selb[DENSE ? 1 : HPW][DENSE ? 1 : C::MAXNB];
+  __shared__ int mcount;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
-  int I, h;
-  work_item(a, blockIdx.x, &I, &h);
-  const int g = h / a.G;
+  const int hh = wave / C::WAVES_PER_HEAD;   // this wave's head within the workgroup
+  const int wq = wave % C::WAVES_PER_HEAD;   // this wave's 32-row slice of the query block
+  int I, h0;
+  work_item(a.NB, a.Hq / HPW, HPW, blockIdx.x, &I, &h0);
+  const int h = h0 + hh;
+  const int g = h0 / a.G;
   const int I0 = I * BLK;
-  const int qloc = wave * 32 + l32;
+  const int qloc = wq * 32 + l32;
   const int qpos = I0 + qloc;
   const bool qvalid = qpos < a.N;
   const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
@@ -341,43 +378,79 @@ void attn_pipe_kernel(AttnArgs a) {
   {
     constexpr int NZ = KT * D * 2 / 16;
     for (int i = t; i < NZ; i += C::THREADS) {
-      reinterpret_cast<u32x4*>(Ks0)[i] = u32x4{0u, 0u, 0u, 0u};
-      reinterpret_cast<u32x4*>(Ks1)[i] = u32x4{0u, 0u, 0u, 0u};
-      reinterpret_cast<u32x4*>(Vs0)[i] = u32x4{0u, 0u, 0u, 0u};
-      reinterpret_cast<u32x4*>(Vs1)[i] = u32x4{0u, 0u, 0u, 0u};
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(K0)[i] = z;
+      reinterpret_cast<u32x4*>(K1)[i] = z;
+      reinterpret_cast<u32x4*>(V0)[i] = z;
+      reinterpret_cast<u32x4*>(V1)[i] = z;
+      if (NBUF > 2) {
+        reinterpret_cast<u32x4*>(K2)[i] = z;
+        reinterpret_cast<u32x4*>(V2)[i] = z;
+      }
     }
   }
 
-  bf16x8 qf[C::KSTEPS];
+  bf16x8 qf[AttnCfg<D, BLK>::KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < C::KSTEPS; ++kk) {
+  for (int kk = 0; kk < AttnCfg<D, BLK>::KSTEPS; ++kk) {
     const uint32_t off = qvalid ? (uint32_t)qpos * a.q_row_bytes + kk * 32 + h2 * 16 : kOutOfRange;
     qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(qr, off));
   }
 
-  int cnt = I + 1;
-  const int32_t* list = nullptr;
+  // merged key-block list: ascending J kept by any of the workgroup's heads
+  int nblk = I + 1;
   if (!DENSE) {
-    cnt = a.count[(size_t)h * a.NB + I];
-    list = a.idx + (size_t)h * ntri + tri_offset(I);
-    if (cnt < 0 || cnt > I + 1) {
-      if (t == 0 && a.err) atomicOr(a.err, 4);
-      cnt = cnt < 0 ? 0 : I + 1;
+    for (int J = t; J <= I; J += C::THREADS)
+#pragma unroll
+      for (int x = 0; x < HPW; ++x) selb[x][J] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < HPW; ++x) {
+      int cnt = a.count[(size_t)(h0 + x) * a.NB + I];
+      if (cnt < 0 || cnt > I + 1) {
+        if (t == 0 && a.err) atomicOr(a.err, 4);
+        cnt = cnt < 0 ? 0 : I + 1;
+      }
+      const int32_t* list = a.idx + (size_t)(h0 + x) * ntri + tri_offset(I);
+      for (int k = t; k < cnt; k += C::THREADS) {
+        const int J = list[k];
+        if (J >= 0 && J <= I) {
+          selb[x][J] = 1;
+        } else if (a.err) {
+          atomicOr(a.err, 1);
+        }
+      }
     }
+    __syncthreads();
+    if (wave == 0) {
+      int base = 0;
+      for (int J0 = 0; J0 <= I; J0 += 64) {
+        const int J = J0 + lane;
+        uint32_t bits = 0;
+        if (J <= I) {
+#pragma unroll
+          for (int x = 0; x < HPW; ++x) bits |= (uint32_t)selb[x][J] << (16 + x);
+        }
+        const unsigned long long bal = __ballot(bits != 0);
+        const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+        if (bits) mlist[pos] = (uint32_t)J | bits;
+        base += __popcll(bal);
+      }
+      if (lane == 0) mcount = base;
+    }
+    __syncthreads();
+    nblk = mcount;
   }
-  const int nst = cnt * C::STAGES;
+  const int nst = nblk * C::STAGES;
   const int sI = a.S > 0 ? I0 / a.S : 0;
-  // key block of stage s (-1 if the list entry is out of range; such stages are skipped)
-  auto block_of = [&](int s) -> int {
-    const int it = s / C::STAGES;
-    if (DENSE) return it;
-    const int J = list[it];
-    return (J >= 0 && J <= I) ? J : -1;
+  const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
+  auto entry_of = [&](int s) -> uint32_t {
+    const int u = s / C::STAGES;
+    return DENSE ? ((uint32_t)u | all_heads) : mlist[u];
   };
-  // physical key row of row j of stage s (-1 when past N, J invalid or perm out of range)
+  // physical key row of row j of stage s (-1 when past N or perm out of range)
   auto phys_row = [&](int s, int j) -> int {
-    const int J = block_of(s);
-    if (J < 0) return -1;
+    const int J = (int)(entry_of(s) & 0xffffu);
     const int p = J * BLK + (s % C::STAGES) * KT + j;
     if (p >= a.N) return -1;
     if (!DENSE && a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI) {
@@ -390,69 +463,73 @@ void attn_pipe_kernel(AttnArgs a) {
     }
     return p;
   };
+  auto gather = [&](int s, uint16_t* Kd, uint16_t* Vd) {
+    if (DENSE) {
+      auto rf = [&](int j) { return phys_row(s, j); };
+      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, a.kv_row_bytes, rf);
+    } else {
+      const int* ids = rowid[s % C::RING];
+      auto rf = [&](int j) { return ids[j]; };
+      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, a.kv_row_bytes, rf);
+    }
+  };
 
   SoftmaxState<D, BLK> st;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+  for (int db = 0; db < AttnCfg<D, BLK>::DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
   st.m = -INFINITY;
   st.l = 0.f;
 
   if (nst > 0) {
-    if (!DENSE && t < KT) {
-      rowid[0][t] = phys_row(0, t);
-      if (nst > 1) rowid[1][t] = phys_row(1, t);
-    }
-    if (!DENSE && t == 0 && a.err)
-      for (int it = 0; it < cnt; ++it)
-        if (block_of(it * C::STAGES) < 0) atomicOr(a.err, 1);
+    if (!DENSE && t < KT)
+      for (int x = 0; x < NBUF && x < nst; ++x) rowid[x][t] = phys_row(x, t);
     __syncthreads();  // zero fill and row ids visible
-    if (DENSE) {
-      auto rf = [&](int j) { return phys_row(0, j); };
-      dma_tile<D, BLK, false>(Ks0, kr, a.kv_row_bytes, rf);
-      dma_tile<D, BLK, true>(Vs0, vr, a.kv_row_bytes, rf);
-    } else {
-      auto rf = [&](int j) { return rowid[0][j]; };
-      dma_tile<D, BLK, false>(Ks0, kr, a.kv_row_bytes, rf);
-      dma_tile<D, BLK, true>(Vs0, vr, a.kv_row_bytes, rf);
-    }
-    wait_dma();
+    gather(0, K0, V0);
+    if (nst > 1 && NBUF > 2) gather(1, K1, V1);
+    wait_vmcnt<0>();
     __syncthreads();
   }
 
-  // one pipeline step: gather stage s + 1 into (Kn, Vn) while computing stage s from (Kc, Vc)
-  auto step = [&](int s, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
-    if (s + 1 < nst) {
-      if (DENSE) {
-        auto rf = [&](int j) { return phys_row(s + 1, j); };
-        dma_tile<D, BLK, false>(Kn, kr, a.kv_row_bytes, rf);
-        dma_tile<D, BLK, true>(Vn, vr, a.kv_row_bytes, rf);
-      } else {
-        const int* ids = rowid[(s + 1) % 3];
-        auto rf = [&](int j) { return ids[j]; };
-        dma_tile<D, BLK, false>(Kn, kr, a.kv_row_bytes, rf);
-        dma_tile<D, BLK, true>(Vn, vr, a.kv_row_bytes, rf);
-      }
-    }
+  // one pipeline step: compute stage s from (Kc, Vc) while stage s + NBUF - 1 is gathered into (Kd, Vd)
+  auto step = [&](int s, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kd, uint16_t* Vd) {
     int pr = -1;
-    if (!DENSE && s + 2 < nst && t < KT) pr = phys_row(s + 2, t);
-    const int J = block_of(s);
-    if (J >= 0) {
+    if (!DENSE && s + NBUF < nst && t < KT) pr = phys_row(s + NBUF, t);
+    const bool issue = s + NBUF - 1 < nst;
+    if (issue) gather(s + NBUF - 1, Kd, Vd);
+    const uint32_t e = entry_of(s);
+    if ((e >> (16 + hh)) & 1u) {
+      const int J = (int)(e & 0xffffu);
       const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
-      if (a.kept && t == 0 && (s % C::STAGES) == 0) {
+      if (a.kept && lane == 0 && wq == 0 && (s % C::STAGES) == 0) {
         const size_t bit = tri_offset(I) + J;
         atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
       }
       stage_compute<D, BLK>(st, Kc, Vc, qf, J == I, qloc - koff - 4 * h2, a.sl2);
     }
-    if (!DENSE && s + 2 < nst && t < KT) rowid[(s + 2) % 3][t] = pr;
-    wait_dma();
+    if (!DENSE && s + NBUF < nst && t < KT) rowid[(s + NBUF) % C::RING][t] = pr;
+    // stage s + 1 must have landed; the newest stage's gathers may stay in flight
+    if (issue && NBUF > 2) {
+      wait_vmcnt<(NBUF - 2) * C::NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __syncthreads();
   };
-  for (int s = 0; s < nst; s += 2) {
-    step(s, Ks0, Vs0, Ks1, Vs1);
-    if (s + 1 < nst) step(s + 1, Ks1, Vs1, Ks0, Vs0);
+  if constexpr (NBUF == 2) {
+    for (int s = 0; s < nst; s += 2) {
+      step(s, K0, V0, K1, V1);
+      if (s + 1 < nst) step(s + 1, K1, V1, K0, V0);
+    }
+  } else {
+    for (int s = 0; s < nst; s += 3) {
+      step(s, K0, V0, K2, V2);
+      if (s + 1 < nst) step(s + 1, K1, V1, K0, V0);
+      if (s + 2 < nst) step(s + 2, K2, V2, K1, V1);
+    }
   }
   write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
 }
@@ -583,10 +660,13 @@ void attn_gated_kernel(AttnArgs a) {
 
 template <int D, int BLK, int MODE>
 static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st) {
-  if constexpr (MODE == MODE_ATTN) {
-    attn_pipe_kernel<D, BLK, false><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
-  } else if constexpr (MODE == MODE_DENSE) {
-    attn_pipe_kernel<D, BLK, true><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
+  if constexpr (MODE == MODE_ATTN || MODE == MODE_DENSE) {
+    constexpr bool DENSE = MODE == MODE_DENSE;
+    if ((a.G & 1) == 0) {
+      attn_pipe_kernel<D, BLK, DENSE, 2><<<nwg / 2, PipeCfg<D, BLK, 2>::THREADS, 0, st>>>(a);
+    } else {
+      attn_pipe_kernel<D, BLK, DENSE, 1><<<nwg, PipeCfg<D, BLK, 1>::THREADS, 0, st>>>(a);
+    }
   } else {
     attn_gated_kernel<D, BLK, MODE><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);
   }
