@@ -89,6 +89,154 @@ def cpu_baseline(w, x, count, budget_s, np):
     }
 
 
+def _events(torch, stream, fn, reps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    xs = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median_ms": xs[len(xs) // 2], "min_ms": xs[0]}
+
+
+def suite(args) -> int:
+    """Secondary measurements, one JSON object per line into --suite-out:
+    128K (as configured and at a bisected ~10% block density), the 64K density sweep with the
+    permutation on and off, and the 64K tile-max early-stop workload with calibrated thresholds."""
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_blocks_amd as pbsa
+    from workloads import WORKLOADS, generate_for
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    out_f = open(args.suite_out, "w")
+
+    def emit(rec):
+        out_f.write(json.dumps(rec) + "\n")
+        out_f.flush()
+        log("[suite] " + json.dumps(rec))
+
+    def load(w, seed=None):
+        x = generate_for(w, seed=seed)
+        return {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+
+    reps = args.suite_reps
+    # ---------------------------------------------------------------- 128K
+    w = WORKLOADS["llama8b_128k"]
+    t0 = time.perf_counter()
+    d = load(w)
+    log(f"[suite] {w.name} inputs in {time.perf_counter() - t0:.1f} s")
+    q, k, v = d["q"], d["k"], d["v"]
+    B, S, NB, Hq = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads
+    causal_tiles = Hq * NB * (NB + 1) // 2
+    shape = pbsa.make_shape(q, k, B, S)
+    ws_p = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_PERMUTATION) + 256, dtype=torch.uint8, device="cuda")
+    ws_m = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_MASK) + 256, dtype=torch.uint8, device="cuda")
+    perm = torch.empty((w.num_kv_heads, w.seq_len), dtype=torch.int32, device="cuda")
+    count = torch.empty((Hq, NB), dtype=torch.int32, device="cuda")
+    idx = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device="cuda")
+    out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Hq, w.seq_len), dtype=torch.float32, device="cuda")
+    fp = lambda: pbsa.build_segment_permutation(q, k, B, S, perm=perm, workspace=ws_p)
+    fp()
+
+    def at_tau(tau, use_perm=True):
+        pbsa.estimate_block_mask(q, k, perm if use_perm else None, B, S, tau, out=(count, idx), workspace=ws_m)
+        torch.cuda.synchronize()
+        return int(count.sum().item()) / causal_tiles
+
+    dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
+    t_dense = _events(torch, stream, dense, max(2, reps // 2))
+    t_perm = _events(torch, stream, fp, reps)
+    for label, tau in (("as_configured", w.mass_tau), ("density_10pct", None)):
+        if tau is None:  # bisect the mass target to a ~10% computed-block fraction
+            lo, hi = 0.0, 1.0
+            for _ in range(18):
+                mid = 0.5 * (lo + hi)
+                if at_tau(mid) < 0.10:
+                    lo = mid
+                else:
+                    hi = mid
+            tau = hi
+        dens = at_tau(tau)
+        fm = lambda: pbsa.estimate_block_mask(q, k, perm, B, S, tau, out=(count, idx), workspace=ws_m)
+        fa = lambda: pbsa.block_sparse_attn_prefill(q, k, v, perm, count, idx, B, S, out=out, lse=lse)
+        t_mask = _events(torch, stream, fm, reps)
+        fm()
+        t_attn = _events(torch, stream, fa, reps)
+        tiles = int(count.sum().item())
+        ta = t_attn["median_ms"]
+        step = t_perm["median_ms"] + t_mask["median_ms"] + ta
+        emit({"workload": w.name, "point": label, "mass_tau": tau, "block_density": dens,
+              "permutation_ms": t_perm["median_ms"], "mask_ms": t_mask["median_ms"], "attention_ms": ta,
+              "step_ms": step, "dense_kernel_ms": t_dense["median_ms"],
+              "attention_speedup_vs_dense": t_dense["median_ms"] / ta,
+              "step_speedup_vs_dense": t_dense["median_ms"] / step,
+              "attention_mfma_tflops": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12,
+              "attention_mfma_frac": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+              "dense_equiv_tflops_step": w.dense_causal_flop / (step * 1e-3) / 1e12})
+    del d, q, k, v, out, lse, ws_p, ws_m, perm, count, idx
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- 64K density sweep
+    w = WORKLOADS["llama8b_64k_sweep"]
+    d = load(w)
+    q, k, v = d["q"], d["k"], d["v"]
+    B, S, NB, Hq = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads
+    causal_tiles = Hq * NB * (NB + 1) // 2
+    perm = pbsa.build_segment_permutation(q, k, B, S)
+    out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
+    dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, return_lse=False)
+    t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+    for tau in w.taus:
+        for use_perm in (True, False):
+            pp = perm if use_perm else None
+            count, idx = pbsa.estimate_block_mask(q, k, pp, B, S, tau)
+            fa = lambda: pbsa.block_sparse_attn_prefill(q, k, v, pp, count, idx, B, S, out=out, return_lse=False)
+            ta = _events(torch, stream, fa, reps)["median_ms"]
+            tiles = int(count.sum().item())
+            emit({"workload": w.name, "mass_tau": tau, "permutation": use_perm, "block_density": tiles / causal_tiles,
+                  "attention_ms": ta, "dense_kernel_ms": t_dense, "attention_speedup_vs_dense": t_dense / ta,
+                  "attention_mfma_frac": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+    del d, q, k, v, out, perm
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- 64K early stop
+    w = WORKLOADS["llama8b_64k_earlystop"]
+    d = load(w)
+    cal = load(w, seed=w.calib_seed)
+    B, NB, Hq = w.block_size, w.num_blocks, w.num_q_heads
+    tmax = pbsa.tile_max(cal["q"], cal["k"], B).cpu().numpy()
+    del cal
+    theta = np.full((Hq, NB), -np.inf, dtype=np.float32)
+    for I in range(NB):
+        if I + 1 > w.calib_keep:
+            row = tmax[:, I * (I + 1) // 2: I * (I + 1) // 2 + I + 1]
+            theta[:, I] = -np.sort(-row, axis=1)[:, w.calib_keep - 1]
+    theta_t = torch.from_numpy(theta).cuda()
+    q, k, v = d["q"], d["k"], d["v"]
+    out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
+    dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, out=out, return_lse=False)
+    gated = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, early_stop_theta=theta_t,
+                                                   out=out, return_lse=False)
+    t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+    t_gate = _events(torch, stream, gated, reps)["median_ms"]
+    _, kept = pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, early_stop_theta=theta_t,
+                                             return_lse=False, return_kept=True)
+    kept_tiles = int(np.unpackbits(kept.cpu().numpy().view(np.uint8)).sum())
+    causal_tiles = Hq * NB * (NB + 1) // 2
+    flop = causal_tiles * 2.0 * B * B * w.head_dim + kept_tiles * 2.0 * B * B * w.head_dim
+    emit({"workload": w.name, "calibration": f"seed {w.calib_seed}, keep top {w.calib_keep} tiles per query block",
+          "kept_tile_fraction": kept_tiles / causal_tiles, "attention_ms": t_gate, "dense_kernel_ms": t_dense,
+          "attention_speedup_vs_dense": t_dense / t_gate,
+          "mfma_frac": flop / (t_gate * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+    out_f.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,12 +245,19 @@ def main() -> int:
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention sampling")
+    ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
+    ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
+    ap.add_argument("--suite-reps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
               "head-parallel sharding across GPUs needs no exchange and is described in the design notes",
               file=sys.stderr)
         return 2
+
+    if args.suite:
+        os.makedirs(os.path.dirname(os.path.abspath(args.suite_out)), exist_ok=True)
+        return suite(args)
 
     import numpy as np
     import torch

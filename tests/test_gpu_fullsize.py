@@ -1,0 +1,154 @@
+"""GPU parity at the benchmarked sizes, on outputs the oracle can compute row by row.
+
+The GPU path runs exactly as bench.py launches it (same workloads, same calls); the oracle then
+checks the whole permutation, every (32K) or sampled (128K) mask row, and a seeded sample of
+attention rows (query head, query block), including the last and first blocks.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, kept_to_mask
+from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_blocks_amd as pbsa
+    return pbsa
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _load(w, seed=None):
+    x = generate_for(w, seed=seed)
+    dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    host = {n: bf16_bits_to_f32(x[n]).astype(np.float64) for n in ("q", "k", "v")}
+    return dev, host
+
+
+def _sample_rows(Hq, NB, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = {(0, NB - 1), (Hq - 1, NB - 1), (Hq // 2, 0), (1, NB // 2)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(Hq)), int(rng.integers(NB))))
+    return sorted(rows)
+
+
+def _rows_slice(out, rows, B, N):
+    """Copy of `out` restricted to the sampled rows (others NaN) for compare_out."""
+    sel = np.full(out.shape, np.nan)
+    for h, I in rows:
+        a, b = I * B, min((I + 1) * B, N)
+        sel[h, a:b] = out[h, a:b]
+    return sel
+
+
+def test_fullsize_32k_pipeline():
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_32k"]
+    _log(f"[fullsize] {w.name}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, S, NB, Hq, N = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads, w.seq_len
+    perm_t, imp_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
+    count_t, idx_t, prob_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, w.mass_tau, w.force_diag,
+                                                      w.force_first, return_prob=True)
+    out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S)
+    torch.cuda.synchronize()
+    imp_o = oracle.key_importance(q, k, B)
+    np.testing.assert_allclose(imp_t.cpu().numpy(), imp_o, rtol=1e-12, atol=1e-300)
+    perm_g = perm_t.cpu().numpy()
+    ties = compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
+    _log(f"[fullsize] permutation ok ({ties} recorded ties)")
+    count_o, idx_o, prob_o = oracle.block_mask(q, k, perm_g, B, S, w.mass_tau, w.force_diag, w.force_first)
+    cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+    ties = compare_mask(cg, ig, count_o, idx_o, prob_o, w.mass_tau)
+    _log(f"[fullsize] mask ok ({ties} tie rows), density {cg.sum() / (Hq * NB * (NB + 1) / 2):.3f}")
+    rows = _sample_rows(Hq, NB, 12, 7)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, perm_g, cg, ig, B, S, rows=rows)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    _log(f"[fullsize] attention rows {rows}: max abs {mx:.2e} mean abs {mean:.2e}")
+    # dense causal mode on sampled rows
+    out_d = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B, return_lse=False)
+    torch.cuda.synchronize()
+    drows = _sample_rows(Hq, NB, 6, 8)
+    ref, _, _, _ = oracle.block_sparse_attention(q, k, v, None, None, None, B, S, rows=drows)
+    compare_out(_rows_slice(out_d.cpu().numpy(), drows, B, N), ref, "dense 32K")
+
+
+def test_fullsize_128k_sampled():
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_128k"]
+    _log(f"[fullsize] {w.name}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, S, NB, Hq, N = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads, w.seq_len
+    perm_t, imp_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
+    count_t, idx_t, prob_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, w.mass_tau, return_prob=True)
+    out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S)
+    torch.cuda.synchronize()
+    imp_o = oracle.key_importance(q, k, B)
+    np.testing.assert_allclose(imp_t.cpu().numpy(), imp_o, rtol=1e-12, atol=1e-300)
+    perm_g = perm_t.cpu().numpy()
+    compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
+    _log("[fullsize] 128K permutation ok")
+    # mask rows of two query heads, in full
+    cg, ig, pg = count_t.cpu().numpy(), idx_t.cpu().numpy(), prob_t.cpu().numpy()
+    for h in (0, Hq - 1):
+        sub = slice(h, h + 1)
+        g = h // (Hq // w.num_kv_heads)
+        co, io, po = oracle.block_mask(q[sub], k[g:g + 1], perm_g[g:g + 1], B, S, w.mass_tau)
+        compare_mask(cg[sub], ig[sub], co, io, po, w.mass_tau)
+    _log("[fullsize] 128K mask rows of heads 0 and last ok")
+    rows = _sample_rows(Hq, NB, 8, 9)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, perm_g, cg, ig, B, S, rows=rows)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    _log(f"[fullsize] 128K attention rows {rows}: max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+def test_fullsize_64k_early_stop_sampled():
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_64k_earlystop"]
+    _log(f"[fullsize] {w.name}")
+    dev, host = _load(w)
+    cal, _ = _load(w, seed=w.calib_seed)
+    B, NB, Hq, N = w.block_size, w.num_blocks, w.num_q_heads, w.seq_len
+    tm_cal = pbsa.tile_max(cal["q"], cal["k"], B).cpu().numpy()
+    del cal
+    theta = oracle.calibrate_thresholds(tm_cal.astype(np.float64), NB, w.calib_keep).astype(np.float32)
+    theta_t = torch.from_numpy(theta).cuda()
+    out_t, lse_t, kept_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B,
+                                                          early_stop_theta=theta_t, return_kept=True)
+    tm_g = pbsa.tile_max(dev["q"], dev["k"], B).cpu().numpy()
+    torch.cuda.synchronize()
+    kept = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+    # the gate equals the fp32 decision on the kernel's own tile maxima, for every row
+    for (h, I), lst in kept.items():
+        o = oracle.tri_offset(I)
+        want = [J for J in range(I + 1) if J == I or tm_g[h, o + J] >= theta[h, I]]
+        assert lst == want, (h, I)
+    # sampled rows: fp64 tile maxima, and outputs on the realised kept set
+    q, k, v = host["q"], host["k"], host["v"]
+    rows = _sample_rows(Hq, NB, 6, 10)
+    tm_o = oracle.tile_max(q, k, B, rows=rows)
+    for h, I in rows:
+        o = oracle.tri_offset(I)
+        assert np.abs(tm_o[h, o:o + I + 1] - tm_g[h, o:o + I + 1]).max() <= 1e-3
+    kc, ki = kept_to_mask(kept, Hq, NB)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, kc, ki, B, None, rows=rows)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
+    frac = sum(len(v) for v in kept.values()) / (Hq * NB * (NB + 1) / 2)
+    _log(f"[fullsize] 64K early stop: kept fraction {frac:.3f}, rows {rows}: max abs {mx:.2e} mean {mean:.2e}")
