@@ -28,6 +28,67 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+COPY_CALIB_BYTES = 1 << 30  # plain device copy of known size used to scale the byte counters
+KERNEL_SOURCES = ("block_sparse_attention_blocks_amd/csrc/attention.hip", "block_sparse_attention_blocks_amd/csrc/common.h")
+TRAFFIC_SUMMARY = "profiles/attn_pipe_kernel_llama8b_32k_traffic.txt"
+ATTN_KERNEL = "attn_pipe_kernel<128, 128, false, 2>"
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the attention kernel from the committed counter summary, or None
+    when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            kk, vv = line.split("=", 1)
+            vals[kk.strip()] = vv.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, out: str, command: str) -> int:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the attention kernel, scaled by what the same
+    counters read for the plain copy of COPY_CALIB_BYTES in the same run."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        attn = [float(r["Counter_Value"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) > COPY_CALIB_BYTES / 1024 / 4]
+        return statistics.median(attn), statistics.median(copy), len(attn)
+
+    fa, fc, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    wa, wc, n_w = per_kernel(write_csv, "WRITE_SIZE")
+    sf = (COPY_CALIB_BYTES / 1024) / fc   # true KiB per counted KiB, reads
+    sw = (COPY_CALIB_BYTES / 1024) / wc   # same for writes
+    traffic = (fa * sf + wa * sw) * 1024
+    with open(out, "w") as f:
+        f.write(f"# {ATTN_KERNEL}, llama8b_32k workload: HBM traffic per launch from rocprofv3 byte counters\n")
+        f.write(f"# command: {command}\n")
+        f.write(f"# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (median of {n_f} / {n_w} dispatches); each is scaled\n")
+        f.write(f"# by the ratio true/counted bytes of a plain {COPY_CALIB_BYTES} B device copy in the same run.\n")
+        f.write(f"attn_fetch_kib = {fa:.1f}\nattn_write_kib = {wa:.1f}\n")
+        f.write(f"copy_fetch_kib = {fc:.1f}\ncopy_write_kib = {wc:.1f}\n")
+        f.write(f"fetch_scale = {sf:.4f}\nwrite_scale = {sw:.4f}\n")
+        f.write(f"traffic_bytes_per_launch = {traffic:.6g}\n")
+        f.write(f"kernel_source_sha256_16 = {kernel_source_hash()}\n")
+    print(open(out).read())
+    return 0
 
 
 def log(msg: str) -> None:
@@ -245,6 +306,12 @@ def main() -> int:
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention sampling")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after timing, copy %d bytes on the device (byte-counter calibration)" % COPY_CALIB_BYTES)
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--summary-out", default=TRAFFIC_SUMMARY)
+    ap.add_argument("--summary-command", default="")
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
     ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
@@ -255,6 +322,8 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_out, args.summary_command)
     if args.suite:
         os.makedirs(os.path.dirname(os.path.abspath(args.suite_out)), exist_ok=True)
         return suite(args)
@@ -365,7 +434,7 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "attn_kernel<128,128,0>", "kernel_ms": t_attn * 1e3,
+                     "kernel": ATTN_KERNEL, "kernel_ms": t_attn * 1e3,
                      "flop_per_launch": tiles * flop_tile},
         "stages_ms": {"permutation": med(ms_perm), "mask": med(ms_mask), "attention": med(ms_attn)},
         "attention_ms": t_attn * 1e3,
@@ -375,6 +444,13 @@ def main() -> int:
         "speedup_vs_dense_kernel": med(ms_dense) / (t_attn * 1e3),
         "dense_kernel_tflops": w.dense_causal_flop / (med(ms_dense) * 1e-3) / 1e12,
     }
+    if args.copy_calib:
+        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dv)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    res["roofline"]["traffic"] = read_traffic()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         cb = cpu_baseline(w, x, count.cpu().numpy(), args.cpu_budget, np)
