@@ -185,7 +185,18 @@ def suite(args) -> int:
         return {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
 
     reps = args.suite_reps
-    # ---------------------------------------------------------------- 128K
+    parts = set(args.suite_parts.split(","))
+    if "128k" in parts:
+        suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
+    if "sweep" in parts:
+        suite_sweep(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
+    if "earlystop" in parts:
+        suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
+    out_f.close()
+    return 0
+
+
+def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     w = WORKLOADS["llama8b_128k"]
     t0 = time.perf_counter()
     d = load(w)
@@ -242,7 +253,8 @@ def suite(args) -> int:
     del d, q, k, v, out, lse, ws_p, ws_m, perm, count, idx
     torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- 64K density sweep
+
+def suite_sweep(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     w = WORKLOADS["llama8b_64k_sweep"]
     d = load(w)
     q, k, v = d["q"], d["k"], d["v"]
@@ -265,7 +277,8 @@ def suite(args) -> int:
     del d, q, k, v, out, perm
     torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- 64K early stop
+
+def suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     w = WORKLOADS["llama8b_64k_earlystop"]
     d = load(w)
     cal = load(w, seed=w.calib_seed)
@@ -294,8 +307,8 @@ def suite(args) -> int:
           "kept_tile_fraction": kept_tiles / causal_tiles, "attention_ms": t_gate, "dense_kernel_ms": t_dense,
           "attention_speedup_vs_dense": t_dense / t_gate,
           "mfma_frac": flop / (t_gate * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
-    out_f.close()
-    return 0
+    del d, q, k, v, out
+    torch.cuda.empty_cache()
 
 
 def main() -> int:
@@ -315,6 +328,8 @@ def main() -> int:
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
     ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
+    ap.add_argument("--suite-parts", default="128k,sweep,earlystop",
+                    help="comma-separated subset of 128k, sweep, earlystop")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "

@@ -86,22 +86,28 @@ __device__ __forceinline__ int vt_swz(int key) {  // V tile: 4 consecutive keys 
   return D == 128 ? ((key & 3) << 2) : ((key & 3) << 1);
 }
 
-// One gathered tile: rows row(j) of the head's slab into LDS [BLK][D] with the chunk swizzle.
+// Byte offset of key row r in a head's slab, or kOutOfRange (the buffer load then returns zeros).
+__device__ __forceinline__ uint32_t row_offset(int r, uint32_t row_bytes) {
+  return r >= 0 ? (uint32_t)r * row_bytes : kOutOfRange;
+}
+
+// One gathered tile: the rows at byte offsets row_off(j) of the head's slab into LDS [ROWS][D]
+// with the chunk swizzle.  An offset of kOutOfRange leaves a zero row.
 template <int D, int BLK, bool IS_V, typename RowFn, int ROWS = AttnCfg<D, BLK>::KT,
           int WAVES = AttnCfg<D, BLK>::WAVES>
-__device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, uint32_t row_bytes, RowFn row) {
+__device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, RowFn row_off) {
   constexpr int RPI = 512 / D;  // rows per 1 KiB wave instruction
   constexpr int LPR = D / 8;    // lanes per row
   constexpr int NI = ROWS / (RPI * WAVES);
   static_assert(NI * RPI * WAVES == ROWS, "tile rows must split evenly over the waves");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row0 = (wave * NI + i) * RPI;
     const int rw = row0 + lane / LPR;
-    const int c = (lane % LPR) ^ (IS_V ? vt_swz<D>(rw) : kt_swz<D>(rw));
-    const int rr = row(rw);
-    const uint32_t off = rr >= 0 ? (uint32_t)rr * row_bytes + c * 16 : kOutOfRange;
+    const uint32_t c = (lane % LPR) ^ (IS_V ? vt_swz<D>(rw) : kt_swz<D>(rw));
+    const uint32_t off = row_off(rw) + c * 16;  // kOutOfRange + c*16 stays out of range
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(dst + row0 * D), 16, off, 0, 0, 0);
   }
 }
@@ -331,6 +337,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Union of the kept key-block lists of query heads h0 .. h0+HPW-1 for query block I, in ascending
+// J, into mlist as J | (bit 16 + x set when head h0 + x kept J).  Returns the list length.  Mask
+// entries out of range are skipped and flagged in a.err.
+template <int HPW, int THREADS>
+__device__ __forceinline__ int union_list(const AttnArgs& a, int h0, int I, size_t ntri, uint8_t* selb, uint32_t* mlist,
+                                          int* mcount) {
+  constexpr int MAXNB = PipeCfg<128, 128, 1>::MAXNB;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int J = t; J <= I; J += THREADS)
+#pragma unroll
+    for (int x = 0; x < HPW; ++x) selb[x * MAXNB + J] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < HPW; ++x) {
+    int cnt = a.count[(size_t)(h0 + x) * a.NB + I];
+    if (cnt < 0 || cnt > I + 1) {
+      if (t == 0 && a.err) atomicOr(a.err, 4);
+      cnt = cnt < 0 ? 0 : I + 1;
+    }
+    const int32_t* list = a.idx + (size_t)(h0 + x) * ntri + tri_offset(I);
+    for (int k = t; k < cnt; k += THREADS) {
+      const int J = list[k];
+      if (J >= 0 && J <= I) {
+        selb[x * MAXNB + J] = 1;
+      } else if (a.err) {
+        atomicOr(a.err, 1);
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int base = 0;
+    for (int J0 = 0; J0 <= I; J0 += 64) {
+      const int J = J0 + lane;
+      uint32_t bits = 0;
+      if (J <= I) {
+#pragma unroll
+        for (int x = 0; x < HPW; ++x) bits |= (uint32_t)selb[x * MAXNB + J] << (16 + x);
+      }
+      const unsigned long long bal = __ballot(bits != 0);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (bits) mlist[pos] = (uint32_t)J | bits;
+      base += __popcll(bal);
+    }
+    if (lane == 0) *mcount = base;
+  }
+  __syncthreads();
+  return *mcount;
+}
+
 // Software-pipelined block-sparse (DENSE = false) or dense causal (DENSE = true) attention for
 // HPW query heads h0 .. h0+HPW-1 of one KV group and one query block I.  The workgroup walks the
 // union of the heads' kept key blocks in ascending order; each KT-key stage of a block is gathered
@@ -352,9 +408,9 @@ void attn_pipe_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t V0[KT * D];
   __shared__ __align__(16) uint16_t V1[KT * D];
   __shared__ __align__(16) uint16_t V2[NBUF > 2 ? KT * D : 8];
-  __shared__ int rowid[DENSE ? 1 : C::RING][KT];
+  __shared__ uint32_t rowid[DENSE ? 1 : C::RING][KT];  // byte offsets of the gathered rows
   __shared__ uint32_t mlist[DENSE ? 1 : C::MAXNB];  // J | kept-by-head bits << 16
-  __shared__ uint8_t selb[DENSE ? 1 : HPW][DENSE ? 1 : C::MAXNB];
+  __shared__ uint8_t selb[DENSE ? 1 : HPW * C::MAXNB];
   __shared__ int mcount;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -398,49 +454,7 @@ void attn_pipe_kernel(AttnArgs a) {
   }
 
   // merged key-block list: ascending J kept by any of the workgroup's heads
-  int nblk = I + 1;
-  if (!DENSE) {
-    for (int J = t; J <= I; J += C::THREADS)
-#pragma unroll
-      for (int x = 0; x < HPW; ++x) selb[x][J] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < HPW; ++x) {
-      int cnt = a.count[(size_t)(h0 + x) * a.NB + I];
-      if (cnt < 0 || cnt > I + 1) {
-        if (t == 0 && a.err) atomicOr(a.err, 4);
-        cnt = cnt < 0 ? 0 : I + 1;
-      }
-      const int32_t* list = a.idx + (size_t)(h0 + x) * ntri + tri_offset(I);
-      for (int k = t; k < cnt; k += C::THREADS) {
-        const int J = list[k];
-        if (J >= 0 && J <= I) {
-          selb[x][J] = 1;
-        } else if (a.err) {
-          atomicOr(a.err, 1);
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      int base = 0;
-      for (int J0 = 0; J0 <= I; J0 += 64) {
-        const int J = J0 + lane;
-        uint32_t bits = 0;
-        if (J <= I) {
-#pragma unroll
-          for (int x = 0; x < HPW; ++x) bits |= (uint32_t)selb[x][J] << (16 + x);
-        }
-        const unsigned long long bal = __ballot(bits != 0);
-        const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-        if (bits) mlist[pos] = (uint32_t)J | bits;
-        base += __popcll(bal);
-      }
-      if (lane == 0) mcount = base;
-    }
-    __syncthreads();
-    nblk = mcount;
-  }
+  const int nblk = DENSE ? I + 1 : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
   const int nst = nblk * C::STAGES;
   const int sI = a.S > 0 ? I0 / a.S : 0;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
@@ -465,14 +479,14 @@ void attn_pipe_kernel(AttnArgs a) {
   };
   auto gather = [&](int s, uint16_t* Kd, uint16_t* Vd) {
     if (DENSE) {
-      auto rf = [&](int j) { return phys_row(s, j); };
-      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, a.kv_row_bytes, rf);
-      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, a.kv_row_bytes, rf);
+      auto rf = [&](int j) { return row_offset(phys_row(s, j), a.kv_row_bytes); };
+      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, rf);
+      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, rf);
     } else {
-      const int* ids = rowid[s % C::RING];
+      const uint32_t* ids = rowid[s % C::RING];
       auto rf = [&](int j) { return ids[j]; };
-      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, a.kv_row_bytes, rf);
-      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, rf);
+      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, rf);
     }
   };
 
@@ -486,7 +500,7 @@ void attn_pipe_kernel(AttnArgs a) {
 
   if (nst > 0) {
     if (!DENSE && t < KT)
-      for (int x = 0; x < NBUF && x < nst; ++x) rowid[x][t] = phys_row(x, t);
+      for (int x = 0; x < NBUF && x < nst; ++x) rowid[x][t] = row_offset(phys_row(x, t), a.kv_row_bytes);
     __syncthreads();  // zero fill and row ids visible
     gather(0, K0, V0);
     if (nst > 1 && NBUF > 2) gather(1, K1, V1);
@@ -496,8 +510,8 @@ void attn_pipe_kernel(AttnArgs a) {
 
   // one pipeline step: compute stage s from (Kc, Vc) while stage s + NBUF - 1 is gathered into (Kd, Vd)
   auto step = [&](int s, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kd, uint16_t* Vd) {
-    int pr = -1;
-    if (!DENSE && s + NBUF < nst && t < KT) pr = phys_row(s + NBUF, t);
+    uint32_t pr = kOutOfRange;
+    if (!DENSE && s + NBUF < nst && t < KT) pr = row_offset(phys_row(s + NBUF, t), a.kv_row_bytes);
     const bool issue = s + NBUF - 1 < nst;
     if (issue) gather(s + NBUF - 1, Kd, Vd);
     const uint32_t e = entry_of(s);
@@ -534,6 +548,285 @@ void attn_pipe_kernel(AttnArgs a) {
   write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
 }
 
+// Score block kb of a tile (S^T, 32 keys x 32 queries) with K operands read from LDS a quarter of
+// the k-steps at a time (fewer live registers than load_k_ops), causal mask on the diagonal.
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 tile_scores(const uint16_t* Ks, const bf16x8* qf, int kb, bool diag, int rel) {
+  using C = AttnCfg<D, BLK>;
+  constexpr int KQ = C::KSTEPS >= 4 ? C::KSTEPS / 4 : 1;  // k-steps per operand batch
+  const int lane = threadIdx.x & 63;
+  const int krow = kb * 32 + (lane & 31), h2 = lane >> 5;
+  const uint16_t* kp = Ks + krow * D;
+  const int ksw = kt_swz<D>(krow);
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int k0 = 0; k0 < C::KSTEPS; k0 += KQ) {
+    bf16x8 kop[KQ];
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kp + ((((k0 + kk) * 2 + h2) ^ ksw) * 8));
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[k0 + kk], s, 0, 0, 0);
+  }
+  if (diag) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) > rel) s[r] = -INFINITY;
+  }
+  return s;
+}
+
+// Row max over a whole key tile (KB score blocks) of this lane's query, both half-waves, unscaled.
+template <int KB>
+__device__ __forceinline__ float tile_row_max(const f32x16* s) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  float x, y;
+  half_swap(mx, &x, &y);
+  return fmaxf(x, y);
+}
+
+// Online-softmax update with a whole kept tile: one lazy rescale on the tile's row max, then the
+// bf16 probabilities of all its keys (pb[2 kb + hf] holds registers 8 hf .. 8 hf + 7 of score
+// block kb) and their sum.  The PV product with pb is issued separately (tile_pv).
+template <int D, int BLK>
+__device__ __forceinline__ void tile_softmax(SoftmaxState<D, BLK>& st, const f32x16* s, float row_max, bf16x8* pb,
+                                             float sl2) {
+  using C = AttnCfg<D, BLK>;
+  const float mx = row_max * sl2;
+  const bool need = mx > st.m + kLazy;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float m_new = need ? mx : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    st.m = m_new;
+  }
+  const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pb[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_use));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pair = {pb[2 * kb + hf][2 * e], pb[2 * kb + hf][2 * e + 1]};
+        st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
+      }
+  }
+}
+
+// O^T += V^T P^T for a whole tile from the transposed V tile in LDS.
+template <int D, int BLK>
+__device__ __forceinline__ void tile_pv(SoftmaxState<D, BLK>& st, const bf16x8* pb, const uint16_t* Vs) {
+  using C = AttnCfg<D, BLK>;
+  const int lane = threadIdx.x & 63;
+  const int h2 = lane >> 5, i16 = lane & 15, dsub = (lane >> 4) & 1;
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  // one 16-key half of a score block at a time keeps the V operands to 4 DB registers
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int key0 = kb * 32 + 16 * hf + 4 * h2 + (i16 >> 2);
+      bf16x8 vop[C::DB];
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const int dcol = db * 32 + dsub * 16 + 4 * (i16 & 3);
+        const uint16_t* p0 = Vs + key0 * D + (((dcol >> 3) ^ vt_swz<D>(key0)) * 8) + (dcol & 7);
+        const uint16_t* p1 = Vs + (key0 + 8) * D + (((dcol >> 3) ^ vt_swz<D>(key0 + 8)) * 8) + (dcol & 7);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p1));
+        const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        vop[db] = __builtin_bit_cast(bf16x8, both);
+      }
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db], pb[2 * kb + hf], st.o[db], 0, 0, 0);
+    }
+}
+
+// Software-pipelined early-stop attention (Block Sparse Flash Attention, Approach) for HPW query
+// heads of one KV group and one query block I.  The workgroup walks the key blocks u = 0, 1, ... of
+// the row (every J <= I when DENSE, else the union of the heads' kept lists).  Iteration u:
+//   - gather the K tile of block u+1 (one block ahead) and resolve the row ids of block u+2;
+//   - S_u = K_u Q^T for every head that has block u, and each wave's max over its valid entries;
+//   - wait for the gathers in flight, barrier;
+//   - O += V_{u-1}^T P_{u-1} for the heads that kept block u-1 (its V gather was hidden behind S_u);
+//   - per head, the exact tile max of S_u against theta[h][I] (the diagonal is always kept); a
+//     kept tile updates (m, l) and yields P_u; the V tile of block u is gathered only if some head
+//     kept it.
+// A tile that no head keeps costs its K gather and QK^T only; a skipped tile leaves (m, l, acc)
+// untouched.  Buffers: K and V double-buffered, row ids in a ring of four, partial maxima double-
+// buffered, so one barrier per key block suffices.
+template <int D, int BLK, bool DENSE, int HPW>
+__global__ __attribute__((amdgpu_flat_work_group_size(PipeCfg<D, BLK, HPW>::THREADS, PipeCfg<D, BLK, HPW>::THREADS),
+                          amdgpu_waves_per_eu(2)))
+void attn_gate_pipe_kernel(AttnArgs a) {
+  using C = PipeCfg<D, BLK, HPW>;
+  using AC = AttnCfg<D, BLK>;
+  constexpr int WPH = C::WAVES_PER_HEAD;
+  constexpr int KB = AC::KB;
+  __shared__ __align__(16) uint16_t K0[BLK * D];
+  __shared__ __align__(16) uint16_t K1[BLK * D];
+  __shared__ __align__(16) uint16_t V0[BLK * D];
+  __shared__ __align__(16) uint16_t V1[BLK * D];
+  __shared__ uint32_t rowid[4][BLK];  // byte offsets of the gathered rows, ring of four blocks
+  __shared__ uint32_t mlist[DENSE ? 1 : C::MAXNB];  // J | kept-by-head bits << 16
+  __shared__ uint8_t selb[DENSE ? 1 : HPW * C::MAXNB];
+  __shared__ int mcount;
+  __shared__ float red[2][C::WAVES];
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int l32 = lane & 31, h2 = lane >> 5;
+  const int hh = wave / WPH;  // this wave's head within the workgroup
+  const int wq = wave % WPH;  // this wave's 32-row slice of the query block
+  int I, h0;
+  work_item(a.NB, a.Hq / HPW, HPW, blockIdx.x, &I, &h0);
+  const int h = h0 + hh;
+  const int g = h0 / a.G;
+  const int I0 = I * BLK;
+  const int qloc = wq * 32 + l32;
+  const int qpos = I0 + qloc;
+  const bool qvalid = qpos < a.N;
+  const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
+  const rsrc_t qr = make_rsrc(a.q + (int64_t)h * a.qsh, a.q_bytes);
+  const rsrc_t kr = make_rsrc(a.k + (int64_t)g * a.kvsh, a.kv_bytes);
+  const rsrc_t vr = make_rsrc(a.v + (int64_t)g * a.kvsh, a.kv_bytes);
+
+  {  // rows past N are never written by the gather: start from finite (zero) tiles
+    constexpr int NZ = BLK * D * 2 / 16;
+    for (int i = t; i < NZ; i += C::THREADS) {
+      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4*>(K0)[i] = z;
+      reinterpret_cast<u32x4*>(K1)[i] = z;
+      reinterpret_cast<u32x4*>(V0)[i] = z;
+      reinterpret_cast<u32x4*>(V1)[i] = z;
+    }
+  }
+  bf16x8 qf[AC::KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < AC::KSTEPS; ++kk) {
+    const uint32_t off = qvalid ? (uint32_t)qpos * a.q_row_bytes + kk * 32 + h2 * 16 : kOutOfRange;
+    qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(qr, off));
+  }
+  float th[HPW];
+#pragma unroll
+  for (int x = 0; x < HPW; ++x) th[x] = a.theta[(size_t)(h0 + x) * a.NB + I];
+
+  const int nblk = DENSE ? I + 1 : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
+  const int sI = a.S > 0 ? I0 / a.S : 0;
+  const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
+  auto entry_of = [&](int u) -> uint32_t { return DENSE ? ((uint32_t)u | all_heads) : mlist[u]; };
+  // physical key row of row j of block u (-1 when past N or perm out of range)
+  auto phys_row = [&](int u, int j) -> int {
+    const int J = (int)(entry_of(u) & 0xffffu);
+    const int p = J * BLK + j;
+    if (p >= a.N) return -1;
+    if (a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI) {
+      const int r = a.perm[(size_t)g * a.N + p];
+      if (r < 0 || r >= a.N) {
+        if (a.err) atomicOr(a.err, 2);
+        return -1;
+      }
+      return r;
+    }
+    return p;
+  };
+  auto gather_k = [&](int u, uint16_t* dst) {
+    const uint32_t* ids = rowid[u & 3];
+    auto rf = [&](int j) { return ids[j]; };
+    dma_tile<D, BLK, false, decltype(rf), BLK, C::WAVES>(dst, kr, rf);
+  };
+  auto gather_v = [&](int u, uint16_t* dst) {
+    const uint32_t* ids = rowid[u & 3];
+    auto rf = [&](int j) { return ids[j]; };
+    dma_tile<D, BLK, true, decltype(rf), BLK, C::WAVES>(dst, vr, rf);
+  };
+
+  SoftmaxState<D, BLK> st;
+#pragma unroll
+  for (int db = 0; db < AC::DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
+  bf16x8 pb[2 * KB];  // probabilities of the last kept tile, consumed one iteration later
+  bool keep_prev = false;
+
+  if (nblk > 0) {
+    if (t < BLK)
+      for (int u = 0; u < 2 && u < nblk; ++u) rowid[u][t] = row_offset(phys_row(u, t), a.kv_row_bytes);
+    __syncthreads();  // zero fill and row ids visible
+    gather_k(0, K0);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  auto step = [&](int u, const uint16_t* Kc, uint16_t* Kn, const uint16_t* Vp, uint16_t* Vc) {
+    uint32_t pr = kOutOfRange;
+    if (u + 2 < nblk && t < BLK) pr = row_offset(phys_row(u + 2, t), a.kv_row_bytes);
+    if (u + 1 < nblk) gather_k(u + 1, Kn);
+    const uint32_t e = entry_of(u);
+    const int J = (int)(e & 0xffffu);
+    const bool diag = J == I;
+    f32x16 sc[KB];
+    float row_max = -INFINITY;
+    if ((e >> (16 + hh)) & 1u) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        int rel = qloc - kb * 32 - 4 * h2;
+        asm volatile("" : "+v"(rel));  // keep the causal compares inside the loop
+        sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, rel);
+      }
+      row_max = tile_row_max<KB>(sc);
+    }
+    const float wm = wave_max_f32(qvalid ? row_max : -INFINITY);
+    if (lane == 0) red[u & 1][wave] = wm;
+    if (u + 2 < nblk && t < BLK) rowid[(u + 2) & 3][t] = pr;
+    wait_vmcnt<0>();  // V of block u-1 and K of block u+1 have landed (this wave's share)
+    __syncthreads();
+    if (keep_prev) tile_pv<D, BLK>(st, pb, Vp);
+    bool any = false, keep = false;
+#pragma unroll
+    for (int x = 0; x < HPW; ++x) {
+      float tm = red[u & 1][x * WPH];
+#pragma unroll
+      for (int y = 1; y < WPH; ++y) tm = fmaxf(tm, red[u & 1][x * WPH + y]);
+      const bool kx = ((e >> (16 + x)) & 1u) && (diag || !(tm * a.scale < th[x]));
+      any = any || kx;
+      if (x == hh) keep = kx;
+    }
+    if (keep) tile_softmax<D, BLK>(st, sc, row_max, pb, a.sl2);
+    if (any) gather_v(u, Vc);
+    if (keep && a.kept && lane == 0 && wq == 0) {
+      const size_t bit = tri_offset(I) + J;
+      atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
+    }
+    keep_prev = keep;
+  };
+  for (int u = 0; u < nblk; u += 2) {
+    step(u, K0, K1, V1, V0);
+    if (u + 1 < nblk) step(u + 1, K1, K0, V0, V1);
+  }
+  if (nblk > 0) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (keep_prev) tile_pv<D, BLK>(st, pb, ((nblk - 1) & 1) ? V1 : V0);
+  }
+  write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
+}
+
 // Early-stop kernel (Block Sparse Flash Attention, Approach) and calibration tile maxima.  Per key
 // block: gather K, compute the whole tile's scores, reduce their exact max across the workgroup,
 // and only when the tile is kept gather V and run the same online-softmax / PV steps as the
@@ -546,7 +839,7 @@ void attn_gated_kernel(AttnArgs a) {
   using C = AttnCfg<D, BLK>;
   __shared__ __align__(16) uint16_t Ks[BLK * D];
   __shared__ __align__(16) uint16_t Vs[(MODE == MODE_TILE_MAX) ? 8 : BLK * D];
-  __shared__ int rowid[BLK];
+  __shared__ uint32_t rowid[BLK];
   __shared__ float red[C::WAVES];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -614,11 +907,11 @@ void attn_gated_kernel(AttnArgs a) {
           r = -1;
         }
       }
-      rowid[t] = r;
+      rowid[t] = row_offset(r, a.kv_row_bytes);
     }
     __syncthreads();
     auto rf = [&](int j) { return rowid[j]; };
-    dma_tile<D, BLK, false, decltype(rf), BLK>(Ks, kr, a.kv_row_bytes, rf);
+    dma_tile<D, BLK, false, decltype(rf), BLK>(Ks, kr, rf);
     wait_dma();
     __syncthreads();
     f32x16 sc[C::KB];
@@ -644,7 +937,7 @@ void attn_gated_kernel(AttnArgs a) {
       if (tm * a.scale < a.theta[(size_t)h * a.NB + I]) continue;  // gate: no V load, no PV
     }
     if (MODE != MODE_TILE_MAX) {
-      dma_tile<D, BLK, true, decltype(rf), BLK>(Vs, vr, a.kv_row_bytes, rf);
+      dma_tile<D, BLK, true, decltype(rf), BLK>(Vs, vr, rf);
       if (a.kept && t == 0) {
         const size_t bit = tri_offset(I) + J;
         atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
@@ -666,6 +959,12 @@ static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st) {
       attn_pipe_kernel<D, BLK, DENSE, 2><<<nwg / 2, PipeCfg<D, BLK, 2>::THREADS, 0, st>>>(a);
     } else {
       attn_pipe_kernel<D, BLK, DENSE, 1><<<nwg, PipeCfg<D, BLK, 1>::THREADS, 0, st>>>(a);
+    }
+  } else if (MODE == MODE_ATTN_GATED && (a.G & 1) == 0) {
+    if (a.count == nullptr) {
+      attn_gate_pipe_kernel<D, BLK, true, 2><<<nwg / 2, PipeCfg<D, BLK, 2>::THREADS, 0, st>>>(a);
+    } else {
+      attn_gate_pipe_kernel<D, BLK, false, 2><<<nwg / 2, PipeCfg<D, BLK, 2>::THREADS, 0, st>>>(a);
     }
   } else {
     attn_gated_kernel<D, BLK, MODE><<<nwg, AttnCfg<D, BLK>::THREADS, 0, st>>>(a);

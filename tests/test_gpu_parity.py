@@ -116,9 +116,10 @@ def test_full_mask_with_permutation_equals_dense():
     compare_out(out.cpu().numpy(), ref, "full mask")
 
 
-def test_early_stop_gate():
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 1)])  # query heads paired per workgroup, and not
+def test_early_stop_gate(Hq, Hkv):
     pbsa = _need_gpu()
-    N, Hq, Hkv, d, B, keep = 2048, 4, 2, 128, 128, 6
+    N, d, B, keep = 2048, 128, 128, 6
     dev, host = _inputs(N, Hq, Hkv, d, 16, 256, 31)
     cal, _ = _inputs(N, Hq, Hkv, d, 16, 256, 32)
     NB = oracle.num_blocks(N, B)
@@ -174,11 +175,64 @@ def test_threshold_limits():
     out_hi = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B, early_stop_theta=hi,
                                             return_lse=False)
     torch.cuda.synchronize()
-    # the gated kernel runs the same per-block softmax steps: theta = -inf changes nothing
-    assert torch.equal(out_lo, ref)
+    # theta = -inf keeps every tile: dense causal attention
+    dense, _ = oracle.dense_attention(host["q"], host["k"], host["v"])
+    compare_out(out_lo.cpu().numpy(), dense, "theta=-inf")
+    assert (out_lo - ref).abs().max().item() <= 2e-2
     blk = np.arange(N) // B
     diag_only, _ = oracle.dense_attention(host["q"], host["k"], host["v"], allowed=blk[:, None] == blk[None, :])
     compare_out(out_hi.cpu().numpy(), diag_only, "theta=+inf")
+
+
+def _tile_max_fp64(q, k, perm, B, S, h, I, J, G):
+    """c * max of q_i . k_j over i in block I, j in the rows block J stands for when read by I, j <= i."""
+    N, d = q.shape[1], q.shape[2]
+    qi = np.arange(I * B, min((I + 1) * B, N))
+    kj = oracle.key_rows_of_block(J, I, None if perm is None else perm[h // G], B, S, N)
+    st = (q[h, qi] @ k[h // G, kj].T) / math.sqrt(d)
+    return np.where(kj[None, :] <= qi[:, None], st, -np.inf).max()
+
+
+def test_early_stop_with_permutation():
+    """The gate on a permuted sparse mask: tile maxima over the gathered (permuted) rows."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 1664, 4, 2, 128, 128, 512
+    dev, host = _inputs(N, Hq, Hkv, d, 12, 256, 61)
+    q, k, v = host["q"], host["k"], host["v"]
+    NB, G = oracle.num_blocks(N, B), Hq // Hkv
+    perm_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    count_t, idx_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, 0.97)
+    perm, cnt, idx = perm_t.cpu().numpy(), count_t.cpu().numpy(), idx_t.cpu().numpy()
+    # thresholds at the median fp64 tile max of each row, so about half the off-diagonal tiles go
+    theta = np.full((Hq, NB), -np.inf, dtype=np.float32)
+    tmax = {}
+    for h in range(Hq):
+        for I in range(NB):
+            o = oracle.tri_offset(I)
+            sel = [int(J) for J in idx[h, o:o + cnt[h, I]]]
+            tmax[(h, I)] = {J: _tile_max_fp64(q, k, perm, B, S, h, I, J, G) for J in sel}
+            off = [m for J, m in tmax[(h, I)].items() if J != I]
+            if off:
+                theta[h, I] = np.float32(np.median(off))
+    out_t, lse_t, kept_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S,
+                                                          early_stop_theta=torch.from_numpy(theta).cuda(),
+                                                          return_kept=True)
+    torch.cuda.synchronize()
+    kept = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+    dropped = 0
+    for (h, I), tm in tmax.items():
+        for J, m in tm.items():
+            if J == I:
+                assert J in kept[(h, I)], (h, I)
+            elif abs(m - float(theta[h, I])) > 1e-3:  # clear of the fp32 error band
+                assert (J in kept[(h, I)]) == (m >= float(theta[h, I])), (h, I, J)
+            dropped += J not in kept[(h, I)]
+        assert set(kept[(h, I)]) <= set(tm), (h, I)
+    assert dropped > 0
+    kc, ki = kept_to_mask(kept, Hq, NB)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, perm, kc, ki, B, S)
+    compare_out(out_t.cpu().numpy(), out_o, "early stop with permutation")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
 
 
 def test_deterministic():
