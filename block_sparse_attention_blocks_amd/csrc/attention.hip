@@ -91,6 +91,40 @@ __device__ __forceinline__ uint32_t row_offset(int r, uint32_t row_bytes) {
   return r >= 0 ? (uint32_t)r * row_bytes : kOutOfRange;
 }
 
+// A key row looked up for a later gather is kept raw (a natural position, a perm entry, or kPastEnd
+// for a row past the sequence) until it is stored, so the perm load is not waited for where it is
+// issued.  checked_row_offset turns it into a byte offset; a perm entry out of range sets bit 2 of
+// err and reads zeros.
+constexpr int kPastEnd = -2147483647 - 1;
+__device__ __forceinline__ uint32_t checked_row_offset(int raw, int N, uint32_t row_bytes, int32_t* err) {
+  if (raw == kPastEnd) return kOutOfRange;
+  if (raw < 0 || raw >= N) {
+    if (err) atomicOr(err, 2);
+    return kOutOfRange;
+  }
+  return (uint32_t)raw * row_bytes;
+}
+
+// One pending row lookup: every lane issues the perm load (a buffer load that returns zero when the
+// row is natural or unused), with no branch around it, so nothing consumes the loaded value before
+// row_lookup_offset at the point where the row id is stored.
+struct RowLook {
+  int pos;   // natural position, or kPastEnd
+  int pv;    // perm entry (valid when via)
+  bool via;  // the row is read through perm
+};
+__device__ __forceinline__ RowLook row_lookup(rsrc_t permr, int p, int N, bool want, bool permuted) {
+  RowLook r;
+  const bool live = want && p < N;
+  r.via = live && permuted;
+  r.pos = live ? p : kPastEnd;
+  r.pv = (int)__builtin_amdgcn_raw_buffer_load_b32(permr, r.via ? (uint32_t)p * 4u : kOutOfRange, 0, 0);
+  return r;
+}
+__device__ __forceinline__ uint32_t row_lookup_offset(const RowLook& r, int N, uint32_t row_bytes, int32_t* err) {
+  return checked_row_offset(r.via ? r.pv : r.pos, N, row_bytes, err);
+}
+
 // One gathered tile: the rows at byte offsets row_off(j) of the head's slab into LDS [ROWS][D]
 // with the chunk swizzle.  An offset of kOutOfRange leaves a zero row.
 template <int D, int BLK, bool IS_V, typename RowFn, int ROWS = AttnCfg<D, BLK>::KT,
@@ -337,6 +371,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier of the pipelined loops: this wave's LDS operations complete, then s_barrier.
+// __syncthreads() would also drain every outstanding global load, including the stage gathers
+// issued for later stages; here each wave first waits (wait_vmcnt) only for the gathers of the
+// stage about to be read, so the later ones stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Union of the kept key-block lists of query heads h0 .. h0+HPW-1 for query block I, in ascending
 // J, into mlist as J | (bit 16 + x set when head h0 + x kept J).  Returns the list length.  Mask
 // entries out of range are skipped and flagged in a.err.
@@ -462,24 +504,17 @@ void attn_pipe_kernel(AttnArgs a) {
     const int u = s / C::STAGES;
     return DENSE ? ((uint32_t)u | all_heads) : mlist[u];
   };
-  // physical key row of row j of stage s (-1 when past N or perm out of range)
-  auto phys_row = [&](int s, int j) -> int {
+  const rsrc_t permr = make_rsrc(a.perm ? a.perm + (size_t)g * a.N : nullptr, a.perm ? (uint32_t)a.N * 4u : 0u);
+  // lookup of row j of stage s (want = false: an unused lookup that reads nothing)
+  auto lookup = [&](int s, int j, bool want) -> RowLook {
     const int J = (int)(entry_of(s) & 0xffffu);
     const int p = J * BLK + (s % C::STAGES) * KT + j;
-    if (p >= a.N) return -1;
-    if (!DENSE && a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI) {
-      const int r = a.perm[(size_t)g * a.N + p];
-      if (r < 0 || r >= a.N) {
-        if (a.err) atomicOr(a.err, 2);
-        return -1;
-      }
-      return r;
-    }
-    return p;
+    return row_lookup(permr, p, a.N, want, !DENSE && a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI);
   };
+  auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.kv_row_bytes, a.err); };
   auto gather = [&](int s, uint16_t* Kd, uint16_t* Vd) {
     if (DENSE) {
-      auto rf = [&](int j) { return row_offset(phys_row(s, j), a.kv_row_bytes); };
+      auto rf = [&](int j) { return row_off(lookup(s, j, true)); };
       dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, rf);
       dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, rf);
     } else {
@@ -500,7 +535,7 @@ void attn_pipe_kernel(AttnArgs a) {
 
   if (nst > 0) {
     if (!DENSE && t < KT)
-      for (int x = 0; x < NBUF && x < nst; ++x) rowid[x][t] = row_offset(phys_row(x, t), a.kv_row_bytes);
+      for (int x = 0; x < NBUF && x < nst; ++x) rowid[x][t] = row_off(lookup(x, t, true));
     __syncthreads();  // zero fill and row ids visible
     gather(0, K0, V0);
     if (nst > 1 && NBUF > 2) gather(1, K1, V1);
@@ -510,8 +545,9 @@ void attn_pipe_kernel(AttnArgs a) {
 
   // one pipeline step: compute stage s from (Kc, Vc) while stage s + NBUF - 1 is gathered into (Kd, Vd)
   auto step = [&](int s, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kd, uint16_t* Vd) {
-    uint32_t pr = kOutOfRange;
-    if (!DENSE && s + NBUF < nst && t < KT) pr = row_offset(phys_row(s + NBUF, t), a.kv_row_bytes);
+    RowLook pr;
+    if (!DENSE) pr = lookup(s + NBUF < nst ? s + NBUF : 0, t & (KT - 1), s + NBUF < nst && t < KT);
+    __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gathers (vmcnt order)
     const bool issue = s + NBUF - 1 < nst;
     if (issue) gather(s + NBUF - 1, Kd, Vd);
     const uint32_t e = entry_of(s);
@@ -524,14 +560,14 @@ void attn_pipe_kernel(AttnArgs a) {
       }
       stage_compute<D, BLK>(st, Kc, Vc, qf, J == I, qloc - koff - 4 * h2, a.sl2);
     }
-    if (!DENSE && s + NBUF < nst && t < KT) rowid[(s + NBUF) % C::RING][t] = pr;
+    if (!DENSE && s + NBUF < nst && t < KT) rowid[(s + NBUF) % C::RING][t] = row_off(pr);
     // stage s + 1 must have landed; the newest stage's gathers may stay in flight
     if (issue && NBUF > 2) {
       wait_vmcnt<(NBUF - 2) * C::NDMA>();
     } else {
       wait_vmcnt<0>();
     }
-    __syncthreads();
+    lds_barrier();
   };
   if constexpr (NBUF == 2) {
     for (int s = 0; s < nst; s += 2) {
@@ -728,21 +764,14 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   const int sI = a.S > 0 ? I0 / a.S : 0;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
   auto entry_of = [&](int u) -> uint32_t { return DENSE ? ((uint32_t)u | all_heads) : mlist[u]; };
-  // physical key row of row j of block u (-1 when past N or perm out of range)
-  auto phys_row = [&](int u, int j) -> int {
+  const rsrc_t permr = make_rsrc(a.perm ? a.perm + (size_t)g * a.N : nullptr, a.perm ? (uint32_t)a.N * 4u : 0u);
+  // lookup of row j of block u (want = false: an unused lookup that reads nothing)
+  auto lookup = [&](int u, int j, bool want) -> RowLook {
     const int J = (int)(entry_of(u) & 0xffffu);
     const int p = J * BLK + j;
-    if (p >= a.N) return -1;
-    if (a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI) {
-      const int r = a.perm[(size_t)g * a.N + p];
-      if (r < 0 || r >= a.N) {
-        if (a.err) atomicOr(a.err, 2);
-        return -1;
-      }
-      return r;
-    }
-    return p;
+    return row_lookup(permr, p, a.N, want, a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI);
   };
+  auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.kv_row_bytes, a.err); };
   auto gather_k = [&](int u, uint16_t* dst) {
     const uint32_t* ids = rowid[u & 3];
     auto rf = [&](int j) { return ids[j]; };
@@ -766,7 +795,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
 
   if (nblk > 0) {
     if (t < BLK)
-      for (int u = 0; u < 2 && u < nblk; ++u) rowid[u][t] = row_offset(phys_row(u, t), a.kv_row_bytes);
+      for (int u = 0; u < 2 && u < nblk; ++u) rowid[u][t] = row_off(lookup(u, t, true));
     __syncthreads();  // zero fill and row ids visible
     gather_k(0, K0);
     wait_vmcnt<0>();
@@ -774,8 +803,8 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   }
 
   auto step = [&](int u, const uint16_t* Kc, uint16_t* Kn, const uint16_t* Vp, uint16_t* Vc) {
-    uint32_t pr = kOutOfRange;
-    if (u + 2 < nblk && t < BLK) pr = row_offset(phys_row(u + 2, t), a.kv_row_bytes);
+    const RowLook pr = lookup(u + 2 < nblk ? u + 2 : 0, t & (BLK - 1), u + 2 < nblk && t < BLK);
+    __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gather (vmcnt order)
     if (u + 1 < nblk) gather_k(u + 1, Kn);
     const uint32_t e = entry_of(u);
     const int J = (int)(e & 0xffffu);
@@ -793,7 +822,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     }
     const float wm = wave_max_f32(qvalid ? row_max : -INFINITY);
     if (lane == 0) red[u & 1][wave] = wm;
-    if (u + 2 < nblk && t < BLK) rowid[(u + 2) & 3][t] = pr;
+    if (u + 2 < nblk && t < BLK) rowid[(u + 2) & 3][t] = row_off(pr);
     wait_vmcnt<0>();  // V of block u-1 and K of block u+1 have landed (this wave's share)
     __syncthreads();
     if (keep_prev) tile_pv<D, BLK>(st, pb, Vp);

@@ -116,6 +116,23 @@ def test_full_mask_with_permutation_equals_dense():
     compare_out(out.cpu().numpy(), ref, "full mask")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 1)])
+def test_mask_without_permutation(Hq, Hkv):
+    """Permutation off (perm = NULL) with a segment size set: every key block is read in natural order."""
+    pbsa = _need_gpu()
+    N, d, B, S = 1700, 128, 128, 512
+    dev, host = _inputs(N, Hq, Hkv, d, 12, 256, 71)
+    count, idx = pbsa.estimate_block_mask(dev["q"], dev["k"], None, B, S, 0.8)
+    out, lse = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], None, count, idx, B, S)
+    torch.cuda.synchronize()
+    cg, ig = count.cpu().numpy(), idx.cpu().numpy()
+    co, io, po = oracle.block_mask(host["q"], host["k"], None, B, S, 0.8)
+    compare_mask(cg, ig, co, io, po, 0.8)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(host["q"], host["k"], host["v"], None, cg, ig, B, S)
+    compare_out(out.cpu().numpy(), out_o, "mask without permutation")
+    compare_lse(lse.cpu().numpy(), lse_o)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 1)])  # query heads paired per workgroup, and not
 def test_early_stop_gate(Hq, Hkv):
     pbsa = _need_gpu()
