@@ -109,20 +109,20 @@ __device__ __forceinline__ uint32_t checked_row_offset(int raw, int N, uint32_t 
 // row is natural or unused), with no branch around it, so nothing consumes the loaded value before
 // row_lookup_offset at the point where the row id is stored.
 struct RowLook {
-  int pos;   // natural position, or kPastEnd
-  int pv;    // perm entry (valid when via)
-  bool via;  // the row is read through perm
+  int code;  // natural position (>= 0), kViaPerm (the row is the perm entry pv), or kPastEnd
+  int pv;    // perm entry
 };
+constexpr int kViaPerm = -1;
 __device__ __forceinline__ RowLook row_lookup(rsrc_t permr, int p, int N, bool want, bool permuted) {
   RowLook r;
   const bool live = want && p < N;
-  r.via = live && permuted;
-  r.pos = live ? p : kPastEnd;
-  r.pv = (int)__builtin_amdgcn_raw_buffer_load_b32(permr, r.via ? (uint32_t)p * 4u : kOutOfRange, 0, 0);
+  const bool via = live && permuted;
+  r.code = via ? kViaPerm : live ? p : kPastEnd;
+  r.pv = (int)__builtin_amdgcn_raw_buffer_load_b32(permr, via ? (uint32_t)p * 4u : kOutOfRange, 0, 0);
   return r;
 }
 __device__ __forceinline__ uint32_t row_lookup_offset(const RowLook& r, int N, uint32_t row_bytes, int32_t* err) {
-  return checked_row_offset(r.via ? r.pv : r.pos, N, row_bytes, err);
+  return checked_row_offset(r.code == kViaPerm ? r.pv : r.code, N, row_bytes, err);
 }
 
 // One gathered tile: the rows at byte offsets row_off(j) of the head's slab into LDS [ROWS][D]
@@ -173,9 +173,20 @@ __device__ __forceinline__ void load_k_ops(bf16x8* kop, const uint16_t* Ks, int 
     kop[kk] = *reinterpret_cast<const bf16x8*>(kp + (((kk * 2 + h2) ^ ksw) * 8));
 }
 
+// Causal mask of a score block on the diagonal tile: rel = query row - first key of the block -
+// 4*h2, so register r holds key offset 8*(r/4) + r%4 relative to it.  The empty volatile asm keeps
+// the enclosing `if (diag)` a real (uniform) branch: if-converted, the compares and selects would
+// run on every block.
+__device__ __forceinline__ void causal_mask(f32x16& s, int rel) {
+  asm volatile("" : "+v"(rel));
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (8 * (r >> 2) + (r & 3) > rel) s[r] = -INFINITY;
+  asm volatile("" : "+v"(s));  // the selects stay inside the caller's diagonal branch
+}
+
 // S^T block (32 keys x this wave's 32 queries) from preloaded K operands, with the causal mask on
-// the diagonal tile.  rel = query row - first key of the block - 4*h2, so register r holds key
-// offset 8*(r/4) + r%4 relative to it.
+// the diagonal tile.
 template <int D, int BLK>
 __device__ __forceinline__ f32x16 block_scores_ops(const bf16x8* kop, const bf16x8* qf, bool diag, int rel) {
   using C = AttnCfg<D, BLK>;
@@ -184,11 +195,7 @@ __device__ __forceinline__ f32x16 block_scores_ops(const bf16x8* kop, const bf16
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < C::KSTEPS; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[kk], s, 0, 0, 0);
-  if (diag) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (8 * (r >> 2) + (r & 3) > rel) s[r] = -INFINITY;
-  }
+  if (diag) causal_mask(s, rel);
   return s;
 }
 
@@ -298,9 +305,7 @@ __device__ __forceinline__ void stage_compute(SoftmaxState<D, BLK>& st, const ui
   for (int kb = 0; kb < NKB; ++kb) {
     bf16x8 vop[2 * C::DB];
     load_v_ops<D, BLK>(vop, Vc, kb);
-    int rel = rel0 - kb * 32;
-    asm volatile("" : "+v"(rel));  // keep the causal compares inside the loop
-    const f32x16 sc = block_scores_ops<D, BLK>(kop, qf, diag, rel);
+    const f32x16 sc = block_scores_ops<D, BLK>(kop, qf, diag, rel0 - kb * 32);
     if (kb + 1 < NKB) load_k_ops<D, BLK>(kop, Kc, kb + 1);
     __builtin_amdgcn_sched_barrier(0);
     block_softmax_pv_ops<D, BLK>(st, sc, vop, sl2);
@@ -340,7 +345,7 @@ struct PipeCfg {
   static constexpr int KT = AttnCfg<D, BLK>::KT;
   static constexpr int STAGES = BLK / KT;
   static constexpr int NBUF = HPW == 1 ? 2 : 3;  // one workgroup per CU has room for three
-  static constexpr int RING = NBUF + 1;          // row-id slots
+  static constexpr int RING = NBUF;              // row-id slots: stage y uses slot y % NBUF
   static constexpr int NDMA = 2 * KT / ((512 / D) * WAVES);  // gather instructions per wave per stage
   static constexpr int MAXNB = 2048;
 };
@@ -447,13 +452,22 @@ void attn_pipe_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t K0[KT * D];
   __shared__ __align__(16) uint16_t K1[KT * D];
   __shared__ __align__(16) uint16_t K2[NBUF > 2 ? KT * D : 8];
+  __shared__ __align__(16) uint16_t K3[NBUF > 3 ? KT * D : 8];
   __shared__ __align__(16) uint16_t V0[KT * D];
   __shared__ __align__(16) uint16_t V1[KT * D];
   __shared__ __align__(16) uint16_t V2[NBUF > 2 ? KT * D : 8];
+  __shared__ __align__(16) uint16_t V3[NBUF > 3 ? KT * D : 8];
   __shared__ uint32_t rowid[DENSE ? 1 : C::RING][KT];  // byte offsets of the gathered rows
   __shared__ uint32_t mlist[DENSE ? 1 : C::MAXNB];  // J | kept-by-head bits << 16
   __shared__ uint8_t selb[DENSE ? 1 : HPW * C::MAXNB];
   __shared__ int mcount;
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four stage buffers");
+  auto Kb = [&](int b) __attribute__((always_inline)) -> uint16_t* {
+    return b == 0 ? K0 : b == 1 ? K1 : b == 2 ? K2 : K3;
+  };
+  auto Vb = [&](int b) __attribute__((always_inline)) -> uint16_t* {
+    return b == 0 ? V0 : b == 1 ? V1 : b == 2 ? V2 : V3;
+  };
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
@@ -475,17 +489,13 @@ void attn_pipe_kernel(AttnArgs a) {
   // rows past N are never written by the gather: start from finite (zero) tiles
   {
     constexpr int NZ = KT * D * 2 / 16;
-    for (int i = t; i < NZ; i += C::THREADS) {
-      const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-      reinterpret_cast<u32x4*>(K0)[i] = z;
-      reinterpret_cast<u32x4*>(K1)[i] = z;
-      reinterpret_cast<u32x4*>(V0)[i] = z;
-      reinterpret_cast<u32x4*>(V1)[i] = z;
-      if (NBUF > 2) {
-        reinterpret_cast<u32x4*>(K2)[i] = z;
-        reinterpret_cast<u32x4*>(V2)[i] = z;
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+    for (int i = t; i < NZ; i += C::THREADS)
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        reinterpret_cast<u32x4*>(Kb(b))[i] = z;
+        reinterpret_cast<u32x4*>(Vb(b))[i] = z;
       }
-    }
   }
 
   bf16x8 qf[AttnCfg<D, BLK>::KSTEPS];
@@ -500,9 +510,9 @@ void attn_pipe_kernel(AttnArgs a) {
   const int nst = nblk * C::STAGES;
   const int sI = a.S > 0 ? I0 / a.S : 0;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
-  auto entry_of = [&](int s) -> uint32_t {
+  auto entry_of = [&](int s) -> uint32_t {  // wave-uniform
     const int u = s / C::STAGES;
-    return DENSE ? ((uint32_t)u | all_heads) : mlist[u];
+    return DENSE ? ((uint32_t)u | all_heads) : (uint32_t)__builtin_amdgcn_readfirstlane(mlist[u]);
   };
   const rsrc_t permr = make_rsrc(a.perm ? a.perm + (size_t)g * a.N : nullptr, a.perm ? (uint32_t)a.N * 4u : 0u);
   // lookup of row j of stage s (want = false: an unused lookup that reads nothing)
@@ -512,13 +522,18 @@ void attn_pipe_kernel(AttnArgs a) {
     return row_lookup(permr, p, a.N, want, !DENSE && a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI);
   };
   auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.kv_row_bytes, a.err); };
-  auto gather = [&](int s, uint16_t* Kd, uint16_t* Vd) {
+  // next row lookup, of stage x (issued one step before its row ids are stored)
+  auto lookup_ahead = [&](int x) -> RowLook { return lookup(x < nst ? x : 0, t & (KT - 1), x < nst && t < KT); };
+  // gather stage s into buffer b = s % NBUF (b is passed separately so that it folds to a constant)
+  auto gather = [&](int s, int b) __attribute__((always_inline)) {
+    uint16_t* Kd = Kb(b);
+    uint16_t* Vd = Vb(b);
     if (DENSE) {
       auto rf = [&](int j) { return row_off(lookup(s, j, true)); };
       dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, rf);
       dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, rf);
     } else {
-      const uint32_t* ids = rowid[s % C::RING];
+      const uint32_t* ids = rowid[b];
       auto rf = [&](int j) { return ids[j]; };
       dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES>(Kd, kr, rf);
       dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES>(Vd, vr, rf);
@@ -533,24 +548,32 @@ void attn_pipe_kernel(AttnArgs a) {
   st.m = -INFINITY;
   st.l = 0.f;
 
+  RowLook pr_prev = RowLook{kPastEnd, 0};  // lookup of stage s + NBUF, issued in step s - 1
   if (nst > 0) {
     if (!DENSE && t < KT)
       for (int x = 0; x < NBUF && x < nst; ++x) rowid[x][t] = row_off(lookup(x, t, true));
+    if (!DENSE) pr_prev = lookup_ahead(NBUF);
     __syncthreads();  // zero fill and row ids visible
-    gather(0, K0, V0);
-    if (nst > 1 && NBUF > 2) gather(1, K1, V1);
+#pragma unroll
+    for (int x = 0; x < NBUF - 1; ++x)
+      if (x < nst) gather(x, x);
     wait_vmcnt<0>();
     __syncthreads();
   }
 
-  // one pipeline step: compute stage s from (Kc, Vc) while stage s + NBUF - 1 is gathered into (Kd, Vd)
-  auto step = [&](int s, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kd, uint16_t* Vd) {
-    RowLook pr;
-    if (!DENSE) pr = lookup(s + NBUF < nst ? s + NBUF : 0, t & (KT - 1), s + NBUF < nst && t < KT);
+  // One pipeline step: compute stage s while stages s+1 .. s+NBUF-2 are in flight and stage
+  // s+NBUF-1 is gathered into the buffer of stage s-1.  The row ids of stage s+NBUF are stored from
+  // the lookup issued one step earlier, and the lookup of stage s+NBUF+1 is issued.
+  constexpr int LOOK = DENSE ? 0 : 1;  // lookup loads per wave per step
+  auto step = [&](int s, int b) __attribute__((always_inline)) {  // b = s % NBUF
+    const uint16_t* Kc = Kb(b);
+    const uint16_t* Vc = Vb(b);
+    RowLook pr_next;
+    if (!DENSE) pr_next = lookup_ahead(s + NBUF + 1);
     __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gathers (vmcnt order)
     const bool issue = s + NBUF - 1 < nst;
-    if (issue) gather(s + NBUF - 1, Kd, Vd);
-    const uint32_t e = entry_of(s);
+    if (issue) gather(s + NBUF - 1, (b + NBUF - 1) % NBUF);
+    const uint32_t e = s < nst ? entry_of(s) : 0u;
     if ((e >> (16 + hh)) & 1u) {
       const int J = (int)(e & 0xffffu);
       const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
@@ -560,26 +583,21 @@ void attn_pipe_kernel(AttnArgs a) {
       }
       stage_compute<D, BLK>(st, Kc, Vc, qf, J == I, qloc - koff - 4 * h2, a.sl2);
     }
-    if (!DENSE && s + NBUF < nst && t < KT) rowid[(s + NBUF) % C::RING][t] = row_off(pr);
-    // stage s + 1 must have landed; the newest stage's gathers may stay in flight
-    if (issue && NBUF > 2) {
-      wait_vmcnt<(NBUF - 2) * C::NDMA>();
+    if (!DENSE && s + NBUF < nst && t < KT) rowid[b][t] = row_off(pr_prev);  // slot of stage s+NBUF
+    if (!DENSE) pr_prev = pr_next;
+    // stage s + 1 must have landed; the loads of the NBUF - 2 newer steps may stay in flight
+    if (issue) {
+      wait_vmcnt<(NBUF - 2) * (C::NDMA + LOOK)>();
     } else {
       wait_vmcnt<0>();
     }
     lds_barrier();
   };
-  if constexpr (NBUF == 2) {
-    for (int s = 0; s < nst; s += 2) {
-      step(s, K0, V0, K1, V1);
-      if (s + 1 < nst) step(s + 1, K1, V1, K0, V0);
-    }
-  } else {
-    for (int s = 0; s < nst; s += 3) {
-      step(s, K0, V0, K2, V2);
-      if (s + 1 < nst) step(s + 1, K1, V1, K0, V0);
-      if (s + 2 < nst) step(s + 2, K2, V2, K1, V1);
-    }
+  // every trip runs all NBUF steps (the ones past the end only wait and synchronise), so the
+  // pending lookup passes from step to step without a copy that would wait for it
+  for (int s = 0; s < nst; s += NBUF) {
+#pragma unroll
+    for (int x = 0; x < NBUF; ++x) step(s + x, x);
   }
   write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
 }
@@ -605,11 +623,7 @@ __device__ __forceinline__ f32x16 tile_scores(const uint16_t* Ks, const bf16x8* 
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[k0 + kk], s, 0, 0, 0);
   }
-  if (diag) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (8 * (r >> 2) + (r & 3) > rel) s[r] = -INFINITY;
-  }
+  if (diag) causal_mask(s, rel);
   return s;
 }
 
@@ -763,7 +777,9 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   const int nblk = DENSE ? I + 1 : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
   const int sI = a.S > 0 ? I0 / a.S : 0;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
-  auto entry_of = [&](int u) -> uint32_t { return DENSE ? ((uint32_t)u | all_heads) : mlist[u]; };
+  auto entry_of = [&](int u) -> uint32_t {  // wave-uniform
+    return DENSE ? ((uint32_t)u | all_heads) : (uint32_t)__builtin_amdgcn_readfirstlane(mlist[u]);
+  };
   const rsrc_t permr = make_rsrc(a.perm ? a.perm + (size_t)g * a.N : nullptr, a.perm ? (uint32_t)a.N * 4u : 0u);
   // lookup of row j of block u (want = false: an unused lookup that reads nothing)
   auto lookup = [&](int u, int j, bool want) -> RowLook {
@@ -813,11 +829,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     float row_max = -INFINITY;
     if ((e >> (16 + hh)) & 1u) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        int rel = qloc - kb * 32 - 4 * h2;
-        asm volatile("" : "+v"(rel));  // keep the causal compares inside the loop
-        sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, rel);
-      }
+      for (int kb = 0; kb < KB; ++kb) sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, qloc - kb * 32 - 4 * h2);
       row_max = tile_row_max<KB>(sc);
     }
     const float wm = wave_max_f32(qvalid ? row_max : -INFINITY);
@@ -947,9 +959,7 @@ void attn_gated_kernel(AttnArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
-      int rel = qloc - kb * 32 - 4 * h2;
-      asm volatile("" : "+v"(rel));
-      sc[kb] = block_scores<D, BLK>(Ks, qf, kb, diag, rel);
+      sc[kb] = block_scores<D, BLK>(Ks, qf, kb, diag, qloc - kb * 32 - 4 * h2);
       mx = fmaxf(mx, block_row_max(sc[kb]));
     }
     if (MODE == MODE_TILE_MAX || !diag) {
