@@ -366,172 +366,220 @@ __global__ __launch_bounds__(POOL_THREADS) void pool_kernel(const uint16_t* src,
 }
 
 // =====================================================================================
-// Stage 2b: block selection.  One workgroup per (query block I, query head h):
-// z_J = c * Qbar . Kbar_J (J <= I), p = softmax(z) in fp64, bitonic sort on (p desc, J asc),
-// inclusive scan of the sorted p, k* = first prefix with mass >= tau, forced blocks, and an
-// ascending compaction of the kept set.
+// Stage 2b: pooled block logits (section 4, Block Selection).  z[h][I][J] = c * Qbar[h][I] . Kbar_J
+// for J <= I, Kbar_J the permuted pooled key when J's segment precedes I's, else the natural one.
+// One workgroup per (tile of TI consecutive query blocks inside one segment, group of up to 16
+// query heads of one KV head): its 16 pooled queries (TI rows x HC heads) form the A operand of
+// v_mfma_f64_16x16x4_f64, held in registers; each wave walks 16-key-block tiles of Kbar as the B
+// operand, so every pooled key row read serves 16 logits.
 // =====================================================================================
 
-constexpr int SEL_THREADS = 256;
-constexpr int SEL_MAX = 2048;
+constexpr int ZL_THREADS = 256;
 
-struct SelArgs {
+struct ZArgs {
   const double* qbar;   // [Hq][NB][d]
   const double* knat;   // [Hkv][NB][d]
   const double* kperm;  // [Hkv][NB][d] or NULL
   int NB, G, d, B, S;
-  double scale, tau;
+  int HC, TI;           // heads per workgroup, query blocks per workgroup (HC * TI <= 16)
+  int nhc;              // head groups per KV head
+  double scale;
+  double* z;            // [Hq][NB(NB+1)/2]
+};
+
+__global__ __launch_bounds__(ZL_THREADS) void block_logits_kernel(ZArgs a) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.y / a.nhc, hc = blockIdx.y % a.nhc;
+  const int I0 = blockIdx.x * a.TI;
+  const int nq = a.HC * a.TI;
+  // A operand row q = l16: head g*G + hc*HC + q / TI, query block I0 + q % TI
+  const int qh = g * a.G + hc * a.HC + l16 / a.TI;
+  const int qI = I0 + l16 % a.TI;
+  const bool qok = l16 < nq && qI < a.NB && hc * a.HC + l16 / a.TI < a.G;
+  const double* qrow = a.qbar + ((size_t)qh * a.NB + qI) * a.d;
+  const int Imax = min(I0 + a.TI, a.NB) - 1;
+  const int sI = a.S > 0 ? (I0 * a.B) / a.S : 0;
+  const int ksteps = a.d / 4;
+  double av[32];  // A operand for every k-step (d <= 128)
+#pragma unroll
+  for (int ks = 0; ks < 32; ++ks) av[ks] = (ks < ksteps && qok) ? qrow[ks * 4 + lg] : 0.0;
+  const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
+  for (int J0 = 16 * w; J0 <= Imax; J0 += 16 * (ZL_THREADS / 64)) {
+    const int J = J0 + l16;
+    const bool jok = J <= Imax;
+    const bool permuted = a.kperm != nullptr && a.S > 0 && (J * a.B) / a.S < sI;
+    const double* krow = (permuted ? a.kperm : a.knat) + ((size_t)g * a.NB + (jok ? J : 0)) * a.d;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      if (ks < ksteps) {
+        const double bv = jok ? krow[ks * 4 + lg] : 0.0;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bv, acc, 0, 0, 0);
+      }
+    }
+    // D: column J (lane l16), rows q = lg + 4 r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = lg + 4 * r;
+      const int h = g * a.G + hc * a.HC + q / a.TI;
+      const int I = I0 + q % a.TI;
+      if (q < nq && hc * a.HC + q / a.TI < a.G && I < a.NB && J <= I)
+        a.z[(size_t)h * ntri + (size_t)tri_offset(I) + J] = a.scale * acc[r];
+    }
+  }
+}
+
+// =====================================================================================
+// Stage 2c: block selection (section 4 with SampleAttention's cumulative-mass rule).  One wave per
+// (query head h, query block I): p = softmax(z) over J <= I in fp64; the kept set is the shortest
+// prefix of the order (p descending, J ascending) whose mass reaches tau.  Instead of sorting, the
+// wave finds the p value t* at which that prefix ends by bisection on the bit pattern of p (for
+// p >= 0 it orders like the value): t* is the largest value with mass(p >= t*) >= tau.  Every J with
+// p > t* is kept, and of the J with p == t* the smallest ones, as many as the mass still needs.
+// Then the forced blocks are added and the kept set is written in ascending J.
+// =====================================================================================
+
+constexpr int SEL_WAVES = 4;
+
+// Wave-wide fp64 sum / max through DPP row shifts and row broadcasts (no LDS round trips): an
+// inclusive scan inside each 16-lane row, then the row totals are carried across rows; lane 63 ends
+// with the result, which is read back as a scalar so every lane takes the same decision.
+__device__ __forceinline__ double dpp_f64(double x, int ctrl_kind) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  int lo = (int)(uint32_t)b, hi = (int)(uint32_t)(b >> 32);
+  switch (ctrl_kind) {  // dpp_ctrl, row_mask, bank_mask, bound_ctrl (reads past a row give 0)
+    case 1: lo = __builtin_amdgcn_update_dpp(0, lo, 0x111, 0xf, 0xf, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x111, 0xf, 0xf, true); break;
+    case 2: lo = __builtin_amdgcn_update_dpp(0, lo, 0x112, 0xf, 0xf, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x112, 0xf, 0xf, true); break;
+    case 4: lo = __builtin_amdgcn_update_dpp(0, lo, 0x114, 0xf, 0xf, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x114, 0xf, 0xf, true); break;
+    case 8: lo = __builtin_amdgcn_update_dpp(0, lo, 0x118, 0xf, 0xf, true); hi = __builtin_amdgcn_update_dpp(0, hi, 0x118, 0xf, 0xf, true); break;
+    case 15: lo = __builtin_amdgcn_update_dpp(0, lo, 0x142, 0xa, 0xf, false); hi = __builtin_amdgcn_update_dpp(0, hi, 0x142, 0xa, 0xf, false); break;
+    default: lo = __builtin_amdgcn_update_dpp(0, lo, 0x143, 0xc, 0xf, false); hi = __builtin_amdgcn_update_dpp(0, hi, 0x143, 0xc, 0xf, false); break;
+  }
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__device__ __forceinline__ double wave_total_f64(double x) {
+  x += dpp_f64(x, 1);
+  x += dpp_f64(x, 2);
+  x += dpp_f64(x, 4);
+  x += dpp_f64(x, 8);
+  x += dpp_f64(x, 15);
+  x += dpp_f64(x, 31);
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, 63), hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+struct SelArgs {
+  const double* z;  // [Hq][NB(NB+1)/2]
+  int NB, Hq;
+  double tau;
   uint32_t flags;
   int32_t* count;
   int32_t* idx;
   double* prob;
 };
 
-__device__ __forceinline__ double block_reduce_max(double x, double* sh) {
-  x = wave_max_f64(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = x;
-  __syncthreads();
-  return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
-}
-
-__device__ __forceinline__ double block_reduce_sum(double x, double* sh) {
-  x = wave_sum_f64(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = x;
-  __syncthreads();
-  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
-}
-
-__global__ __launch_bounds__(SEL_THREADS) void block_select_kernel(SelArgs a) {
-  __shared__ double qb[128];
-  __shared__ double pv[SEL_MAX];     // z, then p (by J), then the inclusive scan (by rank)
-  __shared__ uint64_t key[SEL_MAX];  // ~bits(p), sorted ascending
-  __shared__ uint16_t jid[SEL_MAX];
-  __shared__ uint8_t sel[SEL_MAX];
-  __shared__ double red[4];
-  __shared__ int kstar_sh;
-  const int I = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int g = h / a.G;
+template <int SEL_PL>  // values per lane: 64 * SEL_PL >= NB
+__global__ __launch_bounds__(SEL_WAVES * 64) void block_select_kernel(SelArgs a) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x * SEL_WAVES + w;
+  if (row >= a.Hq * a.NB) return;
+  const int h = row / a.NB, I = a.NB - 1 - row % a.NB;  // long rows first
   const int nJ = I + 1;
-  const int sI = (a.S > 0) ? (I * a.B) / a.S : 0;
-  if (t < a.d) qb[t] = a.qbar[((size_t)h * a.NB + I) * a.d + t];
-  __syncthreads();
-  // pooled logits, one wave per J
-  for (int J = w; J < nJ; J += SEL_THREADS / 64) {
-    const bool permuted = a.kperm && (((J * a.B) / a.S) < sI);
-    const double* kb = (permuted ? a.kperm : a.knat) + ((size_t)g * a.NB + J) * a.d;
-    double s = 0.0;
-    for (int e = lane; e < a.d; e += 64) s = fma(qb[e], kb[e], s);
-    s = wave_sum_f64(s);
-    if (lane == 0) pv[J] = a.scale * s;
-  }
-  __syncthreads();
-  double m = -INFINITY;
-  for (int J = t; J < nJ; J += SEL_THREADS) m = fmax(m, pv[J]);
-  m = block_reduce_max(m, red);
-  double se = 0.0;
-  for (int J = t; J < nJ; J += SEL_THREADS) {
-    const double e = exp(pv[J] - m);
-    pv[J] = e;
-    se += e;
-  }
-  se = block_reduce_sum(se, red);
-  int n = 1;
-  while (n < nJ) n <<= 1;
+  const int npl = (nJ + 63) / 64;
   const size_t tri = (size_t)h * ((size_t)a.NB * (a.NB + 1) / 2) + (size_t)tri_offset(I);
-  for (int J = t; J < n; J += SEL_THREADS) {
+  double v[SEL_PL];
+  double m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < SEL_PL; ++i) {
+    const int J = lane + 64 * i;
+    v[i] = (i < npl && J < nJ) ? a.z[tri + J] : -INFINITY;
+    m = fmax(m, v[i]);
+  }
+  m = wave_max_f64(m);
+  double se = 0.0;
+#pragma unroll
+  for (int i = 0; i < SEL_PL; ++i) {
+    if (i < npl) {
+      v[i] = (v[i] > -INFINITY) ? exp(v[i] - m) : 0.0;
+      se += v[i];
+    }
+  }
+  se = wave_sum_f64(se);
+#pragma unroll
+  for (int i = 0; i < SEL_PL; ++i) {
+    if (i < npl) {
+      v[i] = v[i] / se;
+      const int J = lane + 64 * i;
+      if (a.prob && J < nJ) a.prob[tri + J] = v[i];
+    }
+  }
+  // mass of the values whose bit pattern is >= t (wave-uniform: butterfly sums agree on every lane)
+  auto mass_ge = [&](uint64_t thr) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < SEL_PL; ++i)
+      if (i < npl && (uint64_t)__double_as_longlong(v[i]) >= thr) s += v[i];
+    return wave_total_f64(s);
+  };
+  uint64_t tstar = 0;     // keep every J (tau >= 1, or the mass never reaches tau)
+  bool all = true;
+  int ntie_keep = 0;      // J with p == t* that are kept, smallest J first
+  if (a.tau < 1.0 && mass_ge(0) >= a.tau) {
+    all = false;
+    for (int bit = 62; bit >= 0; --bit) {
+      const uint64_t cand = tstar | (1ull << bit);
+      if (mass_ge(cand) >= a.tau) tstar = cand;
+    }
+    // mass strictly above t*, and how many of the tied values it still needs (at most all of them,
+    // whatever the rounding of the running sum)
+    double above = 0.0;
+    int ntied = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_PL; ++i) {
+      if (i < npl) {
+        const uint64_t key = (uint64_t)__double_as_longlong(v[i]);
+        if (key > tstar) above += v[i];
+        if (key == tstar && lane + 64 * i < nJ) ++ntied;
+      }
+    }
+    above = wave_total_f64(above);
+    ntied = (int)wave_total_f64((double)ntied);
+    const double pt = __longlong_as_double((long long)tstar);
+    double c = above;
+    do {
+      c += pt;
+      ++ntie_keep;
+    } while (c < a.tau && ntie_keep < ntied);
+  }
+  // kept flags, then ascending compaction
+  int base = 0, tie_seen = 0;
+  for (int i = 0; i < npl; ++i) {
+    const int J = lane + 64 * i;
+    const uint64_t key = (uint64_t)__double_as_longlong(v[i]);
+    bool keep = false;
     if (J < nJ) {
-      const double p = pv[J] / se;
-      if (a.prob) a.prob[tri + J] = p;
-      key[J] = ~(uint64_t)__double_as_longlong(p > 0.0 ? p : 0.0);
-      jid[J] = (uint16_t)J;
-      sel[J] = 0;
-    } else {
-      key[J] = ~0ull;
-      jid[J] = 0xffffu;
+      if (all || key > tstar) keep = true;
+      if ((a.flags & 1u) && J == I) keep = true;
+      if ((a.flags & 2u) && J == 0) keep = true;
     }
+    const bool tie = !all && J < nJ && key == tstar;
+    const unsigned long long tb = __ballot(tie);
+    if (tie && tie_seen + __popcll(tb & ((1ull << lane) - 1ull)) < ntie_keep) keep = true;
+    tie_seen += __popcll(tb);
+    const unsigned long long kb = __ballot(keep);
+    if (keep) a.idx[tri + base + __popcll(kb & ((1ull << lane) - 1ull))] = J;
+    base += __popcll(kb);
   }
-  __syncthreads();
-  for (int kk = 2; kk <= n; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int x = t; x < n; x += SEL_THREADS) {
-        const int y = x ^ j;
-        if (y > x) {
-          const uint64_t kx = key[x], ky = key[y];
-          const uint16_t ox = jid[x], oy = jid[y];
-          const bool gt = (kx > ky) || (kx == ky && ox > oy);
-          if (gt == ((x & kk) == 0)) {
-            key[x] = ky;
-            key[y] = kx;
-            jid[x] = oy;
-            jid[y] = ox;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  int kstar = nJ;
-  if (a.tau < 1.0) {
-    // inclusive scan of the sorted probabilities (Hillis-Steele, values staged in registers)
-    constexpr int PER = SEL_MAX / SEL_THREADS;
-    double vals[PER];
-    for (int x = 0; x < PER; ++x) {
-      const int r = t + x * SEL_THREADS;
-      vals[x] = (r < nJ) ? __longlong_as_double((long long)~key[r]) : 0.0;
-      if (r < n) pv[r] = vals[x];
-    }
-    __syncthreads();
-    for (int o = 1; o < n; o <<= 1) {
-      double add[PER];
-      for (int x = 0; x < PER; ++x) {
-        const int r = t + x * SEL_THREADS;
-        add[x] = (r < n && r >= o) ? pv[r - o] : 0.0;
-      }
-      __syncthreads();
-      for (int x = 0; x < PER; ++x) {
-        const int r = t + x * SEL_THREADS;
-        if (r < n) pv[r] += add[x];
-      }
-      __syncthreads();
-    }
-    if (t == 0) kstar_sh = nJ;
-    __syncthreads();
-    int first = nJ;
-    for (int r = t; r < nJ; r += SEL_THREADS)
-      if (pv[r] >= a.tau) first = min(first, r + 1);
-    if (first < nJ) atomicMin(&kstar_sh, first);
-    __syncthreads();
-    kstar = kstar_sh;
-  }
-  for (int r = t; r < kstar; r += SEL_THREADS) sel[jid[r]] = 1;
-  __syncthreads();
-  if (t == 0) {
-    if (a.flags & 1u) sel[I] = 1;
-    if (a.flags & 2u) sel[0] = 1;
-  }
-  __syncthreads();
-  if (w == 0) {
-    int base = 0;
-    for (int J0 = 0; J0 < nJ; J0 += 64) {
-      const int J = J0 + lane;
-      const bool f = (J < nJ) && sel[J];
-      const unsigned long long bal = __ballot(f);
-      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-      if (f) a.idx[tri + pos] = J;
-      base += __popcll(bal);
-    }
-    if (lane == 0) a.count[(size_t)h * a.NB + I] = base;
-  }
+  if (lane == 0) a.count[(size_t)h * a.NB + I] = base;
 }
 
 size_t mask_workspace_bytes(const Geometry& g) {
   const size_t NB = g.NB;
-  return align256(sizeof(double) * g.Hq * NB * g.d) + 2 * align256(sizeof(double) * g.Hkv * NB * g.d);
+  return align256(sizeof(double) * g.Hq * NB * g.d) + 2 * align256(sizeof(double) * g.Hkv * NB * g.d) +
+         align256(sizeof(double) * g.Hq * (NB * (NB + 1) / 2));
 }
 
 hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_t* k, const int32_t* perm,
@@ -543,26 +591,55 @@ hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_
   double* knat = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * (size_t)g.NB * g.d);
   double* kperm = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * (size_t)g.NB * g.d);
+  double* z = reinterpret_cast<double*>(p);
   pool_kernel<<<dim3(g.NB, g.Hq), POOL_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.B, g.d, nullptr, qbar, g.NB);
   pool_kernel<<<dim3(g.NB, g.Hkv), POOL_THREADS, 0, st>>>(k, g.kvsh, g.kvst, g.N, g.B, g.d, nullptr, knat, g.NB);
   if (perm)
     pool_kernel<<<dim3(g.NB, g.Hkv), POOL_THREADS, 0, st>>>(k, g.kvsh, g.kvst, g.N, g.B, g.d, perm, kperm, g.NB);
+  ZArgs za;
+  za.qbar = qbar;
+  za.knat = knat;
+  za.kperm = perm ? kperm : nullptr;
+  za.NB = g.NB;
+  za.G = g.G;
+  za.d = g.d;
+  za.B = g.B;
+  za.S = g.S;
+  za.HC = g.G < 16 ? g.G : 16;
+  za.nhc = (g.G + za.HC - 1) / za.HC;
+  // query blocks per workgroup: as many as fit 16 rows, never crossing a segment boundary
+  const int bps = g.S > 0 ? g.S / g.B : 0;
+  int ti = 16 / za.HC;
+  while (ti > 1 && bps > 0 && bps % ti != 0) ti >>= 1;
+  za.TI = ti < 1 ? 1 : ti;
+  za.scale = g.scale64;
+  za.z = z;
+  block_logits_kernel<<<dim3((g.NB + za.TI - 1) / za.TI, g.Hkv * za.nhc), ZL_THREADS, 0, st>>>(za);
   SelArgs a;
-  a.qbar = qbar;
-  a.knat = knat;
-  a.kperm = perm ? kperm : nullptr;
+  a.z = z;
   a.NB = g.NB;
-  a.G = g.G;
-  a.d = g.d;
-  a.B = g.B;
-  a.S = g.S;
-  a.scale = g.scale64;
+  a.Hq = g.Hq;
   a.tau = tau;
   a.flags = flags;
   a.count = count;
   a.idx = idx;
   a.prob = prob;
-  block_select_kernel<<<dim3(g.NB, g.Hq), SEL_THREADS, 0, st>>>(a);
+  const int rows = g.Hq * g.NB;
+  const int grid = (rows + SEL_WAVES - 1) / SEL_WAVES;
+  if (g.NB <= 64) {
+    block_select_kernel<1><<<grid, SEL_WAVES * 64, 0, st>>>(a);
+  } else if (g.NB <= 128) {
+    block_select_kernel<2><<<grid, SEL_WAVES * 64, 0, st>>>(a);
+  } else if (g.NB <= 256) {
+    block_select_kernel<4><<<grid, SEL_WAVES * 64, 0, st>>>(a);
+  } else if (g.NB <= 512) {
+    block_select_kernel<8><<<grid, SEL_WAVES * 64, 0, st>>>(a);
+  } else if (g.NB <= 1024) {
+    block_select_kernel<16><<<grid, SEL_WAVES * 64, 0, st>>>(a);
+  } else {
+    block_select_kernel<32><<<grid, SEL_WAVES * 64, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
