@@ -20,6 +20,9 @@ HIPCC_FLAGS = [
     "-shared",
     # packed fp32 VALU forms are kept out of generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators stay in VGPRs: the fp64 kernels otherwise move every accumulator between
+    # the AGPR and VGPR files around each MFMA
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

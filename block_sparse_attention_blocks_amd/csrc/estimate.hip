@@ -24,14 +24,15 @@ namespace pbsa {
 // so every logit is computed once and exponentiated once.
 // =====================================================================================
 
-constexpr int IMP_CK = 64;        // keys per workgroup (4 MFMA tiles of 16)
-constexpr int IMP_RT = 64;        // proxy rows per inner tile (4 waves x 16 rows)
+constexpr int IMP_CK = 64;        // keys per chunk (4 MFMA column tiles of 16)
+constexpr int IMP_RT = 64;        // proxy rows per workgroup (4 waves x 16 rows)
 constexpr int IMP_THREADS = 256;
-constexpr int IMP_PITCH = 132;    // fp32 LDS row pitch: 16 rows x 4 k hit 64 distinct banks
+constexpr int IMP_KR = 16;        // chunks per workgroup
 constexpr int COL_KEYS = 256;     // keys per workgroup of imp_colsum
 constexpr int COL_ROWS = 256;     // rows staged per pass of imp_colsum
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 struct ImpWs {
   double* e;       // [Hkv][R][N] chunk-normalised exponentials
@@ -42,6 +43,10 @@ struct ImpWs {
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workgroup barrier that waits for this wave's LDS operations only (__syncthreads() would also wait
+// for every outstanding global store).
+__device__ __forceinline__ void lds_barrier_est() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 static inline int imp_rows(const Geometry& g) { return g.G * (g.N < g.B ? g.N : g.B); }
 static inline int imp_chunks(const Geometry& g) { return (g.N + IMP_CK - 1) / IMP_CK; }
@@ -82,128 +87,215 @@ __device__ __forceinline__ void imp_row(const ImpArgs& a, int g, int r, int* h, 
   *i = a.N - a.R1 + r % a.R1;
 }
 
-// One bf16 row (d values, 16-byte chunks) widened to fp32 into LDS; zeros when src is null.
-__device__ __forceinline__ void imp_row_to_lds(float* dst, const uint16_t* src, int cc) {
-  u32x4 raw = {0u, 0u, 0u, 0u};
-  if (src) raw = *reinterpret_cast<const u32x4*>(src + cc * 8);
-  f32x4 lo = {bf16_bits_to_f32(raw[0] & 0xffffu), bf16_bits_to_f32(raw[0] >> 16), bf16_bits_to_f32(raw[1] & 0xffffu),
-              bf16_bits_to_f32(raw[1] >> 16)};
-  f32x4 hi = {bf16_bits_to_f32(raw[2] & 0xffffu), bf16_bits_to_f32(raw[2] >> 16), bf16_bits_to_f32(raw[3] & 0xffffu),
-              bf16_bits_to_f32(raw[3] >> 16)};
-  *reinterpret_cast<f32x4*>(dst + cc * 8) = lo;
-  *reinterpret_cast<f32x4*>(dst + cc * 8 + 4) = hi;
+// DPP row rotation of a double (16-lane rows): all-reduce helpers for the 16 lanes of one row.
+template <int N>
+__device__ __forceinline__ double row_ror_f64(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x120 + N, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x120 + N, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+__device__ __forceinline__ double row_max_f64(double x) {
+  x = fmax(x, row_ror_f64<1>(x));
+  x = fmax(x, row_ror_f64<2>(x));
+  x = fmax(x, row_ror_f64<4>(x));
+  return fmax(x, row_ror_f64<8>(x));
+}
+__device__ __forceinline__ double row_sum_f64(double x) {  // exact on lane 0 of the row's order
+  x += row_ror_f64<1>(x);
+  x += row_ror_f64<2>(x);
+  x += row_ror_f64<4>(x);
+  return x + row_ror_f64<8>(x);
 }
 
-// v_mfma_f64_16x16x4_f64 layouts (lane l): A holds row l%16, k = l/16; B holds column l%16,
-// k = l/16; D holds column l%16, rows l/16 + 4 r in its four doubles r = 0..3.
+// 16-byte chunk swizzle of a staged key row: the 16 rows a wave reads together hit distinct banks.
+__device__ __forceinline__ int imp_swz(int row, int cpr) { return cpr == 16 ? (row & 15) : ((row >> 1) & 7); }
+
+// v_mfma_f64_16x16x4_f64 (lane l): A holds row l%16 and B column l%16 at contraction slot l/16; D
+// holds column l%16, rows l/16 + 4 r in its four doubles r = 0..3.  The contraction index is
+// assigned as k = (l/16) * (d/4) + ks for MFMA step ks, so every lane reads a contiguous run of a
+// row.  Each wave keeps the A operand (its 16 proxy rows, all of d) in registers for the whole
+// workgroup; the key chunks stream through LDS (prefetched into registers one chunk ahead).
+template <int D>
 __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, double* E, double* part_m,
                                                                  double* part_l) {
-  __shared__ __align__(16) float Kt[IMP_CK * IMP_PITCH];
-  __shared__ __align__(16) float Qt[IMP_RT * IMP_PITCH];
-  __shared__ int qi_s[IMP_RT];
-  const int chunk = blockIdx.x, g = blockIdx.y, nchunk = gridDim.x;
+  __shared__ __align__(16) uint16_t Ks[2][IMP_CK * D];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int j0 = chunk * IMP_CK;
-  const int cpr = a.d / 8;  // 16-byte chunks per row
-  for (int c = t; c < IMP_CK * cpr; c += IMP_THREADS) {
-    const int row = c / cpr, j = j0 + row;
-    imp_row_to_lds(Kt + row * IMP_PITCH, j < a.N ? a.k + (int64_t)g * a.kvsh + (int64_t)j * a.kvst : nullptr,
-                   c % cpr);
-  }
-  const int ksteps = a.d / 4;
-  for (int r0 = 0; r0 < a.R; r0 += IMP_RT) {
-    __syncthreads();  // previous Q tile consumed (and K tile written, first time)
-    for (int c = t; c < IMP_RT * cpr; c += IMP_THREADS) {
-      const int row = c / cpr, r = r0 + row;
-      const uint16_t* src = nullptr;
-      if (r < a.R) {
-        int h, i;
-        imp_row(a, g, r, &h, &i);
-        src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst;
-        if (c % cpr == 0) qi_s[row] = i;
-      } else if (c % cpr == 0) {
-        qi_s[row] = -1;
-      }
-      imp_row_to_lds(Qt + row * IMP_PITCH, src, c % cpr);
-    }
-    __syncthreads();
-    f64x4 acc[4];
+  const int r0 = blockIdx.x * IMP_RT, g = blockIdx.z;
+  const int nchunk = (a.N + IMP_CK - 1) / IMP_CK;
+  const int c0 = blockIdx.y * IMP_KR, c1 = min(c0 + IMP_KR, nchunk);
+  constexpr int kq = D / 4;   // contraction slots per lane (32 or 16)
+  constexpr int cpr = D / 8;  // 16-byte chunks per row
+  const uint16_t* kbase = a.k + (int64_t)g * a.kvsh;
+
+  // A operand: proxy row r = r0 + 16 w + l16, contraction slots lg*kq .. lg*kq + kq - 1
+  const int ra = r0 + 16 * w + l16;
+  double av[kq];
+  {
+    u32x4 raw[kq / 8] = {};
+    if (ra < a.R) {
+      int h, i;
+      imp_row(a, g, ra, &h, &i);
+      const uint16_t* src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst + lg * kq;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = f64x4{0.0, 0.0, 0.0, 0.0};
-    const float* qa = Qt + (16 * w + l16) * IMP_PITCH + lg;
-    const float* kb = Kt + l16 * IMP_PITCH + lg;
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const double av = (double)qa[ks * 4];
+      for (int c = 0; c < kq / 8; ++c) raw[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
+    }
+#pragma unroll
+    for (int x = 0; x < kq; ++x) {
+      const uint32_t wd = raw[x / 8][(x / 2) % 4];
+      av[x] = (double)bf16_bits_to_f32((x & 1) ? (wd >> 16) : (wd & 0xffffu));
+    }
+  }
+  // this lane's D rows (proxy rows r0 + 16 w + lg + 4 rr) and their query positions
+  int qi[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int r = r0 + 16 * w + lg + 4 * rr;
+    int h, i;
+    imp_row(a, g, r, &h, &i);
+    qi[rr] = r < a.R ? i : -1;
+  }
+  // staging of chunk c: thread t copies 16-byte chunks t, t + 256, ... (row = x / cpr)
+  auto prefetch = [&](int c, u32x4* pf) {
+    const int j0 = c * IMP_CK;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int idx = t + x * IMP_THREADS;
+      const int row = idx / cpr, ch = idx % cpr;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row < IMP_CK && j0 + row < a.N) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(j0 + row) * a.kvst + ch * 8);
+      pf[x] = v;
+    }
+  };
+  auto stage = [&](uint16_t* dst, const u32x4* pf) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int idx = t + x * IMP_THREADS;
+      const int row = idx / cpr, ch = idx % cpr;
+      if (row < IMP_CK) *reinterpret_cast<u32x4*>(dst + row * D + ((ch ^ imp_swz(row, cpr)) * 8)) = pf[x];
+    }
+  };
+  u32x4 pf[4];
+  prefetch(c0, pf);
+  stage(Ks[0], pf);
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    const uint16_t* Kc = Ks[(c - c0) & 1];
+    if (c + 1 < c1) prefetch(c + 1, pf);
+    // B operand: key 16 tt + l16 of the chunk, slots lg*kq ..: kq bf16 = kq/8 swizzled chunks; the
+    // four column tiles are interleaved so that four independent accumulation chains are in flight
+    f64x4 acc[4];
+    u32x4 kb[4][kq / 8];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      acc[tt] = f64x4{0.0, 0.0, 0.0, 0.0};
+      const int row = 16 * tt + l16;
+#pragma unroll
+      for (int q = 0; q < kq / 8; ++q)
+        kb[tt][q] = *reinterpret_cast<const u32x4*>(Kc + row * D + (((lg * kq / 8 + q) ^ imp_swz(row, cpr)) * 8));
+    }
+#pragma unroll
+    for (int ks = 0; ks < kq; ++ks)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const double bv = (double)kb[tt * 16 * IMP_PITCH + ks * 4];
-        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[tt], 0, 0, 0);
+        const uint32_t wd = kb[tt][ks / 8][(ks / 2) % 4];
+        const double bv = (double)bf16_bits_to_f32((ks & 1) ? (wd >> 16) : (wd & 0xffffu));
+        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bv, acc[tt], 0, 0, 0);
       }
-    }
+    // per proxy row: chunk max, sum of exponentials, and the exponentials themselves
+    const int j0 = c * IMP_CK;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int row = 16 * w + lg + 4 * rr;
-      const int i = qi_s[row];
-      double s[4];
+      const int i = qi[rr];
+      double sv[4];
       double m = -INFINITY;
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int j = j0 + 16 * tt + l16;
         const bool ok = (i >= 0) && (j < a.N) && (j <= i);
-        s[tt] = ok ? a.scale * acc[tt][rr] : -INFINITY;
-        m = fmax(m, s[tt]);
+        sv[tt] = ok ? a.scale * acc[tt][rr] : -INFINITY;
+        m = fmax(m, sv[tt]);
       }
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 16));
+      m = row_max_f64(m);
       double l = 0.0;
-      double e[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        e[tt] = (s[tt] > -INFINITY) ? exp(s[tt] - m) : 0.0;
-        l += e[tt];
+        sv[tt] = (sv[tt] > -INFINITY) ? exp(sv[tt] - m) : 0.0;
+        l += sv[tt];
       }
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) l += __shfl_xor(l, o, 16);
-      const int r = r0 + row;
+      l = row_sum_f64(l);
+      const int r = r0 + 16 * w + lg + 4 * rr;
       if (r < a.R) {
         double* er = E + ((size_t)g * a.R + r) * a.N;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int j = j0 + 16 * tt + l16;
-          if (j < a.N) er[j] = e[tt];
+          if (j < a.N) er[j] = sv[tt];
         }
         if (l16 == 0) {
-          const size_t o = ((size_t)g * nchunk + chunk) * a.R + r;
+          const size_t o = ((size_t)g * nchunk + c) * a.R + r;
           part_m[o] = m;
           part_l[o] = l;
         }
       }
     }
+    if (c + 1 < c1) stage(Ks[(c + 1 - c0) & 1], pf);
+    lds_barrier_est();
   }
 }
 
+// lse_r = M + log sum_c l_cr exp(m_cr - M) for 8 proxy rows per workgroup: thread t takes row
+// r0 + t % 8 and every 32nd chunk from t / 8, so one load instruction reads 8 consecutive rows of
+// 32 chunks; four chunks are loaded before any is used.
+constexpr int LSE_ROWS = 8, LSE_CG = 32;
 __global__ __launch_bounds__(256) void imp_lse_kernel(const double* part_m, const double* part_l, int nchunk,
                                                       int R, double* lse) {
-  __shared__ double sm[4], sl[4];
-  const int r = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  __shared__ double sm[LSE_CG][LSE_ROWS], sl[LSE_CG][LSE_ROWS];
+  const int t = threadIdx.x, rl = t % LSE_ROWS, cg = t / LSE_ROWS;
+  const int r = blockIdx.x * LSE_ROWS + rl, g = blockIdx.y;
+  const bool ok = r < R;
   const double* pm = part_m + (size_t)g * nchunk * R + r;
   const double* pl = part_l + (size_t)g * nchunk * R + r;
+  constexpr int U = 4;
   double m = -INFINITY;
-  for (int c = t; c < nchunk; c += 256) m = fmax(m, pm[(size_t)c * R]);
-  m = wave_max_f64(m);
-  if ((t & 63) == 0) sm[t >> 6] = m;
+  if (ok)
+    for (int c0 = cg; c0 < nchunk; c0 += U * LSE_CG) {
+      double x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * LSE_CG;
+        x[u] = c < nchunk ? pm[(size_t)c * R] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) m = fmax(m, x[u]);
+    }
+  sm[cg][rl] = m;
   __syncthreads();
-  m = fmax(fmax(sm[0], sm[1]), fmax(sm[2], sm[3]));
+  m = -INFINITY;
+#pragma unroll 8
+  for (int k = 0; k < LSE_CG; ++k) m = fmax(m, sm[k][rl]);
   double l = 0.0;
-  for (int c = t; c < nchunk; c += 256) {
-    const double mc = pm[(size_t)c * R];
-    if (mc > -INFINITY) l += pl[(size_t)c * R] * exp(mc - m);
-  }
-  l = wave_sum_f64(l);
-  if ((t & 63) == 0) sl[t >> 6] = l;
+  if (ok)
+    for (int c0 = cg; c0 < nchunk; c0 += U * LSE_CG) {
+      double x[U], y[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * LSE_CG;
+        x[u] = c < nchunk ? pm[(size_t)c * R] : -INFINITY;
+        y[u] = c < nchunk ? pl[(size_t)c * R] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (x[u] > -INFINITY) l += y[u] * exp(x[u] - m);
+    }
+  sl[cg][rl] = l;
   __syncthreads();
-  if (t == 0) lse[(size_t)g * R + r] = m + log((sl[0] + sl[1]) + (sl[2] + sl[3]));
+  if (cg == 0 && ok) {
+    double tot = 0.0;
+    for (int k = 0; k < LSE_CG; ++k) tot += sl[k][rl];
+    lse[(size_t)g * R + r] = m + log(tot);
+  }
 }
 
 // imp_j = (1/R) sum_r e_rj * exp(m_c(j)r - lse_r), rows summed in order.
@@ -255,8 +347,14 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
   a.kvst = g.kvst;
   a.scale = g.scale64;
   const int nchunk = imp_chunks(g);
-  imp_scores_kernel<<<dim3(nchunk, g.Hkv), IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
-  imp_lse_kernel<<<dim3(a.R, g.Hkv), 256, 0, st>>>(w.part_m, w.part_l, nchunk, a.R, w.lse);
+  const dim3 grid((a.R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
+  if (g.d == 128) {
+    imp_scores_kernel<128><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
+  } else {
+    imp_scores_kernel<64><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
+  }
+  imp_lse_kernel<<<dim3((a.R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(w.part_m, w.part_l, nchunk, a.R,
+                                                                                 w.lse);
   imp_colsum_kernel<<<dim3((g.N + COL_KEYS - 1) / COL_KEYS, g.Hkv), COL_KEYS, 0, st>>>(w.e, w.part_m, w.lse, g.N,
                                                                                        a.R, nchunk, out);
   return hipGetLastError();
@@ -387,6 +485,7 @@ struct ZArgs {
   double* z;            // [Hq][NB(NB+1)/2]
 };
 
+template <int D>
 __global__ __launch_bounds__(ZL_THREADS) void block_logits_kernel(ZArgs a) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -397,27 +496,37 @@ __global__ __launch_bounds__(ZL_THREADS) void block_logits_kernel(ZArgs a) {
   const int qh = g * a.G + hc * a.HC + l16 / a.TI;
   const int qI = I0 + l16 % a.TI;
   const bool qok = l16 < nq && qI < a.NB && hc * a.HC + l16 / a.TI < a.G;
-  const double* qrow = a.qbar + ((size_t)qh * a.NB + qI) * a.d;
+  const double* qrow = a.qbar + ((size_t)qh * a.NB + qI) * D;
   const int Imax = min(I0 + a.TI, a.NB) - 1;
   const int sI = a.S > 0 ? (I0 * a.B) / a.S : 0;
-  const int ksteps = a.d / 4;
-  double av[32];  // A operand for every k-step (d <= 128)
+  // contraction slot of lane group lg at MFMA step ks: k = lg * ksteps + ks, so every lane reads a
+  // contiguous run of its row (16-byte loads)
+  constexpr int ksteps = D / 4;
+  double av[ksteps];  // A operand for every k-step
 #pragma unroll
-  for (int ks = 0; ks < 32; ++ks) av[ks] = (ks < ksteps && qok) ? qrow[ks * 4 + lg] : 0.0;
+  for (int ks = 0; ks < ksteps; ks += 2) {
+    f64x2 x = {0.0, 0.0};
+    if (qok) x = *reinterpret_cast<const f64x2*>(qrow + lg * ksteps + ks);
+    av[ks] = x[0];
+    av[ks + 1] = x[1];
+  }
   const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
   for (int J0 = 16 * w; J0 <= Imax; J0 += 16 * (ZL_THREADS / 64)) {
     const int J = J0 + l16;
     const bool jok = J <= Imax;
     const bool permuted = a.kperm != nullptr && a.S > 0 && (J * a.B) / a.S < sI;
-    const double* krow = (permuted ? a.kperm : a.knat) + ((size_t)g * a.NB + (jok ? J : 0)) * a.d;
+    // (columns past Imax read row 0, a valid row, and are never stored)
+    const double* krow = (permuted ? a.kperm : a.knat) + ((size_t)g * a.NB + (jok ? J : 0)) * D;
+    double bv[ksteps];  // all loads issued before the first MFMA waits on one
+#pragma unroll
+    for (int ks = 0; ks < ksteps; ks += 2) {
+      const f64x2 x = *reinterpret_cast<const f64x2*>(krow + lg * ksteps + ks);
+      bv[ks] = x[0];
+      bv[ks + 1] = x[1];
+    }
     f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) {
-      if (ks < ksteps) {
-        const double bv = jok ? krow[ks * 4 + lg] : 0.0;
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bv, acc, 0, 0, 0);
-      }
-    }
+    for (int ks = 0; ks < ksteps; ++ks) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bv[ks], acc, 0, 0, 0);
     // D: column J (lane l16), rows q = lg + 4 r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -615,7 +724,12 @@ hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_
   za.TI = ti < 1 ? 1 : ti;
   za.scale = g.scale64;
   za.z = z;
-  block_logits_kernel<<<dim3((g.NB + za.TI - 1) / za.TI, g.Hkv * za.nhc), ZL_THREADS, 0, st>>>(za);
+  const dim3 zgrid((g.NB + za.TI - 1) / za.TI, g.Hkv * za.nhc);
+  if (g.d == 128) {
+    block_logits_kernel<128><<<zgrid, ZL_THREADS, 0, st>>>(za);
+  } else {
+    block_logits_kernel<64><<<zgrid, ZL_THREADS, 0, st>>>(za);
+  }
   SelArgs a;
   a.z = z;
   a.NB = g.NB;
