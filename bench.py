@@ -91,6 +91,48 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out: str, command: str) -> int
     return 0
 
 
+def summarize_stats(stats_csv: str, bench_out: str, out: str, command: str, workload: str) -> int:
+    """Per-kernel table from a rocprofv3 --kernel-trace --stats kernel_stats.csv, with the HIP-event
+    kernel time that the bench line of the same run reported beside it."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    kernel_ms = None
+    if bench_out and os.path.exists(bench_out):
+        for line in open(bench_out):
+            line = line.strip()
+            if line.startswith("{") and '"roofline"' in line:
+                kernel_ms = json.loads(line)["roofline"]["kernel_ms"]
+
+    def short(name):
+        own = "pbsa::" in name
+        name = name.replace("pbsa::", "")
+        if name.startswith("void "):
+            name = name[5:]
+        cut = name.find("(")
+        if own:
+            name = name[:cut] if cut > 0 else name
+            for kw, v in (("ImpArgs", ""), ("SelArgs", ""), ("ZArgs", "")):
+                name = name.replace(kw, v)
+            return name
+        return name[:40] + " (torch)"
+
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 kernel-trace statistics, {workload} workload\n")
+        f.write(f"# command (from the repository root, TMPDIR=/tmp):\n#   {command}\n")
+        f.write("# calls include warm-up, timed steps and bench.py's own dense-kernel timing; times in microseconds.\n")
+        if kernel_ms is not None:
+            f.write(f"# bench.py's HIP-event figure for the block-sparse attention kernel in the same run: "
+                    f"kernel_ms = {kernel_ms:.3f}\n")
+        f.write(f"{'kernel':62s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}\n")
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            f.write(f"{short(r['Name'])[:62]:62s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.1f} "
+                    f"{float(r['MinNs']) / 1e3:9.1f} {float(r['MaxNs']) / 1e3:9.1f} "
+                    f"{100.0 * float(r['TotalDurationNs']) / total:6.2f}\n")
+    print(open(out).read())
+    return 0
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -323,6 +365,8 @@ def main() -> int:
                     help="after timing, copy %d bytes on the device (byte-counter calibration)" % COPY_CALIB_BYTES)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc counter_collection.csv files")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "BENCH_OUT"),
+                    help="write a kernel table from a rocprofv3 kernel_stats.csv and the bench line of that run")
     ap.add_argument("--summary-out", default=TRAFFIC_SUMMARY)
     ap.add_argument("--summary-command", default="")
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
@@ -339,6 +383,9 @@ def main() -> int:
 
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_out, args.summary_command)
+    if args.summarize_stats:
+        return summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.summary_out,
+                               args.summary_command, args.workload)
     if args.suite:
         os.makedirs(os.path.dirname(os.path.abspath(args.suite_out)), exist_ok=True)
         return suite(args)
