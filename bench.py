@@ -325,14 +325,10 @@ def suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     d = load(w)
     cal = load(w, seed=w.calib_seed)
     B, NB, Hq = w.block_size, w.num_blocks, w.num_q_heads
-    tmax = pbsa.tile_max(cal["q"], cal["k"], B).cpu().numpy()
-    del cal
-    theta = np.full((Hq, NB), -np.inf, dtype=np.float32)
-    for I in range(NB):
-        if I + 1 > w.calib_keep:
-            row = tmax[:, I * (I + 1) // 2: I * (I + 1) // 2 + I + 1]
-            theta[:, I] = -np.sort(-row, axis=1)[:, w.calib_keep - 1]
-    theta_t = torch.from_numpy(theta).cuda()
+    # offline calibration on the second draw: tile maxima, then the keep-th largest per query block
+    tmax = pbsa.tile_max(cal["q"], cal["k"], B)
+    theta_t = pbsa.calibrate_thresholds(tmax, cal["q"], cal["k"], B, w.calib_keep)
+    del cal, tmax
     q, k, v = d["q"], d["k"], d["v"]
     out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
     dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, out=out, return_lse=False)

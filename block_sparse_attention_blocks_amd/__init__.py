@@ -23,6 +23,7 @@ __all__ = [
     "estimate_block_mask",
     "block_sparse_attn_prefill",
     "tile_max",
+    "calibrate_thresholds",
     "workspace_size",
     "make_shape",
     "num_blocks",
@@ -185,6 +186,24 @@ def tile_max(q: torch.Tensor, k: torch.Tensor, block_size: int, scale: Optional[
     st = _lib.lib().pbsa_tile_max(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(tm), _stream())
     _lib.check(st, "pbsa_tile_max")
     return tm
+
+
+def calibrate_thresholds(tile_max_: torch.Tensor, q: torch.Tensor, k: torch.Tensor, block_size: int,
+                         keep: int) -> torch.Tensor:
+    """Early-stop thresholds fp32 [Hq][NB] from calibration tile maxima (as from tile_max on q, k):
+    the keep-th largest tile max of each query block's row, -inf for rows of at most keep tiles."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, 0)
+    NB = num_blocks(q.shape[1], block_size)
+    if tile_max_.dtype != torch.float32 or tile_max_.shape != (q.shape[0], NB * (NB + 1) // 2) \
+            or not tile_max_.is_contiguous():
+        raise ValueError("tile_max must be contiguous fp32 [Hq][NB(NB+1)/2]")
+    theta = torch.empty((q.shape[0], NB), dtype=torch.float32, device=q.device)
+    st = _lib.lib().pbsa_calibrate_thresholds(ctypes.byref(shape), _ptr(tile_max_), int(keep), _ptr(theta),
+                                             _stream())
+    _lib.check(st, "pbsa_calibrate_thresholds")
+    return theta
 
 
 def default_scale(head_dim: int) -> float:

@@ -62,6 +62,7 @@ _SIG = {
     "pbsa_block_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
                                                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_tile_max": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P]),
+    "pbsa_calibrate_thresholds": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, ctypes.c_int32, _P, _P]),
     "pbsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pbsa_version": (ctypes.c_int32, []),
 }

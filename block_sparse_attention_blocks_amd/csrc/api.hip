@@ -148,6 +148,16 @@ pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint
   return from_hip(pbsa::launch_tile_max(g, q, k, tile_max, static_cast<hipStream_t>(stream)));
 }
 
+pbsa_status pbsa_calibrate_thresholds(const pbsa_shape* shape, const float* tile_max, int32_t keep, float* theta,
+                                      void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (!tile_max || !theta || keep < 1) return PBSA_ERR_INVALID_ARG;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_calibrate(g.Hq, g.NB, tile_max, keep, theta, static_cast<hipStream_t>(stream)));
+}
+
 const char* pbsa_status_string(pbsa_status status) {
   switch (status) {
     case PBSA_OK: return "ok";

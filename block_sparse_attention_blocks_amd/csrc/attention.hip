@@ -1061,6 +1061,53 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
   return dispatch<MODE_ATTN>(g, a, st);
 }
 
+// Early-stop thresholds from calibration tile maxima (Block Sparse Flash Attention, Approach:
+// thresholds fixed offline so that about `keep` tiles per query block survive): theta[h][I] is the
+// keep-th largest of tmax[h][I(I+1)/2 + J] over J <= I, or -inf when the row has at most keep
+// tiles.  One wave per row.  Each value maps to a 32-bit key that orders like the float (sign bit
+// flipped for non-negative values, all bits flipped for negative ones); the wave then builds the
+// largest key t with count(key >= t) >= keep bit by bit from the top, which is exactly the key of
+// the keep-th largest value, so the result is one of the row's own values.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__global__ __launch_bounds__(256) void calibrate_kernel(const float* tmax, int Hq, int NB, int keep, float* theta) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= Hq * NB) return;
+  const int h = row / NB, I = row % NB;
+  const int n = I + 1;
+  if (n <= keep) {
+    if (lane == 0) theta[row] = -INFINITY;
+    return;
+  }
+  const size_t ntri = (size_t)NB * (NB + 1) / 2;
+  const float* r = tmax + (size_t)h * ntri + (size_t)I * (I + 1) / 2;
+  uint32_t t = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      const bool ge = j < n && order_key(r[j]) >= cand;
+      cnt += __popcll(__ballot(ge));
+    }
+    if (cnt >= keep) t = cand;
+  }
+  if (lane == 0) theta[row] = order_key_inv(t);
+}
+
+hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st) {
+  const int rows = Hq * NB;
+  calibrate_kernel<<<(rows + 3) / 4, 256, 0, st>>>(tmax, Hq, NB, keep, theta);
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax, hipStream_t st) {
   AttnArgs a = make_args(g);
   a.q = q;

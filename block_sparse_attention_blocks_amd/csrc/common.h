@@ -78,5 +78,6 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
                             hipStream_t st);
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax,
                            hipStream_t st);
+hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);
 
 }  // namespace pbsa

@@ -11,7 +11,8 @@
  *                                      gathered through perm, online softmax, optional tile-max
  *                                      early stop
  *
- * plus pbsa_tile_max (calibration of early-stop thresholds) and small helpers.
+ * plus pbsa_tile_max and pbsa_calibrate_thresholds (offline calibration of the early-stop
+ * thresholds) and small helpers.
  *
  * Sources of each operation (page title, section):
  *   - Sparser Block-Sparse Attention via Token Permutation: section 2 (segmented permutation),
@@ -183,6 +184,18 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
  */
 pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
                           float* tile_max, void* stream);
+
+/*
+ * Early-stop thresholds from calibration tile maxima (Block Sparse Flash Attention, Approach:
+ * thresholds are set offline so that roughly the top `keep` tiles of each query block survive).
+ *   tile_max  fp32 [Hq][NB(NB+1)/2], as written by pbsa_tile_max on calibration inputs
+ *   keep      >= 1
+ *   theta     out, fp32 [Hq][NB]: theta[h][I] = the keep-th largest of tile_max[h][I(I+1)/2 + J]
+ *             over J <= I (one of those values, chosen exactly), or -inf when I + 1 <= keep
+ * Returns PBSA_ERR_INVALID_ARG for null pointers or keep < 1.  NaN tile maxima are not expected.
+ */
+pbsa_status pbsa_calibrate_thresholds(const pbsa_shape* shape, const float* tile_max, int32_t keep,
+                                      float* theta, void* stream);
 
 /* Static description of a status code. */
 const char* pbsa_status_string(pbsa_status status);

@@ -32,8 +32,8 @@ def shape(N=1024, Hq=4, Hkv=2, d=128, B=128, S=512, scale=0.0):
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"pbsa_build_segment_permutation", "pbsa_estimate_block_mask",
-                          "pbsa_block_sparse_attn_prefill", "pbsa_tile_max", "pbsa_workspace_size",
-                          "pbsa_status_string", "pbsa_version"}
+                          "pbsa_block_sparse_attn_prefill", "pbsa_tile_max", "pbsa_calibrate_thresholds",
+                          "pbsa_workspace_size", "pbsa_status_string", "pbsa_version"}
     lib = _lib.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -109,6 +109,9 @@ def test_null_shape_and_pointers():
     assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), bad, FAKE, FAKE, None, None, None, None, FAKE,
                                             None, None, None, None, 0, None) == E
     assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, None) == E
+    assert l.pbsa_calibrate_thresholds(ctypes.byref(s), None, 64, FAKE, None) == E
+    assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 64, None, None) == E
+    assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 0, FAKE, None) == E
 
 
 def test_permutation_needs_segments_and_mask_needs_valid_tau_and_flags():
@@ -159,3 +162,4 @@ def test_empty_sequence_is_a_no_op():
     assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
                                             None, None, None, None, 0, None) == 0
     assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == 0
+    assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 4, FAKE, None) == 0

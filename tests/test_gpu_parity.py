@@ -149,6 +149,9 @@ def test_early_stop_gate(Hq, Hkv):
     assert np.abs(tm_g - tm_o).max() <= 1e-3, np.abs(tm_g - tm_o).max()
     theta = oracle.calibrate_thresholds(tm_cal.astype(np.float64), NB, keep).astype(np.float32)
     theta_t = torch.from_numpy(theta).cuda()
+    # the library's own calibration picks the same values from the same tile maxima
+    theta_lib = pbsa.calibrate_thresholds(torch.from_numpy(tm_cal).cuda(), cal["q"], cal["k"], B, keep)
+    assert np.array_equal(theta_lib.cpu().numpy(), theta)
 
     for mode in ("dense", "masked"):
         if mode == "dense":
@@ -329,3 +332,24 @@ def test_strided_layout_matches_contiguous():
     torch.cuda.synchronize()
     assert torch.equal(perm, perm_s) and torch.equal(c, cs)
     assert torch.equal(o, os_)
+
+
+@pytest.mark.parametrize("N,B,keep", [(4096, 128, 5), (2100, 64, 1), (1024, 64, 16), (8192, 128, 64)])
+def test_calibrate_thresholds_exact(N, B, keep):
+    """keep-th largest tile max per row, with negative values, heavy ties and ragged NB: the kernel
+    selects one of the row's values, so it must equal the oracle's selection exactly."""
+    pbsa = _need_gpu()
+    Hq, Hkv, d = 3, 1, 64
+    NB = oracle.num_blocks(N, B)
+    rng = np.random.default_rng(N + keep)
+    tm = rng.standard_normal((Hq, NB * (NB + 1) // 2)).astype(np.float32) * 3.0
+    tm[0] = np.round(tm[0])              # many equal values
+    tm[1, ::7] = -0.0                    # signed zeros among negatives and positives
+    tm[1, 3::11] = 0.0
+    q = torch.zeros((Hq, N, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((Hkv, N, d), dtype=torch.bfloat16, device="cuda")
+    got = pbsa.calibrate_thresholds(torch.from_numpy(tm).cuda(), q, k, B, keep).cpu().numpy()
+    want = oracle.calibrate_thresholds(tm.astype(np.float64), NB, keep).astype(np.float32)
+    assert np.array_equal(np.isneginf(got), np.isneginf(want))
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin], want[fin])
