@@ -32,6 +32,7 @@ CASES = [
     ("b64_d128_ragged_1500", 1500, 2, 1, 128, 64, 256, 8, 128, 0.8, 8),
     ("b128_d64_ragged_1000", 1000, 4, 1, 64, 128, 256, 8, 128, 0.95, 9),
     ("shorter_than_a_block_100", 100, 2, 2, 128, 128, 128, 2, 0, 0.9, 10),
+    ("b64_d64_pairs_ragged_777", 777, 4, 2, 64, 64, 128, 8, 64, 0.9, 11),
 ]
 
 
@@ -133,10 +134,12 @@ def test_mask_without_permutation(Hq, Hkv):
     compare_lse(lse.cpu().numpy(), lse_o)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (3, 1)])  # query heads paired per workgroup, and not
-def test_early_stop_gate(Hq, Hkv):
+# query heads paired per workgroup (even G) and not, every supported (d, B), one ragged N
+@pytest.mark.parametrize("Hq,Hkv,d,B,N", [(4, 2, 128, 128, 2048), (3, 1, 128, 128, 2048), (4, 2, 64, 64, 1900),
+                                          (2, 1, 128, 64, 2048), (4, 2, 64, 128, 2048)])
+def test_early_stop_gate(Hq, Hkv, d, B, N):
     pbsa = _need_gpu()
-    N, d, B, keep = 2048, 128, 128, 6
+    keep = 6
     dev, host = _inputs(N, Hq, Hkv, d, 16, 256, 31)
     cal, _ = _inputs(N, Hq, Hkv, d, 16, 256, 32)
     NB = oracle.num_blocks(N, B)
