@@ -140,8 +140,11 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               segment_size: int = 0, early_stop_theta: Optional[torch.Tensor] = None,
                               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-                              return_kept: bool = False, return_error: bool = False):
-    """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word)."""
+                              return_kept: bool = False, return_error: bool = False,
+                              workspace: Optional[torch.Tensor] = None):
+    """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word).
+    workspace: optional preallocated device buffer of at least workspace_size(shape, PBSA_OP_ATTENTION)
+    bytes (the work deques); one is allocated per call otherwise."""
     _check_bf16("q", q)
     _check_bf16("k", k)
     _check_bf16("v", v, heads=k.shape[0])
@@ -161,7 +164,7 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         kept = torch.zeros((Hq, words), dtype=torch.int32, device=q.device)
     err = torch.zeros(1, dtype=torch.int32, device=q.device) if return_error else None
     shape = make_shape(q, k, block_size, segment_size, scale, out=out)
-    ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, None)
+    ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
     st = _lib.lib().pbsa_block_sparse_attn_prefill(
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
         _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())

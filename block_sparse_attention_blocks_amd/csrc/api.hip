@@ -80,7 +80,7 @@ size_t pbsa_workspace_size(const pbsa_shape* shape, int op) {
   switch (op) {
     case PBSA_OP_PERMUTATION: return pbsa::importance_workspace_bytes(g);
     case PBSA_OP_MASK: return pbsa::mask_workspace_bytes(g);
-    case PBSA_OP_ATTENTION: return 0;
+    case PBSA_OP_ATTENTION: return g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0;
     default: return SIZE_MAX;
   }
 }
@@ -124,8 +124,6 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                            const int32_t* block_idx, const float* early_stop_theta, float* out,
                                            float* lse, uint32_t* kept_bitmap, int32_t* device_error,
                                            void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   Geometry g;
   pbsa_status st = make_geometry(shape, &g);
   if (st != PBSA_OK) return st;
@@ -133,9 +131,11 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PBSA_ERR_INVALID_ARG;
   if ((block_count == nullptr) != (block_idx == nullptr)) return PBSA_ERR_INVALID_ARG;
   if (perm && g.S <= 0) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
+    return st;
   if (g.N == 0) return PBSA_OK;
   return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out, lse,
-                                         kept_bitmap, device_error, static_cast<hipStream_t>(stream)));
+                                         kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream)));
 }
 
 pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, float* tile_max,

@@ -58,6 +58,9 @@ struct AttnArgs {
   uint32_t q_bytes, kv_bytes;            // bytes of one head's slab (buffer bound)
   float scale;  // c
   float sl2;    // c * log2(e)
+  unsigned long long* queue;  // work deques of the pipelined kernels (workspace)
+  int nq;                     // number of deques: one per KV group, at most one per XCD
+  int Hkv;
 };
 
 enum { MODE_ATTN = 0, MODE_ATTN_GATED = 1, MODE_TILE_MAX = 2, MODE_DENSE = 3 };
@@ -434,6 +437,60 @@ __device__ __forceinline__ int union_list(const AttnArgs& a, int h0, int I, size
   return *mcount;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Work distribution of the pipelined kernels.  A work item is one query block I for one unit of
+// HPW query heads.  Deque q holds, in order of descending I, the items of the KV groups g with
+// g % nq == q (nq = min(8, Hkv)), so the items of one KV group share a deque and, through it, one
+// XCD's L2.  A persistent workgroup reads the XCD it runs on from the hardware, takes items from
+// the front of that XCD's deque (longest rows first), and once it is empty takes the shortest
+// remaining items from the back of the other deques: the XCDs finish together even when the KV
+// groups keep very different numbers of blocks.
+//
+// Each deque is one 64-bit word, front index in the low half and back index in the high half,
+// changed only by atomic adds: +1 claims the front item f if f < b in the returned word, -2^32
+// claims the back item b-1 if b-1 >= f.  Every add sees one consistent (f, b), the two ends only
+// move towards each other, so no item is claimed twice and a workgroup that finds every deque
+// empty can stop.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int deque_items(const AttnArgs& a, int q, int units_per_group) {
+  const int groups = (a.Hkv - q + a.nq - 1) / a.nq;
+  return a.NB * groups * units_per_group;
+}
+
+__global__ __launch_bounds__(64) void deque_init_kernel(AttnArgs a, int units_per_group) {
+  const int q = threadIdx.x;
+  if (q < a.nq) a.queue[q] = (unsigned long long)deque_items(a, q, units_per_group) << 32;
+}
+
+// item code (q << 24 | index) or -1 when every deque is empty
+__device__ __forceinline__ int claim_item(const AttnArgs& a, int home) {
+  unsigned long long old = atomicAdd(&a.queue[home], 1ull);
+  int f = (int)(uint32_t)old, b = (int)(uint32_t)(old >> 32);
+  if (f < b) return (home << 24) | f;
+  for (int k = 1; k < a.nq; ++k) {
+    const int q = home + k < a.nq ? home + k : home + k - a.nq;
+    old = atomicAdd(&a.queue[q], 0xFFFFFFFF00000000ull);
+    f = (int)(uint32_t)old;
+    b = (int)(uint32_t)(old >> 32);
+    if (b >= 1 && b - 1 >= f) return (q << 24) | (b - 1);
+  }
+  return -1;
+}
+
+// item code -> (query block I, first query head h0)
+__device__ __forceinline__ void item_work(const AttnArgs& a, int code, int hpw, int units_per_group, int* I,
+                                          int* h0) {
+  const int q = code >> 24, i = code & 0xffffff;
+  const int groups = (a.Hkv - q + a.nq - 1) / a.nq;
+  const int per_I = groups * units_per_group;
+  *I = a.NB - 1 - i / per_I;
+  const int j = i % per_I;
+  const int g = q + a.nq * (j / units_per_group);
+  *h0 = (g * units_per_group + j % units_per_group) * hpw;
+}
+
+__device__ __forceinline__ int xcd_id() { return (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xfu); }
+
 // Software-pipelined block-sparse (DENSE = false) or dense causal (DENSE = true) attention for
 // HPW query heads h0 .. h0+HPW-1 of one KV group and one query block I.  The workgroup walks the
 // union of the heads' kept key blocks in ascending order; each KT-key stage of a block is gathered
@@ -469,24 +526,17 @@ void attn_pipe_kernel(AttnArgs a) {
     return b == 0 ? V0 : b == 1 ? V1 : b == 2 ? V2 : V3;
   };
 
+  __shared__ int item_sh;
+
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
   const int hh = wave / C::WAVES_PER_HEAD;   // this wave's head within the workgroup
   const int wq = wave % C::WAVES_PER_HEAD;   // this wave's 32-row slice of the query block
-  int I, h0;
-  work_item(a.NB, a.Hq / HPW, HPW, blockIdx.x, &I, &h0);
-  const int h = h0 + hh;
-  const int g = h0 / a.G;
-  const int I0 = I * BLK;
-  const int qloc = wq * 32 + l32;
-  const int qpos = I0 + qloc;
-  const bool qvalid = qpos < a.N;
-  const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
-  const rsrc_t qr = make_rsrc(a.q + (int64_t)h * a.qsh, a.q_bytes);
-  const rsrc_t kr = make_rsrc(a.k + (int64_t)g * a.kvsh, a.kv_bytes);
-  const rsrc_t vr = make_rsrc(a.v + (int64_t)g * a.kvsh, a.kv_bytes);
+  const int upg = a.G / HPW;                 // head units per KV group
+  const int home = xcd_id() % a.nq;
 
-  // rows past N are never written by the gather: start from finite (zero) tiles
+  // stage buffers start finite (zero); rows a gather leaves unwritten keep finite older data, and
+  // keys past N only occur in the last diagonal block, where the causal mask removes them
   {
     constexpr int NZ = KT * D * 2 / 16;
     const u32x4 z = u32x4{0u, 0u, 0u, 0u};
@@ -497,6 +547,24 @@ void attn_pipe_kernel(AttnArgs a) {
         reinterpret_cast<u32x4*>(Vb(b))[i] = z;
       }
   }
+
+  for (;;) {
+  if (t == 0) item_sh = claim_item(a, home);
+  __syncthreads();
+  const int code = item_sh;
+  if (code < 0) break;
+  int I, h0;
+  item_work(a, code, HPW, upg, &I, &h0);
+  const int h = h0 + hh;
+  const int g = h0 / a.G;
+  const int I0 = I * BLK;
+  const int qloc = wq * 32 + l32;
+  const int qpos = I0 + qloc;
+  const bool qvalid = qpos < a.N;
+  const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
+  const rsrc_t qr = make_rsrc(a.q + (int64_t)h * a.qsh, a.q_bytes);
+  const rsrc_t kr = make_rsrc(a.k + (int64_t)g * a.kvsh, a.kv_bytes);
+  const rsrc_t vr = make_rsrc(a.v + (int64_t)g * a.kvsh, a.kv_bytes);
 
   bf16x8 qf[AttnCfg<D, BLK>::KSTEPS];
 #pragma unroll
@@ -600,6 +668,8 @@ void attn_pipe_kernel(AttnArgs a) {
     for (int x = 0; x < NBUF; ++x) step(s + x, x);
   }
   write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
+  __syncthreads();  // every wave is done with this item's LDS before the next claim
+  }
 }
 
 // Score block kb of a tile (S^T, 32 keys x 32 queries) with K operands read from LDS a quarter of
@@ -990,14 +1060,39 @@ void attn_gated_kernel(AttnArgs a) {
   if (MODE != MODE_TILE_MAX) write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
 }
 
+// Persistent launch of the pipelined kernel: the deques are reset on the stream, then as many
+// workgroups start as fit on the device at once (never more than there are items).
+template <int D, int BLK, bool DENSE, int HPW>
+static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st) {
+  constexpr int THREADS = PipeCfg<D, BLK, HPW>::THREADS;
+  static int resident[64] = {0};  // workgroups resident on the whole device, per device ordinal
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (resident[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_pipe_kernel<D, BLK, DENSE, HPW>, THREADS,
+                                                          0)) != hipSuccess)
+      return e;
+    resident[dev] = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  if ((long long)a.NB * (a.Hq / HPW) >= (1ll << 24)) return hipErrorInvalidValue;  // item index field
+  deque_init_kernel<<<1, 64, 0, st>>>(a, a.G / HPW);
+  const int grid = items < resident[dev] ? items : resident[dev];
+  attn_pipe_kernel<D, BLK, DENSE, HPW><<<grid, THREADS, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <int D, int BLK, int MODE>
 static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st) {
   if constexpr (MODE == MODE_ATTN || MODE == MODE_DENSE) {
     constexpr bool DENSE = MODE == MODE_DENSE;
     if ((a.G & 1) == 0) {
-      attn_pipe_kernel<D, BLK, DENSE, 2><<<nwg / 2, PipeCfg<D, BLK, 2>::THREADS, 0, st>>>(a);
+      return launch_persistent<D, BLK, DENSE, 2>(a, nwg / 2, st);
     } else {
-      attn_pipe_kernel<D, BLK, DENSE, 1><<<nwg, PipeCfg<D, BLK, 1>::THREADS, 0, st>>>(a);
+      return launch_persistent<D, BLK, DENSE, 1>(a, nwg, st);
     }
   } else if (MODE == MODE_ATTN_GATED && (a.G & 1) == 0) {
     if (a.count == nullptr) {
@@ -1035,6 +1130,8 @@ static AttnArgs make_args(const Geometry& g) {
   a.kv_bytes = (uint32_t)((int64_t)g.N * g.kvst * 2);
   a.osh = g.osh;
   a.ost = g.ost;
+  a.Hkv = g.Hkv;
+  a.nq = g.Hkv < kMaxDeques ? g.Hkv : kMaxDeques;
   a.scale = g.scale;
   a.sl2 = g.scale * 1.4426950408889634f;
   return a;
@@ -1043,8 +1140,9 @@ static AttnArgs make_args(const Geometry& g) {
 hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* perm, const int32_t* count, const int32_t* idx,
                             const float* theta, float* out, float* lse, uint32_t* kept, int32_t* err,
-                            hipStream_t st) {
+                            void* ws, hipStream_t st) {
   AttnArgs a = make_args(g);
+  a.queue = static_cast<unsigned long long*>(ws);
   a.q = q;
   a.k = k;
   a.v = v;

@@ -72,10 +72,13 @@ hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_
                              void* ws, hipStream_t st);
 
 // Stage 3 and calibration.
+// Attention workspace: the work deques of the pipelined kernels, one 64-bit word per deque.
+constexpr int kMaxDeques = 8;
+constexpr size_t kAttnWorkspaceBytes = 256;
 hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* perm, const int32_t* count, const int32_t* idx,
                             const float* theta, float* out, float* lse, uint32_t* kept, int32_t* err,
-                            hipStream_t st);
+                            void* ws, hipStream_t st);
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax,
                            hipStream_t st);
 hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);

@@ -139,6 +139,15 @@ def test_workspace_checks():
     assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == W
     assert l.pbsa_build_segment_permutation(ctypes.byref(s), FAKE, FAKE, FAKE, None,
                                             ctypes.c_void_p(0x10010), need, None) == W  # not 256-aligned
+    # attention: the work deques
+    needa = ws_size(s, _lib.PBSA_OP_ATTENTION)
+    assert needa > 0
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                            None, None, None, None, 0, None) == W
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                            None, None, None, FAKE, needa - 1, None) == W
+    assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
+                                            None, None, None, ctypes.c_void_p(0x10010), needa, None) == W
     needm = ws_size(s, _lib.PBSA_OP_MASK)
     assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 3, FAKE, FAKE, None, FAKE,
                                       needm - 8, None) == W
