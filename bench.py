@@ -226,6 +226,18 @@ def suite(args) -> int:
         x = generate_for(w, seed=seed)
         return {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
 
+    class _WithWorkspace:  # every attention call of the suite reuses one preallocated workspace
+        def __init__(self, mod, ws):
+            self._mod, self._ws = mod, ws
+
+        def __getattr__(self, name):
+            return getattr(self._mod, name)
+
+        def block_sparse_attn_prefill(self, *a, **kw):
+            kw.setdefault("workspace", self._ws)
+            return self._mod.block_sparse_attn_prefill(*a, **kw)
+
+    pbsa = _WithWorkspace(pbsa, torch.empty(4096, dtype=torch.uint8, device="cuda"))
     reps = args.suite_reps
     parts = set(args.suite_parts.split(","))
     if "128k" in parts:
@@ -411,6 +423,7 @@ def main() -> int:
     shape = pbsa.make_shape(q, k, B, S)
     ws_p = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_PERMUTATION) + 256, dtype=torch.uint8, device=dv)
     ws_m = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_MASK) + 256, dtype=torch.uint8, device=dv)
+    ws_a = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_ATTENTION) + 256, dtype=torch.uint8, device=dv)
     perm = torch.empty((Hkv, N), dtype=torch.int32, device=dv)
     count = torch.empty((Hq, NB), dtype=torch.int32, device=dv)
     idx = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device=dv)
@@ -425,7 +438,7 @@ def main() -> int:
                                  workspace=ws_m)
 
     def stage_attn():
-        pbsa.block_sparse_attn_prefill(q, k, v, perm, count, idx, B, S, out=out, lse=lse)
+        pbsa.block_sparse_attn_prefill(q, k, v, perm, count, idx, B, S, out=out, lse=lse, workspace=ws_a)
 
     def step():
         stage_perm()
@@ -460,7 +473,7 @@ def main() -> int:
     ms_attn = timed(stage_attn, reps)
 
     def dense():
-        pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
+        pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse, workspace=ws_a)
 
     dense()
     ms_dense = timed(dense, max(3, reps // 2))

@@ -35,8 +35,9 @@
  *   - Query head h reads KV head h / (Hq / Hkv).  Block J = tokens [J*B, min((J+1)*B, N));
  *     NB = ceil(N / B).  Segment of block J = (J*B) / S.  N need not be a multiple of B or S.
  *   - Ownership: every pointer is device memory owned by the caller (except pbsa_shape, which is
- *     host memory read during the call).  The library allocates nothing and keeps no state;
- *     scratch memory is the caller's workspace, sized by pbsa_workspace_size.
+ *     host memory read during the call).  The library allocates nothing; its only state is a
+ *     per-device cache of how many attention workgroups fit on the device at once.  Scratch
+ *     memory is the caller's workspace, sized by pbsa_workspace_size.
  *   - Streams: stream is a hipStream_t (NULL = the default stream).  Every call only enqueues
  *     work on it and returns; outputs are valid once the stream reaches that point.  Inputs,
  *     outputs and workspace must stay alive until then.  Calls that share a workspace must be
@@ -166,7 +167,9 @@ pbsa_status pbsa_estimate_block_mask(const pbsa_shape* shape, const uint16_t* q,
  *                     every tile that was computed through PV; must be zeroed by the caller
  *   device_error      out, int32, or NULL: set to a non-zero code if an index in perm or the mask
  *                     is out of range (the offending entries are skipped); caller zeroes it
- *   workspace         >= pbsa_workspace_size(shape, PBSA_OP_ATTENTION) bytes (may be 0)
+ *   workspace         >= pbsa_workspace_size(shape, PBSA_OP_ATTENTION) bytes (256 when N > 0),
+ *                     256-byte aligned: the work queues of the persistent kernel, reset by this
+ *                     call on the stream (calls sharing it must be ordered on one stream)
  */
 pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16_t* q,
                                            const uint16_t* k, const uint16_t* v,
