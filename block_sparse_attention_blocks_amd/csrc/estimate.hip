@@ -129,23 +129,16 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
   constexpr int cpr = D / 8;  // 16-byte chunks per row
   const uint16_t* kbase = a.k + (int64_t)g * a.kvsh;
 
-  // A operand: proxy row r = r0 + 16 w + l16, contraction slots lg*kq .. lg*kq + kq - 1
+  // A operand: proxy row r = r0 + 16 w + l16, contraction slots lg*kq .. lg*kq + kq - 1, kept as
+  // packed bf16 (a quarter of the registers of doubles) and widened at each k-step
   const int ra = r0 + 16 * w + l16;
-  double av[kq];
-  {
-    u32x4 raw[kq / 8] = {};
-    if (ra < a.R) {
-      int h, i;
-      imp_row(a, g, ra, &h, &i);
-      const uint16_t* src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst + lg * kq;
+  u32x4 araw[kq / 8] = {};
+  if (ra < a.R) {
+    int h, i;
+    imp_row(a, g, ra, &h, &i);
+    const uint16_t* src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst + lg * kq;
 #pragma unroll
-      for (int c = 0; c < kq / 8; ++c) raw[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
-    }
-#pragma unroll
-    for (int x = 0; x < kq; ++x) {
-      const uint32_t wd = raw[x / 8][(x / 2) % 4];
-      av[x] = (double)bf16_bits_to_f32((x & 1) ? (wd >> 16) : (wd & 0xffffu));
-    }
+    for (int c = 0; c < kq / 8; ++c) araw[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
   }
   // this lane's D rows (proxy rows r0 + 16 w + lg + 4 rr) and their query positions
   int qi[4];
@@ -182,6 +175,9 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
   __syncthreads();
   for (int c = c0; c < c1; ++c) {
     const uint16_t* Kc = Ks[(c - c0) & 1];
+    // keep A packed across chunks: without this the widening would be hoisted out of the loop
+#pragma unroll
+    for (int x = 0; x < kq / 8; ++x) asm volatile("" : "+v"(araw[x]));
     if (c + 1 < c1) prefetch(c + 1, pf);
     // B operand: key 16 tt + l16 of the chunk, slots lg*kq ..: kq bf16 = kq/8 swizzled chunks; the
     // four column tiles are interleaved so that four independent accumulation chains are in flight
@@ -196,13 +192,16 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
         kb[tt][q] = *reinterpret_cast<const u32x4*>(Kc + row * D + (((lg * kq / 8 + q) ^ imp_swz(row, cpr)) * 8));
     }
 #pragma unroll
-    for (int ks = 0; ks < kq; ++ks)
+    for (int ks = 0; ks < kq; ++ks) {
+      const uint32_t aw = araw[ks / 8][(ks / 2) % 4];
+      const double av = (double)bf16_bits_to_f32((ks & 1) ? (aw >> 16) : (aw & 0xffffu));
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const uint32_t wd = kb[tt][ks / 8][(ks / 2) % 4];
         const double bv = (double)bf16_bits_to_f32((ks & 1) ? (wd >> 16) : (wd & 0xffffu));
-        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bv, acc[tt], 0, 0, 0);
+        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[tt], 0, 0, 0);
       }
+    }
     // per proxy row: chunk max, sum of exponentials, and the exponentials themselves
     const int j0 = c * IMP_CK;
 #pragma unroll
