@@ -159,9 +159,40 @@ constexpr float kLazy = 8.0f;
 template <int D, int BLK>
 struct SoftmaxState {
   f32x16 o[AttnCfg<D, BLK>::DB];
-  float m;  // reference max, log2 units
-  float l;  // sum of the bf16-rounded probabilities relative to m (this lane's half of the keys)
+  float m;     // reference max, log2 units
+  float l;     // sum of the bf16-rounded probabilities relative to m (this lane's half of the keys)
+  float thr;   // (m + kLazy) in raw score units: a block whose raw max exceeds it moves m
+  float muse;  // m, or 0 while m is -inf (no finite score yet), as the exponent offset
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int db = 0; db < AttnCfg<D, BLK>::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+    thr = -INFINITY;
+    muse = 0.f;
+  }
 };
+
+// Lazy rescale on a block's raw (unscaled) row max: when it exceeds the threshold of any lane of
+// the wave, those lanes move m to the block max (log2 units) and scale l and acc by 2^(m_old - m).
+template <int D, int BLK>
+__device__ __forceinline__ void lazy_rescale(SoftmaxState<D, BLK>& st, float raw_max, float sl2) {
+  const bool need = raw_max > st.thr;
+  if (__builtin_amdgcn_ballot_w64(need)) {
+    const float m_new = need ? raw_max * sl2 : st.m;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < AttnCfg<D, BLK>::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    st.m = m_new;
+    st.thr = (m_new + kLazy) / sl2;
+    st.muse = (m_new == -INFINITY) ? 0.f : m_new;
+  }
+}
 
 // K operands of score block kb: A operand (row = key kb*32 + l32) for every k-step of S^T = K Q^T.
 template <int D, int BLK>
@@ -255,24 +286,12 @@ template <int D, int BLK>
 __device__ __forceinline__ void block_softmax_pv_ops(SoftmaxState<D, BLK>& st, const f32x16& s, const bf16x8* vop,
                                                      float sl2) {
   using C = AttnCfg<D, BLK>;
-  const float mx = block_row_max(s) * sl2;
-  const bool need = mx > st.m + kLazy;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float m_new = need ? mx : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
-    st.m = m_new;
-  }
-  const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+  lazy_rescale<D, BLK>(st, block_row_max(s), sl2);
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8 pb[2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -m_use));
+  for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -st.muse));
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -609,12 +628,7 @@ void attn_pipe_kernel(AttnArgs a) {
   };
 
   SoftmaxState<D, BLK> st;
-#pragma unroll
-  for (int db = 0; db < AttnCfg<D, BLK>::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  st.init();
 
   RowLook pr_prev = RowLook{kPastEnd, 0};  // lookup of stage s + NBUF, issued in step s - 1
   if (nst > 0) {
@@ -717,19 +731,8 @@ template <int D, int BLK>
 __device__ __forceinline__ void tile_softmax(SoftmaxState<D, BLK>& st, const f32x16* s, float row_max, bf16x8* pb,
                                              float sl2) {
   using C = AttnCfg<D, BLK>;
-  const float mx = row_max * sl2;
-  const bool need = mx > st.m + kLazy;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float m_new = need ? mx : st.m;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
-    st.m = m_new;
-  }
-  const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+  lazy_rescale<D, BLK>(st, row_max, sl2);
+  const float m_use = st.muse;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -870,12 +873,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   };
 
   SoftmaxState<D, BLK> st;
-#pragma unroll
-  for (int db = 0; db < AC::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  st.init();
   bf16x8 pb[2 * KB];  // probabilities of the last kept tile, consumed one iteration later
   bool keep_prev = false;
 
@@ -941,7 +939,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
 // Early-stop kernel (Block Sparse Flash Attention, Approach) and calibration tile maxima.  Per key
 // block: gather K, compute the whole tile's scores, reduce their exact max across the workgroup,
 // and only when the tile is kept gather V and run the same online-softmax / PV steps as the
-// pipelined kernel (so a threshold of -inf reproduces it bit for bit).  MODE_TILE_MAX only writes
+// pipelined kernel; a threshold of -inf keeps every tile.  MODE_TILE_MAX only writes
 // the scaled tile maxima.
 template <int D, int BLK, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(AttnCfg<D, BLK>::THREADS, AttnCfg<D, BLK>::THREADS),
@@ -992,12 +990,7 @@ void attn_gated_kernel(AttnArgs a) {
   }
   const int sI = a.S > 0 ? I0 / a.S : 0;
   SoftmaxState<D, BLK> st;
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  st.init();
 
   for (int it = 0; it < cnt; ++it) {
     const int J = list ? list[it] : it;
