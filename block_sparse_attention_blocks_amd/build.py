@@ -11,13 +11,16 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpbsa.so")
 SOURCES = ["api.hip", "estimate.hip", "attention.hip"]
+# per-source extra flags.  attention.hip: no NaN is produced or tested there (masked scores are
+# -inf), so max and compare need no NaN quieting; api.hip validates arguments with comparisons
+# that must keep their NaN meaning and gets no such flag.
+SOURCE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU forms are kept out of generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA accumulators stay in VGPRs: the fp64 kernels otherwise move every accumulator between
@@ -32,10 +35,7 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build_library(verbose: bool = False) -> str:
-    """Build libpbsa.so next to this file (always recompiles) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,6 +45,20 @@ def build_library(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out, flush=True)
+
+
+def build_library(verbose: bool = False) -> str:
+    """Build libpbsa.so next to this file (always recompiles) and return its path."""
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="pbsa_build_") as tmpdir:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            _run([hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+                  os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 
