@@ -108,37 +108,79 @@ __device__ __forceinline__ double row_sum_f64(double x) {  // exact on lane 0 of
   return x + row_ror_f64<8>(x);
 }
 
-// 16-byte chunk swizzle of a staged key row: the 16 rows a wave reads together hit distinct banks.
-__device__ __forceinline__ int imp_swz(int row, int cpr) { return cpr == 16 ? (row & 15) : ((row >> 1) & 7); }
+
+// exp(x) for the logits of the importance pass (x <= 0, -inf allowed), written out in fp64:
+// Cody-Waite reduction x = n ln2 + r with |r| <= ln2/2 (ln2 split into a 32-significant-bit head,
+// so n * head is exact, and the rounded remainder), exp(r) by its Taylor series to degree 11
+// (truncation below 1e-14 relative on that interval; 8.8e-15 worst case measured against the math
+// library on [-60, 0]), then the exact scaling by 2^n.  Below -745 the result is 0.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  constexpr double kLog2e = 1.4426950408889634, kLn2Hi = 0.6931471803691238, kLn2Lo = 1.9082149292705877e-10;
+  const double n = rint(x * kLog2e);
+  double r = fma(-n, kLn2Hi, x);
+  r = fma(-n, kLn2Lo, r);
+  double q = 2.505210838544172e-08;  // 1/11!
+  q = fma(q, r, 2.755731922398589e-07);
+  q = fma(q, r, 2.7557319223985893e-06);
+  q = fma(q, r, 2.48015873015873e-05);
+  q = fma(q, r, 0.0001984126984126984);
+  q = fma(q, r, 0.001388888888888889);
+  q = fma(q, r, 0.008333333333333333);
+  q = fma(q, r, 0.041666666666666664);
+  q = fma(q, r, 0.16666666666666666);
+  q = fma(q, r, 0.5);
+  q = fma(q, r, 1.0);
+  q = fma(q, r, 1.0);
+  const double y = ldexp(q, (int)n);
+  return x < -745.0 ? 0.0 : y;
+}
 
 // v_mfma_f64_16x16x4_f64 (lane l): A holds row l%16 and B column l%16 at contraction slot l/16; D
-// holds column l%16, rows l/16 + 4 r in its four doubles r = 0..3.  The contraction index is
-// assigned as k = (l/16) * (d/4) + ks for MFMA step ks, so every lane reads a contiguous run of a
-// row.  Each wave keeps the A operand (its 16 proxy rows, all of d) in registers for the whole
-// workgroup; the key chunks stream through LDS (prefetched into registers one chunk ahead).
+// holds column l%16, rows l/16 + 4 r in its four doubles r = 0..3.  The contraction index of lane
+// group lg at MFMA step ks is k = 4 ks + lg.  Each wave keeps its 16 proxy rows (all of d) in
+// registers as doubles; every key chunk is widened to doubles once, by the staging threads, into
+// LDS rows padded to D + 4 doubles, so a B operand is one 8-byte read at a fixed offset from the
+// lane's base address and the 64 lanes of a read fall on distinct bank pairs two at a time.  The
+// next chunk's bf16 rows are loaded into registers while the current one is multiplied.
 template <int D>
 __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, double* E, double* part_m,
                                                                  double* part_l) {
-  __shared__ __align__(16) uint16_t Ks[2][IMP_CK * D];
+  constexpr int KS = D / 4;         // MFMA k-steps
+  constexpr int PITCH = D + 4;      // doubles per staged key row
+  constexpr int cpr = D / 8;        // 16-byte bf16 chunks per key row
+  constexpr int NLD = IMP_CK * cpr / IMP_THREADS;  // chunks per thread per stage
+  __shared__ __align__(16) double Kf[IMP_CK * PITCH];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int r0 = blockIdx.x * IMP_RT, g = blockIdx.z;
   const int nchunk = (a.N + IMP_CK - 1) / IMP_CK;
   const int c0 = blockIdx.y * IMP_KR, c1 = min(c0 + IMP_KR, nchunk);
-  constexpr int kq = D / 4;   // contraction slots per lane (32 or 16)
-  constexpr int cpr = D / 8;  // 16-byte chunks per row
   const uint16_t* kbase = a.k + (int64_t)g * a.kvsh;
 
-  // A operand: proxy row r = r0 + 16 w + l16, contraction slots lg*kq .. lg*kq + kq - 1, kept as
-  // packed bf16 (a quarter of the registers of doubles) and widened at each k-step
+  // A operand: proxy row r0 + 16 w + l16, slots k = 4 ks + lg
   const int ra = r0 + 16 * w + l16;
-  u32x4 araw[kq / 8] = {};
-  if (ra < a.R) {
-    int h, i;
-    imp_row(a, g, ra, &h, &i);
-    const uint16_t* src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst + lg * kq;
+  double av[KS];
+  {
+    const uint16_t* src = nullptr;
+    if (ra < a.R) {
+      int h, i;
+      imp_row(a, g, ra, &h, &i);
+      src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst;
+    }
 #pragma unroll
-    for (int c = 0; c < kq / 8; ++c) araw[c] = *reinterpret_cast<const u32x4*>(src + 8 * c);
+    for (int p = 0; p < D / 32; ++p) {  // 32 elements (8 k-steps) at a time
+      u32x4 raw[4] = {};
+      if (src)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(src + 32 * p + 8 * c);
+#pragma unroll
+      for (int kl = 0; kl < 8; ++kl) {
+        // element 4 kl + lg of these 32: 16-byte chunk kl / 2, word 2 (kl % 2) + lg / 2, half lg % 2
+        const u32x4 v = raw[kl >> 1];
+        const uint32_t wd = (lg >> 1) ? v[2 * (kl & 1) + 1] : v[2 * (kl & 1)];
+        av[8 * p + kl] = (double)bf16_bits_to_f32((lg & 1) ? (wd >> 16) : (wd & 0xffffu));
+      }
+    }
   }
   // this lane's D rows (proxy rows r0 + 16 w + lg + 4 rr) and their query positions
   int qi[4];
@@ -149,80 +191,78 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
     imp_row(a, g, r, &h, &i);
     qi[rr] = r < a.R ? i : -1;
   }
-  // staging of chunk c: thread t copies 16-byte chunks t, t + 256, ... (row = x / cpr)
+  const int first_proxy = a.N - a.R1;  // every key j <= first_proxy is visible to every proxy row
+
   auto prefetch = [&](int c, u32x4* pf) {
     const int j0 = c * IMP_CK;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < NLD; ++x) {
       const int idx = t + x * IMP_THREADS;
       const int row = idx / cpr, ch = idx % cpr;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < IMP_CK && j0 + row < a.N) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(j0 + row) * a.kvst + ch * 8);
+      if (j0 + row < a.N) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(j0 + row) * a.kvst + ch * 8);
       pf[x] = v;
     }
   };
-  auto stage = [&](uint16_t* dst, const u32x4* pf) {
+  // widen the prefetched bf16 rows to doubles into the padded LDS rows
+  auto stage = [&](const u32x4* pf) {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < NLD; ++x) {
       const int idx = t + x * IMP_THREADS;
       const int row = idx / cpr, ch = idx % cpr;
-      if (row < IMP_CK) *reinterpret_cast<u32x4*>(dst + row * D + ((ch ^ imp_swz(row, cpr)) * 8)) = pf[x];
+      double* dst = Kf + row * PITCH + ch * 8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wd = pf[x][e];
+        const f64x2 two = {(double)bf16_bits_to_f32(wd & 0xffffu), (double)bf16_bits_to_f32(wd >> 16)};
+        *reinterpret_cast<f64x2*>(dst + 2 * e) = two;
+      }
     }
   };
-  u32x4 pf[4];
+  const double* bbase = Kf + l16 * PITCH + lg;  // B operand of column tile tt, step ks: bbase[16 tt PITCH + 4 ks]
+
+  u32x4 pf[NLD];
   prefetch(c0, pf);
-  stage(Ks[0], pf);
-  __syncthreads();
   for (int c = c0; c < c1; ++c) {
-    const uint16_t* Kc = Ks[(c - c0) & 1];
-    // keep A packed across chunks: without this the widening would be hoisted out of the loop
-#pragma unroll
-    for (int x = 0; x < kq / 8; ++x) asm volatile("" : "+v"(araw[x]));
+    stage(pf);
+    __syncthreads();
     if (c + 1 < c1) prefetch(c + 1, pf);
-    // B operand: key 16 tt + l16 of the chunk, slots lg*kq ..: kq bf16 = kq/8 swizzled chunks; the
-    // four column tiles are interleaved so that four independent accumulation chains are in flight
     f64x4 acc[4];
-    u32x4 kb[4][kq / 8];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      acc[tt] = f64x4{0.0, 0.0, 0.0, 0.0};
-      const int row = 16 * tt + l16;
+    for (int tt = 0; tt < 4; ++tt) acc[tt] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int q = 0; q < kq / 8; ++q)
-        kb[tt][q] = *reinterpret_cast<const u32x4*>(Kc + row * D + (((lg * kq / 8 + q) ^ imp_swz(row, cpr)) * 8));
-    }
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < kq; ++ks) {
-      const uint32_t aw = araw[ks / 8][(ks / 2) % 4];
-      const double av = (double)bf16_bits_to_f32((ks & 1) ? (aw >> 16) : (aw & 0xffffu));
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const uint32_t wd = kb[tt][ks / 8][(ks / 2) % 4];
-        const double bv = (double)bf16_bits_to_f32((ks & 1) ? (wd >> 16) : (wd & 0xffffu));
-        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[tt], 0, 0, 0);
-      }
-    }
+      for (int tt = 0; tt < 4; ++tt)
+        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bbase[16 * tt * PITCH + 4 * ks], acc[tt], 0, 0, 0);
     // per proxy row: chunk max, sum of exponentials, and the exponentials themselves
     const int j0 = c * IMP_CK;
+    const bool open = j0 + IMP_CK - 1 <= first_proxy && j0 + IMP_CK <= a.N;  // no key of the chunk is masked
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
-      const int i = qi[rr];
       double sv[4];
-      double m = -INFINITY;
+      double m;
+      if (open) {
+        double mx = fmax(fmax(acc[0][rr], acc[1][rr]), fmax(acc[2][rr], acc[3][rr]));
+        m = a.scale * row_max_f64(mx);  // scale > 0 keeps the max
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int j = j0 + 16 * tt + l16;
-        const bool ok = (i >= 0) && (j < a.N) && (j <= i);
-        sv[tt] = ok ? a.scale * acc[tt][rr] : -INFINITY;
-        m = fmax(m, sv[tt]);
-      }
-      m = row_max_f64(m);
-      double l = 0.0;
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_nonpos(fma(a.scale, acc[tt][rr], -m));
+      } else {
+        const int i = qi[rr];
+        m = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        sv[tt] = (sv[tt] > -INFINITY) ? exp(sv[tt] - m) : 0.0;
-        l += sv[tt];
+        for (int tt = 0; tt < 4; ++tt) {
+          const int j = j0 + 16 * tt + l16;
+          const bool ok = (i >= 0) && (j < a.N) && (j <= i);
+          sv[tt] = ok ? a.scale * acc[tt][rr] : -INFINITY;
+          m = fmax(m, sv[tt]);
+        }
+        m = row_max_f64(m);
+        const double mm = m > -INFINITY ? m : 0.0;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_nonpos(sv[tt] - mm);
       }
+      double l = (sv[0] + sv[1]) + (sv[2] + sv[3]);
       l = row_sum_f64(l);
       const int r = r0 + 16 * w + lg + 4 * rr;
       if (r < a.R) {
@@ -239,8 +279,7 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
         }
       }
     }
-    if (c + 1 < c1) stage(Ks[(c + 1 - c0) & 1], pf);
-    lds_barrier_est();
+    __syncthreads();  // every wave is done with this chunk's rows before they are replaced
   }
 }
 
