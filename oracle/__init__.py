@@ -22,6 +22,8 @@ from .pbsa_oracle import (  # noqa: F401
     num_blocks,
     pool_blocks,
     pool_permuted_blocks,
+    ranked_blocks,
+    s2o_attention,
     segment_of_block,
     segment_permutation,
     tile_max,

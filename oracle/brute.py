@@ -159,3 +159,58 @@ def attention(q, k, v, perm, sel: Dict[Tuple[int, int], List[int]], B: int, S: O
                              for t in range(d)]
                 lse[h][i] = m + math.log(z)
     return out, lse, kept
+
+
+def s2o_processed(q, k, perm, B: int, S: int, gain_tau: float, scale: float) -> Dict[Tuple[int, int], List[int]]:
+    """Blocks the marginal-gain early stop processes per (h, I), from its definition.
+
+    Order: the blocks of I's own segment ascending, then the earlier-segment blocks picked one by
+    one as the remaining block with the largest pooled logit (the smallest J among equals).  The
+    stop is the first earlier-segment block b of that order after which, for every query i of
+    block I, the exact share of b in the softmax denominator over all processed keys (each sum an
+    fsum of exp(s - M_i) with M_i the max over every key <= i of the row) is below gain_tau.
+    """
+    Hq, N, d = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    NB = -(-N // B)
+    out = {}
+    for h in range(Hq):
+        g = h // G
+        pg = None if perm is None else perm[g]
+        for I in range(NB):
+            qrows = list(range(I * B, min((I + 1) * B, N)))
+            qbar = [math.fsum(float(q[h][i][t]) for i in qrows) / len(qrows) for t in range(d)]
+            z = {}
+            for J in range(I + 1):
+                kr = _key_rows(J, I, pg, B, S, N)
+                kbar = [math.fsum(float(k[g][j][t]) for j in kr) / len(kr) for t in range(d)]
+                z[J] = scale * _dot(qbar, kbar)
+            own = [J for J in range(I + 1) if _seg(J * B, S) == _seg(I * B, S)]
+            rest = [J for J in range(I + 1) if _seg(J * B, S) < _seg(I * B, S)]
+            order = list(own)
+            while rest:
+                best = max(rest, key=lambda J: (z[J], -J))
+                order.append(best)
+                rest.remove(best)
+            logit = {(i, j): scale * _dot(q[h][i], k[g][j]) for i in qrows
+                     for J in order for j in _key_rows(J, I, pg, B, S, N) if j <= i}
+            ref = {i: max(v for (ii, _), v in logit.items() if ii == i) for i in qrows}
+            done = []
+            for t, J in enumerate(order):
+                done.append(J)
+                if _seg(J * B, S) == _seg(I * B, S):
+                    continue
+                stop = True
+                for i in qrows:
+                    keys_all = [j for JJ in done for j in _key_rows(JJ, I, pg, B, S, N) if j <= i]
+                    keys_b = [j for j in _key_rows(J, I, pg, B, S, N) if j <= i]
+                    ell = math.fsum(math.exp(logit[(i, j)] - ref[i]) for j in keys_all)
+                    dl = math.fsum(math.exp(logit[(i, j)] - ref[i]) for j in keys_b)
+                    if not dl < gain_tau * ell:
+                        stop = False
+                        break
+                if stop:
+                    break
+            out[(h, I)] = done
+    return out

@@ -20,7 +20,11 @@ design notes of the repository):
   * the mask keeps the shortest prefix of the (p desc, J asc) order whose cumulative mass
     reaches tau (>=), plus the forced blocks; tau >= 1 keeps every J <= I;
   * the early-stop gate is decided per whole tile on the exact max of the scaled causal
-    logits; a skipped tile contributes nothing to the softmax state.
+    logits; a skipped tile contributes nothing to the softmax state;
+  * the marginal-gain early stop visits the query block's own segment first (ascending), then the
+    earlier-segment blocks by pooled logit descending (ties by J), and stops a tile row after the
+    first earlier-segment block whose share of every query's softmax denominator (that block
+    included) is below the threshold; that block stays processed.
 """
 from __future__ import annotations
 
@@ -145,6 +149,27 @@ def pool_permuted_blocks(k: np.ndarray, perm: np.ndarray, block_size: int) -> np
     return out
 
 
+class _PooledLogits:
+    """z_IJ = c * Qbar_{h,I} . Kbar_J for J <= I (Sparser Block-Sparse Attention via Token
+    Permutation, §4: mean pooling, on the permuted keys for blocks of earlier segments)."""
+
+    def __init__(self, q, k, perm, block_size, segment_size, scale):
+        Hq, N, d = q.shape
+        self.G = Hq // k.shape[0]
+        self.B, self.S = block_size, segment_size
+        self.c = default_scale(d) if scale is None else scale
+        self.qbar = pool_blocks(q, block_size)
+        self.knat = pool_blocks(k, block_size)
+        self.kperm = pool_permuted_blocks(k, perm, block_size) if perm is not None else self.knat
+
+    def row(self, h: int, I: int) -> np.ndarray:
+        g = h // self.G
+        sI = segment_of_block(I, self.B, self.S)
+        kbar = np.stack([self.kperm[g, J] if segment_of_block(J, self.B, self.S) < sI else self.knat[g, J]
+                         for J in range(I + 1)])
+        return self.c * (kbar @ self.qbar[h, I])
+
+
 def block_mask(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_size: int,
                segment_size: Optional[int], mass_tau: float, force_diag: bool = True,
                force_first: bool = True, scale: Optional[float] = None):
@@ -164,25 +189,16 @@ def block_mask(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_s
     prob [Hq][NB(NB+1)/2] fp64 = p per row).
     """
     Hq, N, d = q.shape
-    Hkv = k.shape[0]
-    G = Hq // Hkv
-    B, S = block_size, segment_size
+    B = block_size
     NB = num_blocks(N, B)
-    c = default_scale(d) if scale is None else scale
-    qbar = pool_blocks(q, B)
-    knat = pool_blocks(k, B)
-    kperm = pool_permuted_blocks(k, perm, B) if perm is not None else knat
+    logits = _PooledLogits(q, k, perm, block_size, segment_size, scale)
     ntri = NB * (NB + 1) // 2
     count = np.zeros((Hq, NB), dtype=np.int64)
     idx = np.full((Hq, ntri), -1, dtype=np.int64)
     prob = np.full((Hq, ntri), np.nan)
     for h in range(Hq):
-        g = h // G
         for I in range(NB):
-            sI = segment_of_block(I, B, S)
-            kbar = np.stack([kperm[g, J] if segment_of_block(J, B, S) < sI else knat[g, J]
-                             for J in range(I + 1)])
-            z = c * (kbar @ qbar[h, I])
+            z = logits.row(h, I)
             e = np.exp(z - z.max())
             p = e / e.sum()
             order = np.lexsort((np.arange(I + 1), -p))
@@ -202,6 +218,106 @@ def block_mask(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_s
             idx[h, o:o + len(lst)] = lst
             prob[h, o:o + I + 1] = p
     return count, idx, prob
+
+
+def ranked_blocks(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_size: int,
+                  segment_size: int, scale: Optional[float] = None):
+    """Order in which the marginal-gain early stop visits the key blocks of each query block.
+
+    S2O, "Early-Stopping Rule": candidate blocks are processed in descending order of estimated
+    importance; "Kernel Implementation": pass 1 computes the dense causal window inside the query's
+    own segment, pass 2 walks the historical prefix in the permuted order.  Reading: row (h, I)
+    lists every J <= I; first the blocks of I's own segment, ascending (pass 1), then the blocks of
+    earlier segments (pass 2) by the pooled block logit z of stage 2 (the estimate of Sparser
+    Block-Sparse Attention via Token Permutation, §4; softmax is monotone in z, so this is also the
+    order by p), descending, ties by J ascending.
+
+    Returns (count [Hq][NB] = I + 1, idx [Hq][NB(NB+1)/2] int64, n_intra [Hq][NB]).
+    """
+    Hq, N, d = q.shape
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    logits = _PooledLogits(q, k, perm, block_size, segment_size, scale)
+    count = np.zeros((Hq, NB), dtype=np.int64)
+    idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    n_intra = np.zeros((Hq, NB), dtype=np.int64)
+    for h in range(Hq):
+        for I in range(NB):
+            sI = segment_of_block(I, B, S)
+            intra = [J for J in range(I + 1) if segment_of_block(J, B, S) == sI]
+            hist = [J for J in range(I + 1) if segment_of_block(J, B, S) < sI]
+            z = logits.row(h, I)
+            hist.sort(key=lambda J: (-z[J], J))
+            o = tri_offset(I)
+            idx[h, o:o + I + 1] = intra + hist
+            count[h, I] = I + 1
+            n_intra[h, I] = len(intra)
+    return count, idx, n_intra
+
+
+def s2o_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: Optional[np.ndarray],
+                  count: np.ndarray, idx: np.ndarray, block_size: int, segment_size: int,
+                  gain_tau: float, scale: Optional[float] = None,
+                  rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """Attention with the marginal-gain early stop over a ranked block list.
+
+    S2O, "Early-Stopping Rule": the attention mass each processed block adds (delta l) is tracked,
+    and once it falls below a threshold relative to the accumulated score the rest of the list is
+    skipped.  Reading: row (h, I) takes the list in order; the blocks of I's own segment are always
+    processed; after each earlier-segment block b, with l_i the softmax denominator of query i over
+    every key processed so far (b included) and dl_i the part b contributed, the row stops when
+    dl_i < gain_tau * l_i for every query i of the block; b itself stays processed.  Both sums use
+    one reference per query, which cancels in the ratio.  The output is exact softmax attention
+    over the processed blocks (block_sparse_attention on that set).
+
+    Returns (out [Hq][N][d], lse [Hq][N], processed {(h, I): [J in processing order]}).
+    """
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    todo = [(h, I) for h in range(Hq) for I in range(NB)] if rows is None else list(rows)
+    processed: Dict[Tuple[int, int], List[int]] = {}
+    for h, I in todo:
+        g = h // G
+        perm_g = None if perm is None else perm[g]
+        qi = block_range(I, B, N)
+        o = tri_offset(I)
+        lst = [int(J) for J in idx[h, o:o + int(count[h, I])]]
+        sI = segment_of_block(I, B, S)
+        # per-block masked logits and a common reference per query (the max over every listed key)
+        blk = []
+        for J in lst:
+            kj = key_rows_of_block(J, I, perm_g, B, S, N)
+            st = c * (q[h, qi] @ k[g, kj].T)
+            blk.append(np.where(kj[None, :] <= qi[:, None], st, -np.inf))
+        ref = np.max(np.concatenate(blk, axis=1), axis=1)
+        ell = np.zeros(len(qi))
+        done: List[int] = []
+        for J, st in zip(lst, blk):
+            dl = np.exp(st - ref[:, None]).sum(axis=1)
+            ell = ell + dl
+            done.append(J)
+            if segment_of_block(J, B, S) < sI and np.all(dl < gain_tau * ell):
+                break
+        processed[(h, I)] = done
+    kc, ki = _lists_to_mask(processed, Hq, NB)
+    rows_done = list(processed.keys())
+    out, lse, _, _ = block_sparse_attention(q, k, v, perm, kc, ki, B, S, scale=scale, rows=rows_done)
+    return out, lse, processed
+
+
+def _lists_to_mask(lists: Dict[Tuple[int, int], Sequence[int]], Hq: int, NB: int):
+    count = np.zeros((Hq, NB), dtype=np.int64)
+    idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    for (h, I), lst in lists.items():
+        srt = sorted(lst)
+        o = tri_offset(I)
+        count[h, I] = len(srt)
+        idx[h, o:o + len(srt)] = srt
+    return count, idx
 
 
 # ----------------------------------------------------------------------------- stage 3: attention

@@ -71,3 +71,19 @@ def test_oracle_matches_brute_force(c):
     assert kept == kept_b
     np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)
+
+
+@settings(max_examples=30, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case(), st.sampled_from([0.0, 1e-3, 1e-2, 5e-2, 0.2, 1.0]))
+def test_marginal_gain_stop_matches_brute_force(c, gain_tau):
+    N, Hq, Hkv, d, B, S = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"], c["S"]
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S) if c["perm_on"] else None
+    count, idx, n_intra = oracle.ranked_blocks(q, k, perm, B, S)
+    out, lse, done = oracle.s2o_attention(q, k, v, perm, count, idx, B, S, gain_tau)
+    done_b = brute.s2o_processed(q, k, perm, B, S, gain_tau, scale)
+    assert done == done_b
+    out_b, lse_b, _ = brute.attention(q, k, v, perm, {key: sorted(val) for key, val in done_b.items()}, B, S, scale)
+    np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)

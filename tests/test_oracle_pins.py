@@ -290,3 +290,71 @@ def test_tile_max_matches_dense_logits():
             for J in range(I + 1):
                 blockvals = [s[i, j] for i in range(I * B, (I + 1) * B) for j in range(J * B, (J + 1) * B) if j <= i]
                 assert abs(tm[h, oracle.tri_offset(I) + J] - max(blockvals)) <= 1e-13 * max(1.0, abs(max(blockvals)))
+
+
+
+# ---------------------------------------------------------------- marginal-gain early stop (S2O)
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ranked_order_is_own_segment_then_history_by_pooled_probability(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=21)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S)
+    count, idx, n_intra = oracle.ranked_blocks(q, k, perm, B, S)
+    _, _, prob = oracle.block_mask(q, k, perm, B, S, 1.0, False, False)
+    NB = oracle.num_blocks(N, B)
+    for h in range(Hq):
+        for I in range(NB):
+            o = oracle.tri_offset(I)
+            row = idx[h, o:o + count[h, I]].tolist()
+            assert count[h, I] == I + 1 and sorted(row) == list(range(I + 1))
+            ni = int(n_intra[h, I])
+            sI = oracle.segment_of_block(I, B, S)
+            assert row[:ni] == [J for J in range(I + 1) if oracle.segment_of_block(J, B, S) == sI]
+            p = prob[h, o:o + I + 1]
+            hist = row[ni:]
+            assert all(oracle.segment_of_block(J, B, S) < sI for J in hist)
+            # softmax of the pooled logits is non-increasing along the history order
+            assert all(p[a] >= p[b] for a, b in zip(hist, hist[1:]))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_marginal_gain_zero_threshold_is_dense_causal(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=22)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S)
+    count, idx, _ = oracle.ranked_blocks(q, k, perm, B, S)
+    out, lse, done = oracle.s2o_attention(q, k, v, perm, count, idx, B, S, 0.0)
+    assert all(len(lst) == I + 1 for (h, I), lst in done.items())
+    ref, ref_lse = oracle.dense_attention(q, k, v)
+    assert np.abs(out - ref).max() <= 1e-12
+    assert np.abs(lse - ref_lse).max() <= 1e-12
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_marginal_gain_threshold_one_stops_after_one_history_block(shape):
+    # a block's share of a denominator that also holds the own-segment keys is always below 1
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=23)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S)
+    count, idx, n_intra = oracle.ranked_blocks(q, k, perm, B, S)
+    _, _, done = oracle.s2o_attention(q, k, v, perm, count, idx, B, S, 1.0)
+    for (h, I), lst in done.items():
+        o = oracle.tri_offset(I)
+        ni = int(n_intra[h, I])
+        want = idx[h, o:o + min(ni + 1, I + 1)].tolist()
+        assert lst == want, (h, I)
+
+
+def test_marginal_gain_stop_is_monotone_in_threshold():
+    N, Hq, Hkv, d, B, S = 96, 2, 1, 8, 8, 32
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=24)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S)
+    count, idx, _ = oracle.ranked_blocks(q, k, perm, B, S)
+    prev = None
+    for tau in (0.0, 1e-4, 1e-3, 1e-2, 0.1, 1.0):
+        _, _, done = oracle.s2o_attention(q, k, v, perm, count, idx, B, S, tau)
+        n = {key: len(val) for key, val in done.items()}
+        if prev is not None:
+            assert all(n[key] <= prev[key] for key in n)
+        prev = n
