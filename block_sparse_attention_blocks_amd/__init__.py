@@ -15,7 +15,7 @@ from typing import Optional, Tuple
 import torch
 
 from . import _lib
-from ._lib import (PBSA_FORCE_DIAG, PBSA_FORCE_FIRST, PBSA_OP_ATTENTION, PBSA_OP_MASK,  # noqa: F401
+from ._lib import (PBSA_FORCE_DIAG, PBSA_FORCE_FIRST, PBSA_MASK_RANKED, PBSA_OP_ATTENTION, PBSA_OP_MASK,  # noqa: F401
                    PBSA_OP_PERMUTATION, PbsaError, PbsaShape)
 
 __all__ = [
@@ -24,6 +24,7 @@ __all__ = [
     "block_sparse_attn_prefill",
     "tile_max",
     "calibrate_thresholds",
+    "s2o_attn_prefill",
     "workspace_size",
     "make_shape",
     "num_blocks",
@@ -113,8 +114,11 @@ def estimate_block_mask(q: torch.Tensor, k: torch.Tensor, perm: Optional[torch.T
                         segment_size: int, mass_tau: float, force_diag: bool = True, force_first: bool = True,
                         scale: Optional[float] = None, return_prob: bool = False,
                         out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
-                        workspace: Optional[torch.Tensor] = None):
-    """Stage 2: (block_count int32 [Hq][NB], block_idx int32 [Hq][NB(NB+1)/2][, prob fp64])."""
+                        workspace: Optional[torch.Tensor] = None, ranked: bool = False):
+    """Stage 2: (block_count int32 [Hq][NB], block_idx int32 [Hq][NB(NB+1)/2][, prob fp64]).
+
+    ranked: list every J <= I in the order of the marginal-gain early stop instead of applying the
+    mass cut (mass_tau and the force flags are then not used, and no probabilities are written)."""
     _check_bf16("q", q)
     _check_bf16("k", k)
     shape = make_shape(q, k, block_size, segment_size, scale)
@@ -127,6 +131,10 @@ def estimate_block_mask(q: torch.Tensor, k: torch.Tensor, perm: Optional[torch.T
         count, idx = out
     prob = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.float64, device=q.device) if return_prob else None
     flags = (PBSA_FORCE_DIAG if force_diag else 0) | (PBSA_FORCE_FIRST if force_first else 0)
+    if ranked:
+        if return_prob:
+            raise ValueError("the ranked order writes no probabilities")
+        flags |= PBSA_MASK_RANKED
     ws, nbytes = _workspace(shape, PBSA_OP_MASK, q.device, workspace)
     st = _lib.lib().pbsa_estimate_block_mask(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(perm), float(mass_tau),
                                              flags, _ptr(count), _ptr(idx), _ptr(prob), _ptr(ws), nbytes, _stream())
@@ -169,6 +177,45 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
         _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
     _lib.check(st, "pbsa_block_sparse_attn_prefill")
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_kept:
+        res.append(kept)
+    if return_error:
+        res.append(err)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def s2o_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, perm: Optional[torch.Tensor],
+                     block_count: torch.Tensor, block_idx: torch.Tensor, block_size: int, segment_size: int,
+                     gain_tau: float, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, return_lse: bool = True, return_kept: bool = False,
+                     return_error: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Attention with the marginal-gain early stop over a ranked list (estimate_block_mask with
+    ranked=True): out fp32 [Hq][N][d] (+ lse, processed-block bitmap, device error word)."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    _check_bf16("v", v, heads=k.shape[0])
+    if v.stride() != k.stride():
+        raise ValueError("k and v must share strides")
+    Hq, N, d = q.shape
+    if out is None:
+        out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    NB = num_blocks(N, block_size)
+    kept = None
+    if return_kept:
+        words = -(-(NB * (NB + 1) // 2) // 32)
+        kept = torch.zeros((Hq, words), dtype=torch.int32, device=q.device)
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if return_error else None
+    shape = make_shape(q, k, block_size, segment_size, scale, out=out)
+    ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
+    st = _lib.lib().pbsa_s2o_attn_prefill(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
+        float(gain_tau), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_s2o_attn_prefill")
     res = [out]
     if return_lse:
         res.append(lse)

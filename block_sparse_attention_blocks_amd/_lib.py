@@ -22,6 +22,7 @@ PBSA_OP_ATTENTION = 2
 
 PBSA_FORCE_DIAG = 1
 PBSA_FORCE_FIRST = 2
+PBSA_MASK_RANKED = 4
 
 SIZE_MAX = ctypes.c_size_t(-1).value
 
@@ -61,6 +62,8 @@ _SIG = {
                                                 ctypes.c_uint32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_block_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
                                                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pbsa_s2o_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                             _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_tile_max": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P]),
     "pbsa_calibrate_thresholds": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, ctypes.c_int32, _P, _P]),
     "pbsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -111,7 +111,8 @@ pbsa_status pbsa_estimate_block_mask(const pbsa_shape* shape, const uint16_t* q,
   if (!q || !k || !block_count || !block_idx || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
   if (perm && g.S <= 0) return PBSA_ERR_INVALID_ARG;
   if (!(mass_tau > 0.0 && mass_tau <= 1.0)) return PBSA_ERR_INVALID_ARG;
-  if (flags & ~(uint32_t)(PBSA_FORCE_DIAG | PBSA_FORCE_FIRST)) return PBSA_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(PBSA_FORCE_DIAG | PBSA_FORCE_FIRST | PBSA_MASK_RANKED)) return PBSA_ERR_INVALID_ARG;
+  if ((flags & PBSA_MASK_RANKED) && (g.S <= 0 || block_prob)) return PBSA_ERR_INVALID_ARG;
   if (block_prob && (reinterpret_cast<uintptr_t>(block_prob) & 7u)) return PBSA_ERR_INVALID_ARG;
   if ((st = check_workspace(pbsa::mask_workspace_bytes(g), workspace, workspace_bytes)) != PBSA_OK) return st;
   if (g.N == 0) return PBSA_OK;
@@ -136,6 +137,25 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
   if (g.N == 0) return PBSA_OK;
   return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out, lse,
                                          kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream)));
+}
+
+pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* perm, const int32_t* block_count,
+                                  const int32_t* block_idx, float gain_tau, float* out, float* lse,
+                                  uint32_t* kept_bitmap, int32_t* device_error, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (!q || !k || !v || !out || !block_count || !block_idx) return PBSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PBSA_ERR_INVALID_ARG;
+  if (g.S <= 0 || !(gain_tau >= 0.f) || !(gain_tau < INFINITY)) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
+    return st;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_s2o_attention(g, q, k, v, perm, block_count, block_idx, gain_tau, out, lse,
+                                             kept_bitmap, device_error, workspace,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, float* tile_max,

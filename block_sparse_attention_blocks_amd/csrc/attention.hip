@@ -58,6 +58,7 @@ struct AttnArgs {
   uint32_t q_bytes, kv_bytes;            // bytes of one head's slab (buffer bound)
   float scale;  // c
   float sl2;    // c * log2(e)
+  float gain_tau;             // marginal-gain early stop threshold (S2O kernels)
   unsigned long long* queue;  // work deques of the pipelined kernels (workspace)
   int nq;                     // number of deques: one per KV group, at most one per XCD
   int Hkv;
@@ -163,6 +164,7 @@ struct SoftmaxState {
   float l;     // sum of the bf16-rounded probabilities relative to m (this lane's half of the keys)
   float thr;   // (m + kLazy) in raw score units: a block whose raw max exceeds it moves m
   float muse;  // m, or 0 while m is -inf (no finite score yet), as the exponent offset
+  float lb;    // l when the current key block started, rescaled with l (marginal-gain stop)
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int db = 0; db < AttnCfg<D, BLK>::DB; ++db)
@@ -172,6 +174,7 @@ struct SoftmaxState {
     l = 0.f;
     thr = -INFINITY;
     muse = 0.f;
+    lb = 0.f;
   }
 };
 
@@ -184,6 +187,7 @@ __device__ __forceinline__ void lazy_rescale(SoftmaxState<D, BLK>& st, float raw
     const float m_new = need ? raw_max * sl2 : st.m;
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     st.l *= alpha;
+    st.lb *= alpha;
 #pragma unroll
     for (int db = 0; db < AttnCfg<D, BLK>::DB; ++db)
 #pragma unroll
@@ -456,6 +460,34 @@ __device__ __forceinline__ int union_list(const AttnArgs& a, int h0, int I, size
   return *mcount;
 }
 
+// The ranked key-block list of one head (marginal-gain early stop), kept in its order, into mlist
+// as J | head bit.  An entry out of range is flagged in a.err and kept without the head bit, so its
+// stage is gathered but not computed.  Returns the list length.
+template <int THREADS>
+__device__ __forceinline__ int ranked_list(const AttnArgs& a, int h, int I, size_t ntri, uint32_t* mlist,
+                                           int* mcount) {
+  const int t = threadIdx.x;
+  if (t == 0) {
+    int cnt = a.count[(size_t)h * a.NB + I];
+    if (cnt < 0 || cnt > I + 1) {
+      if (a.err) atomicOr(a.err, 4);
+      cnt = cnt < 0 ? 0 : I + 1;
+    }
+    *mcount = cnt;
+  }
+  __syncthreads();
+  const int cnt = *mcount;
+  const int32_t* list = a.idx + (size_t)h * ntri + tri_offset(I);
+  for (int k = t; k < cnt; k += THREADS) {
+    const int J = list[k];
+    const bool ok = J >= 0 && J <= I;
+    if (!ok && a.err) atomicOr(a.err, 1);
+    mlist[k] = ok ? ((uint32_t)J | (1u << 16)) : 0u;
+  }
+  __syncthreads();
+  return cnt;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Work distribution of the pipelined kernels.  A work item is one query block I for one unit of
 // HPW query heads.  Deque q holds, in order of descending I, the items of the KV groups g with
@@ -516,10 +548,15 @@ __device__ __forceinline__ int xcd_id() { return (int)(__builtin_amdgcn_s_getreg
 // once into LDS and used by the waves of every head that kept the block (the query heads of a
 // group usually keep nearly the same blocks).  While stage s is computed, stages s+1 .. s+NBUF-1
 // are in flight, and the physical row ids of stage s+NBUF are fetched from perm.
-template <int D, int BLK, bool DENSE, int HPW>
+//
+// S2O = true (one head per workgroup): the list is the head's ranked list, taken in its order, and
+// after every earlier-segment block the workgroup stops the row when each query's share of that
+// block in its softmax denominator is below a.gain_tau (S2O, Early-Stopping Rule).
+template <int D, int BLK, bool DENSE, int HPW, bool S2O = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PipeCfg<D, BLK, HPW>::THREADS, PipeCfg<D, BLK, HPW>::THREADS),
                           amdgpu_waves_per_eu(2)))
 void attn_pipe_kernel(AttnArgs a) {
+  static_assert(!S2O || (HPW == 1 && !DENSE), "the marginal-gain stop runs one head per workgroup");
   using C = PipeCfg<D, BLK, HPW>;
   constexpr int KT = C::KT;
   constexpr int NBUF = C::NBUF;
@@ -546,6 +583,7 @@ void attn_pipe_kernel(AttnArgs a) {
   };
 
   __shared__ int item_sh;
+  __shared__ int stop_flag[2][S2O ? C::WAVES : 1];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int l32 = lane & 31, h2 = lane >> 5;
@@ -593,7 +631,9 @@ void attn_pipe_kernel(AttnArgs a) {
   }
 
   // merged key-block list: ascending J kept by any of the workgroup's heads
-  const int nblk = DENSE ? I + 1 : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
+  const int nblk = DENSE ? I + 1
+                   : S2O ? ranked_list<C::THREADS>(a, h0, I, ntri, mlist, &mcount)
+                         : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
   const int nst = nblk * C::STAGES;
   const int sI = a.S > 0 ? I0 / a.S : 0;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
@@ -647,7 +687,7 @@ void attn_pipe_kernel(AttnArgs a) {
   // s+NBUF-1 is gathered into the buffer of stage s-1.  The row ids of stage s+NBUF are stored from
   // the lookup issued one step earlier, and the lookup of stage s+NBUF+1 is issued.
   constexpr int LOOK = DENSE ? 0 : 1;  // lookup loads per wave per step
-  auto step = [&](int s, int b) __attribute__((always_inline)) {  // b = s % NBUF
+  auto step = [&](int s, int b) __attribute__((always_inline)) -> bool {  // b = s % NBUF
     const uint16_t* Kc = Kb(b);
     const uint16_t* Vc = Vb(b);
     RowLook pr_next;
@@ -663,7 +703,17 @@ void attn_pipe_kernel(AttnArgs a) {
         const size_t bit = tri_offset(I) + J;
         atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
       }
+      if (S2O && (s % C::STAGES) == 0) st.lb = st.l;  // a new key block starts
       stage_compute<D, BLK>(st, Kc, Vc, qf, J == I, qloc - koff - 4 * h2, a.sl2);
+      if (S2O && (s % C::STAGES) == C::STAGES - 1) {
+        // this block's share of each query's denominator (both half-waves of the query summed)
+        float la, lbh, da, db;
+        half_swap(st.l, &la, &lbh);
+        half_swap(st.l - st.lb, &da, &db);
+        const bool small = !qvalid || (da + db < a.gain_tau * (la + lbh));
+        const bool wave_small = __builtin_amdgcn_ballot_w64(small) == ~0ull;  // taken by the whole wave
+        if (lane == 0) stop_flag[(s / C::STAGES) & 1][wave] = wave_small;
+      }
     }
     if (!DENSE && s + NBUF < nst && t < KT) rowid[b][t] = row_off(pr_prev);  // slot of stage s+NBUF
     if (!DENSE) pr_prev = pr_next;
@@ -674,12 +724,38 @@ void attn_pipe_kernel(AttnArgs a) {
       wait_vmcnt<0>();
     }
     lds_barrier();
+    if (S2O && s < nst && (s % C::STAGES) == C::STAGES - 1) {
+      // after an earlier-segment block: stop when every wave found its share below the threshold
+      const uint32_t e2 = entry_of(s);
+      const int J = (int)(e2 & 0xffffu);
+      if (((e2 >> 16) & 1u) && a.S > 0 && (J * BLK) / a.S < sI) {
+        bool all = true;
+#pragma unroll
+        for (int x = 0; x < C::WAVES; ++x) all = all && stop_flag[(s / C::STAGES) & 1][x];
+        return all;
+      }
+    }
+    return false;
   };
   // every trip runs all NBUF steps (the ones past the end only wait and synchronise), so the
   // pending lookup passes from step to step without a copy that would wait for it
-  for (int s = 0; s < nst; s += NBUF) {
+  if constexpr (S2O) {
+    bool stopped = false;
+    for (int s = 0; s < nst && !stopped; s += NBUF) {
 #pragma unroll
-    for (int x = 0; x < NBUF; ++x) step(s + x, x);
+      for (int x = 0; x < NBUF; ++x) {
+        if (step(s + x, x)) {
+          stopped = true;
+          break;
+        }
+      }
+    }
+    if (stopped) wait_vmcnt<0>();  // gathers already issued for later stages land before reuse
+  } else {
+    for (int s = 0; s < nst; s += NBUF) {
+#pragma unroll
+      for (int x = 0; x < NBUF; ++x) step(s + x, x);
+    }
   }
   write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
   __syncthreads();  // every wave is done with this item's LDS before the next claim
@@ -1055,7 +1131,7 @@ void attn_gated_kernel(AttnArgs a) {
 
 // Persistent launch of the pipelined kernel: the deques are reset on the stream, then as many
 // workgroups start as fit on the device at once (never more than there are items).
-template <int D, int BLK, bool DENSE, int HPW>
+template <int D, int BLK, bool DENSE, int HPW, bool S2O = false>
 static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st) {
   constexpr int THREADS = PipeCfg<D, BLK, HPW>::THREADS;
   static int resident[64] = {0};  // workgroups resident on the whole device, per device ordinal
@@ -1066,15 +1142,15 @@ static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st
   if (resident[dev] == 0) {
     int cus = 0, per_cu = 0;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_pipe_kernel<D, BLK, DENSE, HPW>, THREADS,
-                                                          0)) != hipSuccess)
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_pipe_kernel<D, BLK, DENSE, HPW, S2O>,
+                                                          THREADS, 0)) != hipSuccess)
       return e;
     resident[dev] = cus * (per_cu > 0 ? per_cu : 1);
   }
   if ((long long)a.NB * (a.Hq / HPW) >= (1ll << 24)) return hipErrorInvalidValue;  // item index field
   deque_init_kernel<<<1, 64, 0, st>>>(a, a.G / HPW);
   const int grid = items < resident[dev] ? items : resident[dev];
-  attn_pipe_kernel<D, BLK, DENSE, HPW><<<grid, THREADS, 0, st>>>(a);
+  attn_pipe_kernel<D, BLK, DENSE, HPW, S2O><<<grid, THREADS, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -1197,6 +1273,29 @@ hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* 
   const int rows = Hq * NB;
   calibrate_kernel<<<(rows + 3) / 4, 256, 0, st>>>(tmax, Hq, NB, keep, theta);
   return hipGetLastError();
+}
+
+hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* perm, const int32_t* count, const int32_t* idx, float gain_tau,
+                                float* out, float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st) {
+  AttnArgs a = make_args(g);
+  a.queue = static_cast<unsigned long long*>(ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.perm = perm;
+  a.count = count;
+  a.idx = idx;
+  a.out = out;
+  a.lse = lse;
+  a.kept = kept;
+  a.err = err;
+  a.gain_tau = gain_tau;
+  const int items = g.Hq * g.NB;
+  if (g.d == 128 && g.B == 128) return launch_persistent<128, 128, false, 1, true>(a, items, st);
+  if (g.d == 128 && g.B == 64) return launch_persistent<128, 64, false, 1, true>(a, items, st);
+  if (g.d == 64 && g.B == 128) return launch_persistent<64, 128, false, 1, true>(a, items, st);
+  return launch_persistent<64, 64, false, 1, true>(a, items, st);
 }
 
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax, hipStream_t st) {

@@ -67,6 +67,7 @@ hipError_t launch_build_permutation(const Geometry& g, const uint16_t* q, const 
 
 // Stage 2.
 size_t mask_workspace_bytes(const Geometry& g);
+constexpr uint32_t kMaskRanked = 4u;  // PBSA_MASK_RANKED
 hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_t* k, const int32_t* perm,
                              double tau, uint32_t flags, int32_t* count, int32_t* idx, double* prob,
                              void* ws, hipStream_t st);
@@ -79,6 +80,9 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
                             const int32_t* perm, const int32_t* count, const int32_t* idx,
                             const float* theta, float* out, float* lse, uint32_t* kept, int32_t* err,
                             void* ws, hipStream_t st);
+hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* perm, const int32_t* count, const int32_t* idx, float gain_tau,
+                                float* out, float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st);
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax,
                            hipStream_t st);
 hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);

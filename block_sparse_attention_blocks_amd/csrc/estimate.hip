@@ -729,6 +729,65 @@ size_t mask_workspace_bytes(const Geometry& g) {
          align256(sizeof(double) * g.Hq * (NB * (NB + 1) / 2));
 }
 
+// =====================================================================================
+// Ranked block order of the marginal-gain early stop (S2O, Early-Stopping Rule: blocks are visited
+// in descending estimated importance; Kernel Implementation: the dense window of the query's own
+// segment first).  Row (h, I) lists every J <= I: the blocks of I's segment ascending, then the
+// earlier-segment blocks by pooled logit z descending, ties by J ascending.  One workgroup per row:
+// a bitonic sort in LDS on (order-preserving 64-bit key of -z, J).
+// =====================================================================================
+constexpr int RANK_THREADS = 256;
+constexpr int RANK_MAX = 2048;
+
+__device__ __forceinline__ uint64_t desc_key(double x) {  // ascending in this key = descending in x
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint64_t o = (b & 0x8000000000000000ull) ? ~b : (b | 0x8000000000000000ull);
+  return ~o;
+}
+
+__global__ __launch_bounds__(RANK_THREADS) void block_rank_kernel(const double* z, int NB, int bps, int32_t* count,
+                                                                  int32_t* idx) {
+  __shared__ uint64_t key[RANK_MAX];
+  __shared__ uint16_t jj[RANK_MAX];
+  const int t = threadIdx.x;
+  const int row = blockIdx.x, h = row / NB, I = row % NB;
+  const int J0 = (I / bps) * bps;  // first block of I's segment; J < J0 are the earlier segments
+  const size_t ntri = (size_t)NB * (NB + 1) / 2;
+  const double* zr = z + (size_t)h * ntri + (size_t)tri_offset(I);
+  int n = 1;
+  while (n < J0) n <<= 1;
+  for (int x = t; x < n; x += RANK_THREADS) {
+    const bool live = x < J0;
+    key[x] = live ? desc_key(zr[x]) : ~0ull;
+    jj[x] = live ? (uint16_t)x : (uint16_t)0xffffu;
+  }
+  __syncthreads();
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int x = t; x < n / 2; x += RANK_THREADS) {
+        const int lo = 2 * x - (x & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t ka = key[lo], kb = key[hi];
+        const uint16_t ja = jj[lo], jb = jj[hi];
+        const bool a_after_b = (ka > kb) || (ka == kb && ja > jb);
+        if (a_after_b == up) {
+          key[lo] = kb;
+          key[hi] = ka;
+          jj[lo] = jb;
+          jj[hi] = ja;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* out = idx + (size_t)h * ntri + (size_t)tri_offset(I);
+  const int nin = I + 1 - J0;
+  for (int x = t; x < nin; x += RANK_THREADS) out[x] = J0 + x;
+  for (int x = t; x < J0; x += RANK_THREADS) out[nin + x] = jj[x];
+  if (t == 0) count[row] = I + 1;
+}
+
 hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_t* k, const int32_t* perm,
                              double tau, uint32_t flags, int32_t* count, int32_t* idx, double* prob,
                              void* ws, hipStream_t st) {
@@ -767,6 +826,10 @@ hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_
     block_logits_kernel<128><<<zgrid, ZL_THREADS, 0, st>>>(za);
   } else {
     block_logits_kernel<64><<<zgrid, ZL_THREADS, 0, st>>>(za);
+  }
+  if (flags & kMaskRanked) {
+    block_rank_kernel<<<g.Hq * g.NB, RANK_THREADS, 0, st>>>(z, g.NB, g.S / g.B, count, idx);
+    return hipGetLastError();
   }
   SelArgs a;
   a.z = z;

@@ -89,7 +89,13 @@ enum {
 /* Flags of pbsa_estimate_block_mask. */
 enum {
   PBSA_FORCE_DIAG = 1u,   /* always keep the diagonal block J = I */
-  PBSA_FORCE_FIRST = 2u   /* always keep block J = 0 of the row's (permuted) order */
+  PBSA_FORCE_FIRST = 2u,  /* always keep block J = 0 of the row's (permuted) order */
+  /* instead of a mass cut: list every J <= I in the order of the marginal-gain early stop (S2O,
+   * Early-Stopping Rule and Kernel Implementation): the blocks of I's own segment ascending, then
+   * the earlier-segment blocks by pooled logit z descending, ties by J ascending; count = I + 1.
+   * The force flags are then not used (mass_tau is still checked to lie in (0, 1]).  Needs
+   * segment_size > 0 and block_prob == NULL (no probabilities are written). */
+  PBSA_MASK_RANKED = 4u
 };
 
 /*
@@ -178,6 +184,28 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                            const float* early_stop_theta, float* out, float* lse,
                                            uint32_t* kept_bitmap, int32_t* device_error,
                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Attention with the marginal-gain early stop (S2O, Early-Stopping Rule; Kernel Implementation).
+ * block_count/block_idx must hold the ranked order of pbsa_estimate_block_mask with
+ * PBSA_MASK_RANKED (every J <= I: the blocks of I's own segment first, then the earlier-segment
+ * blocks by descending pooled logit).  For query block I of head h the list is processed in that
+ * order; the blocks of I's own segment are always processed.  After each earlier-segment block b,
+ * with l_i the softmax denominator of query i over every key processed so far (b included) and
+ * dl_i the part b contributed, the row stops when dl_i < gain_tau * l_i for every query i of the
+ * block (b itself stays processed).  out/lse are then softmax attention over the processed blocks,
+ * keys gathered through perm as in pbsa_block_sparse_attn_prefill.  The kernel sums bf16-rounded
+ * probabilities in fp32, so a decision within about 1% of the threshold can differ from an exact
+ * evaluation.
+ *   gain_tau     >= 0 and finite (0: never stop, every J <= I is processed)
+ *   kept_bitmap  out, or NULL: bit I(I+1)/2 + J set for every processed block (caller zeroes it)
+ *   other arguments as for pbsa_block_sparse_attn_prefill; segment_size must be > 0.
+ */
+pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                  const uint16_t* v, const int32_t* perm, const int32_t* block_count,
+                                  const int32_t* block_idx, float gain_tau, float* out, float* lse,
+                                  uint32_t* kept_bitmap, int32_t* device_error, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Early-stop calibration helper (Block Sparse Flash Attention, Approach: offline thresholds).

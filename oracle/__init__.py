@@ -22,8 +22,10 @@ from .pbsa_oracle import (  # noqa: F401
     num_blocks,
     pool_blocks,
     pool_permuted_blocks,
+    pooled_block_logits,
     ranked_blocks,
     s2o_attention,
+    s2o_gain_ratios,
     segment_of_block,
     segment_permutation,
     tile_max,

@@ -170,6 +170,20 @@ class _PooledLogits:
         return self.c * (kbar @ self.qbar[h, I])
 
 
+def pooled_block_logits(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_size: int,
+                        segment_size: Optional[int], scale: Optional[float] = None) -> np.ndarray:
+    """z of every row, fp64 [Hq][NB(NB+1)/2], row (h, I) at I(I+1)/2: the logits whose softmax is
+    block_mask's prob and whose order ranked_blocks follows."""
+    Hq, N, _ = q.shape
+    NB = num_blocks(N, block_size)
+    logits = _PooledLogits(q, k, perm, block_size, segment_size, scale)
+    z = np.full((Hq, NB * (NB + 1) // 2), np.nan)
+    for h in range(Hq):
+        for I in range(NB):
+            z[h, tri_offset(I):tri_offset(I) + I + 1] = logits.row(h, I)
+    return z
+
+
 def block_mask(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], block_size: int,
                segment_size: Optional[int], mass_tau: float, force_diag: bool = True,
                force_first: bool = True, scale: Optional[float] = None):
@@ -255,6 +269,22 @@ def ranked_blocks(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], bloc
     return count, idx, n_intra
 
 
+def _s2o_row_gains(q, k, perm_g, h, g, I, lst, B, S, N, c):
+    """For row (h, I) and its list in order: (dl, ell), each [len(lst)][rows of block I], where dl[p]
+    is what block lst[p] adds to each query's softmax denominator and ell[p] the denominator over
+    lst[0..p].  One reference per query (the max over every listed key) scales both; it cancels in
+    the ratio dl / ell."""
+    qi = block_range(I, B, N)
+    blk = []
+    for J in lst:
+        kj = key_rows_of_block(J, I, perm_g, B, S, N)
+        st = c * (q[h, qi] @ k[g, kj].T)
+        blk.append(np.where(kj[None, :] <= qi[:, None], st, -np.inf))
+    ref = np.max(np.concatenate(blk, axis=1), axis=1)
+    dl = np.stack([np.exp(st - ref[:, None]).sum(axis=1) for st in blk])
+    return dl, np.cumsum(dl, axis=0)
+
+
 def s2o_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: Optional[np.ndarray],
                   count: np.ndarray, idx: np.ndarray, block_size: int, segment_size: int,
                   gain_tau: float, scale: Optional[float] = None,
@@ -266,15 +296,13 @@ def s2o_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: Optional[np
     skipped.  Reading: row (h, I) takes the list in order; the blocks of I's own segment are always
     processed; after each earlier-segment block b, with l_i the softmax denominator of query i over
     every key processed so far (b included) and dl_i the part b contributed, the row stops when
-    dl_i < gain_tau * l_i for every query i of the block; b itself stays processed.  Both sums use
-    one reference per query, which cancels in the ratio.  The output is exact softmax attention
-    over the processed blocks (block_sparse_attention on that set).
+    dl_i < gain_tau * l_i for every query i of the block; b itself stays processed.  The output is
+    exact softmax attention over the processed blocks (block_sparse_attention on that set).
 
     Returns (out [Hq][N][d], lse [Hq][N], processed {(h, I): [J in processing order]}).
     """
     Hq, N, d = q.shape
-    Hkv = k.shape[0]
-    G = Hq // Hkv
+    G = Hq // k.shape[0]
     B, S = block_size, segment_size
     NB = num_blocks(N, B)
     c = default_scale(d) if scale is None else scale
@@ -282,31 +310,50 @@ def s2o_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: Optional[np
     processed: Dict[Tuple[int, int], List[int]] = {}
     for h, I in todo:
         g = h // G
-        perm_g = None if perm is None else perm[g]
-        qi = block_range(I, B, N)
         o = tri_offset(I)
         lst = [int(J) for J in idx[h, o:o + int(count[h, I])]]
         sI = segment_of_block(I, B, S)
-        # per-block masked logits and a common reference per query (the max over every listed key)
-        blk = []
-        for J in lst:
-            kj = key_rows_of_block(J, I, perm_g, B, S, N)
-            st = c * (q[h, qi] @ k[g, kj].T)
-            blk.append(np.where(kj[None, :] <= qi[:, None], st, -np.inf))
-        ref = np.max(np.concatenate(blk, axis=1), axis=1)
-        ell = np.zeros(len(qi))
+        dl, ell = _s2o_row_gains(q, k, None if perm is None else perm[g], h, g, I, lst, B, S, N, c)
         done: List[int] = []
-        for J, st in zip(lst, blk):
-            dl = np.exp(st - ref[:, None]).sum(axis=1)
-            ell = ell + dl
+        for p, J in enumerate(lst):
             done.append(J)
-            if segment_of_block(J, B, S) < sI and np.all(dl < gain_tau * ell):
+            if segment_of_block(J, B, S) < sI and np.all(dl[p] < gain_tau * ell[p]):
                 break
         processed[(h, I)] = done
     kc, ki = _lists_to_mask(processed, Hq, NB)
     rows_done = list(processed.keys())
     out, lse, _, _ = block_sparse_attention(q, k, v, perm, kc, ki, B, S, scale=scale, rows=rows_done)
     return out, lse, processed
+
+
+def s2o_gain_ratios(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], count: np.ndarray,
+                    idx: np.ndarray, block_size: int, segment_size: int, scale: Optional[float] = None,
+                    rows: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], np.ndarray]:
+    """The statistic the marginal-gain stop compares with its threshold, at every list position.
+
+    For row (h, I), position p of the list (the whole list, no stop applied): max over the queries
+    i of block I of dl_i / l_i as defined in s2o_attention; NaN at positions of I's own segment,
+    where the rule does not apply.  s2o_attention stops at the first position whose value is below
+    gain_tau (up to the rounding of the division), so the value at the stop position is how close
+    that decision was.
+    """
+    Hq, N, d = q.shape
+    G = Hq // k.shape[0]
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    todo = [(h, I) for h in range(Hq) for I in range(NB)] if rows is None else list(rows)
+    out: Dict[Tuple[int, int], np.ndarray] = {}
+    for h, I in todo:
+        g = h // G
+        o = tri_offset(I)
+        lst = [int(J) for J in idx[h, o:o + int(count[h, I])]]
+        sI = segment_of_block(I, B, S)
+        dl, ell = _s2o_row_gains(q, k, None if perm is None else perm[g], h, g, I, lst, B, S, N, c)
+        r = (dl / ell).max(axis=1)
+        r[[segment_of_block(J, B, S) >= sI for J in lst]] = np.nan
+        out[(h, I)] = r
+    return out
 
 
 def _lists_to_mask(lists: Dict[Tuple[int, int], Sequence[int]], Hq: int, NB: int):

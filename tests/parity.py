@@ -7,7 +7,12 @@ Tie rules, used wherever a floating-point comparison decides an integer result:
     |p_J - p_(k*)| <= 1e-6, or the oracle's running mass C_{k*-1} or C_{k*} is within 1e-6 of tau;
   * early stop: the GPU gate must equal the decision  fp32 tile max >= theta  taken on the GPU's
     own fp32 tile maxima (same precision as the kernel); against the fp64 oracle, decisions must
-    agree wherever the oracle's tile max is further than the fp32 error bound from theta.
+    agree wherever the oracle's tile max is further than the fp32 error bound from theta;
+  * ranked order (marginal-gain stop): a position where GPU and oracle list different blocks is a
+    recorded tie iff the two blocks' oracle pooled logits differ by at most 1e-6 relative;
+  * marginal-gain stop: the kernel forms dl_i / l_i from bf16-rounded probabilities (each off by
+    at most 2^-9 relative, so the ratio by under 0.4%); a stop or a go-on must agree with the
+    oracle's exact ratio wherever that ratio is more than S2O_BAND (relative) from gain_tau.
 """
 from __future__ import annotations
 
@@ -18,6 +23,7 @@ import oracle
 TIE = 1e-6
 O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
+S2O_BAND = 1e-2
 
 
 def compare_perm(perm_gpu: np.ndarray, perm_o: np.ndarray, imp_o: np.ndarray, S: int) -> int:
@@ -65,6 +71,47 @@ def compare_mask(count_g, idx_g, count_o, idx_o, prob_o, tau: float) -> int:
             assert near_p or near_c, f"mask row ({h},{I}): gpu {rg} vs oracle {ro}"
             ties += 1
     return ties
+
+
+def compare_ranked(count_g, idx_g, count_o, idx_o, z_o) -> int:
+    """Assert the GPU ranked lists equal the oracle's up to recorded ties; return the tie count."""
+    Hq, NB = count_o.shape
+    assert np.array_equal(count_g, count_o), "ranked counts differ"
+    ties = 0
+    for h in range(Hq):
+        for I in range(NB):
+            rg, ro = _row(idx_g, count_g, h, I), _row(idx_o, count_o, h, I)
+            assert sorted(rg) == list(range(I + 1)), f"ranked row ({h},{I}) is not a permutation of 0..I"
+            o = oracle.tri_offset(I)
+            for p, (a, b) in enumerate(zip(rg, ro)):
+                if a != b:
+                    za, zb = z_o[h, o + a], z_o[h, o + b]
+                    assert abs(za - zb) <= TIE * max(abs(za), abs(zb), 1.0), \
+                        f"ranked row ({h},{I}) position {p}: gpu {a} (z {za!r}) vs oracle {b} (z {zb!r})"
+                    ties += 1
+    return ties
+
+
+def compare_s2o_stops(kept, count_g, idx_g, ratios, gain_tau: float, band: float = S2O_BAND):
+    """Assert each row's processed blocks (kept: {(h, I): ascending J}) are a prefix of the GPU's
+    ranked list whose end the oracle's gain ratios allow; return (rows, rows decided in the band)."""
+    near = 0
+    for (h, I), r in ratios.items():
+        lst = _row(idx_g, count_g, h, I)
+        got = kept[(h, I)]
+        n = len(got)
+        assert n >= 1 and sorted(lst[:n]) == got, f"s2o row ({h},{I}): processed {got} is not a prefix of {lst}"
+        hist = ~np.isnan(r)
+        for p in range(n - 1):
+            assert not hist[p] or r[p] >= gain_tau * (1 - band), \
+                f"s2o row ({h},{I}): went on past position {p} with ratio {r[p]!r} < {gain_tau}"
+        if n < len(lst):
+            assert hist[n - 1] and r[n - 1] < gain_tau * (1 + band), \
+                f"s2o row ({h},{I}): stopped at position {n - 1} (ratio {r[n - 1]!r}, threshold {gain_tau})"
+        stop = np.nonzero(hist & (r < gain_tau))[0]
+        exact_n = int(stop[0]) + 1 if stop.size else len(lst)
+        near += exact_n != n
+    return len(ratios), near
 
 
 def compare_out(out_g: np.ndarray, out_o: np.ndarray, what: str = "out"):

@@ -125,8 +125,33 @@ def test_permutation_needs_segments_and_mask_needs_valid_tau_and_flags():
     for tau in (0.0, -0.5, 1.0000001, float("nan")):
         assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, tau, 3, FAKE, FAKE, None, FAKE,
                                           1 << 40, None) == E
-    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 4, FAKE, FAKE, None, FAKE,
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, None, 0.9, 8, FAKE, FAKE, None, FAKE,
                                       1 << 40, None) == E
+    # the ranked order (flag 4) needs segments
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s0), FAKE, FAKE, None, 0.9, _lib.PBSA_MASK_RANKED, FAKE, FAKE,
+                                      None, FAKE, 1 << 40, None) == E
+    # and writes no probabilities
+    assert l.pbsa_estimate_block_mask(ctypes.byref(s), FAKE, FAKE, FAKE, 0.9, _lib.PBSA_MASK_RANKED, FAKE, FAKE,
+                                      FAKE, FAKE, 1 << 40, None) == E
+
+
+def test_marginal_gain_entry_validates_before_launch():
+    l = _lib.lib()
+    E = _lib.PBSA_ERR_INVALID_ARG
+    s = shape()
+    ws = ctypes.c_void_p(0x10000)
+    args = lambda sh, cnt, idx, tau: (ctypes.byref(sh), FAKE, FAKE, FAKE, None, cnt, idx, tau, FAKE, None, None,
+                                      None, ws, 1 << 20, None)
+    assert l.pbsa_s2o_attn_prefill(*args(s, None, FAKE, 0.01)) == E        # no mask
+    assert l.pbsa_s2o_attn_prefill(*args(s, FAKE, None, 0.01)) == E
+    assert l.pbsa_s2o_attn_prefill(*args(s, FAKE, FAKE, -0.5)) == E        # threshold < 0
+    assert l.pbsa_s2o_attn_prefill(*args(s, FAKE, FAKE, float("nan"))) == E
+    assert l.pbsa_s2o_attn_prefill(*args(s, FAKE, FAKE, float("inf"))) == E
+    assert l.pbsa_s2o_attn_prefill(*args(shape(S=0), FAKE, FAKE, 0.01)) == E  # needs segments
+    assert l.pbsa_s2o_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, 0.01, FAKE, None, None,
+                                   None, None, 0, None) == _lib.PBSA_ERR_WORKSPACE
+    s0 = shape(N=0)
+    assert l.pbsa_s2o_attn_prefill(*args(s0, FAKE, FAKE, 0.01)) == 0
 
 
 def test_workspace_checks():

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, kept_to_mask
+from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_ranked,
+                    compare_s2o_stops, kept_to_mask)
 from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
 
 pytestmark = pytest.mark.gpu
@@ -152,3 +153,34 @@ def test_fullsize_64k_early_stop_sampled():
     mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
     frac = sum(len(v) for v in kept.values()) / (Hq * NB * (NB + 1) / 2)
     _log(f"[fullsize] 64K early stop: kept fraction {frac:.3f}, rows {rows}: max abs {mx:.2e} mean {mean:.2e}")
+
+
+def test_fullsize_32k_marginal_gain_sampled():
+    """Marginal-gain early stop at 32K: every ranked row, and the stop and outputs of sampled rows."""
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_32k"]
+    gain_tau = 0.01
+    _log(f"[fullsize] {w.name} marginal-gain stop, gain_tau {gain_tau}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, S, NB, Hq, N = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads, w.seq_len
+    perm_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    count_t, idx_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, w.mass_tau, ranked=True)
+    out_t, lse_t, kept_t = pbsa.s2o_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S,
+                                                 gain_tau, return_kept=True)
+    torch.cuda.synchronize()
+    perm_g, cg, ig = perm_t.cpu().numpy(), count_t.cpu().numpy(), idx_t.cpu().numpy()
+    count_o, idx_o, _ = oracle.ranked_blocks(q, k, perm_g, B, S)
+    ties = compare_ranked(cg, ig, count_o, idx_o, oracle.pooled_block_logits(q, k, perm_g, B, S))
+    _log(f"[fullsize] ranked order ok ({ties} recorded ties)")
+    kept = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+    rows = _sample_rows(Hq, NB, 12, 11)
+    ratios = oracle.s2o_gain_ratios(q, k, perm_g, cg, ig, B, S, rows=rows)
+    _, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau)
+    kc, ki = kept_to_mask({r: kept[r] for r in rows}, Hq, NB)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, perm_g, kc, ki, B, S, rows=rows)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o, "s2o 32K")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    frac = sum(len(x) for x in kept.values()) / (Hq * NB * (NB + 1) / 2)
+    _log(f"[fullsize] 32K marginal-gain stop: processed {frac:.3f}, sampled rows {rows} ({near} in band): "
+         f"max abs {mx:.2e} mean {mean:.2e}")

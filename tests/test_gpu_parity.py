@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, kept_to_mask)
+from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_ranked,
+                    compare_s2o_stops, kept_to_mask)
 from workloads import bf16_bits_to_f32, generate
 
 pytestmark = pytest.mark.gpu
@@ -356,3 +357,94 @@ def test_calibrate_thresholds_exact(N, B, keep):
     assert np.array_equal(np.isneginf(got), np.isneginf(want))
     fin = np.isfinite(want)
     assert np.array_equal(got[fin], want[fin])
+
+
+# marginal-gain early stop: (name, N, Hq, Hkv, d, B, S, stripes, band, gain_tau, seed); without
+# stripes the stop falls in the middle of most lists, with them right after the first history block
+S2O_CASES = [
+    ("flat_b64_d128_gqa_2048", 2048, 4, 2, 128, 64, 256, 0, 0, 0.05, 31),
+    ("band_b128_d64_ragged_4000", 4000, 4, 1, 64, 128, 512, 0, 256, 0.02, 32),
+    ("stripes_b128_d128_ragged_3000", 3000, 2, 1, 128, 128, 512, 4, 256, 0.05, 33),
+    ("flat_b64_d64_ragged_1100", 1100, 2, 2, 64, 64, 128, 0, 64, 0.1, 34),
+    ("flat_b128_d128_threshold_one_2048", 2048, 2, 1, 128, 128, 256, 0, 128, 1.0, 35),
+]
+
+
+@pytest.mark.parametrize("case", S2O_CASES, ids=[c[0] for c in S2O_CASES])
+def test_marginal_gain_stagewise(case):
+    pbsa = _need_gpu()
+    name, N, Hq, Hkv, d, B, S, stripes, band, gain_tau, seed = case
+    _log(f"[parity] s2o {name}: N={N} Hq={Hq} Hkv={Hkv} d={d} B={B} S={S} gain_tau={gain_tau}")
+    dev, host = _inputs(N, Hq, Hkv, d, stripes, band, seed)
+    q, k, v = host["q"], host["k"], host["v"]
+    NB = oracle.num_blocks(N, B)
+    perm_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    torch.cuda.synchronize()
+    perm_g = perm_t.cpu().numpy()
+
+    # ranked order, on the GPU's permutation
+    count_t, idx_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, 0.9, ranked=True)
+    torch.cuda.synchronize()
+    cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+    count_o, idx_o, _ = oracle.ranked_blocks(q, k, perm_g, B, S)
+    ties = compare_ranked(cg, ig, count_o, idx_o, oracle.pooled_block_logits(q, k, perm_g, B, S))
+
+    # the stop, on the GPU's ranked lists
+    out_t, lse_t, kept_t, err_t = pbsa.s2o_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S,
+                                                        gain_tau, return_kept=True, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err_t.item()) == 0
+    kept = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+    ratios = oracle.s2o_gain_ratios(q, k, perm_g, cg, ig, B, S)
+    rows, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau)
+    frac = sum(len(x) for x in kept.values()) / float(Hq * NB * (NB + 1) // 2)
+
+    # softmax attention over what was processed
+    kc, ki = kept_to_mask(kept, Hq, NB)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, perm_g, kc, ki, B, S)
+    mx, mean = compare_out(out_t.cpu().numpy(), out_o, "s2o")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    _log(f"[parity] s2o {name}: rank ties {ties}, rows {rows}, decided in band {near}, processed {frac:.3f}, "
+         f"max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("d,B,N", [(128, 128, 2048), (64, 64, 1500)])
+def test_marginal_gain_zero_threshold_is_dense(d, B, N):
+    """gain_tau = 0 never stops: every J <= I is processed and the result is dense causal attention."""
+    pbsa = _need_gpu()
+    Hq, Hkv, S = 4, 2, 4 * B
+    dev, host = _inputs(N, Hq, Hkv, d, 8, 2 * B, 41)
+    NB = oracle.num_blocks(N, B)
+    perm = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    count, idx = pbsa.estimate_block_mask(dev["q"], dev["k"], perm, B, S, 0.9, ranked=True)
+    out, lse, kept = pbsa.s2o_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count, idx, B, S, 0.0,
+                                           return_kept=True)
+    torch.cuda.synchronize()
+    assert all(lst == list(range(I + 1)) for (h, I), lst in bitmap_to_kept(kept.cpu().numpy(), NB).items())
+    ref, ref_lse = oracle.dense_attention(host["q"], host["k"], host["v"])
+    compare_out(out.cpu().numpy(), ref, "s2o gain_tau 0")
+    compare_lse(lse.cpu().numpy(), ref_lse)
+
+
+def test_marginal_gain_is_deterministic_and_skips_bad_entries():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 2048, 2, 1, 128, 128, 512
+    dev, _ = _inputs(N, Hq, Hkv, d, 0, 256, 42)
+    NB = oracle.num_blocks(N, B)
+    perm = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S)
+    count, idx = pbsa.estimate_block_mask(dev["q"], dev["k"], perm, B, S, 0.9, ranked=True)
+    a = pbsa.s2o_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count, idx, B, S, 0.03, return_kept=True)
+    b = pbsa.s2o_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count, idx, B, S, 0.03, return_kept=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # an entry past I and a count past I + 1 are flagged and not read
+    idx2, count2 = idx.clone(), count.clone()
+    idx2[0, oracle.tri_offset(9) + 1] = 12
+    count2[1, 2] = 7
+    out, err = pbsa.s2o_attn_prefill(dev["q"], dev["k"], dev["v"], perm, count2, idx2, B, S, 0.03,
+                                     return_lse=False, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 1 and int(err.item()) & 4
+    assert torch.isfinite(out).all()
+    assert NB == 16

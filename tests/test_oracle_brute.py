@@ -87,3 +87,29 @@ def test_marginal_gain_stop_matches_brute_force(c, gain_tau):
     out_b, lse_b, _ = brute.attention(q, k, v, perm, {key: sorted(val) for key, val in done_b.items()}, B, S, scale)
     np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)
+
+
+@settings(max_examples=15, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case())
+def test_marginal_gain_ratios_place_the_brute_force_stop(c):
+    # at each position whose ratio is a new low among the earlier-segment positions, a threshold
+    # just above it makes the brute force stop exactly there, and one just below lets it go on
+    N, Hq, Hkv, d, B, S = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"], c["S"]
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S) if c["perm_on"] else None
+    count, idx, _ = oracle.ranked_blocks(q, k, perm, B, S)
+    ratios = oracle.s2o_gain_ratios(q, k, perm, count, idx, B, S)
+    checks = []
+    for (h, I), r in ratios.items():
+        assert np.all(np.isnan(r) | ((r > 0) & (r <= 1 + 1e-12))), (h, I, r)
+        low = math.inf
+        for p, x in enumerate(r):
+            if not np.isnan(x) and x < low * (1 - 1e-6):
+                checks.append((h, I, p, float(x), low))
+                low = x
+    for h, I, p, x, low in checks[:6]:
+        above = brute.s2o_processed(q, k, perm, B, S, x * (1 + 1e-9), scale)[(h, I)]
+        assert len(above) == p + 1, (h, I, p, x, above)
+        below = brute.s2o_processed(q, k, perm, B, S, x * (1 - 1e-9), scale)[(h, I)]
+        assert len(below) > p + 1 or len(below) == int(count[h, I]), (h, I, p, x, below)
