@@ -31,7 +31,7 @@ PEAK_HBM_GBS = 8000.0
 COPY_CALIB_BYTES = 1 << 30  # plain device copy of known size used to scale the byte counters
 KERNEL_SOURCES = ("block_sparse_attention_blocks_amd/csrc/attention.hip", "block_sparse_attention_blocks_amd/csrc/common.h")
 TRAFFIC_SUMMARY = "profiles/attn_pipe_kernel_llama8b_32k_traffic.txt"
-ATTN_KERNEL = "attn_pipe_kernel<128, 128, false, 2>"
+ATTN_KERNEL = "attn_pipe_kernel<128, 128, false, 2, false>"
 
 
 def kernel_source_hash() -> str:
