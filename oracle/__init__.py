@@ -20,14 +20,21 @@ from .pbsa_oracle import (  # noqa: F401
     key_importance,
     key_rows_of_block,
     num_blocks,
+    num_segments,
     pool_blocks,
     pool_permuted_blocks,
     pooled_block_logits,
+    prefix_kv_ranking,
+    prefix_offset,
+    prefix_ranking_length,
     ranked_blocks,
     s2o_attention,
     s2o_gain_ratios,
+    s2o_prefix_attention,
+    s2o_prefix_gain_ratios,
     segment_of_block,
     segment_permutation,
+    segment_representatives,
     tile_max,
     tri_offset,
 )

@@ -214,3 +214,95 @@ def s2o_processed(q, k, perm, B: int, S: int, gain_tau: float, scale: float) -> 
                     break
             out[(h, I)] = done
     return out
+
+
+def prefix_ranking(q, k, S: int) -> Dict[Tuple[int, int], List[int]]:
+    """{(g, sigma): keys of the prefix [0, sigma*S) in ranked order} for sigma >= 1, from the
+    definition: the representative is the fsum mean of the segment's query rows over the G heads of
+    KV head g; keys are picked one by one as the remaining key with the largest r . k_j (the
+    smallest j among equals)."""
+    Hq, N, d = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    nseg = -(-N // S)
+    res = {}
+    for g in range(Hkv):
+        for sigma in range(1, nseg):
+            qrows = [q[h][i] for h in range(g * G, (g + 1) * G) for i in range(sigma * S, min((sigma + 1) * S, N))]
+            r = [math.fsum(float(x[t]) for x in qrows) / len(qrows) for t in range(d)]
+            z = {j: _dot(r, k[g][j]) for j in range(sigma * S)}
+            rest = list(range(sigma * S))
+            order = []
+            while rest:
+                best = max(rest, key=lambda j: (z[j], -j))
+                order.append(best)
+                rest.remove(best)
+            res[(g, sigma)] = order
+    return res
+
+
+def s2o_prefix_processed(q, k, ranking: Dict[Tuple[int, int], List[int]], B: int, S: int, gain_tau: float,
+                         scale: float) -> Dict[Tuple[int, int], List[int]]:
+    """Entries the two-pass marginal-gain stop processes per (h, I), from its definition: the
+    blocks of I's own segment in natural order (J0 .. I, J0 its first block), then history blocks
+    J = 0, 1, ... holding ranked keys J*B .. J*B+B-1 of the segment's order; stop after the first
+    history block whose exact share (fsum of exp(s - M_i), M_i the max over every listed key <= i)
+    of every query's denominator over the processed keys is below gain_tau."""
+    Hq, N = len(q), len(q[0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    NB = -(-N // B)
+    out = {}
+    for h in range(Hq):
+        g = h // G
+        for I in range(NB):
+            sigma = (I * B) // S
+            J0 = sigma * S // B
+            rank = ranking.get((g, sigma), [])
+
+            def rows_of(J):
+                if J >= J0:
+                    return list(range(J * B, min((J + 1) * B, N)))
+                return rank[J * B:(J + 1) * B]
+            order = list(range(J0, I + 1)) + list(range(J0))
+            qrows = list(range(I * B, min((I + 1) * B, N)))
+            logit = {(i, j): scale * _dot(q[h][i], k[g][j]) for i in qrows for J in order for j in rows_of(J) if j <= i}
+            ref = {i: max(v for (ii, _), v in logit.items() if ii == i) for i in qrows}
+            done = []
+            for J in order:
+                done.append(J)
+                if J >= J0:
+                    continue
+                stop = True
+                for i in qrows:
+                    keys_all = [j for JJ in done for j in rows_of(JJ) if j <= i]
+                    keys_b = [j for j in rows_of(J) if j <= i]
+                    ell = math.fsum(math.exp(logit[(i, j)] - ref[i]) for j in keys_all)
+                    dl = math.fsum(math.exp(logit[(i, j)] - ref[i]) for j in keys_b)
+                    if not dl < gain_tau * ell:
+                        stop = False
+                        break
+                if stop:
+                    break
+            out[(h, I)] = done
+    return out
+
+
+def attention_over_keys(q, k, v, keysets: Dict[Tuple[int, int], List[int]], B: int, scale: float):
+    """out[h][i], lse[h][i] for the rows of the given (h, I): softmax over keysets[(h, I)] restricted
+    to j <= i, each sum an fsum (rows not listed stay None)."""
+    Hq, N, d = len(q), len(q[0]), len(q[0][0])
+    G = Hq // len(k)
+    out = [[None] * N for _ in range(Hq)]
+    lse = [[None] * N for _ in range(Hq)]
+    for (h, I), keys in keysets.items():
+        g = h // G
+        for i in range(I * B, min((I + 1) * B, N)):
+            ks = [j for j in keys if j <= i]
+            s = [scale * _dot(q[h][i], k[g][j]) for j in ks]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = math.fsum(w)
+            out[h][i] = [math.fsum(w[a] * float(v[g][ks[a]][t]) for a in range(len(ks))) / z for t in range(d)]
+            lse[h][i] = m + math.log(z)
+    return out, lse

@@ -24,7 +24,10 @@ design notes of the repository):
   * the marginal-gain early stop visits the query block's own segment first (ascending), then the
     earlier-segment blocks by pooled logit descending (ties by J), and stops a tile row after the
     first earlier-segment block whose share of every query's softmax denominator (that block
-    included) is below the threshold; that block stays processed.
+    included) is below the threshold; that block stays processed;
+  * S2O's historical ranking uses one representative query per (KV head, segment): the mean of the
+    segment's query rows over the G query heads; it orders every key of the causal prefix (the
+    earlier segments) by its dot product with that query, descending, ties by position.
 """
 from __future__ import annotations
 
@@ -269,15 +272,18 @@ def ranked_blocks(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], bloc
     return count, idx, n_intra
 
 
-def _s2o_row_gains(q, k, perm_g, h, g, I, lst, B, S, N, c):
+def _s2o_row_gains(q, k, perm_g, h, g, I, lst, B, S, N, c, rows_of=None):
     """For row (h, I) and its list in order: (dl, ell), each [len(lst)][rows of block I], where dl[p]
     is what block lst[p] adds to each query's softmax denominator and ell[p] the denominator over
     lst[0..p].  One reference per query (the max over every listed key) scales both; it cancels in
-    the ratio dl / ell."""
+    the ratio dl / ell.  rows_of(J) gives a list entry's key positions (default: key_rows_of_block
+    through perm_g)."""
     qi = block_range(I, B, N)
+    if rows_of is None:
+        rows_of = lambda J: key_rows_of_block(J, I, perm_g, B, S, N)  # noqa: E731
     blk = []
     for J in lst:
-        kj = key_rows_of_block(J, I, perm_g, B, S, N)
+        kj = rows_of(J)
         st = c * (q[h, qi] @ k[g, kj].T)
         blk.append(np.where(kj[None, :] <= qi[:, None], st, -np.inf))
     ref = np.max(np.concatenate(blk, axis=1), axis=1)
@@ -356,6 +362,146 @@ def s2o_gain_ratios(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], co
     return out
 
 
+# ----------------------------------------------------------------------------- S2O prefix ranking
+
+def num_segments(n: int, segment_size: int) -> int:
+    return -(-n // segment_size)
+
+
+def prefix_offset(sigma: int, segment_size: int) -> int:
+    """Start of segment sigma's prefix order in a [Hkv][...] prefix ranking: the orders of segments
+    1 .. sigma-1 come first, of lengths S, 2S, ..."""
+    return segment_size * sigma * (sigma - 1) // 2
+
+
+def prefix_ranking_length(n: int, segment_size: int) -> int:
+    nseg = num_segments(n, segment_size)
+    return prefix_offset(nseg, segment_size)
+
+
+def segment_representatives(q: np.ndarray, num_kv_heads: int, segment_size: int) -> np.ndarray:
+    """r[g][sigma] = mean of the query rows of segment sigma over the G query heads of KV head g.
+
+    S2O, Methodology §1, Historical KV Permutation: the keys before a segment are scored against a
+    representative query of the segment.  Reading: that query is the mean of the segment's query
+    rows, taken over every query head that shares the KV head (one order per KV head, as K and V
+    are stored per KV head)."""
+    Hq, N, d = q.shape
+    G = Hq // num_kv_heads
+    S = segment_size
+    nseg = num_segments(N, S)
+    r = np.empty((num_kv_heads, nseg, d))
+    for g in range(num_kv_heads):
+        for sigma in range(nseg):
+            rows = q[g * G:(g + 1) * G, sigma * S:min((sigma + 1) * S, N)].reshape(-1, d)
+            r[g, sigma] = rows.mean(axis=0)
+    return r
+
+
+def prefix_kv_ranking(q: np.ndarray, k: np.ndarray, segment_size: int):
+    """Per KV head g and segment sigma >= 1: every key j < sigma*S (the causal prefix of the
+    segment) ordered by the score r_{g,sigma} . k_j, descending, ties by j ascending.
+
+    S2O, Methodology §1, Historical KV Permutation (scores against a representative query, only
+    prefix tokens, one global order over the prefix).  Returns (pi, score), both [Hkv][L] with
+    L = prefix_ranking_length(N, S): segment sigma's order at prefix_offset(sigma, S), int64 key
+    positions and their fp64 scores."""
+    Hkv, N, d = k.shape
+    S = segment_size
+    nseg = num_segments(N, S)
+    L = prefix_ranking_length(N, S)
+    r = segment_representatives(q, Hkv, S)
+    pi = np.zeros((Hkv, L), dtype=np.int64)
+    score = np.zeros((Hkv, L))
+    for g in range(Hkv):
+        for sigma in range(1, nseg):
+            n = sigma * S
+            z = k[g, :n] @ r[g, sigma]
+            order = np.lexsort((np.arange(n), -z))
+            o = prefix_offset(sigma, S)
+            pi[g, o:o + n] = order
+            score[g, o:o + n] = z[order]
+    return pi, score
+
+
+def _prefix_rows_of(pi, g, I, B, S, N):
+    """Key positions of list entry J for query block I: natural block J in I's own segment
+    (J >= J0, the first block of the segment), else block J of the segment's prefix order."""
+    sigma = segment_of_block(I, B, S)
+    J0 = sigma * S // B
+    o = prefix_offset(sigma, S)
+
+    def rows_of(J):
+        if J >= J0:
+            return block_range(J, B, N)
+        return np.asarray(pi[g, o + J * B:o + (J + 1) * B], dtype=np.int64)
+    return rows_of, J0
+
+
+def s2o_prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.ndarray, block_size: int,
+                         segment_size: int, gain_tau: float, scale: Optional[float] = None,
+                         rows: Optional[Iterable[Tuple[int, int]]] = None):
+    """S2O's two passes with the marginal-gain stop, history read through the prefix ranking.
+
+    S2O, Kernel Implementation: pass 1 runs the dense causal window of the query block's own
+    segment; pass 2 continues over the historical prefix in the permuted order of
+    prefix_kv_ranking, cut into blocks of B keys (block J = entries J*B .. J*B+B-1 of the
+    segment's order, so J = 0 holds the highest-scoring keys); S2O, Early-Stopping Rule: after
+    each history block, the row stops as in s2o_attention (every query's share of that block in
+    its denominator below gain_tau; that block stays processed).  The output is exact softmax
+    attention over the processed keys.
+
+    Returns (out [Hq][N][d], lse [Hq][N], processed {(h, I): [J in processing order]}), where
+    J >= J0 names a natural block of the own segment and J < J0 a prefix-order block.
+    """
+    Hq, N, d = q.shape
+    G = Hq // k.shape[0]
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    todo = [(h, I) for h in range(Hq) for I in range(NB)] if rows is None else list(rows)
+    out = np.full((Hq, N, d), np.nan)
+    lse = np.full((Hq, N), np.nan)
+    processed: Dict[Tuple[int, int], List[int]] = {}
+    for h, I in todo:
+        g = h // G
+        rows_of, J0 = _prefix_rows_of(pi, g, I, B, S, N)
+        lst = list(range(J0, I + 1)) + list(range(J0))
+        dl, ell = _s2o_row_gains(q, k, None, h, g, I, lst, B, S, N, c, rows_of=rows_of)
+        done: List[int] = []
+        for p, J in enumerate(lst):
+            done.append(J)
+            if J < J0 and np.all(dl[p] < gain_tau * ell[p]):
+                break
+        processed[(h, I)] = done
+        keys = np.concatenate([rows_of(J) for J in done])
+        _attend(q, k, v, h, g, block_range(I, B, N), keys, c, out, lse)
+    return out, lse, processed
+
+
+def s2o_prefix_gain_ratios(q: np.ndarray, k: np.ndarray, pi: np.ndarray, block_size: int, segment_size: int,
+                           scale: Optional[float] = None,
+                           rows: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], np.ndarray]:
+    """s2o_gain_ratios for the lists of s2o_prefix_attention: max_i dl_i / l_i at every position of
+    the whole list (own segment ascending, then prefix blocks 0 .. J0-1), NaN on the own segment."""
+    Hq, N, d = q.shape
+    G = Hq // k.shape[0]
+    B, S = block_size, segment_size
+    NB = num_blocks(N, B)
+    c = default_scale(d) if scale is None else scale
+    todo = [(h, I) for h in range(Hq) for I in range(NB)] if rows is None else list(rows)
+    res: Dict[Tuple[int, int], np.ndarray] = {}
+    for h, I in todo:
+        g = h // G
+        rows_of, J0 = _prefix_rows_of(pi, g, I, B, S, N)
+        lst = list(range(J0, I + 1)) + list(range(J0))
+        dl, ell = _s2o_row_gains(q, k, None, h, g, I, lst, B, S, N, c, rows_of=rows_of)
+        r = (dl / ell).max(axis=1)
+        r[:I + 1 - J0] = np.nan
+        res[(h, I)] = r
+    return res
+
+
 def _lists_to_mask(lists: Dict[Tuple[int, int], Sequence[int]], Hq: int, NB: int):
     count = np.zeros((Hq, NB), dtype=np.int64)
     idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
@@ -427,24 +573,31 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, perm: Op
             kept_J.append(J)
         kept[(h, I)] = kept_J
         keys = np.concatenate(keep_lists) if keep_lists else np.zeros(0, dtype=np.int64)
-        s = c * (q[h, qi] @ k[g, keys].T)                      # [rows of I][keys]
-        s = np.where(keys[None, :] <= qi[:, None], s, -np.inf)
-        for r, i in enumerate(qi):
-            ok = keys <= i
-            if not ok.any():                                   # no key left: output 0, lse -inf
-                out[h, i] = 0.0
-                lse[h, i] = -np.inf
-                if return_weights:
-                    weights[(h, int(i))] = (keys[:0], np.zeros(0))
-                continue
-            m = s[r].max()
-            e = np.exp(s[r] - m)
-            l = e.sum()
-            out[h, i] = (e @ v[g, keys]) / l
-            lse[h, i] = m + np.log(l)
-            if return_weights:
-                weights[(h, int(i))] = (keys, e / l)
+        _attend(q, k, v, h, g, qi, keys, c, out, lse, weights)
     return out, lse, kept, weights
+
+
+def _attend(q, k, v, h, g, qi, keys, c, out, lse, weights=None):
+    """Softmax attention of the queries qi of head h over the key positions `keys`, each query
+    seeing only keys j <= i; writes out[h, qi] and lse[h, qi].  A query with no key gets out = 0
+    and lse = -inf."""
+    s = c * (q[h, qi] @ k[g, keys].T)                          # [rows of I][keys]
+    s = np.where(keys[None, :] <= qi[:, None], s, -np.inf)
+    for r, i in enumerate(qi):
+        ok = keys <= i
+        if not ok.any():
+            out[h, i] = 0.0
+            lse[h, i] = -np.inf
+            if weights is not None:
+                weights[(h, int(i))] = (keys[:0], np.zeros(0))
+            continue
+        m = s[r].max()
+        e = np.exp(s[r] - m)
+        l = e.sum()
+        out[h, i] = (e @ v[g, keys]) / l
+        lse[h, i] = m + np.log(l)
+        if weights is not None:
+            weights[(h, int(i))] = (keys, e / l)
 
 
 def dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: Optional[float] = None,

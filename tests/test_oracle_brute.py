@@ -113,3 +113,43 @@ def test_marginal_gain_ratios_place_the_brute_force_stop(c):
         assert len(above) == p + 1, (h, I, p, x, above)
         below = brute.s2o_processed(q, k, perm, B, S, x * (1 - 1e-9), scale)[(h, I)]
         assert len(below) > p + 1 or len(below) == int(count[h, I]), (h, I, p, x, below)
+
+
+def _same_ranking(got, want, score_of, tol=1e-12):
+    """Equal lists up to swaps of keys whose scores agree within tol (relative)."""
+    assert sorted(got) == sorted(want)
+    for a, b in zip(got, want):
+        if a != b:
+            za, zb = score_of(a), score_of(b)
+            assert abs(za - zb) <= tol * max(abs(za), abs(zb), 1e-300), (a, b, za, zb)
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case(), st.sampled_from([0.0, 1e-2, 5e-2, 0.2, 1.0]))
+def test_prefix_ranking_and_two_pass_stop_match_brute_force(c, gain_tau):
+    N, Hq, Hkv, d, B, S = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"], c["S"]
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+    pi, score = oracle.prefix_kv_ranking(q, k, S)
+    rank_b = brute.prefix_ranking(q, k, S)
+    r = oracle.segment_representatives(q, Hkv, S)
+    for (g, sigma), order in rank_b.items():
+        o = oracle.prefix_offset(sigma, S)
+        got = pi[g, o:o + sigma * S].tolist()
+        _same_ranking(got, order, lambda j: float(k[g, j] @ r[g, sigma]))
+        np.testing.assert_allclose(score[g, o:o + sigma * S], k[g, got] @ r[g, sigma], rtol=0, atol=0)
+    # the stop and the output, both on the oracle's ranking
+    ranking = {(g, sigma): pi[g, oracle.prefix_offset(sigma, S):oracle.prefix_offset(sigma, S) + sigma * S].tolist()
+               for g in range(Hkv) for sigma in range(1, oracle.num_segments(N, S))}
+    out, lse, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, gain_tau)
+    done_b = brute.s2o_prefix_processed(q, k, ranking, B, S, gain_tau, scale)
+    assert done == done_b
+    keysets = {}
+    for (h, I), lst in done_b.items():
+        sigma = (I * B) // S
+        J0 = sigma * S // B
+        rank = ranking.get((h // (Hq // Hkv), sigma), [])
+        keysets[(h, I)] = [j for J in lst for j in (range(J * B, min((J + 1) * B, N)) if J >= J0 else rank[J * B:(J + 1) * B])]
+    out_b, lse_b = brute.attention_over_keys(q, k, v, keysets, B, scale)
+    np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)

@@ -358,3 +358,97 @@ def test_marginal_gain_stop_is_monotone_in_threshold():
         if prev is not None:
             assert all(n[key] <= prev[key] for key in n)
         prev = n
+
+
+# ----------------------------------------------------------------------------- S2O prefix ranking
+
+def test_prefix_ranking_orders_each_prefix_by_the_segment_mean_query():
+    """Segment rows u + w and u - w (every head of the group) have mean u; keys k_j = a_j u with
+    known a_j, so the order by r . k_j is the order of a_j: descending, ties by position."""
+    N, Hq, Hkv, d, S = 48, 4, 2, 6, 16
+    rng = np.random.default_rng(5)
+    q = np.zeros((Hq, N, d))
+    k = np.zeros((Hkv, N, d))
+    a = {}
+    for g in range(Hkv):
+        u = rng.standard_normal(d)
+        w = rng.standard_normal(d) * 3.0
+        for h in range(g * 2, g * 2 + 2):
+            for i in range(N):
+                q[h, i] = u + (w if i % 2 == 0 else -w)
+        a[g] = rng.permutation(N).astype(np.float64) - 20.0
+        a[g][7] = a[g][3]                      # one tie: position 3 before 7
+        k[g] = a[g][:, None] * u[None, :]
+    pi, score = oracle.prefix_kv_ranking(q, k, S)
+    assert pi.shape == (Hkv, oracle.prefix_ranking_length(N, S)) == (Hkv, S + 2 * S)
+    for g in range(Hkv):
+        for sigma in (1, 2):
+            o = oracle.prefix_offset(sigma, S)
+            got = pi[g, o:o + sigma * S].tolist()
+            want = sorted(range(sigma * S), key=lambda j: (-a[g][j], j))
+            assert got == want, (g, sigma)
+            assert got.index(3) < got.index(7)
+            assert np.all(np.diff(score[g, o:o + sigma * S]) <= 0)
+
+
+def test_prefix_ranking_ignores_the_order_of_queries_inside_a_segment():
+    N, Hq, Hkv, d, B, S = 96, 4, 2, 8, 8, 32
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=31)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    q2 = q.copy()
+    rng = np.random.default_rng(1)
+    for sigma in range(N // S):
+        rows = np.arange(sigma * S, (sigma + 1) * S)
+        q2[:, rows] = q[:, rng.permutation(rows)]
+    q2[[0, 1]] = q2[[1, 0]]                    # swap the two heads of KV group 0
+    pi2, _ = oracle.prefix_kv_ranking(q2, k, S)
+    assert np.array_equal(pi, pi2)
+    # and it does depend on the queries of the segment: negate segment 2's rows of group 0
+    q3 = q.copy()
+    q3[0:2, 2 * S:3 * S] *= -1.0
+    pi3, _ = oracle.prefix_kv_ranking(q3, k, S)
+    o = oracle.prefix_offset(2, S)
+    assert not np.array_equal(pi3[0, o:o + 2 * S], pi[0, o:o + 2 * S])
+    assert np.array_equal(pi3[0, :o], pi[0, :o]) and np.array_equal(pi3[0, o + 2 * S:], pi[0, o + 2 * S:])
+    assert np.array_equal(pi3[1], pi[1])
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_two_pass_zero_threshold_is_dense_causal(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=32)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    out, lse, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, 0.0)
+    assert all(sorted(lst) == list(range(I + 1)) for (h, I), lst in done.items())
+    ref, ref_lse = oracle.dense_attention(q, k, v)
+    assert np.abs(out - ref).max() <= 1e-12
+    assert np.abs(lse - ref_lse).max() <= 1e-12
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_two_pass_threshold_one_stops_after_the_first_history_block(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=33)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    _, _, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, 1.0)
+    for (h, I), lst in done.items():
+        J0 = ((I * B) // S) * S // B
+        assert lst == list(range(J0, I + 1)) + ([0] if J0 > 0 else []), (h, I, lst)
+
+
+def test_two_pass_stop_is_monotone_and_history_blocks_hold_the_top_keys():
+    N, Hq, Hkv, d, B, S = 96, 2, 1, 8, 8, 32
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=34)
+    pi, score = oracle.prefix_kv_ranking(q, k, S)
+    prev = None
+    for tau in (0.0, 1e-4, 1e-3, 1e-2, 0.1, 1.0):
+        _, _, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, tau)
+        n = {key: len(val) for key, val in done.items()}
+        if prev is not None:
+            assert all(n[key] <= prev[key] for key in n)
+        prev = n
+    # history block 0 of segment 2 holds the B prefix keys of largest score
+    r = oracle.segment_representatives(q, Hkv, S)
+    z = k[0, :2 * S] @ r[0, 2]
+    o = oracle.prefix_offset(2, S)
+    assert set(pi[0, o:o + B].tolist()) == set(np.argsort(-z, kind="stable")[:B].tolist())
