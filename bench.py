@@ -241,6 +241,10 @@ def suite(args) -> int:
             kw.setdefault("workspace", self._ws)
             return self._mod.s2o_attn_prefill(*a, **kw)
 
+        def s2o_prefix_attn_prefill(self, *a, **kw):
+            kw.setdefault("workspace", self._ws)
+            return self._mod.s2o_prefix_attn_prefill(*a, **kw)
+
     pbsa = _WithWorkspace(pbsa, torch.empty(4096, dtype=torch.uint8, device="cuda"))
     reps = args.suite_reps
     parts = set(args.suite_parts.split(","))
@@ -252,6 +256,8 @@ def suite(args) -> int:
         suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
     if "s2o" in parts:
         suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
+    if "twopass" in parts:
+        suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=True)
     out_f.close()
     return 0
 
@@ -367,9 +373,10 @@ def suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     torch.cuda.empty_cache()
 
 
-def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
-    """Marginal-gain early stop over the ranked list at 32K and 128K, and at 32K on inputs drawn
-    without stripe keys (there the stop falls in the middle of most lists)."""
+def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=False):
+    """Marginal-gain early stop at 32K and 128K, and at 32K on inputs drawn without stripe keys
+    (there the stop falls in the middle of most lists): over the pooled-logit ranked list (PBS
+    permutation + PBSA_MASK_RANKED), or with two_pass over S2O's historical ranking."""
     from workloads import generate
     cases = [("llama8b_32k", None), ("llama8b_32k", "no_stripes"), ("llama8b_128k", None)]
     for name, variant in cases:
@@ -383,24 +390,39 @@ def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
         q, k, v = d["q"], d["k"], d["v"]
         B, S, NB, Hq = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads
         causal_tiles = Hq * NB * (NB + 1) // 2
-        perm = pbsa.build_segment_permutation(q, k, B, S)
-        count, idx = pbsa.estimate_block_mask(q, k, perm, B, S, 1.0, ranked=True)
         out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
         lse = torch.empty((Hq, w.seq_len), dtype=torch.float32, device="cuda")
-        fr = lambda: pbsa.estimate_block_mask(q, k, perm, B, S, 1.0, ranked=True, out=(count, idx))
+        if two_pass:
+            shape = pbsa.make_shape(q, k, B, S)
+            ws_r = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_PREFIX_RANK) + 256, dtype=torch.uint8,
+                               device="cuda")
+            rank = pbsa.build_prefix_kv_ranking(q, k, B, S, workspace=ws_r)
+            fr = lambda: pbsa.build_prefix_kv_ranking(q, k, B, S, out=rank, workspace=ws_r)
+            perm = count = idx = None
+        else:
+            perm = pbsa.build_segment_permutation(q, k, B, S)
+            count, idx = pbsa.estimate_block_mask(q, k, perm, B, S, 1.0, ranked=True)
+            fr = lambda: pbsa.estimate_block_mask(q, k, perm, B, S, 1.0, ranked=True, out=(count, idx))
         t_rank = _events(torch, stream, fr, reps)["median_ms"]
         dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
         t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
         for gain_tau in (0.001, 0.01, 0.05):
-            fa = lambda: pbsa.s2o_attn_prefill(q, k, v, perm, count, idx, B, S, gain_tau, out=out, lse=lse)
+            if two_pass:
+                fa = lambda: pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, out=out, lse=lse)
+                _, _, kept = pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, return_kept=True)
+            else:
+                fa = lambda: pbsa.s2o_attn_prefill(q, k, v, perm, count, idx, B, S, gain_tau, out=out, lse=lse)
+                _, _, kept = pbsa.s2o_attn_prefill(q, k, v, perm, count, idx, B, S, gain_tau, return_kept=True)
             ta = _events(torch, stream, fa, reps)["median_ms"]
-            _, _, kept = pbsa.s2o_attn_prefill(q, k, v, perm, count, idx, B, S, gain_tau, return_kept=True)
             tiles = int(np.unpackbits(kept.cpu().numpy().view(np.uint8)).sum())
             emit({"workload": w.name + ("" if variant is None else "_" + variant), "gain_tau": gain_tau,
-                  "processed_fraction": tiles / causal_tiles, "ranked_order_ms": t_rank, "attention_ms": ta,
+                  "lists": "two-pass historical ranking" if two_pass else "pooled-logit ranked",
+                  "processed_fraction": tiles / causal_tiles, "ranking_ms": t_rank, "attention_ms": ta,
                   "dense_kernel_ms": t_dense, "attention_speedup_vs_dense": t_dense / ta,
                   "attention_mfma_frac": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
         del d, q, k, v, out, lse, perm, count, idx
+        if two_pass:
+            del rank, ws_r
         torch.cuda.empty_cache()
 
 
@@ -423,8 +445,8 @@ def main() -> int:
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
     ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
-    ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o",
-                    help="comma-separated subset of 128k, sweep, earlystop, s2o")
+    ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o,twopass",
+                    help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "

@@ -16,7 +16,7 @@ import torch
 
 from . import _lib
 from ._lib import (PBSA_FORCE_DIAG, PBSA_FORCE_FIRST, PBSA_MASK_RANKED, PBSA_OP_ATTENTION, PBSA_OP_MASK,  # noqa: F401
-                   PBSA_OP_PERMUTATION, PbsaError, PbsaShape)
+                   PBSA_OP_PERMUTATION, PBSA_OP_PREFIX_RANK, PbsaError, PbsaShape)
 
 __all__ = [
     "build_segment_permutation",
@@ -25,6 +25,9 @@ __all__ = [
     "tile_max",
     "calibrate_thresholds",
     "s2o_attn_prefill",
+    "build_prefix_kv_ranking",
+    "prefix_rank_length",
+    "s2o_prefix_attn_prefill",
     "workspace_size",
     "make_shape",
     "num_blocks",
@@ -216,6 +219,75 @@ def s2o_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, perm: Op
         ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
         float(gain_tau), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
     _lib.check(st, "pbsa_s2o_attn_prefill")
+    res = [out]
+    if return_lse:
+        res.append(lse)
+    if return_kept:
+        res.append(kept)
+    if return_error:
+        res.append(err)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def prefix_rank_length(q: torch.Tensor, k: torch.Tensor, block_size: int, segment_size: int) -> int:
+    """Entries per KV head of the historical ranking (S * nseg * (nseg - 1) / 2)."""
+    n = _lib.lib().pbsa_prefix_rank_length(ctypes.byref(make_shape(q, k, block_size, segment_size)))
+    if n < 0:
+        raise PbsaError(_lib.PBSA_ERR_UNSUPPORTED, "pbsa_prefix_rank_length")
+    return n
+
+
+def build_prefix_kv_ranking(q: torch.Tensor, k: torch.Tensor, block_size: int, segment_size: int,
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """S2O historical ranking: int32 [Hkv][prefix_rank_length] holding, for every segment sigma >= 1
+    at offset S*sigma*(sigma-1)/2, the keys before the segment by descending score against the
+    segment's mean query."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, segment_size)
+    L = prefix_rank_length(q, k, block_size, segment_size)
+    if out is None:
+        out = torch.empty((k.shape[0], L), dtype=torch.int32, device=q.device)
+    elif out.dtype != torch.int32 or out.shape != (k.shape[0], L) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [Hkv][prefix_rank_length] tensor")
+    ws, nbytes = _workspace(shape, PBSA_OP_PREFIX_RANK, q.device, workspace)
+    st = _lib.lib().pbsa_build_prefix_kv_ranking(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(out) if L else None,
+                                                 _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_build_prefix_kv_ranking")
+    return out
+
+
+def s2o_prefix_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_rank: torch.Tensor,
+                            block_size: int, segment_size: int, gain_tau: float, scale: Optional[float] = None,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            return_lse: bool = True, return_kept: bool = False, return_error: bool = False,
+                            workspace: Optional[torch.Tensor] = None):
+    """S2O two-pass attention with the marginal-gain stop over the historical ranking of
+    build_prefix_kv_ranking: out fp32 [Hq][N][d] (+ lse, processed-entry bitmap, device error word)."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    _check_bf16("v", v, heads=k.shape[0])
+    if v.stride() != k.stride():
+        raise ValueError("k and v must share strides")
+    Hq, N, d = q.shape
+    L = prefix_rank_length(q, k, block_size, segment_size)
+    if kv_rank.dtype != torch.int32 or kv_rank.shape != (k.shape[0], L) or not kv_rank.is_contiguous():
+        raise ValueError("kv_rank must be the contiguous int32 [Hkv][prefix_rank_length] ranking")
+    if out is None:
+        out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    NB = num_blocks(N, block_size)
+    kept = None
+    if return_kept:
+        kept = torch.zeros((Hq, -(-(NB * (NB + 1) // 2) // 32)), dtype=torch.int32, device=q.device)
+    err = torch.zeros(1, dtype=torch.int32, device=q.device) if return_error else None
+    shape = make_shape(q, k, block_size, segment_size, scale, out=out)
+    ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
+    st = _lib.lib().pbsa_s2o_prefix_attn_prefill(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_rank) if L else None, float(gain_tau), _ptr(out),
+        _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_s2o_prefix_attn_prefill")
     res = [out]
     if return_lse:
         res.append(lse)

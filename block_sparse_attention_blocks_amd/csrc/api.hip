@@ -13,6 +13,8 @@ namespace {
 
 constexpr int kMaxSegment = 8192;  // segment sort holds one segment in LDS
 constexpr int kMaxBlocks = 2048;   // block selection holds one row of block scores in LDS
+constexpr int kMaxPrefixSegments = 256;       // historical ranking: segments per sequence
+constexpr int64_t kMaxRankEntries = 1ll << 31;  // historical ranking: entries over all KV heads
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -70,6 +72,15 @@ pbsa_status check_workspace(size_t need, const void* ws, size_t bytes) {
 
 pbsa_status from_hip(hipError_t e) { return e == hipSuccess ? PBSA_OK : PBSA_ERR_HIP; }
 
+// Shapes the historical ranking supports: segments on, at most kMaxPrefixSegments of them, and a
+// ranking that fits kMaxRankEntries.
+bool prefix_rank_ok(const Geometry& g) {
+  if (g.S <= 0) return false;
+  const int64_t nseg = ((int64_t)g.N + g.S - 1) / g.S;
+  if (nseg > kMaxPrefixSegments) return false;
+  return (int64_t)g.Hkv * pbsa::prefix_rank_length(g) <= kMaxRankEntries;
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,8 +92,32 @@ size_t pbsa_workspace_size(const pbsa_shape* shape, int op) {
     case PBSA_OP_PERMUTATION: return pbsa::importance_workspace_bytes(g);
     case PBSA_OP_MASK: return pbsa::mask_workspace_bytes(g);
     case PBSA_OP_ATTENTION: return g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0;
+    case PBSA_OP_PREFIX_RANK: return prefix_rank_ok(g) ? pbsa::prefix_rank_workspace_bytes(g) : SIZE_MAX;
     default: return SIZE_MAX;
   }
+}
+
+int64_t pbsa_prefix_rank_length(const pbsa_shape* shape) {
+  Geometry g;
+  if (make_geometry(shape, &g) != PBSA_OK || !prefix_rank_ok(g)) return -1;
+  return pbsa::prefix_rank_length(g);
+}
+
+pbsa_status pbsa_build_prefix_kv_ranking(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                         int32_t* kv_rank, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (g.S <= 0) return PBSA_ERR_INVALID_ARG;
+  if (!prefix_rank_ok(g)) return PBSA_ERR_UNSUPPORTED;
+  if (!q || !k || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
+  const int64_t L = pbsa::prefix_rank_length(g);
+  if (L > 0 && !kv_rank) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(L > 0 ? pbsa::prefix_rank_workspace_bytes(g) : 0, workspace, workspace_bytes)) !=
+      PBSA_OK)
+    return st;
+  if (L == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_prefix_rank(g, q, k, kv_rank, workspace, static_cast<hipStream_t>(stream)));
 }
 
 pbsa_status pbsa_build_segment_permutation(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
@@ -156,6 +191,26 @@ pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, co
   return from_hip(pbsa::launch_s2o_attention(g, q, k, v, perm, block_count, block_idx, gain_tau, out, lse,
                                              kept_bitmap, device_error, workspace,
                                              static_cast<hipStream_t>(stream)));
+}
+
+pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                         const uint16_t* v, const int32_t* kv_rank, float gain_tau, float* out,
+                                         float* lse, uint32_t* kept_bitmap, int32_t* device_error, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (g.S <= 0 || !(gain_tau >= 0.f) || !(gain_tau < INFINITY)) return PBSA_ERR_INVALID_ARG;
+  if (!prefix_rank_ok(g)) return PBSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !out) return PBSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PBSA_ERR_INVALID_ARG;
+  const int64_t L = pbsa::prefix_rank_length(g);
+  if (L > 0 && !kv_rank) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
+    return st;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_s2o_prefix_attention(g, q, k, v, kv_rank, L, gain_tau, out, lse, kept_bitmap,
+                                                    device_error, workspace, static_cast<hipStream_t>(stream)));
 }
 
 pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, float* tile_max,

@@ -62,6 +62,9 @@ struct AttnArgs {
   unsigned long long* queue;  // work deques of the pipelined kernels (workspace)
   int nq;                     // number of deques: one per KV group, at most one per XCD
   int Hkv;
+  int two_pass;               // S2O kernels: two-pass lists over the per-segment prefix order kvr
+  const int32_t* kvr;         // per-segment prefix key order (NULL when no segment has a prefix)
+  int64_t kvr_L;              // entries of kvr per KV head
 };
 
 enum { MODE_ATTN = 0, MODE_ATTN_GATED = 1, MODE_TILE_MAX = 2, MODE_DENSE = 3 };
@@ -125,8 +128,11 @@ __device__ __forceinline__ RowLook row_lookup(rsrc_t permr, int p, int N, bool w
   r.pv = (int)__builtin_amdgcn_raw_buffer_load_b32(permr, via ? (uint32_t)p * 4u : kOutOfRange, 0, 0);
   return r;
 }
-__device__ __forceinline__ uint32_t row_lookup_offset(const RowLook& r, int N, uint32_t row_bytes, int32_t* err) {
-  return checked_row_offset(r.code == kViaPerm ? r.pv : r.code, N, row_bytes, err);
+// plim bounds a row taken from the index map (N for perm; the segment's prefix length for the
+// per-segment prefix order, so that a history row always precedes the query block's segment).
+__device__ __forceinline__ uint32_t row_lookup_offset(const RowLook& r, int N, int plim, uint32_t row_bytes,
+                                                      int32_t* err) {
+  return checked_row_offset(r.code == kViaPerm ? r.pv : r.code, r.code == kViaPerm ? plim : N, row_bytes, err);
 }
 
 // One gathered tile: the rows at byte offsets row_off(j) of the head's slab into LDS [ROWS][D]
@@ -488,6 +494,18 @@ __device__ __forceinline__ int ranked_list(const AttnArgs& a, int h, int I, size
   return cnt;
 }
 
+// The two-pass list of S2O (Kernel Implementation) for query block I whose segment starts at block
+// J0: pass 1, the own segment's blocks J0 .. I ascending; pass 2, blocks 0 .. J0-1 of the segment's
+// prefix key order (block J = ranked keys J*B .. J*B+B-1).  Returns the list length, I + 1.
+template <int THREADS>
+__device__ __forceinline__ int two_pass_list(int I, int J0, uint32_t* mlist) {
+  const int nin = I + 1 - J0;
+  for (int x = threadIdx.x; x <= I; x += THREADS)
+    mlist[x] = (uint32_t)(x < nin ? J0 + x : x - nin) | (1u << 16);
+  __syncthreads();
+  return I + 1;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Work distribution of the pipelined kernels.  A work item is one query block I for one unit of
 // HPW query heads.  Deque q holds, in order of descending I, the items of the KV groups g with
@@ -631,24 +649,32 @@ void attn_pipe_kernel(AttnArgs a) {
   }
 
   // merged key-block list: ascending J kept by any of the workgroup's heads
-  const int nblk = DENSE ? I + 1
-                   : S2O ? ranked_list<C::THREADS>(a, h0, I, ntri, mlist, &mcount)
-                         : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
-  const int nst = nblk * C::STAGES;
   const int sI = a.S > 0 ? I0 / a.S : 0;
+  const bool two_pass = S2O && a.two_pass;  // history through the segment's prefix order
+  const int nblk = DENSE     ? I + 1
+                   : two_pass ? two_pass_list<C::THREADS>(I, sI * a.S / BLK, mlist)
+                   : S2O      ? ranked_list<C::THREADS>(a, h0, I, ntri, mlist, &mcount)
+                              : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
+  const int nst = nblk * C::STAGES;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
   auto entry_of = [&](int s) -> uint32_t {  // wave-uniform
     const int u = s / C::STAGES;
     return DENSE ? ((uint32_t)u | all_heads) : (uint32_t)__builtin_amdgcn_readfirstlane(mlist[u]);
   };
-  const rsrc_t permr = make_rsrc(a.perm ? a.perm + (size_t)g * a.N : nullptr, a.perm ? (uint32_t)a.N * 4u : 0u);
+  // index map of the history rows: perm of the KV head, or segment sI's prefix order
+  const int plim = two_pass ? sI * a.S : a.N;
+  const int32_t* pbase = two_pass ? (sI > 0 ? a.kvr + (size_t)g * a.kvr_L + (size_t)a.S * sI * (sI - 1) / 2 : nullptr)
+                         : a.perm ? a.perm + (size_t)g * a.N
+                                  : nullptr;
+  const rsrc_t permr = make_rsrc(pbase, pbase ? (uint32_t)plim * 4u : 0u);
+  const bool mapped = a.perm != nullptr || two_pass;
   // lookup of row j of stage s (want = false: an unused lookup that reads nothing)
   auto lookup = [&](int s, int j, bool want) -> RowLook {
     const int J = (int)(entry_of(s) & 0xffffu);
     const int p = J * BLK + (s % C::STAGES) * KT + j;
-    return row_lookup(permr, p, a.N, want, !DENSE && a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI);
+    return row_lookup(permr, p, a.N, want, !DENSE && mapped && a.S > 0 && (J * BLK) / a.S < sI);
   };
-  auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.kv_row_bytes, a.err); };
+  auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, plim, a.kv_row_bytes, a.err); };
   // next row lookup, of stage x (issued one step before its row ids are stored)
   auto lookup_ahead = [&](int x) -> RowLook { return lookup(x < nst ? x : 0, t & (KT - 1), x < nst && t < KT); };
   // gather stage s into buffer b = s % NBUF (b is passed separately so that it folds to a constant)
@@ -936,7 +962,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     const int p = J * BLK + j;
     return row_lookup(permr, p, a.N, want, a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI);
   };
-  auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.kv_row_bytes, a.err); };
+  auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.N, a.kv_row_bytes, a.err); };
   auto gather_k = [&](int u, uint16_t* dst) {
     const uint32_t* ids = rowid[u & 3];
     auto rf = [&](int j) { return ids[j]; };
@@ -1275,6 +1301,16 @@ hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* 
   return hipGetLastError();
 }
 
+// One head per workgroup with the marginal-gain stop, over ranked lists (a.count / a.idx) or over
+// the two-pass lists of the per-segment prefix order (a.kvr).
+static hipError_t launch_s2o_kernel(const Geometry& g, const AttnArgs& a, hipStream_t st) {
+  const int items = g.Hq * g.NB;
+  if (g.d == 128 && g.B == 128) return launch_persistent<128, 128, false, 1, true>(a, items, st);
+  if (g.d == 128 && g.B == 64) return launch_persistent<128, 64, false, 1, true>(a, items, st);
+  if (g.d == 64 && g.B == 128) return launch_persistent<64, 128, false, 1, true>(a, items, st);
+  return launch_persistent<64, 64, false, 1, true>(a, items, st);
+}
+
 hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* perm, const int32_t* count, const int32_t* idx, float gain_tau,
                                 float* out, float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st) {
@@ -1291,11 +1327,26 @@ hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint
   a.kept = kept;
   a.err = err;
   a.gain_tau = gain_tau;
-  const int items = g.Hq * g.NB;
-  if (g.d == 128 && g.B == 128) return launch_persistent<128, 128, false, 1, true>(a, items, st);
-  if (g.d == 128 && g.B == 64) return launch_persistent<128, 64, false, 1, true>(a, items, st);
-  if (g.d == 64 && g.B == 128) return launch_persistent<64, 128, false, 1, true>(a, items, st);
-  return launch_persistent<64, 64, false, 1, true>(a, items, st);
+  return launch_s2o_kernel(g, a, st);
+}
+
+hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const int32_t* kv_rank, int64_t rank_len, float gain_tau, float* out,
+                                       float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st) {
+  AttnArgs a = make_args(g);
+  a.queue = static_cast<unsigned long long*>(ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.two_pass = 1;
+  a.kvr = kv_rank;
+  a.kvr_L = rank_len;
+  a.out = out;
+  a.lse = lse;
+  a.kept = kept;
+  a.err = err;
+  a.gain_tau = gain_tau;
+  return launch_s2o_kernel(g, a, st);
 }
 
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax, hipStream_t st) {

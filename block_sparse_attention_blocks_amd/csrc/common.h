@@ -83,6 +83,15 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
 hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* perm, const int32_t* count, const int32_t* idx, float gain_tau,
                                 float* out, float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st);
+// Historical KV ranking of S2O: workspace, entries per KV head, and the launch (kv_rank int32
+// [Hkv][rank_len]).
+size_t prefix_rank_workspace_bytes(const Geometry& g);
+int64_t prefix_rank_length(const Geometry& g);
+hipError_t launch_prefix_rank(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* kv_rank, void* ws,
+                              hipStream_t st);
+hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                       const int32_t* kv_rank, int64_t rank_len, float gain_tau, float* out,
+                                       float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st);
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax,
                            hipStream_t st);
 hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);

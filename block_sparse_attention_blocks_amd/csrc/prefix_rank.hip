@@ -1,0 +1,369 @@
+// Historical KV ranking of S2O (Methodology 1, Historical KV Permutation): per KV head g and
+// segment sigma >= 1, every key of the causal prefix [0, sigma*S) ordered by its dot product with a
+// representative query of the segment (the mean of the segment's query rows over the G query heads
+// of g), descending, ties by position.  Three steps:
+//   seg_rep_kernel       fp64 representative queries (exact bf16 widening, fp64 sums)
+//   prefix_score_kernel  fp64 scores r . k_j, rounded to fp32 and written as order-preserving keys
+//   radix_*              stable least-significant-digit radix sort of every (g, sigma) list
+// Output layout: kv_rank[g][S*sigma*(sigma-1)/2 + r] = key of rank r for segment sigma.
+#include "common.h"
+
+namespace pbsa {
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+constexpr int RK_THREADS = 256;
+constexpr int RADIX_BITS = 4;
+constexpr int DIGITS = 1 << RADIX_BITS;
+constexpr int RADIX_PASSES = 32 / RADIX_BITS;
+
+// List and tile geometry of the ranking.  The radix tile is the largest power of two <= 2048 that
+// divides S, so every list (sigma*S keys) is a whole number of tiles.
+struct PrefixGeom {
+  int nseg;                // segments, ceil(N / S)
+  int S;
+  int64_t L;               // entries per KV head: S * nseg * (nseg - 1) / 2
+  int tile;                // radix tile (elements)
+  int tps;                 // tiles per S keys
+  int64_t tiles_per_head;  // tps * nseg * (nseg - 1) / 2
+};
+
+PrefixGeom prefix_geom(const Geometry& g) {
+  PrefixGeom p;
+  p.S = g.S;
+  p.nseg = (g.N + g.S - 1) / g.S;
+  p.L = (int64_t)g.S * p.nseg * (p.nseg - 1) / 2;
+  int t = 2048;
+  while (g.S % t) t >>= 1;
+  p.tile = t;
+  p.tps = g.S / t;
+  p.tiles_per_head = (int64_t)p.tps * p.nseg * (p.nseg - 1) / 2;
+  return p;
+}
+
+struct RankWs {
+  double* rep;      // [Hkv][nseg][d]
+  uint32_t* keysA;  // [Hkv][L]
+  uint32_t* keysB;
+  int32_t* valsA;
+  int32_t* valsB;
+  uint32_t* hist;   // [Hkv * tiles_per_head][DIGITS], per list digit-major
+};
+
+RankWs carve(const Geometry& g, const PrefixGeom& p, void* ws) {
+  char* c = static_cast<char*>(ws);
+  RankWs w;
+  const size_t n = (size_t)g.Hkv * p.L;
+  w.rep = reinterpret_cast<double*>(c);
+  c += align256(sizeof(double) * g.Hkv * (size_t)p.nseg * g.d);
+  w.keysA = reinterpret_cast<uint32_t*>(c);
+  c += align256(4 * n);
+  w.keysB = reinterpret_cast<uint32_t*>(c);
+  c += align256(4 * n);
+  w.valsA = reinterpret_cast<int32_t*>(c);
+  c += align256(4 * n);
+  w.valsB = reinterpret_cast<int32_t*>(c);
+  c += align256(4 * n);
+  w.hist = reinterpret_cast<uint32_t*>(c);
+  return w;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Representative queries: r[g][sigma] = (1 / (G * rows)) * sum over the G heads of g and the rows
+// of segment sigma of q.  Each thread sums 8 columns (one 16-byte load per row) over a strided
+// share of the rows in fp64; the row groups are combined in LDS in a fixed order.
+template <int D>
+__global__ __launch_bounds__(RK_THREADS) void seg_rep_kernel(const uint16_t* q, int64_t qsh, int64_t qst, int N,
+                                                             int S, int G, int nseg, double* rep) {
+  constexpr int CPR = D / 8;              // threads per row
+  constexpr int RP = RK_THREADS / CPR;    // rows per pass
+  __shared__ double part[RP][D];
+  const int sigma = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int c8 = t % CPR, rg = t / CPR;
+  const int i0 = sigma * S, len = min(S, N - i0);
+  const int rows = G * len;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int r = rg; r < rows; r += RP) {
+    const int h = g * G + r / len, i = i0 + r % len;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q + h * qsh + (int64_t)i * qst + c8 * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += (double)bf16_bits_to_f32(v[e] & 0xffffu);
+      acc[2 * e + 1] += (double)bf16_bits_to_f32(v[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][c8 * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < D) {
+    double s = 0.0;
+    for (int x = 0; x < RP; ++x) s += part[x][t];
+    rep[((size_t)g * nseg + sigma) * D + t] = s / (double)rows;
+  }
+}
+
+// Order-preserving key of a score: ascending key = descending score.  The fp64 score is rounded to
+// fp32 first, so scores within one fp32 rounding of each other may come out tied (then the
+// stable sort keeps them in position order).
+__device__ __forceinline__ uint32_t desc_key32(double z) {
+  const uint32_t b = __float_as_uint((float)z);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ~o;
+}
+
+// Scores of the keys that lie in some prefix (j < (nseg-1)*S), one key per lane (its row read in
+// 16-byte chunks), against the representatives of every later segment, 16 at a time; fp64 FMAs.
+template <int D>
+__global__ __launch_bounds__(RK_THREADS) void prefix_score_kernel(const uint16_t* k, int64_t ksh, int64_t kst,
+                                                                  const double* __restrict__ rep, int S, int nseg,
+                                                                  int64_t L, uint32_t* keys) {
+  constexpr int RG = 16;
+  const int g = blockIdx.y, t = threadIdx.x;
+  const int nh = (nseg - 1) * S;  // keys that belong to some prefix
+  const int j0 = blockIdx.x * RK_THREADS, j = j0 + t;
+  const bool live = j < nh;
+  const int sj = (live ? j : j0) / S;
+  const uint16_t* kp = k + g * ksh + (int64_t)(live ? j : j0) * kst;
+  const double* rg_base = rep + (size_t)g * nseg * D;
+  for (int s0 = j0 / S + 1; s0 < nseg; s0 += RG) {
+    double acc[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) acc[r] = 0.0;
+#pragma unroll 2
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 kc = *reinterpret_cast<const u32x4*>(kp + c * 8);  // this lane's key, 8 columns
+      double kd[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kd[2 * e] = (double)bf16_bits_to_f32(kc[e] & 0xffffu);
+        kd[2 * e + 1] = (double)bf16_bits_to_f32(kc[e] >> 16);
+      }
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const int sr = min(s0 + r, nseg - 1);  // rows past the last segment repeat it (not written)
+        const double* rr = rg_base + (size_t)sr * D + c * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r] = fma(kd[e], rr[e], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int sigma = s0 + r;
+      if (live && sigma < nseg && sigma > sj)
+        keys[(size_t)g * L + (size_t)S * sigma * (sigma - 1) / 2 + j] = desc_key32(acc[r]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stable LSD radix sort of every (g, sigma) list, RADIX_BITS per pass.  A tile of `tile` elements
+// is split into contiguous runs of E per thread (E = tile / 256, or one element for the first tile
+// threads when tile < 256), so thread order then element order is position order.
+struct RadixArgs {
+  uint32_t* keys_in;
+  uint32_t* keys_out;
+  const int32_t* vals_in;  // NULL in the first pass: the value is the position in the list
+  int32_t* vals_out;
+  uint32_t* hist;
+  int S, nseg, tile, tps;
+  int64_t L, tiles_per_head;
+  int shift;
+  bool write_keys;
+};
+
+struct TileRef {
+  int64_t elem;   // first element of the tile
+  int64_t hbase;  // hist base of the tile's list
+  int nt;         // tiles of the list
+  int t;          // tile within the list
+};
+
+__device__ __forceinline__ TileRef tile_ref(const RadixArgs& a, int64_t f) {
+  const int g = (int)(f / a.tiles_per_head);
+  const int64_t r = f - (int64_t)g * a.tiles_per_head;
+  int sigma = 1;
+  while ((int64_t)a.tps * sigma * (sigma + 1) / 2 <= r) ++sigma;
+  const int64_t first = (int64_t)a.tps * sigma * (sigma - 1) / 2;  // first tile of the list
+  TileRef x;
+  x.t = (int)(r - first);
+  x.nt = a.tps * sigma;
+  x.elem = (int64_t)g * a.L + (int64_t)a.S * sigma * (sigma - 1) / 2 + (int64_t)x.t * a.tile;
+  x.hbase = (int64_t)DIGITS * ((int64_t)g * a.tiles_per_head + first);
+  return x;
+}
+
+// Block-wide exclusive scan of cnt[DIGITS * 256] in place (digit-major); thread t owns entries
+// 16t .. 16t+15.  Returns nothing; cnt then holds each (digit, thread) start within the tile.
+__device__ __forceinline__ void scan_counts(uint32_t* cnt, uint32_t* wsum) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t v[16];
+  uint32_t run = 0;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    v[x] = run;
+    run += cnt[t * 16 + x];
+  }
+  uint32_t inc = run;  // inclusive scan of the per-thread totals across the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t base = inc - run;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) cnt[t * 16 + x] = base + v[x];
+  __syncthreads();
+}
+
+// Per-thread digit counts of its run, 4 bits per digit (a run holds at most 8 elements).
+__device__ __forceinline__ int run_len(int tile) { return tile >= RK_THREADS ? tile / RK_THREADS : 1; }
+
+__global__ __launch_bounds__(RK_THREADS) void radix_hist_kernel(RadixArgs a) {
+  __shared__ uint32_t cnt[DIGITS * RK_THREADS];
+  __shared__ uint32_t wsum[RK_THREADS / 64];
+  const int t = threadIdx.x;
+  const TileRef x = tile_ref(a, blockIdx.x);
+  const int E = run_len(a.tile);
+  const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
+  uint64_t c = 0;
+  for (int e = 0; e < n; ++e) {
+    const uint32_t d = (a.keys_in[x.elem + (int64_t)t * E + e] >> a.shift) & (DIGITS - 1);
+    c += 1ull << (4 * d);
+  }
+#pragma unroll
+  for (int d = 0; d < DIGITS; ++d) cnt[d * RK_THREADS + t] = (uint32_t)(c >> (4 * d)) & 15u;
+  __syncthreads();
+  scan_counts(cnt, wsum);
+  if (t < DIGITS) {
+    const uint32_t start = cnt[t * RK_THREADS];
+    const uint32_t end = t + 1 < DIGITS ? cnt[(t + 1) * RK_THREADS] : (uint32_t)a.tile;
+    a.hist[x.hbase + (int64_t)t * x.nt + x.t] = end - start;
+  }
+}
+
+// Exclusive scan of one list's histogram in (digit, tile) order: the first output position of
+// every (digit, tile) in the list.
+__global__ __launch_bounds__(RK_THREADS) void radix_scan_kernel(RadixArgs a) {
+  __shared__ uint32_t wsum[RK_THREADS / 64];
+  __shared__ uint32_t carry;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int g = blockIdx.x / (a.nseg - 1), sigma = blockIdx.x % (a.nseg - 1) + 1;
+  const int64_t first = (int64_t)a.tps * sigma * (sigma - 1) / 2;
+  uint32_t* h = a.hist + (int64_t)DIGITS * ((int64_t)g * a.tiles_per_head + first);
+  const int n = DIGITS * a.tps * sigma;
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int b = 0; b < n; b += RK_THREADS) {
+    const uint32_t v = b + t < n ? h[b + t] : 0u;
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    uint32_t base = carry;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    if (b + t < n) h[b + t] = base + inc - v;
+    __syncthreads();
+    if (t == RK_THREADS - 1) carry = base + inc;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(RK_THREADS) void radix_scatter_kernel(RadixArgs a) {
+  __shared__ uint32_t cnt[DIGITS * RK_THREADS];
+  __shared__ uint32_t wsum[RK_THREADS / 64];
+  const int t = threadIdx.x;
+  const TileRef x = tile_ref(a, blockIdx.x);
+  const int E = run_len(a.tile);
+  const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
+  const int64_t e0 = x.elem + (int64_t)t * E;
+  uint32_t kv[8];
+  int32_t vv[8];
+  uint64_t c = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < n) {
+      kv[e] = a.keys_in[e0 + e];
+      vv[e] = a.vals_in ? a.vals_in[e0 + e] : (int32_t)(x.t * a.tile + t * E + e);
+      c += 1ull << (4 * ((kv[e] >> a.shift) & (DIGITS - 1)));
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DIGITS; ++d) cnt[d * RK_THREADS + t] = (uint32_t)(c >> (4 * d)) & 15u;
+  __syncthreads();
+  scan_counts(cnt, wsum);
+  const int64_t lbase = x.elem - (int64_t)x.t * a.tile;  // first element of the list
+  uint64_t seen = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e >= n) break;
+    const uint32_t d = (kv[e] >> a.shift) & (DIGITS - 1);
+    const uint32_t rank = cnt[d * RK_THREADS + t] - cnt[d * RK_THREADS] + ((uint32_t)(seen >> (4 * d)) & 15u);
+    seen += 1ull << (4 * d);
+    const int64_t dst = lbase + a.hist[x.hbase + (int64_t)d * x.nt + x.t] + rank;
+    if (a.write_keys) a.keys_out[dst] = kv[e];
+    a.vals_out[dst] = vv[e];
+  }
+}
+
+}  // namespace
+
+size_t prefix_rank_workspace_bytes(const Geometry& g) {
+  const PrefixGeom p = prefix_geom(g);
+  const size_t n = (size_t)g.Hkv * p.L;
+  return align256(sizeof(double) * g.Hkv * (size_t)p.nseg * g.d) + 4 * align256(4 * n) +
+         align256(sizeof(uint32_t) * DIGITS * (size_t)g.Hkv * p.tiles_per_head);
+}
+
+int64_t prefix_rank_length(const Geometry& g) { return prefix_geom(g).L; }
+
+hipError_t launch_prefix_rank(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* kv_rank, void* ws,
+                              hipStream_t st) {
+  const PrefixGeom p = prefix_geom(g);
+  if (p.nseg < 2) return hipSuccess;  // no segment has a prefix
+  const RankWs w = carve(g, p, ws);
+  if (g.d == 128)
+    seg_rep_kernel<128><<<dim3(p.nseg, g.Hkv), RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.S, g.G, p.nseg, w.rep);
+  else
+    seg_rep_kernel<64><<<dim3(p.nseg, g.Hkv), RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.S, g.G, p.nseg, w.rep);
+  const int nh = (p.nseg - 1) * g.S;
+  const dim3 sgrid((nh + RK_THREADS - 1) / RK_THREADS, g.Hkv);
+  if (g.d == 128)
+    prefix_score_kernel<128><<<sgrid, RK_THREADS, 0, st>>>(k, g.kvsh, g.kvst, w.rep, g.S, p.nseg, p.L, w.keysA);
+  else
+    prefix_score_kernel<64><<<sgrid, RK_THREADS, 0, st>>>(k, g.kvsh, g.kvst, w.rep, g.S, p.nseg, p.L, w.keysA);
+  RadixArgs a;
+  a.hist = w.hist;
+  a.S = g.S;
+  a.nseg = p.nseg;
+  a.tile = p.tile;
+  a.tps = p.tps;
+  a.L = p.L;
+  a.tiles_per_head = p.tiles_per_head;
+  const int64_t tiles = (int64_t)g.Hkv * p.tiles_per_head;
+  const int lists = g.Hkv * (p.nseg - 1);
+  for (int pass = 0; pass < RADIX_PASSES; ++pass) {
+    const bool even = (pass & 1) == 0;
+    a.keys_in = even ? w.keysA : w.keysB;
+    a.keys_out = even ? w.keysB : w.keysA;
+    a.vals_in = pass == 0 ? nullptr : (even ? w.valsA : w.valsB);
+    a.vals_out = pass == RADIX_PASSES - 1 ? kv_rank : (even ? w.valsB : w.valsA);
+    a.shift = pass * RADIX_BITS;
+    a.write_keys = pass != RADIX_PASSES - 1;
+    radix_hist_kernel<<<(unsigned)tiles, RK_THREADS, 0, st>>>(a);
+    radix_scan_kernel<<<lists, RK_THREADS, 0, st>>>(a);
+    radix_scatter_kernel<<<(unsigned)tiles, RK_THREADS, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pbsa

@@ -83,7 +83,8 @@ typedef struct {
 enum {
   PBSA_OP_PERMUTATION = 0,
   PBSA_OP_MASK = 1,
-  PBSA_OP_ATTENTION = 2
+  PBSA_OP_ATTENTION = 2,
+  PBSA_OP_PREFIX_RANK = 3
 };
 
 /* Flags of pbsa_estimate_block_mask. */
@@ -206,6 +207,50 @@ pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, co
                                   const int32_t* block_idx, float gain_tau, float* out, float* lse,
                                   uint32_t* kept_bitmap, int32_t* device_error, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Historical KV ranking (S2O, Methodology 1, Historical KV Permutation): the keys before each
+ * segment ranked against a representative query of the segment.
+ *
+ * For KV head g and segment sigma >= 1 (segments of segment_size S, nseg = ceil(N / S)): the
+ * representative r = mean of the query rows of segment sigma over the G query heads of g (fp64, from
+ * the bf16 values); every key j < sigma*S (the causal prefix) gets the score r . k_j (fp64, then
+ * rounded to fp32); the prefix is listed by score descending, equal fp32 scores by position.
+ *
+ *   kv_rank    out, int32 [Hkv][pbsa_prefix_rank_length(shape)]: segment sigma's order (key
+ *              positions, a permutation of 0 .. sigma*S-1) at offset S*sigma*(sigma-1)/2
+ *   workspace  >= pbsa_workspace_size(shape, PBSA_OP_PREFIX_RANK) bytes, 256-byte aligned
+ * Requires segment_size > 0; PBSA_ERR_UNSUPPORTED for more than 256 segments or more than 2^31
+ * entries over all KV heads.  Scores within one fp32 rounding of each other may come out in
+ * position order rather than in exact fp64 order.
+ */
+pbsa_status pbsa_build_prefix_kv_ranking(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                         int32_t* kv_rank, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* Entries per KV head of the historical ranking, S * nseg * (nseg - 1) / 2, or -1 if the shape is
+ * invalid or unsupported for it.  Host-only. */
+int64_t pbsa_prefix_rank_length(const pbsa_shape* shape);
+
+/*
+ * S2O's two-pass attention with the marginal-gain early stop (Kernel Implementation; Early-Stopping
+ * Rule).  For query block I of head h (segment sigma, first block J0 = sigma*S/B): pass 1 takes the
+ * own segment's blocks J0 .. I in natural order (causal mask on the diagonal); pass 2 takes blocks
+ * J = 0, 1, ..., J0-1 of the prefix order kv_rank (block J = the keys of ranks J*B .. J*B+B-1 of
+ * segment sigma, KV head g(h)).  After each pass-2 block the row stops as in pbsa_s2o_attn_prefill
+ * (every query's share of that block in its softmax denominator below gain_tau; that block stays
+ * processed).  out/lse: softmax attention over the processed keys.
+ *   kv_rank      from pbsa_build_prefix_kv_ranking (entries must lie in the segment's prefix: an
+ *                entry outside it is skipped and sets bit 2 of device_error)
+ *   kept_bitmap  out, or NULL: bit I(I+1)/2 + J set for every processed entry J (J >= J0: natural
+ *                block J; J < J0: prefix-order block J); caller zeroes it
+ *   other arguments as for pbsa_s2o_attn_prefill; segment_size must be > 0.
+ */
+pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                         const uint16_t* v, const int32_t* kv_rank, float gain_tau,
+                                         float* out, float* lse, uint32_t* kept_bitmap,
+                                         int32_t* device_error, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /*
  * Early-stop calibration helper (Block Sparse Flash Attention, Approach: offline thresholds).

@@ -37,4 +37,5 @@ from .pbsa_oracle import (  # noqa: F401
     segment_representatives,
     tile_max,
     tri_offset,
+    two_pass_attention_on,
 )

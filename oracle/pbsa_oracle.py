@@ -479,6 +479,26 @@ def s2o_prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.nda
     return out, lse, processed
 
 
+def two_pass_attention_on(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.ndarray,
+                          entries: Dict[Tuple[int, int], Sequence[int]], block_size: int, segment_size: int,
+                          scale: Optional[float] = None):
+    """Softmax attention of each listed row (h, I) over the keys of the given two-pass entries
+    (J >= J0: natural block J; J < J0: block J of the segment's prefix order), causal per query;
+    the output of s2o_prefix_attention for a given processed set.  Returns (out, lse), NaN on rows
+    not listed."""
+    Hq, N, d = q.shape
+    G = Hq // k.shape[0]
+    B, S = block_size, segment_size
+    c = default_scale(d) if scale is None else scale
+    out = np.full((Hq, N, d), np.nan)
+    lse = np.full((Hq, N), np.nan)
+    for (h, I), lst in entries.items():
+        rows_of, _ = _prefix_rows_of(pi, h // G, I, B, S, N)
+        keys = np.concatenate([rows_of(J) for J in lst]) if len(lst) else np.zeros(0, dtype=np.int64)
+        _attend(q, k, v, h, h // G, block_range(I, B, N), keys, c, out, lse)
+    return out, lse
+
+
 def s2o_prefix_gain_ratios(q: np.ndarray, k: np.ndarray, pi: np.ndarray, block_size: int, segment_size: int,
                            scale: Optional[float] = None,
                            rows: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], np.ndarray]:

@@ -10,6 +10,9 @@ Tie rules, used wherever a floating-point comparison decides an integer result:
     agree wherever the oracle's tile max is further than the fp32 error bound from theta;
   * ranked order (marginal-gain stop): a position where GPU and oracle list different blocks is a
     recorded tie iff the two blocks' oracle pooled logits differ by at most 1e-6 relative;
+  * historical ranking (S2O prefix order): the GPU ranks fp32-rounded scores; a rank where GPU and
+    oracle list different keys is a recorded tie iff the two keys' oracle scores differ by at most
+    1e-6 relative;
   * marginal-gain stop: the kernel forms dl_i / l_i from bf16-rounded probabilities (each off by
     at most 2^-9 relative, so the ratio by under 0.4%); a stop or a go-on must agree with the
     oracle's exact ratio wherever that ratio is more than S2O_BAND (relative) from gain_tau.
@@ -112,6 +115,45 @@ def compare_s2o_stops(kept, count_g, idx_g, ratios, gain_tau: float, band: float
         exact_n = int(stop[0]) + 1 if stop.size else len(lst)
         near += exact_n != n
     return len(ratios), near
+
+
+def compare_prefix_rank(pi_g, pi_o, score_o, S: int) -> int:
+    """Assert every (g, sigma) list of the GPU's historical ranking is a permutation of its prefix and
+    equals the oracle's up to recorded ties; return the tie count."""
+    Hkv, L = pi_o.shape
+    assert pi_g.shape == pi_o.shape, (pi_g.shape, pi_o.shape)
+    ties = 0
+    sigma = 1
+    while oracle.prefix_offset(sigma, S) < L:
+        o, n = oracle.prefix_offset(sigma, S), sigma * S
+        for g in range(Hkv):
+            a, b = pi_g[g, o:o + n], pi_o[g, o:o + n]
+            assert np.array_equal(np.sort(a), np.arange(n)), f"ranking ({g},{sigma}) is not a permutation of its prefix"
+            diff = np.nonzero(a != b)[0]
+            if diff.size:
+                z = np.empty(n)
+                z[b] = score_o[g, o:o + n]
+                za, zb = z[a[diff]], z[b[diff]]
+                tol = TIE * np.maximum(np.maximum(np.abs(za), np.abs(zb)), 1e-30)
+                bad = np.nonzero(np.abs(za - zb) > tol)[0]
+                assert bad.size == 0, (f"ranking ({g},{sigma}) rank {diff[bad[0]]}: gpu key {a[diff[bad[0]]]} "
+                                       f"(score {za[bad[0]]!r}) vs oracle key {b[diff[bad[0]]]} ({zb[bad[0]]!r})")
+                ties += diff.size
+        sigma += 1
+    return ties
+
+
+def two_pass_lists(Hq: int, N: int, B: int, S: int):
+    """count/idx of S2O's two-pass lists: the own segment's blocks ascending, then prefix blocks 0 .. J0-1."""
+    NB = -(-N // B)
+    count = np.zeros((Hq, NB), dtype=np.int64)
+    idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    for I in range(NB):
+        J0 = ((I * B) // S) * S // B
+        o = oracle.tri_offset(I)
+        count[:, I] = I + 1
+        idx[:, o:o + I + 1] = list(range(J0, I + 1)) + list(range(J0))
+    return count, idx
 
 
 def compare_out(out_g: np.ndarray, out_o: np.ndarray, what: str = "out"):

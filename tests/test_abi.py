@@ -197,3 +197,46 @@ def test_empty_sequence_is_a_no_op():
                                             None, None, None, None, 0, None) == 0
     assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == 0
     assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 4, FAKE, None) == 0
+
+
+def test_prefix_rank_length_and_workspace():
+    l = _lib.lib()
+    assert l.pbsa_prefix_rank_length(ctypes.byref(shape(N=1024, S=512))) == 512          # 2 segments
+    assert l.pbsa_prefix_rank_length(ctypes.byref(shape(N=2000, S=512))) == 512 * 4 * 3 // 2
+    assert l.pbsa_prefix_rank_length(ctypes.byref(shape(N=512, S=512))) == 0             # one segment
+    assert l.pbsa_prefix_rank_length(ctypes.byref(shape(N=0))) == 0
+    assert l.pbsa_prefix_rank_length(ctypes.byref(shape(S=0))) == -1                     # segments off
+    assert l.pbsa_prefix_rank_length(ctypes.byref(shape(N=64 * 300, B=64, S=64))) == -1  # > 256 segments
+    assert ws_size(shape(S=0), _lib.PBSA_OP_PREFIX_RANK) == _lib.SIZE_MAX
+    prev = 0
+    for n in (512, 1024, 2048, 4096, 8192):
+        w = ws_size(shape(N=n, S=512), _lib.PBSA_OP_PREFIX_RANK)
+        assert w != _lib.SIZE_MAX and w >= prev
+        prev = w
+
+
+def test_prefix_ranking_and_two_pass_entry_validate_before_launch():
+    l = _lib.lib()
+    E, W, U = _lib.PBSA_ERR_INVALID_ARG, _lib.PBSA_ERR_WORKSPACE, _lib.PBSA_ERR_UNSUPPORTED
+    s = shape(N=2048, S=512)
+    ws = ctypes.c_void_p(0x10000)
+    big = 1 << 40
+    rank = l.pbsa_build_prefix_kv_ranking
+    assert rank(ctypes.byref(shape(S=0)), FAKE, FAKE, FAKE, ws, big, None) == E
+    assert rank(ctypes.byref(s), None, FAKE, FAKE, ws, big, None) == E
+    assert rank(ctypes.byref(s), FAKE, FAKE, None, ws, big, None) == E          # output missing
+    assert rank(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None) == W          # workspace missing
+    assert rank(ctypes.byref(shape(N=64 * 300, B=64, S=64)), FAKE, FAKE, FAKE, ws, big, None) == U
+    assert rank(ctypes.byref(shape(N=0)), FAKE, FAKE, None, None, 0, None) == 0       # nothing to rank
+    assert rank(ctypes.byref(shape(N=400, S=512)), FAKE, FAKE, None, None, 0, None) == 0
+    att = l.pbsa_s2o_prefix_attn_prefill
+    args = lambda sh, kvr, tau, w=ws: (ctypes.byref(sh), FAKE, FAKE, FAKE, kvr, tau, FAKE, None, None, None, w,
+                                       big if w else 0, None)
+    assert att(*args(s, FAKE, -1.0)) == E
+    assert att(*args(s, FAKE, float("nan"))) == E
+    assert att(*args(s, FAKE, float("inf"))) == E
+    assert att(*args(shape(S=0), FAKE, 0.01)) == E
+    assert att(*args(s, None, 0.01)) == E                                       # ranking missing
+    assert att(*args(s, FAKE, 0.01, None)) == W
+    assert att(*args(shape(N=64 * 300, B=64, S=64), FAKE, 0.01)) == U
+    assert att(*args(shape(N=0), None, 0.01)) == 0

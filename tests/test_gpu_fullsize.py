@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_ranked,
-                    compare_s2o_stops, kept_to_mask)
+from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_prefix_rank,
+                    compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
 from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
 
 pytestmark = pytest.mark.gpu
@@ -183,4 +183,35 @@ def test_fullsize_32k_marginal_gain_sampled():
     compare_lse(lse_t.cpu().numpy(), lse_o)
     frac = sum(len(x) for x in kept.values()) / (Hq * NB * (NB + 1) / 2)
     _log(f"[fullsize] 32K marginal-gain stop: processed {frac:.3f}, sampled rows {rows} ({near} in band): "
+         f"max abs {mx:.2e} mean {mean:.2e}")
+
+
+def test_fullsize_32k_two_pass_sampled():
+    """S2O two-pass attention at 32K: the whole historical ranking, and the stop and outputs of
+    sampled rows."""
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_32k"]
+    gain_tau = 0.01
+    _log(f"[fullsize] {w.name} two-pass, gain_tau {gain_tau}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, S, NB, Hq, N = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads, w.seq_len
+    rank_t = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    out_t, lse_t, kept_t = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank_t, B, S, gain_tau,
+                                                        return_kept=True)
+    torch.cuda.synchronize()
+    pi_g = rank_t.cpu().numpy().astype(np.int64)
+    pi_o, score_o = oracle.prefix_kv_ranking(q, k, S)
+    ties = compare_prefix_rank(pi_g, pi_o, score_o, S)
+    _log(f"[fullsize] historical ranking ok ({ties} recorded ties)")
+    kept = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+    rows = _sample_rows(Hq, NB, 12, 12)
+    cg, ig = two_pass_lists(Hq, N, B, S)
+    ratios = oracle.s2o_prefix_gain_ratios(q, k, pi_g, B, S, rows=rows)
+    _, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau)
+    out_o, lse_o = oracle.two_pass_attention_on(q, k, v, pi_g, {r: kept[r] for r in rows}, B, S)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o, "two-pass 32K")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    frac = sum(len(x) for x in kept.values()) / (Hq * NB * (NB + 1) / 2)
+    _log(f"[fullsize] 32K two-pass: processed {frac:.3f}, sampled rows {rows} ({near} in band): "
          f"max abs {mx:.2e} mean {mean:.2e}")

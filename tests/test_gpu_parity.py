@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_ranked,
-                    compare_s2o_stops, kept_to_mask)
+from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_prefix_rank,
+                    compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
 from workloads import bf16_bits_to_f32, generate
 
 pytestmark = pytest.mark.gpu
@@ -448,3 +448,85 @@ def test_marginal_gain_is_deterministic_and_skips_bad_entries():
     assert int(err.item()) & 1 and int(err.item()) & 4
     assert torch.isfinite(out).all()
     assert NB == 16
+
+
+# S2O two-pass attention over the historical ranking: (name, N, Hq, Hkv, d, B, S, stripes, band,
+# gain_tau, seed).  S = 128 and 192 exercise radix tiles shorter than a workgroup and a segment that
+# is not a power of two; 8192 with S = 4096 the widest tiles.
+TWO_PASS_CASES = [
+    ("flat_b64_d128_gqa_2048", 2048, 4, 2, 128, 64, 256, 0, 0, 0.05, 51),
+    ("band_b128_d64_ragged_4000", 4000, 4, 1, 64, 128, 512, 0, 256, 0.02, 52),
+    ("stripes_b128_d128_ragged_3000", 3000, 2, 1, 128, 128, 512, 4, 256, 0.05, 53),
+    ("flat_b64_d64_s128_ragged_1100", 1100, 2, 2, 64, 64, 128, 0, 64, 0.1, 54),
+    ("s192_b64_d128_1536", 1536, 2, 1, 128, 64, 192, 0, 64, 0.05, 55),
+    ("s4096_b128_d128_8192", 8192, 2, 1, 128, 128, 4096, 8, 512, 0.01, 56),
+    ("one_segment_b128_700", 700, 2, 1, 128, 128, 1024, 0, 0, 0.05, 57),
+]
+
+
+@pytest.mark.parametrize("case", TWO_PASS_CASES, ids=[c[0] for c in TWO_PASS_CASES])
+def test_two_pass_stagewise(case):
+    pbsa = _need_gpu()
+    name, N, Hq, Hkv, d, B, S, stripes, band, gain_tau, seed = case
+    _log(f"[parity] two-pass {name}: N={N} Hq={Hq} Hkv={Hkv} d={d} B={B} S={S} gain_tau={gain_tau}")
+    dev, host = _inputs(N, Hq, Hkv, d, stripes, band, seed)
+    q, k, v = host["q"], host["k"], host["v"]
+    NB = oracle.num_blocks(N, B)
+
+    rank_t = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    torch.cuda.synchronize()
+    pi_g = rank_t.cpu().numpy().astype(np.int64)
+    pi_o, score_o = oracle.prefix_kv_ranking(q, k, S)
+    ties = compare_prefix_rank(pi_g, pi_o, score_o, S)
+
+    out_t, lse_t, kept_t, err_t = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank_t, B, S, gain_tau,
+                                                               return_kept=True, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err_t.item()) == 0
+    kept = bitmap_to_kept(kept_t.cpu().numpy(), NB)
+    cg, ig = two_pass_lists(Hq, N, B, S)
+    ratios = oracle.s2o_prefix_gain_ratios(q, k, pi_g, B, S)
+    rows, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau)
+    out_o, lse_o = oracle.two_pass_attention_on(q, k, v, pi_g, kept, B, S)
+    mx, mean = compare_out(out_t.cpu().numpy(), out_o, "two-pass")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    frac = sum(len(x) for x in kept.values()) / float(Hq * NB * (NB + 1) // 2)
+    _log(f"[parity] two-pass {name}: rank ties {ties}, rows {rows}, decided in band {near}, processed {frac:.3f}, "
+         f"max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+@pytest.mark.parametrize("d,B,N,S", [(128, 128, 2048, 512), (64, 64, 1500, 256)])
+def test_two_pass_zero_threshold_is_dense(d, B, N, S):
+    pbsa = _need_gpu()
+    Hq, Hkv = 4, 2
+    dev, host = _inputs(N, Hq, Hkv, d, 8, 2 * B, 58)
+    NB = oracle.num_blocks(N, B)
+    rank = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    out, lse, kept = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank, B, S, 0.0, return_kept=True)
+    torch.cuda.synchronize()
+    assert all(lst == list(range(I + 1)) for (h, I), lst in bitmap_to_kept(kept.cpu().numpy(), NB).items())
+    ref, ref_lse = oracle.dense_attention(host["q"], host["k"], host["v"])
+    compare_out(out.cpu().numpy(), ref, "two-pass gain_tau 0")
+    compare_lse(lse.cpu().numpy(), ref_lse)
+
+
+def test_two_pass_is_deterministic_and_bounds_the_ranking():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 2048, 2, 1, 128, 128, 512
+    dev, _ = _inputs(N, Hq, Hkv, d, 0, 256, 59)
+    r1 = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    r2 = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    a = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], r1, B, S, 0.03, return_kept=True)
+    b = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], r1, B, S, 0.03, return_kept=True)
+    torch.cuda.synchronize()
+    assert torch.equal(r1, r2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    # an entry of segment 2's order that is not in its prefix (a key of segment 2 itself) is skipped
+    bad = r1.clone()
+    bad[0, oracle.prefix_offset(2, S) + 3] = 2 * S + 10
+    out, err = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], bad, B, S, 0.0, return_lse=False,
+                                            return_error=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
+    assert torch.isfinite(out).all()

@@ -452,3 +452,16 @@ def test_two_pass_stop_is_monotone_and_history_blocks_hold_the_top_keys():
     z = k[0, :2 * S] @ r[0, 2]
     o = oracle.prefix_offset(2, S)
     assert set(pi[0, o:o + B].tolist()) == set(np.argsort(-z, kind="stable")[:B].tolist())
+
+
+def test_two_pass_attention_on_a_given_processed_set():
+    N, Hq, Hkv, d, B, S = 96, 4, 2, 8, 8, 32
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=35)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    out, lse, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, 0.05)
+    out2, lse2 = oracle.two_pass_attention_on(q, k, v, pi, done, B, S)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    full = {(h, I): list(range(I + 1)) for h in range(Hq) for I in range(N // B)}
+    out3, lse3 = oracle.two_pass_attention_on(q, k, v, pi, full, B, S)
+    ref, ref_lse = oracle.dense_attention(q, k, v)
+    assert np.abs(out3 - ref).max() <= 1e-12 and np.abs(lse3 - ref_lse).max() <= 1e-12
