@@ -2,7 +2,7 @@
 // segment sigma >= 1, every key of the causal prefix [0, sigma*S) ordered by its dot product with a
 // representative query of the segment (the mean of the segment's query rows over the G query heads
 // of g), descending, ties by position.  Three steps:
-//   seg_rep_kernel       fp64 representative queries (exact bf16 widening, fp64 sums)
+//   seg_rep_*            fp64 representative queries (exact bf16 widening, fp64 sums)
 //   prefix_score_kernel  fp64 scores r . k_j, rounded to fp32 and written as order-preserving keys
 //   radix_*              stable least-significant-digit radix sort of every (g, sigma) list
 // Output layout: kv_rank[g][S*sigma*(sigma-1)/2 + r] = key of rank r for segment sigma.
@@ -42,8 +42,13 @@ PrefixGeom prefix_geom(const Geometry& g) {
   return p;
 }
 
+constexpr int REP_ROWS = 256;  // query rows summed by one workgroup of seg_rep_partial_kernel
+
+int rep_chunks(const Geometry& g) { return (g.G * g.S + REP_ROWS - 1) / REP_ROWS; }
+
 struct RankWs {
   double* rep;      // [Hkv][nseg][d]
+  double* rpart;    // [Hkv][nseg][rep_chunks][d] partial sums
   uint32_t* keysA;  // [Hkv][L]
   uint32_t* keysB;
   int32_t* valsA;
@@ -57,6 +62,8 @@ RankWs carve(const Geometry& g, const PrefixGeom& p, void* ws) {
   const size_t n = (size_t)g.Hkv * p.L;
   w.rep = reinterpret_cast<double*>(c);
   c += align256(sizeof(double) * g.Hkv * (size_t)p.nseg * g.d);
+  w.rpart = reinterpret_cast<double*>(c);
+  c += align256(sizeof(double) * g.Hkv * (size_t)p.nseg * rep_chunks(g) * g.d);
   w.keysA = reinterpret_cast<uint32_t*>(c);
   c += align256(4 * n);
   w.keysB = reinterpret_cast<uint32_t*>(c);
@@ -71,22 +78,25 @@ RankWs carve(const Geometry& g, const PrefixGeom& p, void* ws) {
 
 // ---------------------------------------------------------------------------------------------
 // Representative queries: r[g][sigma] = (1 / (G * rows)) * sum over the G heads of g and the rows
-// of segment sigma of q.  Each thread sums 8 columns (one 16-byte load per row) over a strided
-// share of the rows in fp64; the row groups are combined in LDS in a fixed order.
+// of segment sigma of q.  The segment's G * rows query rows (head-major) are cut into chunks of
+// REP_ROWS; one workgroup sums one chunk in fp64 (each thread 8 columns, one 16-byte load per row,
+// its row group combined in LDS in a fixed order), and a second kernel adds the chunk sums in
+// chunk order, so the result does not depend on scheduling.
 template <int D>
-__global__ __launch_bounds__(RK_THREADS) void seg_rep_kernel(const uint16_t* q, int64_t qsh, int64_t qst, int N,
-                                                             int S, int G, int nseg, double* rep) {
+__global__ __launch_bounds__(RK_THREADS) void seg_rep_partial_kernel(const uint16_t* q, int64_t qsh, int64_t qst,
+                                                                     int N, int S, int G, int nseg, int nch,
+                                                                     double* rpart) {
   constexpr int CPR = D / 8;              // threads per row
   constexpr int RP = RK_THREADS / CPR;    // rows per pass
   __shared__ double part[RP][D];
-  const int sigma = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int ch = blockIdx.x, sigma = blockIdx.y, g = blockIdx.z, t = threadIdx.x;
   const int c8 = t % CPR, rg = t / CPR;
   const int i0 = sigma * S, len = min(S, N - i0);
-  const int rows = G * len;
+  const int r0 = ch * REP_ROWS, r1 = min(r0 + REP_ROWS, G * len);
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-  for (int r = rg; r < rows; r += RP) {
+  for (int r = r0 + rg; r < r1; r += RP) {
     const int h = g * G + r / len, i = i0 + r % len;
     const u32x4 v = *reinterpret_cast<const u32x4*>(q + h * qsh + (int64_t)i * qst + c8 * 8);
 #pragma unroll
@@ -101,8 +111,20 @@ __global__ __launch_bounds__(RK_THREADS) void seg_rep_kernel(const uint16_t* q, 
   if (t < D) {
     double s = 0.0;
     for (int x = 0; x < RP; ++x) s += part[x][t];
-    rep[((size_t)g * nseg + sigma) * D + t] = s / (double)rows;
+    rpart[(((size_t)g * nseg + sigma) * nch + ch) * D + t] = s;
   }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void seg_rep_combine_kernel(const double* rpart, int N, int S, int G, int nseg,
+                                                            int nch, double* rep) {
+  const int sigma = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
+  const int rows = G * min(S, N - sigma * S);
+  const int used = (rows + REP_ROWS - 1) / REP_ROWS;
+  const double* p = rpart + ((size_t)g * nseg + sigma) * nch * D + t;
+  double s = 0.0;
+  for (int c = 0; c < used; ++c) s += p[(size_t)c * D];
+  rep[((size_t)g * nseg + sigma) * D + t] = s / (double)rows;
 }
 
 // Order-preserving key of a score: ascending key = descending score.  The fp64 score is rounded to
@@ -231,9 +253,9 @@ __global__ __launch_bounds__(RK_THREADS) void radix_hist_kernel(RadixArgs a) {
   const TileRef x = tile_ref(a, blockIdx.x);
   const int E = run_len(a.tile);
   const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
-  uint64_t c = 0;
+  uint64_t c = 0;  // only the digit totals are needed here, so the reads are striped (coalesced)
   for (int e = 0; e < n; ++e) {
-    const uint32_t d = (a.keys_in[x.elem + (int64_t)t * E + e] >> a.shift) & (DIGITS - 1);
+    const uint32_t d = (a.keys_in[x.elem + t + (int64_t)RK_THREADS * e] >> a.shift) & (DIGITS - 1);
     c += 1ull << (4 * d);
   }
 #pragma unroll
@@ -278,40 +300,60 @@ __global__ __launch_bounds__(RK_THREADS) void radix_scan_kernel(RadixArgs a) {
   }
 }
 
+// Scatter of one tile: the tile is read with striped loads into LDS, each thread takes its run of
+// E consecutive elements, the tile is reordered in LDS by digit (stable: digit, then position),
+// and the reordered tile goes out with striped stores, so each digit's run lands contiguously at
+// its list offset.
+constexpr int MAX_TILE = 2048;
 __global__ __launch_bounds__(RK_THREADS) void radix_scatter_kernel(RadixArgs a) {
   __shared__ uint32_t cnt[DIGITS * RK_THREADS];
   __shared__ uint32_t wsum[RK_THREADS / 64];
+  __shared__ uint32_t skey[MAX_TILE];
+  __shared__ int32_t sval[MAX_TILE];
+  __shared__ uint32_t dst0[DIGITS];
   const int t = threadIdx.x;
   const TileRef x = tile_ref(a, blockIdx.x);
   const int E = run_len(a.tile);
   const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
-  const int64_t e0 = x.elem + (int64_t)t * E;
+  const int64_t lbase = x.elem - (int64_t)x.t * a.tile;  // first element of the list
+  for (int i = t; i < a.tile; i += RK_THREADS) {
+    skey[i] = a.keys_in[x.elem + i];
+    sval[i] = a.vals_in ? a.vals_in[x.elem + i] : (int32_t)(x.t * a.tile + i);
+  }
+  if (t < DIGITS) dst0[t] = a.hist[x.hbase + (int64_t)t * x.nt + x.t];
+  __syncthreads();
   uint32_t kv[8];
   int32_t vv[8];
   uint64_t c = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < n) {
-      kv[e] = a.keys_in[e0 + e];
-      vv[e] = a.vals_in ? a.vals_in[e0 + e] : (int32_t)(x.t * a.tile + t * E + e);
+      kv[e] = skey[t * E + e];
+      vv[e] = sval[t * E + e];
       c += 1ull << (4 * ((kv[e] >> a.shift) & (DIGITS - 1)));
     }
   }
 #pragma unroll
   for (int d = 0; d < DIGITS; ++d) cnt[d * RK_THREADS + t] = (uint32_t)(c >> (4 * d)) & 15u;
-  __syncthreads();
+  __syncthreads();  // also: every run is in registers before the tile is reordered in place
   scan_counts(cnt, wsum);
-  const int64_t lbase = x.elem - (int64_t)x.t * a.tile;  // first element of the list
   uint64_t seen = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e >= n) break;
     const uint32_t d = (kv[e] >> a.shift) & (DIGITS - 1);
-    const uint32_t rank = cnt[d * RK_THREADS + t] - cnt[d * RK_THREADS] + ((uint32_t)(seen >> (4 * d)) & 15u);
+    const uint32_t pos = cnt[d * RK_THREADS + t] + ((uint32_t)(seen >> (4 * d)) & 15u);
     seen += 1ull << (4 * d);
-    const int64_t dst = lbase + a.hist[x.hbase + (int64_t)d * x.nt + x.t] + rank;
-    if (a.write_keys) a.keys_out[dst] = kv[e];
-    a.vals_out[dst] = vv[e];
+    skey[pos] = kv[e];
+    sval[pos] = vv[e];
+  }
+  __syncthreads();
+  for (int i = t; i < a.tile; i += RK_THREADS) {
+    const uint32_t key = skey[i];
+    const uint32_t d = (key >> a.shift) & (DIGITS - 1);
+    const int64_t dst = lbase + dst0[d] + (i - cnt[d * RK_THREADS]);
+    if (a.write_keys) a.keys_out[dst] = key;
+    a.vals_out[dst] = sval[i];
   }
 }
 
@@ -320,7 +362,8 @@ __global__ __launch_bounds__(RK_THREADS) void radix_scatter_kernel(RadixArgs a) 
 size_t prefix_rank_workspace_bytes(const Geometry& g) {
   const PrefixGeom p = prefix_geom(g);
   const size_t n = (size_t)g.Hkv * p.L;
-  return align256(sizeof(double) * g.Hkv * (size_t)p.nseg * g.d) + 4 * align256(4 * n) +
+  return align256(sizeof(double) * g.Hkv * (size_t)p.nseg * g.d) +
+         align256(sizeof(double) * g.Hkv * (size_t)p.nseg * rep_chunks(g) * g.d) + 4 * align256(4 * n) +
          align256(sizeof(uint32_t) * DIGITS * (size_t)g.Hkv * p.tiles_per_head);
 }
 
@@ -331,10 +374,15 @@ hipError_t launch_prefix_rank(const Geometry& g, const uint16_t* q, const uint16
   const PrefixGeom p = prefix_geom(g);
   if (p.nseg < 2) return hipSuccess;  // no segment has a prefix
   const RankWs w = carve(g, p, ws);
-  if (g.d == 128)
-    seg_rep_kernel<128><<<dim3(p.nseg, g.Hkv), RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.S, g.G, p.nseg, w.rep);
-  else
-    seg_rep_kernel<64><<<dim3(p.nseg, g.Hkv), RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.S, g.G, p.nseg, w.rep);
+  const int nch = rep_chunks(g);
+  const dim3 rgrid(nch, p.nseg, g.Hkv);
+  if (g.d == 128) {
+    seg_rep_partial_kernel<128><<<rgrid, RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.S, g.G, p.nseg, nch, w.rpart);
+    seg_rep_combine_kernel<128><<<dim3(p.nseg, g.Hkv), 128, 0, st>>>(w.rpart, g.N, g.S, g.G, p.nseg, nch, w.rep);
+  } else {
+    seg_rep_partial_kernel<64><<<rgrid, RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.S, g.G, p.nseg, nch, w.rpart);
+    seg_rep_combine_kernel<64><<<dim3(p.nseg, g.Hkv), 64, 0, st>>>(w.rpart, g.N, g.S, g.G, p.nseg, nch, w.rep);
+  }
   const int nh = (p.nseg - 1) * g.S;
   const dim3 sgrid((nh + RK_THREADS - 1) / RK_THREADS, g.Hkv);
   if (g.d == 128)
