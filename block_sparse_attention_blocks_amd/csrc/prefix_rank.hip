@@ -4,7 +4,8 @@
 // of g), descending, ties by position.  Three steps:
 //   seg_rep_*            fp64 representative queries (exact bf16 widening, fp64 sums)
 //   prefix_score_kernel  fp64 scores r . k_j, rounded to fp32 and written as order-preserving keys
-//   radix_*              stable least-significant-digit radix sort of every (g, sigma) list
+//   radix_*              stable least-significant-digit radix sort of every (g, sigma) list,
+//                        8-bit digits, four passes
 // Output layout: kv_rank[g][S*sigma*(sigma-1)/2 + r] = key of rank r for segment sigma.
 #include "common.h"
 
@@ -14,9 +15,11 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int RK_THREADS = 256;
-constexpr int RADIX_BITS = 4;
-constexpr int DIGITS = 1 << RADIX_BITS;
+constexpr int RADIX_BITS = 8;
+constexpr int DIGITS = 1 << RADIX_BITS;  // one bin per thread of a workgroup
 constexpr int RADIX_PASSES = 32 / RADIX_BITS;
+constexpr int NIB = 16;                  // a tile is reordered in LDS 4 bits at a time
+static_assert(DIGITS == RK_THREADS, "one histogram bin per thread");
 
 // List and tile geometry of the ranking.  The radix tile is the largest power of two <= 2048 that
 // divides S, so every list (sigma*S keys) is a whole number of tiles.
@@ -217,8 +220,16 @@ __device__ __forceinline__ TileRef tile_ref(const RadixArgs& a, int64_t f) {
   return x;
 }
 
-// Block-wide exclusive scan of cnt[DIGITS * 256] in place (digit-major); thread t owns entries
-// 16t .. 16t+15.  Returns nothing; cnt then holds each (digit, thread) start within the tile.
+// LDS layouts padded by one word every 16 counts / every 8 elements, so that a thread walking its
+// own 16 counts (or its run of up to 8 elements) and a wave walking consecutive entries both hit
+// distinct banks.
+__device__ __forceinline__ int cpad(int p) { return p + (p >> 4); }
+__device__ __forceinline__ int epad(int i) { return i + (i >> 3); }
+constexpr int CNT_WORDS = NIB * RK_THREADS + NIB * RK_THREADS / 16;
+
+// Block-wide exclusive scan, in place, of the NIB x 256 counts in nibble-major order (entry
+// p = nibble * 256 + thread at cpad(p)); thread t owns entries 16t .. 16t+15.  cnt then holds each
+// (nibble, thread) start within the tile.
 __device__ __forceinline__ void scan_counts(uint32_t* cnt, uint32_t* wsum) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t v[16];
@@ -226,7 +237,7 @@ __device__ __forceinline__ void scan_counts(uint32_t* cnt, uint32_t* wsum) {
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     v[x] = run;
-    run += cnt[t * 16 + x];
+    run += cnt[cpad(t * 16 + x)];
   }
   uint32_t inc = run;  // inclusive scan of the per-thread totals across the wave
 #pragma unroll
@@ -239,121 +250,130 @@ __device__ __forceinline__ void scan_counts(uint32_t* cnt, uint32_t* wsum) {
   uint32_t base = inc - run;
   for (int w = 0; w < wave; ++w) base += wsum[w];
 #pragma unroll
-  for (int x = 0; x < 16; ++x) cnt[t * 16 + x] = base + v[x];
+  for (int x = 0; x < 16; ++x) cnt[cpad(t * 16 + x)] = base + v[x];
   __syncthreads();
 }
 
-// Per-thread digit counts of its run, 4 bits per digit (a run holds at most 8 elements).
 __device__ __forceinline__ int run_len(int tile) { return tile >= RK_THREADS ? tile / RK_THREADS : 1; }
 
+// Digit histogram of one tile (LDS counters, one per thread), into the list's (digit, tile) table.
 __global__ __launch_bounds__(RK_THREADS) void radix_hist_kernel(RadixArgs a) {
-  __shared__ uint32_t cnt[DIGITS * RK_THREADS];
-  __shared__ uint32_t wsum[RK_THREADS / 64];
+  __shared__ uint32_t bins[DIGITS];
   const int t = threadIdx.x;
   const TileRef x = tile_ref(a, blockIdx.x);
-  const int E = run_len(a.tile);
-  const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
-  uint64_t c = 0;  // only the digit totals are needed here, so the reads are striped (coalesced)
-  for (int e = 0; e < n; ++e) {
-    const uint32_t d = (a.keys_in[x.elem + t + (int64_t)RK_THREADS * e] >> a.shift) & (DIGITS - 1);
-    c += 1ull << (4 * d);
-  }
-#pragma unroll
-  for (int d = 0; d < DIGITS; ++d) cnt[d * RK_THREADS + t] = (uint32_t)(c >> (4 * d)) & 15u;
+  bins[t] = 0;
   __syncthreads();
-  scan_counts(cnt, wsum);
-  if (t < DIGITS) {
-    const uint32_t start = cnt[t * RK_THREADS];
-    const uint32_t end = t + 1 < DIGITS ? cnt[(t + 1) * RK_THREADS] : (uint32_t)a.tile;
-    a.hist[x.hbase + (int64_t)t * x.nt + x.t] = end - start;
+  for (int i = t; i < a.tile; i += RK_THREADS) atomicAdd(&bins[(a.keys_in[x.elem + i] >> a.shift) & (DIGITS - 1)], 1u);
+  __syncthreads();
+  a.hist[x.hbase + (int64_t)t * x.nt + x.t] = bins[t];
+}
+
+// Exclusive scan over the workgroup of one value per thread (wsum: one word per wave).
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
   }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  uint32_t base = inc - v;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  __syncthreads();
+  return base;
 }
 
 // Exclusive scan of one list's histogram in (digit, tile) order: the first output position of
-// every (digit, tile) in the list.
-__global__ __launch_bounds__(RK_THREADS) void radix_scan_kernel(RadixArgs a) {
-  __shared__ uint32_t wsum[RK_THREADS / 64];
-  __shared__ uint32_t carry;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+// every (digit, tile) in the list.  Each thread scans one contiguous slice of the table.
+constexpr int SCAN_THREADS = 1024;
+__global__ __launch_bounds__(SCAN_THREADS) void radix_scan_kernel(RadixArgs a) {
+  __shared__ uint32_t wsum[SCAN_THREADS / 64];
+  const int t = threadIdx.x;
   const int g = blockIdx.x / (a.nseg - 1), sigma = blockIdx.x % (a.nseg - 1) + 1;
   const int64_t first = (int64_t)a.tps * sigma * (sigma - 1) / 2;
   uint32_t* h = a.hist + (int64_t)DIGITS * ((int64_t)g * a.tiles_per_head + first);
   const int n = DIGITS * a.tps * sigma;
-  if (t == 0) carry = 0;
-  __syncthreads();
-  for (int b = 0; b < n; b += RK_THREADS) {
-    const uint32_t v = b + t < n ? h[b + t] : 0u;
-    uint32_t inc = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
-    }
-    if (lane == 63) wsum[wave] = inc;
-    __syncthreads();
-    uint32_t base = carry;
-    for (int w = 0; w < wave; ++w) base += wsum[w];
-    if (b + t < n) h[b + t] = base + inc - v;
-    __syncthreads();
-    if (t == RK_THREADS - 1) carry = base + inc;
-    __syncthreads();
+  const int m = (n + SCAN_THREADS - 1) / SCAN_THREADS;
+  const int b = min(t * m, n), e = min(b + m, n);
+  uint32_t sum = 0;
+  for (int i = b; i < e; ++i) sum += h[i];
+  uint32_t run = block_exclusive_scan(sum, wsum);
+  for (int i = b; i < e; ++i) {
+    const uint32_t v = h[i];
+    h[i] = run;
+    run += v;
   }
 }
 
-// Scatter of one tile: the tile is read with striped loads into LDS, each thread takes its run of
-// E consecutive elements, the tile is reordered in LDS by digit (stable: digit, then position),
-// and the reordered tile goes out with striped stores, so each digit's run lands contiguously at
-// its list offset.
-constexpr int MAX_TILE = 2048;
-__global__ __launch_bounds__(RK_THREADS) void radix_scatter_kernel(RadixArgs a) {
-  __shared__ uint32_t cnt[DIGITS * RK_THREADS];
-  __shared__ uint32_t wsum[RK_THREADS / 64];
-  __shared__ uint32_t skey[MAX_TILE];
-  __shared__ int32_t sval[MAX_TILE];
-  __shared__ uint32_t dst0[DIGITS];
+// Stable reorder of the tile in LDS by the 4 key bits at `shift`: each thread ranks its run of E
+// consecutive elements, the 16 x 256 counts are scanned block-wide.
+__device__ __forceinline__ void lds_nibble_sort(uint32_t* skey, int32_t* sval, uint32_t* cnt, uint32_t* wsum, int E,
+                                                int n, int shift) {
   const int t = threadIdx.x;
-  const TileRef x = tile_ref(a, blockIdx.x);
-  const int E = run_len(a.tile);
-  const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
-  const int64_t lbase = x.elem - (int64_t)x.t * a.tile;  // first element of the list
-  for (int i = t; i < a.tile; i += RK_THREADS) {
-    skey[i] = a.keys_in[x.elem + i];
-    sval[i] = a.vals_in ? a.vals_in[x.elem + i] : (int32_t)(x.t * a.tile + i);
-  }
-  if (t < DIGITS) dst0[t] = a.hist[x.hbase + (int64_t)t * x.nt + x.t];
-  __syncthreads();
   uint32_t kv[8];
   int32_t vv[8];
   uint64_t c = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < n) {
-      kv[e] = skey[t * E + e];
-      vv[e] = sval[t * E + e];
-      c += 1ull << (4 * ((kv[e] >> a.shift) & (DIGITS - 1)));
+      kv[e] = skey[epad(t * E + e)];
+      vv[e] = sval[epad(t * E + e)];
+      c += 1ull << (4 * ((kv[e] >> shift) & (NIB - 1)));
     }
   }
 #pragma unroll
-  for (int d = 0; d < DIGITS; ++d) cnt[d * RK_THREADS + t] = (uint32_t)(c >> (4 * d)) & 15u;
+  for (int d = 0; d < NIB; ++d) cnt[cpad(d * RK_THREADS + t)] = (uint32_t)(c >> (4 * d)) & 15u;
   __syncthreads();  // also: every run is in registers before the tile is reordered in place
   scan_counts(cnt, wsum);
   uint64_t seen = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e >= n) break;
-    const uint32_t d = (kv[e] >> a.shift) & (DIGITS - 1);
-    const uint32_t pos = cnt[d * RK_THREADS + t] + ((uint32_t)(seen >> (4 * d)) & 15u);
+    const uint32_t d = (kv[e] >> shift) & (NIB - 1);
+    const int pos = (int)(cnt[cpad(d * RK_THREADS + t)] + ((uint32_t)(seen >> (4 * d)) & 15u));
     seen += 1ull << (4 * d);
-    skey[pos] = kv[e];
-    sval[pos] = vv[e];
+    skey[epad(pos)] = kv[e];
+    sval[epad(pos)] = vv[e];
   }
   __syncthreads();
+}
+
+// Scatter of one tile: the tile is read with striped loads into LDS, sorted there by its 8-bit
+// digit (two stable 4-bit reorders), and stored with striped stores, so each digit's run lands
+// contiguously at its offset in the list.
+constexpr int MAX_TILE = 2048;
+__global__ __launch_bounds__(RK_THREADS) void radix_scatter_kernel(RadixArgs a) {
+  __shared__ uint32_t cnt[CNT_WORDS];
+  __shared__ uint32_t wsum[RK_THREADS / 64];
+  __shared__ uint32_t skey[MAX_TILE + MAX_TILE / 8];
+  __shared__ int32_t sval[MAX_TILE + MAX_TILE / 8];
+  __shared__ uint32_t bins[DIGITS];   // tile counts, then the tile-local start of each digit
+  __shared__ uint32_t gofs[DIGITS];   // list offset of each digit's run from this tile
+  const int t = threadIdx.x;
+  const TileRef x = tile_ref(a, blockIdx.x);
+  const int E = run_len(a.tile);
+  const int n = (a.tile >= RK_THREADS || t < a.tile) ? E : 0;
+  const int64_t lbase = x.elem - (int64_t)x.t * a.tile;  // first element of the list
+  // this tile's count of digit t: the gap to the next (digit, tile) entry of the scanned table
+  const int64_t hi = x.hbase + (int64_t)t * x.nt + x.t;
+  const uint32_t o = a.hist[hi];
+  const uint32_t next = (t == DIGITS - 1 && x.t == x.nt - 1) ? (uint32_t)(x.nt * a.tile) : a.hist[hi + 1];
+  gofs[t] = o;
   for (int i = t; i < a.tile; i += RK_THREADS) {
-    const uint32_t key = skey[i];
+    skey[epad(i)] = a.keys_in[x.elem + i];
+    sval[epad(i)] = a.vals_in ? a.vals_in[x.elem + i] : (int32_t)(x.t * a.tile + i);
+  }
+  bins[t] = block_exclusive_scan(next - o, wsum);  // its barriers also publish skey, sval
+  lds_nibble_sort(skey, sval, cnt, wsum, E, n, a.shift);
+  lds_nibble_sort(skey, sval, cnt, wsum, E, n, a.shift + 4);
+  for (int i = t; i < a.tile; i += RK_THREADS) {
+    const uint32_t key = skey[epad(i)];
     const uint32_t d = (key >> a.shift) & (DIGITS - 1);
-    const int64_t dst = lbase + dst0[d] + (i - cnt[d * RK_THREADS]);
+    const int64_t dst = lbase + gofs[d] + (i - bins[d]);
     if (a.write_keys) a.keys_out[dst] = key;
-    a.vals_out[dst] = sval[i];
+    a.vals_out[dst] = sval[epad(i)];
   }
 }
 
@@ -408,7 +428,7 @@ hipError_t launch_prefix_rank(const Geometry& g, const uint16_t* q, const uint16
     a.shift = pass * RADIX_BITS;
     a.write_keys = pass != RADIX_PASSES - 1;
     radix_hist_kernel<<<(unsigned)tiles, RK_THREADS, 0, st>>>(a);
-    radix_scan_kernel<<<lists, RK_THREADS, 0, st>>>(a);
+    radix_scan_kernel<<<lists, SCAN_THREADS, 0, st>>>(a);
     radix_scatter_kernel<<<(unsigned)tiles, RK_THREADS, 0, st>>>(a);
   }
   return hipGetLastError();
