@@ -24,6 +24,8 @@ from .pbsa_oracle import (  # noqa: F401
     pool_blocks,
     pool_permuted_blocks,
     pooled_block_logits,
+    query_guide_scores,
+    query_permutation,
     prefix_kv_ranking,
     prefix_offset,
     prefix_ranking_length,

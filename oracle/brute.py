@@ -241,13 +241,36 @@ def prefix_ranking(q, k, S: int) -> Dict[Tuple[int, int], List[int]]:
     return res
 
 
+def query_order(q, k, S: int) -> List[List[int]]:
+    """qperm[g] from the definition: guide u = fsum mean of KV head g's keys; score of position i =
+    fsum mean over the G heads of q_{h,i} . u; inside each segment positions picked one by one as
+    the remaining one of largest score (smallest position among equals)."""
+    Hq, N, d = len(q), len(q[0]), len(q[0][0])
+    Hkv = len(k)
+    G = Hq // Hkv
+    res = []
+    for g in range(Hkv):
+        u = [math.fsum(float(k[g][j][t]) for j in range(N)) / N for t in range(d)]
+        z = [math.fsum(_dot(q[h][i], u) for h in range(g * G, (g + 1) * G)) / G for i in range(N)]
+        order = []
+        for a in range(0, N, S):
+            rest = list(range(a, min(a + S, N)))
+            while rest:
+                best = max(rest, key=lambda i: (z[i], -i))
+                order.append(best)
+                rest.remove(best)
+        res.append(order)
+    return res
+
+
 def s2o_prefix_processed(q, k, ranking: Dict[Tuple[int, int], List[int]], B: int, S: int, gain_tau: float,
-                         scale: float) -> Dict[Tuple[int, int], List[int]]:
+                         scale: float, qorder: Optional[List[List[int]]] = None) -> Dict[Tuple[int, int], List[int]]:
     """Entries the two-pass marginal-gain stop processes per (h, I), from its definition: the
     blocks of I's own segment in natural order (J0 .. I, J0 its first block), then history blocks
     J = 0, 1, ... holding ranked keys J*B .. J*B+B-1 of the segment's order; stop after the first
     history block whose exact share (fsum of exp(s - M_i), M_i the max over every listed key <= i)
-    of every query's denominator over the processed keys is below gain_tau."""
+    of every query's denominator over the processed keys is below gain_tau.  With qorder, query
+    block I holds positions qorder[g][I*B ...] and pass 1 spans every block of the own segment."""
     Hq, N = len(q), len(q[0])
     Hkv = len(k)
     G = Hq // Hkv
@@ -264,8 +287,13 @@ def s2o_prefix_processed(q, k, ranking: Dict[Tuple[int, int], List[int]], B: int
                 if J >= J0:
                     return list(range(J * B, min((J + 1) * B, N)))
                 return rank[J * B:(J + 1) * B]
-            order = list(range(J0, I + 1)) + list(range(J0))
-            qrows = list(range(I * B, min((I + 1) * B, N)))
+            if qorder is None:
+                order = list(range(J0, I + 1)) + list(range(J0))
+                qrows = list(range(I * B, min((I + 1) * B, N)))
+            else:
+                last = -(-min((sigma + 1) * S, N) // B) - 1
+                order = list(range(J0, last + 1)) + list(range(J0))
+                qrows = qorder[g][I * B:min((I + 1) * B, N)]
             logit = {(i, j): scale * _dot(q[h][i], k[g][j]) for i in qrows for J in order for j in rows_of(J) if j <= i}
             ref = {i: max(v for (ii, _), v in logit.items() if ii == i) for i in qrows}
             done = []
@@ -288,16 +316,19 @@ def s2o_prefix_processed(q, k, ranking: Dict[Tuple[int, int], List[int]], B: int
     return out
 
 
-def attention_over_keys(q, k, v, keysets: Dict[Tuple[int, int], List[int]], B: int, scale: float):
+def attention_over_keys(q, k, v, keysets: Dict[Tuple[int, int], List[int]], B: int, scale: float,
+                        qorder: Optional[List[List[int]]] = None):
     """out[h][i], lse[h][i] for the rows of the given (h, I): softmax over keysets[(h, I)] restricted
-    to j <= i, each sum an fsum (rows not listed stay None)."""
+    to j <= i, each sum an fsum (rows not listed stay None).  Row (h, I) holds query positions
+    I*B ... or, with qorder, qorder[g][I*B ...]."""
     Hq, N, d = len(q), len(q[0]), len(q[0][0])
     G = Hq // len(k)
     out = [[None] * N for _ in range(Hq)]
     lse = [[None] * N for _ in range(Hq)]
     for (h, I), keys in keysets.items():
         g = h // G
-        for i in range(I * B, min((I + 1) * B, N)):
+        qrows = range(I * B, min((I + 1) * B, N)) if qorder is None else qorder[g][I * B:min((I + 1) * B, N)]
+        for i in qrows:
             ks = [j for j in keys if j <= i]
             s = [scale * _dot(q[h][i], k[g][j]) for j in ks]
             m = max(s)

@@ -27,7 +27,11 @@ design notes of the repository):
     included) is below the threshold; that block stays processed;
   * S2O's historical ranking uses one representative query per (KV head, segment): the mean of the
     segment's query rows over the G query heads; it orders every key of the causal prefix (the
-    earlier segments) by its dot product with that query, descending, ties by position.
+    earlier segments) by its dot product with that query, descending, ties by position;
+  * S2O's query permutation scores each query against one guide vector per KV head, the mean key,
+    averaged over the G query heads, and sorts each segment's positions by it (descending, ties by
+    position); a permuted query block then needs the whole own segment in pass 1 under the
+    per-token causal mask, and its output rows go back to their natural positions.
 """
 from __future__ import annotations
 
@@ -272,13 +276,14 @@ def ranked_blocks(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], bloc
     return count, idx, n_intra
 
 
-def _s2o_row_gains(q, k, perm_g, h, g, I, lst, B, S, N, c, rows_of=None):
+def _s2o_row_gains(q, k, perm_g, h, g, I, lst, B, S, N, c, rows_of=None, qi=None):
     """For row (h, I) and its list in order: (dl, ell), each [len(lst)][rows of block I], where dl[p]
     is what block lst[p] adds to each query's softmax denominator and ell[p] the denominator over
     lst[0..p].  One reference per query (the max over every listed key) scales both; it cancels in
     the ratio dl / ell.  rows_of(J) gives a list entry's key positions (default: key_rows_of_block
-    through perm_g)."""
-    qi = block_range(I, B, N)
+    through perm_g); qi: the query positions of the row (default: natural block I)."""
+    if qi is None:
+        qi = block_range(I, B, N)
     if rows_of is None:
         rows_of = lambda J: key_rows_of_block(J, I, perm_g, B, S, N)  # noqa: E731
     blk = []
@@ -424,6 +429,42 @@ def prefix_kv_ranking(q: np.ndarray, k: np.ndarray, segment_size: int):
     return pi, score
 
 
+def query_guide_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """score[g][i] = (1/G) * sum over the G query heads of g of q_{h,i} . u_g, with the guide vector
+    u_g the mean key of KV head g over the sequence.
+
+    S2O, Methodology §1, Query Permutation: queries are reordered inside a segment by a coarse
+    importance score against one shared guide vector.  Reading: the guide is the mean key, so the
+    score is a query's mean logit over the keys (up to the scale), large for the queries that form
+    bright horizontal stripes."""
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    score = np.zeros((Hkv, N))
+    for g in range(Hkv):
+        u = k[g].mean(axis=0)
+        score[g] = np.mean([q[h] @ u for h in range(g * G, (g + 1) * G)], axis=0)
+    return score
+
+
+def query_permutation(q: np.ndarray, k: np.ndarray, segment_size: int) -> np.ndarray:
+    """qperm[g][N]: inside each segment, the query positions by guide score descending, ties by
+    position (one order per KV head, shared by its G query heads).  Query block I of the permuted
+    order holds positions qperm[g][I*B ...]; segments keep their place (PBS-Attn §2: permutations
+    stay inside segments)."""
+    Hkv = k.shape[0]
+    N = q.shape[1]
+    S = segment_size
+    score = query_guide_scores(q, k)
+    qperm = np.zeros((Hkv, N), dtype=np.int64)
+    for g in range(Hkv):
+        for a in range(0, N, S):
+            b = min(a + S, N)
+            pos = np.arange(a, b)
+            qperm[g, a:b] = pos[np.lexsort((pos, -score[g, a:b]))]
+    return qperm
+
+
 def _prefix_rows_of(pi, g, I, B, S, N):
     """Key positions of list entry J for query block I: natural block J in I's own segment
     (J >= J0, the first block of the segment), else block J of the segment's prefix order."""
@@ -438,9 +479,23 @@ def _prefix_rows_of(pi, g, I, B, S, N):
     return rows_of, J0
 
 
+def _two_pass_row(qperm, g, I, B, S, N):
+    """(query positions, list) of row I: natural block I and own blocks J0 .. I without a query
+    permutation; with one, the positions qperm[g][I*B ...] and every block of the own segment (a
+    permuted block may hold any of the segment's positions; the causal mask is per token).  The
+    history blocks 0 .. J0-1 follow in both cases."""
+    sigma = segment_of_block(I, B, S)
+    J0 = sigma * S // B
+    if qperm is None:
+        return block_range(I, B, N), list(range(J0, I + 1)) + list(range(J0))
+    Jend = min(-(-min((sigma + 1) * S, N) // B), num_blocks(N, B)) - 1
+    qi = np.asarray(qperm[g, I * B:min((I + 1) * B, N)], dtype=np.int64)
+    return qi, list(range(J0, Jend + 1)) + list(range(J0))
+
+
 def s2o_prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.ndarray, block_size: int,
                          segment_size: int, gain_tau: float, scale: Optional[float] = None,
-                         rows: Optional[Iterable[Tuple[int, int]]] = None):
+                         rows: Optional[Iterable[Tuple[int, int]]] = None, qperm: Optional[np.ndarray] = None):
     """S2O's two passes with the marginal-gain stop, history read through the prefix ranking.
 
     S2O, Kernel Implementation: pass 1 runs the dense causal window of the query block's own
@@ -450,6 +505,11 @@ def s2o_prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.nda
     each history block, the row stops as in s2o_attention (every query's share of that block in
     its denominator below gain_tau; that block stays processed).  The output is exact softmax
     attention over the processed keys.
+
+    qperm (query_permutation): query block I holds positions qperm[g][I*B ...]; pass 1 then spans
+    the whole own segment under the per-token causal mask, and every output row lands at its
+    natural position (PBS-Attn §1: permuting queries permutes the output; the inverse permutation
+    restores it).
 
     Returns (out [Hq][N][d], lse [Hq][N], processed {(h, I): [J in processing order]}), where
     J >= J0 names a natural block of the own segment and J < J0 a prefix-order block.
@@ -466,8 +526,8 @@ def s2o_prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.nda
     for h, I in todo:
         g = h // G
         rows_of, J0 = _prefix_rows_of(pi, g, I, B, S, N)
-        lst = list(range(J0, I + 1)) + list(range(J0))
-        dl, ell = _s2o_row_gains(q, k, None, h, g, I, lst, B, S, N, c, rows_of=rows_of)
+        qi, lst = _two_pass_row(qperm, g, I, B, S, N)
+        dl, ell = _s2o_row_gains(q, k, None, h, g, I, lst, B, S, N, c, rows_of=rows_of, qi=qi)
         done: List[int] = []
         for p, J in enumerate(lst):
             done.append(J)
@@ -475,13 +535,13 @@ def s2o_prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.nda
                 break
         processed[(h, I)] = done
         keys = np.concatenate([rows_of(J) for J in done])
-        _attend(q, k, v, h, g, block_range(I, B, N), keys, c, out, lse)
+        _attend(q, k, v, h, g, qi, keys, c, out, lse)
     return out, lse, processed
 
 
 def two_pass_attention_on(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.ndarray,
                           entries: Dict[Tuple[int, int], Sequence[int]], block_size: int, segment_size: int,
-                          scale: Optional[float] = None):
+                          scale: Optional[float] = None, qperm: Optional[np.ndarray] = None):
     """Softmax attention of each listed row (h, I) over the keys of the given two-pass entries
     (J >= J0: natural block J; J < J0: block J of the segment's prefix order), causal per query;
     the output of s2o_prefix_attention for a given processed set.  Returns (out, lse), NaN on rows
@@ -494,16 +554,17 @@ def two_pass_attention_on(q: np.ndarray, k: np.ndarray, v: np.ndarray, pi: np.nd
     lse = np.full((Hq, N), np.nan)
     for (h, I), lst in entries.items():
         rows_of, _ = _prefix_rows_of(pi, h // G, I, B, S, N)
+        qi, _ = _two_pass_row(qperm, h // G, I, B, S, N)
         keys = np.concatenate([rows_of(J) for J in lst]) if len(lst) else np.zeros(0, dtype=np.int64)
-        _attend(q, k, v, h, h // G, block_range(I, B, N), keys, c, out, lse)
+        _attend(q, k, v, h, h // G, qi, keys, c, out, lse)
     return out, lse
 
 
 def s2o_prefix_gain_ratios(q: np.ndarray, k: np.ndarray, pi: np.ndarray, block_size: int, segment_size: int,
-                           scale: Optional[float] = None,
-                           rows: Optional[Iterable[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], np.ndarray]:
+                           scale: Optional[float] = None, rows: Optional[Iterable[Tuple[int, int]]] = None,
+                           qperm: Optional[np.ndarray] = None) -> Dict[Tuple[int, int], np.ndarray]:
     """s2o_gain_ratios for the lists of s2o_prefix_attention: max_i dl_i / l_i at every position of
-    the whole list (own segment ascending, then prefix blocks 0 .. J0-1), NaN on the own segment."""
+    the whole list (pass 1, then prefix blocks 0 .. J0-1), NaN on the own segment."""
     Hq, N, d = q.shape
     G = Hq // k.shape[0]
     B, S = block_size, segment_size
@@ -514,10 +575,10 @@ def s2o_prefix_gain_ratios(q: np.ndarray, k: np.ndarray, pi: np.ndarray, block_s
     for h, I in todo:
         g = h // G
         rows_of, J0 = _prefix_rows_of(pi, g, I, B, S, N)
-        lst = list(range(J0, I + 1)) + list(range(J0))
-        dl, ell = _s2o_row_gains(q, k, None, h, g, I, lst, B, S, N, c, rows_of=rows_of)
+        qi, lst = _two_pass_row(qperm, g, I, B, S, N)
+        dl, ell = _s2o_row_gains(q, k, None, h, g, I, lst, B, S, N, c, rows_of=rows_of, qi=qi)
         r = (dl / ell).max(axis=1)
-        r[:I + 1 - J0] = np.nan
+        r[[J >= J0 for J in lst]] = np.nan
         res[(h, I)] = r
     return res
 

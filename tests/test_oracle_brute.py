@@ -153,3 +153,32 @@ def test_prefix_ranking_and_two_pass_stop_match_brute_force(c, gain_tau):
     out_b, lse_b = brute.attention_over_keys(q, k, v, keysets, B, scale)
     np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)
+
+
+@settings(max_examples=20, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case(), st.sampled_from([0.0, 1e-2, 0.2, 1.0]))
+def test_query_permutation_and_its_two_pass_stop_match_brute_force(c, gain_tau):
+    N, Hq, Hkv, d, B, S = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"], c["S"]
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+    qperm = oracle.query_permutation(q, k, S)
+    qorder_b = brute.query_order(q, k, S)
+    z = oracle.query_guide_scores(q, k)
+    for g in range(Hkv):
+        _same_ranking(qperm[g].tolist(), qorder_b[g], lambda i: float(z[g, i]))
+    qorder = [qperm[g].tolist() for g in range(Hkv)]  # both sides on the oracle's order from here
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    ranking = {(g, sigma): pi[g, oracle.prefix_offset(sigma, S):oracle.prefix_offset(sigma, S) + sigma * S].tolist()
+               for g in range(Hkv) for sigma in range(1, oracle.num_segments(N, S))}
+    out, lse, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, gain_tau, qperm=qperm)
+    done_b = brute.s2o_prefix_processed(q, k, ranking, B, S, gain_tau, scale, qorder=qorder)
+    assert done == done_b
+    keysets = {}
+    for (h, I), lst in done_b.items():
+        sigma = (I * B) // S
+        J0 = sigma * S // B
+        rank = ranking.get((h // (Hq // Hkv), sigma), [])
+        keysets[(h, I)] = [j for J in lst for j in (range(J * B, min((J + 1) * B, N)) if J >= J0 else rank[J * B:(J + 1) * B])]
+    out_b, lse_b = brute.attention_over_keys(q, k, v, keysets, B, scale, qorder=qorder)
+    np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)

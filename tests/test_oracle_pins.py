@@ -465,3 +465,66 @@ def test_two_pass_attention_on_a_given_processed_set():
     out3, lse3 = oracle.two_pass_attention_on(q, k, v, pi, full, B, S)
     ref, ref_lse = oracle.dense_attention(q, k, v)
     assert np.abs(out3 - ref).max() <= 1e-12 and np.abs(lse3 - ref_lse).max() <= 1e-12
+
+
+# ----------------------------------------------------------------------------- S2O query permutation
+
+def test_query_permutation_orders_each_segment_by_the_guide_score():
+    """Keys all equal u (guide = u); query rows a_i w in every head: score a_i (w . u), so each
+    segment lists its positions by a_i descending (ascending when w . u < 0), ties by position."""
+    N, Hq, Hkv, d, S = 40, 4, 2, 5, 16
+    rng = np.random.default_rng(8)
+    q = np.zeros((Hq, N, d))
+    k = np.zeros((Hkv, N, d))
+    a = rng.permutation(N).astype(np.float64)
+    a[9] = a[4]                                   # a tie inside segment 0
+    for g in range(Hkv):
+        u = rng.standard_normal(d)
+        w = u if g == 0 else -u                   # group 1 scores are -a_i |u|^2
+        k[g] = u
+        for h in range(2 * g, 2 * g + 2):
+            q[h] = a[:, None] * w[None, :]
+    qperm = oracle.query_permutation(q, k, S)
+    for g in range(Hkv):
+        sgn = 1.0 if g == 0 else -1.0
+        for s0 in range(0, N, S):
+            pos = list(range(s0, min(s0 + S, N)))
+            assert qperm[g, s0:s0 + len(pos)].tolist() == sorted(pos, key=lambda i: (-sgn * a[i], i))
+    assert qperm[0, :16].tolist().index(4) < qperm[0, :16].tolist().index(9)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_query_permuted_two_pass_zero_threshold_is_dense_causal(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=36)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    qperm = oracle.query_permutation(q, k, S)
+    assert not np.array_equal(qperm, np.broadcast_to(np.arange(N), qperm.shape))
+    out, lse, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, 0.0, qperm=qperm)
+    ref, ref_lse = oracle.dense_attention(q, k, v)
+    assert np.abs(out - ref).max() <= 1e-12 and np.abs(lse - ref_lse).max() <= 1e-12
+
+
+def test_identity_query_permutation_changes_nothing_but_the_listed_own_blocks():
+    N, Hq, Hkv, d, B, S = 96, 4, 2, 8, 8, 32
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=37)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    ident = np.broadcast_to(np.arange(N), (Hkv, N)).copy()
+    for tau in (0.0, 0.05, 1.0):
+        out, lse, done = oracle.s2o_prefix_attention(q, k, v, pi, B, S, tau)
+        out2, lse2, done2 = oracle.s2o_prefix_attention(q, k, v, pi, B, S, tau, qperm=ident)
+        assert np.abs(out - out2).max() <= 1e-13 and np.abs(lse - lse2).max() <= 1e-13
+        for key in done:
+            assert [J for J in done2[key] if J <= key[1]] == done[key]
+
+
+def test_query_permutation_moves_rows_not_results():
+    """Permuting the queries of a segment only moves which block a query sits in: with tau = 0 the
+    result is the same dense attention; with tau > 0 the stop sees other blocks, yet every row is
+    written at its own position (no row is left NaN)."""
+    N, Hq, Hkv, d, B, S = 96, 2, 1, 8, 8, 32
+    q, k, v = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=38)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    qperm = oracle.query_permutation(q, k, S)
+    out, lse, _ = oracle.s2o_prefix_attention(q, k, v, pi, B, S, 0.1, qperm=qperm)
+    assert not np.isnan(out).any() and not np.isnan(lse).any()
