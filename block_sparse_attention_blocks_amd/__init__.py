@@ -16,7 +16,7 @@ import torch
 
 from . import _lib
 from ._lib import (PBSA_FORCE_DIAG, PBSA_FORCE_FIRST, PBSA_MASK_RANKED, PBSA_OP_ATTENTION, PBSA_OP_MASK,  # noqa: F401
-                   PBSA_OP_PERMUTATION, PBSA_OP_PREFIX_RANK, PbsaError, PbsaShape)
+                   PBSA_OP_PERMUTATION, PBSA_OP_PREFIX_RANK, PBSA_OP_QUERY_PERM, PbsaError, PbsaShape)
 
 __all__ = [
     "build_segment_permutation",
@@ -28,6 +28,7 @@ __all__ = [
     "build_prefix_kv_ranking",
     "prefix_rank_length",
     "s2o_prefix_attn_prefill",
+    "build_query_permutation",
     "workspace_size",
     "make_shape",
     "num_blocks",
@@ -257,13 +258,33 @@ def build_prefix_kv_ranking(q: torch.Tensor, k: torch.Tensor, block_size: int, s
     return out
 
 
+def build_query_permutation(q: torch.Tensor, k: torch.Tensor, block_size: int, segment_size: int,
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """S2O query permutation: int32 [Hkv][N], each segment's positions by descending score against the
+    KV head's mean key (averaged over its query heads), ties by position."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, segment_size)
+    if out is None:
+        out = torch.empty((k.shape[0], q.shape[1]), dtype=torch.int32, device=q.device)
+    elif out.dtype != torch.int32 or out.shape != (k.shape[0], q.shape[1]) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [Hkv][N] tensor")
+    ws, nbytes = _workspace(shape, PBSA_OP_QUERY_PERM, q.device, workspace)
+    st = _lib.lib().pbsa_build_query_permutation(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(out), _ptr(ws), nbytes,
+                                                 _stream())
+    _lib.check(st, "pbsa_build_query_permutation")
+    return out
+
+
 def s2o_prefix_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, kv_rank: torch.Tensor,
                             block_size: int, segment_size: int, gain_tau: float, scale: Optional[float] = None,
                             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                             return_lse: bool = True, return_kept: bool = False, return_error: bool = False,
-                            workspace: Optional[torch.Tensor] = None):
+                            workspace: Optional[torch.Tensor] = None, qperm: Optional[torch.Tensor] = None):
     """S2O two-pass attention with the marginal-gain stop over the historical ranking of
-    build_prefix_kv_ranking: out fp32 [Hq][N][d] (+ lse, processed-entry bitmap, device error word)."""
+    build_prefix_kv_ranking: out fp32 [Hq][N][d] (+ lse, processed-entry bitmap, device error word).
+    qperm (build_query_permutation) permutes the queries inside segments; rows still come back at
+    their natural positions, and the kept bitmap then has NB bits per (h, I) row."""
     _check_bf16("q", q)
     _check_bf16("k", k)
     _check_bf16("v", v, heads=k.shape[0])
@@ -277,16 +298,20 @@ def s2o_prefix_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
         out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    if qperm is not None and (qperm.dtype != torch.int32 or qperm.shape != (k.shape[0], N)
+                              or not qperm.is_contiguous()):
+        raise ValueError("qperm must be the contiguous int32 [Hkv][N] query permutation")
     NB = num_blocks(N, block_size)
     kept = None
     if return_kept:
-        kept = torch.zeros((Hq, -(-(NB * (NB + 1) // 2) // 32)), dtype=torch.int32, device=q.device)
+        bits = NB * NB if qperm is not None else NB * (NB + 1) // 2
+        kept = torch.zeros((Hq, -(-bits // 32)), dtype=torch.int32, device=q.device)
     err = torch.zeros(1, dtype=torch.int32, device=q.device) if return_error else None
     shape = make_shape(q, k, block_size, segment_size, scale, out=out)
     ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
     st = _lib.lib().pbsa_s2o_prefix_attn_prefill(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_rank) if L else None, float(gain_tau), _ptr(out),
-        _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_rank) if L else None, _ptr(qperm), float(gain_tau),
+        _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
     _lib.check(st, "pbsa_s2o_prefix_attn_prefill")
     res = [out]
     if return_lse:

@@ -20,6 +20,7 @@ PBSA_OP_PERMUTATION = 0
 PBSA_OP_MASK = 1
 PBSA_OP_ATTENTION = 2
 PBSA_OP_PREFIX_RANK = 3
+PBSA_OP_QUERY_PERM = 4
 
 PBSA_FORCE_DIAG = 1
 PBSA_FORCE_FIRST = 2
@@ -67,8 +68,9 @@ _SIG = {
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_build_prefix_kv_ranking": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_prefix_rank_length": (ctypes.c_int64, [ctypes.POINTER(PbsaShape)]),
-    "pbsa_s2o_prefix_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, ctypes.c_float, _P, _P,
-                                                    _P, _P, _P, ctypes.c_size_t, _P]),
+    "pbsa_s2o_prefix_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, ctypes.c_float,
+                                                    _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pbsa_build_query_permutation": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_tile_max": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P]),
     "pbsa_calibrate_thresholds": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, ctypes.c_int32, _P, _P]),
     "pbsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -93,6 +93,7 @@ size_t pbsa_workspace_size(const pbsa_shape* shape, int op) {
     case PBSA_OP_MASK: return pbsa::mask_workspace_bytes(g);
     case PBSA_OP_ATTENTION: return g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0;
     case PBSA_OP_PREFIX_RANK: return prefix_rank_ok(g) ? pbsa::prefix_rank_workspace_bytes(g) : SIZE_MAX;
+    case PBSA_OP_QUERY_PERM: return g.S > 0 ? (g.N > 0 ? pbsa::query_perm_workspace_bytes(g) : 0) : SIZE_MAX;
     default: return SIZE_MAX;
   }
 }
@@ -193,10 +194,25 @@ pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, co
                                              static_cast<hipStream_t>(stream)));
 }
 
+pbsa_status pbsa_build_query_permutation(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                         int32_t* qperm, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (g.S <= 0) return PBSA_ERR_INVALID_ARG;
+  if (!q || !k || !qperm || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(g.N > 0 ? pbsa::query_perm_workspace_bytes(g) : 0, workspace, workspace_bytes)) !=
+      PBSA_OK)
+    return st;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_query_permutation(g, q, k, qperm, workspace, static_cast<hipStream_t>(stream)));
+}
+
 pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
-                                         const uint16_t* v, const int32_t* kv_rank, float gain_tau, float* out,
-                                         float* lse, uint32_t* kept_bitmap, int32_t* device_error, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
+                                         const uint16_t* v, const int32_t* kv_rank, const int32_t* qperm,
+                                         float gain_tau, float* out, float* lse, uint32_t* kept_bitmap,
+                                         int32_t* device_error, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
   Geometry g;
   pbsa_status st = make_geometry(shape, &g);
   if (st != PBSA_OK) return st;
@@ -209,7 +225,7 @@ pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t
   if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
     return st;
   if (g.N == 0) return PBSA_OK;
-  return from_hip(pbsa::launch_s2o_prefix_attention(g, q, k, v, kv_rank, L, gain_tau, out, lse, kept_bitmap,
+  return from_hip(pbsa::launch_s2o_prefix_attention(g, q, k, v, kv_rank, L, qperm, gain_tau, out, lse, kept_bitmap,
                                                     device_error, workspace, static_cast<hipStream_t>(stream)));
 }
 

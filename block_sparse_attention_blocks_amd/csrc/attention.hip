@@ -65,6 +65,7 @@ struct AttnArgs {
   int two_pass;               // S2O kernels: two-pass lists over the per-segment prefix order kvr
   const int32_t* kvr;         // per-segment prefix key order (NULL when no segment has a prefix)
   int64_t kvr_L;              // entries of kvr per KV head
+  const int32_t* qperm;       // two-pass lists: query order inside segments [Hkv][N], or NULL
 };
 
 enum { MODE_ATTN = 0, MODE_ATTN_GATED = 1, MODE_TILE_MAX = 2, MODE_DENSE = 3 };
@@ -494,16 +495,17 @@ __device__ __forceinline__ int ranked_list(const AttnArgs& a, int h, int I, size
   return cnt;
 }
 
-// The two-pass list of S2O (Kernel Implementation) for query block I whose segment starts at block
-// J0: pass 1, the own segment's blocks J0 .. I ascending; pass 2, blocks 0 .. J0-1 of the segment's
-// prefix key order (block J = ranked keys J*B .. J*B+B-1).  Returns the list length, I + 1.
+// The two-pass list of S2O (Kernel Implementation) for a query block of the segment that starts at
+// block J0: pass 1, the own segment's blocks J0 .. Jend ascending (Jend = I in natural query order,
+// the segment's last block when queries are permuted); pass 2, blocks 0 .. J0-1 of the segment's
+// prefix key order (block J = ranked keys J*B .. J*B+B-1).  Returns the list length, Jend + 1.
 template <int THREADS>
-__device__ __forceinline__ int two_pass_list(int I, int J0, uint32_t* mlist) {
-  const int nin = I + 1 - J0;
-  for (int x = threadIdx.x; x <= I; x += THREADS)
+__device__ __forceinline__ int two_pass_list(int Jend, int J0, uint32_t* mlist) {
+  const int nin = Jend + 1 - J0;
+  for (int x = threadIdx.x; x <= Jend; x += THREADS)
     mlist[x] = (uint32_t)(x < nin ? J0 + x : x - nin) | (1u << 16);
   __syncthreads();
-  return I + 1;
+  return Jend + 1;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -634,8 +636,22 @@ void attn_pipe_kernel(AttnArgs a) {
   const int g = h0 / a.G;
   const int I0 = I * BLK;
   const int qloc = wq * 32 + l32;
-  const int qpos = I0 + qloc;
-  const bool qvalid = qpos < a.N;
+  const int qpos = I0 + qloc;  // slot of this lane's query in the (possibly permuted) order
+  const int sI = a.S > 0 ? I0 / a.S : 0;
+  const bool two_pass = S2O && a.two_pass;  // history through the segment's prefix order
+  const bool qperm_on = two_pass && a.qperm != nullptr;
+  const int J0 = sI * a.S / BLK;             // first block of the query block's segment
+  bool qvalid = qpos < a.N;
+  int qnat = qpos;  // natural position of the query (its causal limit and output row)
+  if (qperm_on && qvalid) {
+    const int v = a.qperm[(size_t)g * a.N + qpos];
+    if (v < sI * a.S || v >= min((sI + 1) * a.S, a.N)) {  // not a position of this segment
+      if (a.err) atomicOr(a.err, 8);
+      qvalid = false;
+    } else {
+      qnat = v;
+    }
+  }
   const size_t ntri = (size_t)a.NB * (a.NB + 1) / 2;
   const rsrc_t qr = make_rsrc(a.q + (int64_t)h * a.qsh, a.q_bytes);
   const rsrc_t kr = make_rsrc(a.k + (int64_t)g * a.kvsh, a.kv_bytes);
@@ -644,15 +660,14 @@ void attn_pipe_kernel(AttnArgs a) {
   bf16x8 qf[AttnCfg<D, BLK>::KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < AttnCfg<D, BLK>::KSTEPS; ++kk) {
-    const uint32_t off = qvalid ? (uint32_t)qpos * a.q_row_bytes + kk * 32 + h2 * 16 : kOutOfRange;
+    const uint32_t off = qvalid ? (uint32_t)qnat * a.q_row_bytes + kk * 32 + h2 * 16 : kOutOfRange;
     qf[kk] = __builtin_bit_cast(bf16x8, buf_load16(qr, off));
   }
 
   // merged key-block list: ascending J kept by any of the workgroup's heads
-  const int sI = a.S > 0 ? I0 / a.S : 0;
-  const bool two_pass = S2O && a.two_pass;  // history through the segment's prefix order
+  const int Jend = qperm_on ? min((min((sI + 1) * a.S, a.N) + BLK - 1) / BLK, a.NB) - 1 : I;
   const int nblk = DENSE     ? I + 1
-                   : two_pass ? two_pass_list<C::THREADS>(I, sI * a.S / BLK, mlist)
+                   : two_pass ? two_pass_list<C::THREADS>(Jend, J0, mlist)
                    : S2O      ? ranked_list<C::THREADS>(a, h0, I, ntri, mlist, &mcount)
                               : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
   const int nst = nblk * C::STAGES;
@@ -726,11 +741,16 @@ void attn_pipe_kernel(AttnArgs a) {
       const int J = (int)(e & 0xffffu);
       const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
       if (a.kept && lane == 0 && wq == 0 && (s % C::STAGES) == 0) {
-        const size_t bit = tri_offset(I) + J;
-        atomicOr(&a.kept[(size_t)h * ((ntri + 31) / 32) + bit / 32], 1u << (bit % 32));
+        // row (h, I) of the kept bitmap: packed triangle, or NB bits per row with permuted queries
+        const size_t bit = qperm_on ? (size_t)I * a.NB + J : tri_offset(I) + J;
+        const size_t words = qperm_on ? ((size_t)a.NB * a.NB + 31) / 32 : (ntri + 31) / 32;
+        atomicOr(&a.kept[(size_t)h * words + bit / 32], 1u << (bit % 32));
       }
       if (S2O && (s % C::STAGES) == 0) st.lb = st.l;  // a new key block starts
-      stage_compute<D, BLK>(st, Kc, Vc, qf, J == I, qloc - koff - 4 * h2, a.sl2);
+      // causal mask: on the diagonal tile, or on every own-segment tile when queries are permuted
+      // (key j is visible to the query at natural position qnat iff j <= qnat)
+      stage_compute<D, BLK>(st, Kc, Vc, qf, qperm_on ? J >= J0 : J == I,
+                            (qperm_on ? qnat - J * BLK : qloc) - koff - 4 * h2, a.sl2);
       if (S2O && (s % C::STAGES) == C::STAGES - 1) {
         // this block's share of each query's denominator (both half-waves of the query summed)
         float la, lbh, da, db;
@@ -783,7 +803,7 @@ void attn_pipe_kernel(AttnArgs a) {
       for (int x = 0; x < NBUF; ++x) step(s + x, x);
     }
   }
-  write_output<D, BLK>(a, st, h, qpos, qvalid, h2);
+  write_output<D, BLK>(a, st, h, qnat, qvalid, h2);
   __syncthreads();  // every wave is done with this item's LDS before the next claim
   }
 }
@@ -1331,8 +1351,9 @@ hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint
 }
 
 hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                       const int32_t* kv_rank, int64_t rank_len, float gain_tau, float* out,
-                                       float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st) {
+                                       const int32_t* kv_rank, int64_t rank_len, const int32_t* qperm,
+                                       float gain_tau, float* out, float* lse, uint32_t* kept, int32_t* err,
+                                       void* ws, hipStream_t st) {
   AttnArgs a = make_args(g);
   a.queue = static_cast<unsigned long long*>(ws);
   a.q = q;
@@ -1341,6 +1362,7 @@ hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, con
   a.two_pass = 1;
   a.kvr = kv_rank;
   a.kvr_L = rank_len;
+  a.qperm = qperm;
   a.out = out;
   a.lse = lse;
   a.kept = kept;

@@ -65,6 +65,9 @@ size_t importance_workspace_bytes(const Geometry& g);
 hipError_t launch_build_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* perm,
                                     double* imp, void* ws, hipStream_t st);
 
+// Sort of fp64 scores [Hkv][N] inside segments of g.S: descending, ties by position, into perm.
+hipError_t launch_segment_sort(const Geometry& g, const double* score, int32_t* perm, hipStream_t st);
+
 // Stage 2.
 size_t mask_workspace_bytes(const Geometry& g);
 constexpr uint32_t kMaskRanked = 4u;  // PBSA_MASK_RANKED
@@ -90,8 +93,13 @@ int64_t prefix_rank_length(const Geometry& g);
 hipError_t launch_prefix_rank(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* kv_rank, void* ws,
                               hipStream_t st);
 hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                       const int32_t* kv_rank, int64_t rank_len, float gain_tau, float* out,
-                                       float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st);
+                                       const int32_t* kv_rank, int64_t rank_len, const int32_t* qperm,
+                                       float gain_tau, float* out, float* lse, uint32_t* kept, int32_t* err,
+                                       void* ws, hipStream_t st);
+// S2O query permutation: workspace and launch (qperm int32 [Hkv][N]).
+size_t query_perm_workspace_bytes(const Geometry& g);
+hipError_t launch_query_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* qperm, void* ws,
+                                    hipStream_t st);
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax,
                            hipStream_t st);
 hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);

@@ -400,9 +400,9 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
 
 // =====================================================================================
 // Stage 1b: sort inside segments (section 3, "Sorting"): importance descending, ties by
-// position ascending.  One workgroup per (segment, KV head); bitonic sort in LDS on the
-// 64-bit key ~bits(imp) (imp >= 0, so the bit pattern orders like the value) with the
-// position as the second key.
+// position ascending.  One workgroup per (segment, KV head); bitonic sort in LDS on a 64-bit key
+// that orders like the negated value (sign-folded bit pattern), with the position as the second
+// key.  The same sort orders S2O's query guide scores, which may be negative.
 // =====================================================================================
 
 constexpr int SORT_MAX = 8192;
@@ -418,9 +418,9 @@ __global__ __launch_bounds__(SORT_THREADS) void segment_sort_kernel(const double
   while (n < L) n <<= 1;
   for (int x = t; x < n; x += SORT_THREADS) {
     if (x < L) {
-      double v = imp[(size_t)g * N + a + x];
-      uint64_t b = (v > 0.0) ? (uint64_t)__double_as_longlong(v) : 0ull;
-      key[x] = ~b;
+      const uint64_t b = (uint64_t)__double_as_longlong(imp[(size_t)g * N + a + x]);
+      const uint64_t o = (b >> 63) ? ~b : (b | 0x8000000000000000ull);  // ascending in the value
+      key[x] = ~o;
       off[x] = (uint16_t)x;
     } else {
       key[x] = ~0ull;
@@ -449,6 +449,12 @@ __global__ __launch_bounds__(SORT_THREADS) void segment_sort_kernel(const double
     }
   }
   for (int x = t; x < L; x += SORT_THREADS) perm[(size_t)g * N + a + x] = a + (int)off[x];
+}
+
+hipError_t launch_segment_sort(const Geometry& g, const double* score, int32_t* perm, hipStream_t st) {
+  const int nseg = (g.N + g.S - 1) / g.S;
+  segment_sort_kernel<<<dim3(nseg, g.Hkv), SORT_THREADS, 0, st>>>(score, perm, g.N, g.S);
+  return hipGetLastError();
 }
 
 hipError_t launch_build_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* perm,

@@ -7,6 +7,7 @@
 //   radix_*              stable least-significant-digit radix sort of every (g, sigma) list,
 //                        8-bit digits, four passes
 // Output layout: kv_rank[g][S*sigma*(sigma-1)/2 + r] = key of rank r for segment sigma.
+// Also S2O's query permutation (query_guide_kernel + the segment sort of stage 1).
 #include "common.h"
 
 namespace pbsa {
@@ -377,7 +378,66 @@ __global__ __launch_bounds__(RK_THREADS) void radix_scatter_kernel(RadixArgs a) 
   }
 }
 
+// S2O query permutation (Methodology 1, Query Permutation): score of position i for KV head g =
+// (1/G) * sum over the G query heads of q_{h,i} . u_g, u_g the mean key (the shared guide vector);
+// one lane per position, u_g read through scalar loads, fp64.
+template <int D>
+__global__ __launch_bounds__(RK_THREADS) void query_guide_kernel(const uint16_t* q, int64_t qsh, int64_t qst, int N,
+                                                                 int G, const double* __restrict__ u, double* score) {
+  const int g = blockIdx.y, i = blockIdx.x * RK_THREADS + threadIdx.x;
+  if (i >= N) return;
+  const double* ug = u + (size_t)g * D;
+  double tot = 0.0;
+  for (int h = g * G; h < (g + 1) * G; ++h) {
+    const uint16_t* qp = q + h * qsh + (int64_t)i * qst;
+    double acc = 0.0;
+#pragma unroll 4
+    for (int c = 0; c < D / 8; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fma((double)bf16_bits_to_f32(v[e] & 0xffffu), ug[c * 8 + 2 * e], acc);
+        acc = fma((double)bf16_bits_to_f32(v[e] >> 16), ug[c * 8 + 2 * e + 1], acc);
+      }
+    }
+    tot += acc;
+  }
+  score[(size_t)g * N + i] = tot / (double)G;
+}
+
 }  // namespace
+
+size_t query_perm_workspace_bytes(const Geometry& g) {
+  const int nch = (g.N + REP_ROWS - 1) / REP_ROWS;
+  return align256(sizeof(double) * g.Hkv * (size_t)nch * g.d) + align256(sizeof(double) * g.Hkv * g.d) +
+         align256(sizeof(double) * g.Hkv * (size_t)g.N);
+}
+
+hipError_t launch_query_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* qperm, void* ws,
+                                    hipStream_t st) {
+  // the mean key of each KV head: the representative-query kernels over one "segment" of all N
+  // key rows of one head (G = 1)
+  const int nch = (g.N + REP_ROWS - 1) / REP_ROWS;
+  char* c = static_cast<char*>(ws);
+  double* upart = reinterpret_cast<double*>(c);
+  c += align256(sizeof(double) * g.Hkv * (size_t)nch * g.d);
+  double* u = reinterpret_cast<double*>(c);
+  c += align256(sizeof(double) * g.Hkv * g.d);
+  double* score = reinterpret_cast<double*>(c);
+  const dim3 rgrid(nch, 1, g.Hkv), sgrid((g.N + RK_THREADS - 1) / RK_THREADS, g.Hkv);
+  if (g.d == 128) {
+    seg_rep_partial_kernel<128><<<rgrid, RK_THREADS, 0, st>>>(k, g.kvsh, g.kvst, g.N, g.N, 1, 1, nch, upart);
+    seg_rep_combine_kernel<128><<<dim3(1, g.Hkv), 128, 0, st>>>(upart, g.N, g.N, 1, 1, nch, u);
+    query_guide_kernel<128><<<sgrid, RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.G, u, score);
+  } else {
+    seg_rep_partial_kernel<64><<<rgrid, RK_THREADS, 0, st>>>(k, g.kvsh, g.kvst, g.N, g.N, 1, 1, nch, upart);
+    seg_rep_combine_kernel<64><<<dim3(1, g.Hkv), 64, 0, st>>>(upart, g.N, g.N, 1, 1, nch, u);
+    query_guide_kernel<64><<<sgrid, RK_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.G, u, score);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_segment_sort(g, score, qperm, st);
+}
 
 size_t prefix_rank_workspace_bytes(const Geometry& g) {
   const PrefixGeom p = prefix_geom(g);

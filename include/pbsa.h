@@ -84,7 +84,8 @@ enum {
   PBSA_OP_PERMUTATION = 0,
   PBSA_OP_MASK = 1,
   PBSA_OP_ATTENTION = 2,
-  PBSA_OP_PREFIX_RANK = 3
+  PBSA_OP_PREFIX_RANK = 3,
+  PBSA_OP_QUERY_PERM = 4
 };
 
 /* Flags of pbsa_estimate_block_mask. */
@@ -233,6 +234,22 @@ pbsa_status pbsa_build_prefix_kv_ranking(const pbsa_shape* shape, const uint16_t
 int64_t pbsa_prefix_rank_length(const pbsa_shape* shape);
 
 /*
+ * Query permutation (S2O, Methodology 1, Query Permutation; PBS-Attn 1, query permutation
+ * equivariance and the inverse transformation).
+ *
+ * For KV head g: the guide vector u = mean of the keys of g over the sequence (fp64); the score of
+ * position i = (1/G) * sum over the G query heads of g of q_{h,i} . u (fp64); inside each segment
+ * (segment_size S) the positions are listed by score descending, ties by position.
+ *   qperm      out, int32 [Hkv][N]: entries a .. b-1 of each segment [a, b) are that segment's
+ *              positions in this order; shared by the G query heads of g
+ *   workspace  >= pbsa_workspace_size(shape, PBSA_OP_QUERY_PERM) bytes, 256-byte aligned
+ * Requires segment_size > 0.
+ */
+pbsa_status pbsa_build_query_permutation(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                         int32_t* qperm, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/*
  * S2O's two-pass attention with the marginal-gain early stop (Kernel Implementation; Early-Stopping
  * Rule).  For query block I of head h (segment sigma, first block J0 = sigma*S/B): pass 1 takes the
  * own segment's blocks J0 .. I in natural order (causal mask on the diagonal); pass 2 takes blocks
@@ -242,13 +259,21 @@ int64_t pbsa_prefix_rank_length(const pbsa_shape* shape);
  * processed).  out/lse: softmax attention over the processed keys.
  *   kv_rank      from pbsa_build_prefix_kv_ranking (entries must lie in the segment's prefix: an
  *                entry outside it is skipped and sets bit 2 of device_error)
- *   kept_bitmap  out, or NULL: bit I(I+1)/2 + J set for every processed entry J (J >= J0: natural
- *                block J; J < J0: prefix-order block J); caller zeroes it
+ *   qperm        from pbsa_build_query_permutation, or NULL (queries in natural order).  With it,
+ *                query block I holds the queries at positions qperm[g][I*B ...], pass 1 takes every
+ *                block of the own segment under the per-token causal mask (key j visible to the
+ *                query at position i iff j <= i), and each output and lse row is written at the
+ *                query's own position.  An entry outside its segment sets bit 4 (value 8) of
+ *                device_error and that query is skipped (its row is not written).
+ *   kept_bitmap  out, or NULL: one bit per processed entry J (J >= J0: natural block J; J < J0:
+ *                prefix-order block J) of row (h, I): bit I(I+1)/2 + J, words
+ *                ceil(NB(NB+1)/2 / 32) per head; with qperm bit I*NB + J, words ceil(NB*NB / 32)
+ *                per head.  The caller zeroes it.
  *   other arguments as for pbsa_s2o_attn_prefill; segment_size must be > 0.
  */
 pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
-                                         const uint16_t* v, const int32_t* kv_rank, float gain_tau,
-                                         float* out, float* lse, uint32_t* kept_bitmap,
+                                         const uint16_t* v, const int32_t* kv_rank, const int32_t* qperm,
+                                         float gain_tau, float* out, float* lse, uint32_t* kept_bitmap,
                                          int32_t* device_error, void* workspace,
                                          size_t workspace_bytes, void* stream);
 

@@ -95,12 +95,16 @@ def compare_ranked(count_g, idx_g, count_o, idx_o, z_o) -> int:
     return ties
 
 
-def compare_s2o_stops(kept, count_g, idx_g, ratios, gain_tau: float, band: float = S2O_BAND):
+def compare_s2o_stops(kept, count_g, idx_g, ratios, gain_tau: float, band: float = S2O_BAND, row_stride=None):
     """Assert each row's processed blocks (kept: {(h, I): ascending J}) are a prefix of the GPU's
-    ranked list whose end the oracle's gain ratios allow; return (rows, rows decided in the band)."""
+    ranked list whose end the oracle's gain ratios allow; return (rows, rows decided in the band).
+    row_stride: entries per row when the lists are not packed as a triangle."""
     near = 0
     for (h, I), r in ratios.items():
-        lst = _row(idx_g, count_g, h, I)
+        if row_stride is None:
+            lst = _row(idx_g, count_g, h, I)
+        else:
+            lst = [int(x) for x in idx_g[h, I * row_stride:I * row_stride + int(count_g[h, I])]]
         got = kept[(h, I)]
         n = len(got)
         assert n >= 1 and sorted(lst[:n]) == got, f"s2o row ({h},{I}): processed {got} is not a prefix of {lst}"
@@ -143,17 +147,32 @@ def compare_prefix_rank(pi_g, pi_o, score_o, S: int) -> int:
     return ties
 
 
-def two_pass_lists(Hq: int, N: int, B: int, S: int):
-    """count/idx of S2O's two-pass lists: the own segment's blocks ascending, then prefix blocks 0 .. J0-1."""
+def two_pass_lists(Hq: int, N: int, B: int, S: int, permuted_queries: bool = False):
+    """count/idx of S2O's two-pass lists: the own segment's blocks ascending (up to I, or to the
+    segment's last block with permuted queries), then prefix blocks 0 .. J0-1.  Rows are laid out
+    as the packed triangle, or NB entries per row with permuted queries."""
     NB = -(-N // B)
     count = np.zeros((Hq, NB), dtype=np.int64)
-    idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    idx = np.full((Hq, NB * NB if permuted_queries else NB * (NB + 1) // 2), -1, dtype=np.int64)
     for I in range(NB):
-        J0 = ((I * B) // S) * S // B
-        o = oracle.tri_offset(I)
-        count[:, I] = I + 1
-        idx[:, o:o + I + 1] = list(range(J0, I + 1)) + list(range(J0))
+        sigma = (I * B) // S
+        J0 = sigma * S // B
+        Jend = -(-min((sigma + 1) * S, N) // B) - 1 if permuted_queries else I
+        o = I * NB if permuted_queries else oracle.tri_offset(I)
+        lst = list(range(J0, Jend + 1)) + list(range(J0))
+        count[:, I] = len(lst)
+        idx[:, o:o + len(lst)] = lst
     return count, idx
+
+
+def bitmap_to_kept_square(bm: np.ndarray, NB: int):
+    """{(h, I): [J ...]} from a [Hq][words] bitmap with NB bits per row (bit I*NB + J)."""
+    bm = bm.astype(np.uint32)
+    kept = {}
+    for h in range(bm.shape[0]):
+        for I in range(NB):
+            kept[(h, I)] = [J for J in range(NB) if (bm[h, (I * NB + J) // 32] >> np.uint32((I * NB + J) % 32)) & 1]
+    return kept
 
 
 def compare_out(out_g: np.ndarray, out_o: np.ndarray, what: str = "out"):

@@ -230,8 +230,8 @@ def test_prefix_ranking_and_two_pass_entry_validate_before_launch():
     assert rank(ctypes.byref(shape(N=0)), FAKE, FAKE, None, None, 0, None) == 0       # nothing to rank
     assert rank(ctypes.byref(shape(N=400, S=512)), FAKE, FAKE, None, None, 0, None) == 0
     att = l.pbsa_s2o_prefix_attn_prefill
-    args = lambda sh, kvr, tau, w=ws: (ctypes.byref(sh), FAKE, FAKE, FAKE, kvr, tau, FAKE, None, None, None, w,
-                                       big if w else 0, None)
+    args = lambda sh, kvr, tau, w=ws: (ctypes.byref(sh), FAKE, FAKE, FAKE, kvr, None, tau, FAKE, None, None, None,
+                                       w, big if w else 0, None)
     assert att(*args(s, FAKE, -1.0)) == E
     assert att(*args(s, FAKE, float("nan"))) == E
     assert att(*args(s, FAKE, float("inf"))) == E
@@ -240,3 +240,20 @@ def test_prefix_ranking_and_two_pass_entry_validate_before_launch():
     assert att(*args(s, FAKE, 0.01, None)) == W
     assert att(*args(shape(N=64 * 300, B=64, S=64), FAKE, 0.01)) == U
     assert att(*args(shape(N=0), None, 0.01)) == 0
+
+
+def test_query_permutation_entry_validates_before_launch():
+    l = _lib.lib()
+    E, W = _lib.PBSA_ERR_INVALID_ARG, _lib.PBSA_ERR_WORKSPACE
+    s = shape(N=2048, S=512)
+    ws = ctypes.c_void_p(0x10000)
+    big = 1 << 40
+    qp = l.pbsa_build_query_permutation
+    assert ws_size(shape(S=0), _lib.PBSA_OP_QUERY_PERM) == _lib.SIZE_MAX
+    assert ws_size(shape(N=0), _lib.PBSA_OP_QUERY_PERM) == 0
+    assert ws_size(s, _lib.PBSA_OP_QUERY_PERM) >= 8 * 2 * 2048      # fp64 scores at least
+    assert qp(ctypes.byref(shape(S=0)), FAKE, FAKE, FAKE, ws, big, None) == E
+    assert qp(ctypes.byref(s), FAKE, FAKE, None, ws, big, None) == E
+    assert qp(ctypes.byref(s), None, FAKE, FAKE, ws, big, None) == E
+    assert qp(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None) == W
+    assert qp(ctypes.byref(shape(N=0)), FAKE, FAKE, FAKE, None, 0, None) == 0

@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_prefix_rank,
-                    compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
+from parity import (bitmap_to_kept, bitmap_to_kept_square, compare_lse, compare_mask, compare_out, compare_perm,
+                    compare_prefix_rank, compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
 from workloads import bf16_bits_to_f32, generate
 
 pytestmark = pytest.mark.gpu
@@ -530,3 +530,63 @@ def test_two_pass_is_deterministic_and_bounds_the_ranking():
     torch.cuda.synchronize()
     assert int(err.item()) & 2
     assert torch.isfinite(out).all()
+
+
+# S2O query permutation in the two-pass path: (name, N, Hq, Hkv, d, B, S, stripes, band, gain_tau, seed)
+QPERM_CASES = [
+    ("flat_b64_d128_gqa_2048", 2048, 4, 2, 128, 64, 256, 0, 0, 0.05, 61),
+    ("band_b128_d64_ragged_4000", 4000, 4, 1, 64, 128, 512, 0, 256, 0.02, 62),
+    ("stripes_b128_d128_ragged_3000", 3000, 2, 1, 128, 128, 512, 4, 256, 0.05, 63),
+    ("s192_b64_d64_ragged_1500", 1500, 2, 2, 64, 64, 192, 0, 64, 0.1, 64),
+]
+
+
+@pytest.mark.parametrize("case", QPERM_CASES, ids=[c[0] for c in QPERM_CASES])
+def test_query_permuted_two_pass_stagewise(case):
+    pbsa = _need_gpu()
+    name, N, Hq, Hkv, d, B, S, stripes, band, gain_tau, seed = case
+    _log(f"[parity] qperm {name}: N={N} Hq={Hq} Hkv={Hkv} d={d} B={B} S={S} gain_tau={gain_tau}")
+    dev, host = _inputs(N, Hq, Hkv, d, stripes, band, seed)
+    q, k, v = host["q"], host["k"], host["v"]
+    NB = oracle.num_blocks(N, B)
+    qperm_t = pbsa.build_query_permutation(dev["q"], dev["k"], B, S)
+    rank_t = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    torch.cuda.synchronize()
+    qp_g = qperm_t.cpu().numpy().astype(np.int64)
+    qties = compare_perm(qp_g, oracle.query_permutation(q, k, S), oracle.query_guide_scores(q, k), S)
+    pi_g = rank_t.cpu().numpy().astype(np.int64)
+    out_t, lse_t, kept_t, err_t = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank_t, B, S, gain_tau,
+                                                               qperm=qperm_t, return_kept=True, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err_t.item()) == 0
+    kept = bitmap_to_kept_square(kept_t.cpu().numpy(), NB)
+    cg, ig = two_pass_lists(Hq, N, B, S, permuted_queries=True)
+    ratios = oracle.s2o_prefix_gain_ratios(q, k, pi_g, B, S, qperm=qp_g)
+    rows, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau, row_stride=NB)
+    out_o, lse_o = oracle.two_pass_attention_on(q, k, v, pi_g, kept, B, S, qperm=qp_g)
+    assert not np.isnan(out_o).any()
+    mx, mean = compare_out(out_t.cpu().numpy(), out_o, "qperm two-pass")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    _log(f"[parity] qperm {name}: query-order ties {qties}, rows {rows}, decided in band {near}, "
+         f"max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+def test_query_permuted_two_pass_zero_threshold_is_dense_and_flags_bad_entries():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 1800, 4, 2, 128, 128, 512
+    dev, host = _inputs(N, Hq, Hkv, d, 8, 256, 65)
+    qperm = pbsa.build_query_permutation(dev["q"], dev["k"], B, S)
+    rank = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    out, lse = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank, B, S, 0.0, qperm=qperm)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.dense_attention(host["q"], host["k"], host["v"])
+    compare_out(out.cpu().numpy(), ref, "qperm gain_tau 0")
+    compare_lse(lse.cpu().numpy(), ref_lse)
+    # a query-order entry outside its segment is flagged and that query skipped
+    bad = qperm.clone()
+    bad[0, 700] = 100                           # segment 1 slot pointing into segment 0
+    out2, err = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank, B, S, 0.0, qperm=bad,
+                                             return_lse=False, return_error=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) & 8
+    assert torch.isfinite(out2[:, :100]).all()
