@@ -258,6 +258,8 @@ def suite(args) -> int:
         suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
     if "twopass" in parts:
         suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=True)
+    if "qperm" in parts:
+        suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=True, qperm=True)
     out_f.close()
     return 0
 
@@ -373,10 +375,11 @@ def suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     torch.cuda.empty_cache()
 
 
-def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=False):
+def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=False, qperm=False):
     """Marginal-gain early stop at 32K and 128K, and at 32K on inputs drawn without stripe keys
     (there the stop falls in the middle of most lists): over the pooled-logit ranked list (PBS
-    permutation + PBSA_MASK_RANKED), or with two_pass over S2O's historical ranking."""
+    permutation + PBSA_MASK_RANKED), or with two_pass over S2O's historical ranking (qperm: with
+    the query permutation too, whose build time is added to ranking_ms)."""
     from workloads import generate
     cases = [("llama8b_32k", None), ("llama8b_32k", "no_stripes"), ("llama8b_128k", None)]
     for name, variant in cases:
@@ -397,7 +400,12 @@ def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pa
             ws_r = torch.empty(pbsa.workspace_size(shape, pbsa.PBSA_OP_PREFIX_RANK) + 256, dtype=torch.uint8,
                                device="cuda")
             rank = pbsa.build_prefix_kv_ranking(q, k, B, S, workspace=ws_r)
-            fr = lambda: pbsa.build_prefix_kv_ranking(q, k, B, S, out=rank, workspace=ws_r)
+            qp = pbsa.build_query_permutation(q, k, B, S) if qperm else None
+
+            def fr():
+                pbsa.build_prefix_kv_ranking(q, k, B, S, out=rank, workspace=ws_r)
+                if qperm:
+                    pbsa.build_query_permutation(q, k, B, S, out=qp)
             perm = count = idx = None
         else:
             perm = pbsa.build_segment_permutation(q, k, B, S)
@@ -408,21 +416,22 @@ def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pa
         t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
         for gain_tau in (0.001, 0.01, 0.05):
             if two_pass:
-                fa = lambda: pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, out=out, lse=lse)
-                _, _, kept = pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, return_kept=True)
+                fa = lambda: pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, out=out, lse=lse, qperm=qp)
+                _, _, kept = pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, return_kept=True, qperm=qp)
             else:
                 fa = lambda: pbsa.s2o_attn_prefill(q, k, v, perm, count, idx, B, S, gain_tau, out=out, lse=lse)
                 _, _, kept = pbsa.s2o_attn_prefill(q, k, v, perm, count, idx, B, S, gain_tau, return_kept=True)
             ta = _events(torch, stream, fa, reps)["median_ms"]
             tiles = int(np.unpackbits(kept.cpu().numpy().view(np.uint8)).sum())
             emit({"workload": w.name + ("" if variant is None else "_" + variant), "gain_tau": gain_tau,
-                  "lists": "two-pass historical ranking" if two_pass else "pooled-logit ranked",
+                  "lists": ("two-pass historical ranking" + (", query permutation" if qperm else "")) if two_pass
+                  else "pooled-logit ranked",
                   "processed_fraction": tiles / causal_tiles, "ranking_ms": t_rank, "attention_ms": ta,
                   "dense_kernel_ms": t_dense, "attention_speedup_vs_dense": t_dense / ta,
                   "attention_mfma_frac": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
         del d, q, k, v, out, lse, perm, count, idx
         if two_pass:
-            del rank, ws_r
+            del rank, ws_r, qp
         torch.cuda.empty_cache()
 
 
@@ -445,8 +454,8 @@ def main() -> int:
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
     ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
-    ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o,twopass",
-                    help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass")
+    ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o,twopass,qperm",
+                    help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass, qperm")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "

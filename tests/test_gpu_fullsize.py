@@ -10,8 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import (bitmap_to_kept, compare_lse, compare_mask, compare_out, compare_perm, compare_prefix_rank,
-                    compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
+from parity import (bitmap_to_kept, bitmap_to_kept_square, compare_lse, compare_mask, compare_out, compare_perm,
+                    compare_prefix_rank, compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
 from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
 
 pytestmark = pytest.mark.gpu
@@ -215,3 +215,33 @@ def test_fullsize_32k_two_pass_sampled():
     frac = sum(len(x) for x in kept.values()) / (Hq * NB * (NB + 1) / 2)
     _log(f"[fullsize] 32K two-pass: processed {frac:.3f}, sampled rows {rows} ({near} in band): "
          f"max abs {mx:.2e} mean {mean:.2e}")
+
+
+def test_fullsize_32k_query_permuted_two_pass_sampled():
+    """Query permutation at 32K: the whole query order, and the stop and outputs of sampled rows."""
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_32k"]
+    gain_tau = 0.01
+    _log(f"[fullsize] {w.name} query-permuted two-pass, gain_tau {gain_tau}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, S, NB, Hq, N = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads, w.seq_len
+    qperm_t = pbsa.build_query_permutation(dev["q"], dev["k"], B, S)
+    rank_t = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    out_t, lse_t, kept_t = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank_t, B, S, gain_tau,
+                                                        qperm=qperm_t, return_kept=True)
+    torch.cuda.synchronize()
+    qp_g = qperm_t.cpu().numpy().astype(np.int64)
+    ties = compare_perm(qp_g, oracle.query_permutation(q, k, S), oracle.query_guide_scores(q, k), S)
+    _log(f"[fullsize] query order ok ({ties} recorded ties)")
+    pi_g = rank_t.cpu().numpy().astype(np.int64)
+    kept = bitmap_to_kept_square(kept_t.cpu().numpy(), NB)
+    rows = _sample_rows(Hq, NB, 10, 13)
+    cg, ig = two_pass_lists(Hq, N, B, S, permuted_queries=True)
+    ratios = oracle.s2o_prefix_gain_ratios(q, k, pi_g, B, S, rows=rows, qperm=qp_g)
+    _, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau, row_stride=NB)
+    out_o, lse_o = oracle.two_pass_attention_on(q, k, v, pi_g, {r: kept[r] for r in rows}, B, S, qperm=qp_g)
+    ok = ~np.isnan(out_o)
+    mx, mean = compare_out(np.where(ok, out_t.cpu().numpy(), np.nan), out_o, "qperm two-pass 32K")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    _log(f"[fullsize] 32K query-permuted two-pass: sampled rows {rows} ({near} in band): max abs {mx:.2e} mean {mean:.2e}")
