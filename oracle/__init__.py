@@ -34,10 +34,13 @@ from .pbsa_oracle import (  # noqa: F401
     s2o_gain_ratios,
     s2o_prefix_attention,
     s2o_prefix_gain_ratios,
+    sample_attention_mask,
+    sampled_masses,
     segment_of_block,
     segment_permutation,
     segment_representatives,
     tile_max,
     tri_offset,
+    trunk_rows,
     two_pass_attention_on,
 )

@@ -337,3 +337,60 @@ def attention_over_keys(q, k, v, keysets: Dict[Tuple[int, int], List[int]], B: i
             out[h][i] = [math.fsum(w[a] * float(v[g][ks[a]][t]) for a in range(len(ks))) / z for t in range(d)]
             lse[h][i] = m + math.log(z)
     return out, lse
+
+
+def sample_mask(q, k, B: int, tau: float, n_trunks: int, rows_per_trunk: int, force_diag: bool, force_first: bool,
+                scale: float):
+    """SampleAttention's mask from its definition: sampled rows (last rows of equal chunks), exact
+    causal softmax rows (fsum), per-column and per-diagonal mean mass (fsum), each family cut by
+    repeated selection of its heaviest member (smallest index among equals) until the fsum of the
+    chosen reaches tau (all members when tau >= 1 or never reached), and tile (I, J) kept when some
+    pair i in I, j in J, j <= i has j a chosen column or i - j a chosen diagonal, or when forced.
+    Returns ({(h, I): [J ...]}, [col set per head], [slash set per head], col, slash)."""
+    Hq, N = len(q), len(q[0])
+    G = Hq // len(k)
+    C = -(-N // n_trunks)
+    rows = [i for t in range(n_trunks) for i in range(min((t + 1) * C, N) - rows_per_trunk, min((t + 1) * C, N))]
+    NB = -(-N // B)
+    masks, cols, slashes, colm, slm = {}, [], [], [], []
+    for h in range(Hq):
+        g = h // G
+        pc = [[] for _ in range(N)]
+        ps = [[] for _ in range(N)]
+        for i in rows:
+            s = [scale * _dot(q[h][i], k[g][j]) for j in range(i + 1)]
+            m = max(s)
+            z = math.fsum(math.exp(x - m) for x in s)
+            for j in range(i + 1):
+                p = math.exp(s[j] - m) / z
+                pc[j].append(p)
+                ps[i - j].append(p)
+        col = [math.fsum(x) / len(rows) for x in pc]
+        sl = [math.fsum(x) / len(rows) for x in ps]
+
+        def cut(mv):
+            if tau >= 1.0:
+                return set(range(N))
+            rest, chosen = list(range(N)), []
+            while rest and math.fsum(mv[x] for x in chosen) < tau:
+                best = max(rest, key=lambda x: (mv[x], -x))
+                chosen.append(best)
+                rest.remove(best)
+            return set(chosen)
+        cs, ss = cut(col), cut(sl)
+        for I in range(NB):
+            lst = []
+            for J in range(I + 1):
+                keep = (force_diag and J == I) or (force_first and J == 0)
+                for i in range(I * B, min((I + 1) * B, N)):
+                    for j in range(J * B, min((J + 1) * B, N)):
+                        if j <= i and (j in cs or (i - j) in ss):
+                            keep = True
+                if keep:
+                    lst.append(J)
+            masks[(h, I)] = lst
+        cols.append(cs)
+        slashes.append(ss)
+        colm.append(col)
+        slm.append(sl)
+    return masks, cols, slashes, colm, slm

@@ -31,7 +31,11 @@ design notes of the repository):
   * S2O's query permutation scores each query against one guide vector per KV head, the mean key,
     averaged over the G query heads, and sorts each segment's positions by it (descending, ties by
     position); a permuted query block then needs the whole own segment in pass 1 under the
-    per-token causal mask, and its output rows go back to their natural positions.
+    per-token causal mask, and its output rows go back to their natural positions;
+  * SampleAttention's estimator samples the last rows of n_trunks equal chunks, takes the exact
+    causal softmax of those rows, averages it per key column and per diagonal offset, keeps for
+    each family separately the heaviest members up to the CIA mass target (the block_mask rule),
+    and keeps every tile that holds a kept column or that a kept diagonal crosses.
 """
 from __future__ import annotations
 
@@ -365,6 +369,110 @@ def s2o_gain_ratios(q: np.ndarray, k: np.ndarray, perm: Optional[np.ndarray], co
         r[[segment_of_block(J, B, S) >= sI for J in lst]] = np.nan
         out[(h, I)] = r
     return out
+
+
+# ----------------------------------------------------------------------------- SampleAttention estimator
+
+def trunk_rows(n: int, n_trunks: int, rows_per_trunk: int) -> np.ndarray:
+    """Query positions sampled by SampleAttention's trunk sampling (Technical Deep Dive, Stage 1:
+    queries are sampled from chunks spread over the whole sequence, not from one place).
+
+    Reading: the sequence is cut into n_trunks chunks of C = ceil(n / n_trunks) positions and the
+    last rows_per_trunk positions of every chunk are sampled (the rows of a chunk that see its whole
+    causal prefix).  Every chunk must hold at least rows_per_trunk positions."""
+    C = -(-n // n_trunks)
+    rows = []
+    for t in range(n_trunks):
+        end = min((t + 1) * C, n)
+        if end - rows_per_trunk < t * C:
+            raise ValueError("a trunk holds fewer positions than rows_per_trunk")
+        rows.extend(range(end - rows_per_trunk, end))
+    return np.asarray(rows, dtype=np.int64)
+
+
+def sampled_masses(q: np.ndarray, k: np.ndarray, n_trunks: int, rows_per_trunk: int,
+                   scale: Optional[float] = None):
+    """(col [Hq][N], slash [Hq][N]) from the exact causal softmax rows of the sampled queries.
+
+    SampleAttention, Technical Deep Dive: stage 1 estimates the attention scores from the sampled
+    rows; stage 2 looks for key columns and slashes (diagonals) that hold the attention mass.
+    col[h][j] is the mean over the sampled rows i of head h of p_ij; slash[h][delta] the mean of
+    p_{i, i-delta} (zero where delta > i).  Each sums to 1 over its index."""
+    Hq, N, d = q.shape
+    G = Hq // k.shape[0]
+    c = default_scale(d) if scale is None else scale
+    rows = trunk_rows(N, n_trunks, rows_per_trunk)
+    R = len(rows)
+    col = np.zeros((Hq, N))
+    slash = np.zeros((Hq, N))
+    j = np.arange(N)
+    for h in range(Hq):
+        s = c * (q[h, rows] @ k[h // G].T)
+        s = np.where(j[None, :] <= rows[:, None], s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        p = e / e.sum(axis=1, keepdims=True)
+        col[h] = p.sum(axis=0) / R
+        for r, i in enumerate(rows):
+            slash[h, :i + 1] += p[r, i::-1]            # delta = i - j for j = i, i-1, ..., 0
+        slash[h] /= R
+    return col, slash
+
+
+def _mass_cut(m: np.ndarray, tau: float) -> np.ndarray:
+    """Shortest prefix of the order (m descending, index ascending) whose running sum reaches tau,
+    as a boolean mask; every index when tau >= 1 or the sum stays below tau (the mass rule of
+    block_mask, applied to key columns or diagonals)."""
+    n = len(m)
+    if tau >= 1.0:
+        return np.ones(n, dtype=bool)
+    order = np.lexsort((np.arange(n), -m))
+    hit = np.nonzero(np.cumsum(m[order]) >= tau)[0]
+    keep = np.zeros(n, dtype=bool)
+    keep[order[:int(hit[0]) + 1] if hit.size else order] = True
+    return keep
+
+
+def sample_attention_mask(q: np.ndarray, k: np.ndarray, block_size: int, cia_tau: float, n_trunks: int,
+                          rows_per_trunk: int, force_diag: bool = True, force_first: bool = False,
+                          scale: Optional[float] = None):
+    """Block mask of SampleAttention's two stages (Technical Deep Dive).
+
+    Stage 1: sampled_masses.  Stage 2, decoupled filtering: the key columns and the slashes are
+    filtered separately, each family keeping the shortest set of its heaviest members whose mass
+    reaches the CIA target cia_tau (the mass every query should keep).  The block-level mask keeps
+    tile (I, J), J <= I, when it holds a kept column, when a kept slash crosses it (some i in I,
+    j in J, j <= i with i - j = delta), or when forced (J = I with force_diag, J = 0 with
+    force_first).
+
+    Returns (count [Hq][NB], idx [Hq][NB(NB+1)/2] ascending per row, col_keep [Hq][N],
+    slash_keep [Hq][N], col, slash)."""
+    Hq, N, d = q.shape
+    B = block_size
+    NB = num_blocks(N, B)
+    col, slash = sampled_masses(q, k, n_trunks, rows_per_trunk, scale)
+    count = np.zeros((Hq, NB), dtype=np.int64)
+    idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    col_keep = np.zeros((Hq, N), dtype=bool)
+    slash_keep = np.zeros((Hq, N), dtype=bool)
+    for h in range(Hq):
+        col_keep[h] = _mass_cut(col[h], cia_tau)
+        slash_keep[h] = _mass_cut(slash[h], cia_tau)
+        for I in range(NB):
+            qi = block_range(I, B, N)
+            lst = []
+            for J in range(I + 1):
+                kj = block_range(J, B, N)
+                keep = (force_diag and J == I) or (force_first and J == 0) or bool(col_keep[h, kj].any())
+                if not keep:
+                    lo = max(0, int(qi[0]) - int(kj[-1]))
+                    hi = int(qi[-1]) - int(kj[0])
+                    keep = bool(slash_keep[h, lo:hi + 1].any())
+                if keep:
+                    lst.append(J)
+            o = tri_offset(I)
+            count[h, I] = len(lst)
+            idx[h, o:o + len(lst)] = lst
+    return count, idx, col_keep, slash_keep, col, slash
 
 
 # ----------------------------------------------------------------------------- S2O prefix ranking

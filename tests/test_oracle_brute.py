@@ -182,3 +182,25 @@ def test_query_permutation_and_its_two_pass_stop_match_brute_force(c, gain_tau):
     out_b, lse_b = brute.attention_over_keys(q, k, v, keysets, B, scale, qorder=qorder)
     np.testing.assert_allclose(out, np.array(out_b, dtype=np.float64), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(lse, np.array(lse_b, dtype=np.float64), rtol=1e-12, atol=1e-12)
+
+
+@settings(max_examples=25, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case(), st.sampled_from([(1, 1), (2, 2), (3, 1), (4, 2)]), st.sampled_from([0.3, 0.6, 0.9, 1.0]))
+def test_sample_attention_mask_matches_brute_force(c, trunks, tau):
+    N, Hq, Hkv, d, B = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"]
+    nt, rpt = trunks
+    C = -(-N // nt)
+    if (nt - 1) * C + rpt > N:
+        return  # the sampling needs rpt positions in every trunk
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+    count, idx, ck, sk, col, sl = oracle.sample_attention_mask(q, k, B, tau, nt, rpt, c["diag"], c["first"])
+    masks_b, cols_b, sl_b, colm_b, slm_b = brute.sample_mask(q, k, B, tau, nt, rpt, c["diag"], c["first"], scale)
+    np.testing.assert_allclose(col, np.array(colm_b), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(sl, np.array(slm_b), rtol=1e-12, atol=1e-15)
+    for h in range(Hq):
+        assert set(np.nonzero(ck[h])[0].tolist()) == cols_b[h], h
+        assert set(np.nonzero(sk[h])[0].tolist()) == sl_b[h], h
+        for I in range(oracle.num_blocks(N, B)):
+            o = oracle.tri_offset(I)
+            assert idx[h, o:o + int(count[h, I])].tolist() == masks_b[(h, I)], (h, I)

@@ -528,3 +528,71 @@ def test_query_permutation_moves_rows_not_results():
     qperm = oracle.query_permutation(q, k, S)
     out, lse, _ = oracle.s2o_prefix_attention(q, k, v, pi, B, S, 0.1, qperm=qperm)
     assert not np.isnan(out).any() and not np.isnan(lse).any()
+
+
+# ----------------------------------------------------------------------------- SampleAttention
+
+def test_trunk_rows_closed_form():
+    assert oracle.trunk_rows(100, 4, 5).tolist() == (list(range(20, 25)) + list(range(45, 50))
+                                                     + list(range(70, 75)) + list(range(95, 100)))
+    assert oracle.trunk_rows(10, 3, 2).tolist() == [2, 3, 6, 7, 8, 9]   # chunks of 4, 4, 2
+    with pytest.raises(ValueError):
+        oracle.trunk_rows(10, 3, 3)                                   # the last trunk has 2 positions
+
+
+def test_sampled_masses_of_uniform_attention():
+    """Q = 0: every sampled row i spreads 1/(i+1) over keys 0..i, so col[j] = mean_i [j <= i]/(i+1)
+    and slash[delta] = mean_i [delta <= i]/(i+1)."""
+    N, Hq, Hkv, d = 64, 2, 1, 4
+    q = np.zeros((Hq, N, d))
+    k = np.random.default_rng(2).standard_normal((Hkv, N, d))
+    rows = oracle.trunk_rows(N, 4, 3)
+    col, slash = oracle.sampled_masses(q, k, 4, 3)
+    want = np.array([np.mean([(1.0 / (i + 1)) if x <= i else 0.0 for i in rows]) for x in range(N)])
+    np.testing.assert_allclose(col[0], want, rtol=1e-13, atol=1e-16)
+    np.testing.assert_allclose(slash[1], want, rtol=1e-13, atol=1e-16)   # the same formula in delta
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_sampled_masses_are_distributions(shape):
+    N, Hq, Hkv, d, B, S = shape
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=40)
+    col, slash = oracle.sampled_masses(q, k, 4, 2)
+    assert np.all(col >= 0) and np.all(slash >= 0)
+    np.testing.assert_allclose(col.sum(axis=1), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(slash.sum(axis=1), 1.0, rtol=1e-12)
+    last = oracle.trunk_rows(N, 4, 2).max()
+    assert np.all(col[:, last + 1:] == 0) and np.all(slash[:, last + 1:] == 0)
+
+
+def test_sample_attention_finds_a_planted_column_and_a_planted_slash():
+    N, Hq, Hkv, d, B = 128, 2, 1, 16, 16
+    rng = np.random.default_rng(4)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((Hq, N, d)) * 0.1
+    k = rng.standard_normal((Hkv, N, d)) * 0.1
+    # head 0: a strong column at key 37 (every query aligned with u)
+    q[0] += 4.0 * u
+    k[0, 37] += 4.0 * u
+    # head 1 shares the keys; give its queries a strong diagonal 5 back: q_i ~ k_{i-5}
+    q[1] = 0.1 * rng.standard_normal((N, d))
+    q[1, 5:] += 6.0 * k[0, :N - 5] / np.linalg.norm(k[0, :N - 5], axis=1, keepdims=True)
+    count, idx, ck, sk, col, slash = oracle.sample_attention_mask(q, k, B, 0.5, 4, 4)
+    assert np.argmax(col[0]) == 37 and ck[0, 37]
+    assert np.argmax(slash[1]) == 5 and sk[1, 5]
+    for I in range(N // B):
+        row = idx[0, oracle.tri_offset(I):oracle.tri_offset(I) + count[0, I]].tolist()
+        if I >= 37 // B:
+            assert 37 // B in row
+    # tile (3, 2) holds pairs i - j = 5 (i = 48, j = 43), tile (5, 2) does not (smallest i - j is 49)
+    row3 = idx[1, oracle.tri_offset(3):oracle.tri_offset(3) + count[1, 3]].tolist()
+    assert 2 in row3
+
+
+def test_sample_attention_full_target_keeps_every_tile():
+    N, Hq, Hkv, d, B = 96, 2, 1, 8, 8
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=41)
+    count, _, ck, sk, _, _ = oracle.sample_attention_mask(q, k, B, 1.0, 3, 4)
+    assert ck.all() and sk.all()
+    assert (count == np.arange(1, N // B + 1)[None, :]).all()
