@@ -29,6 +29,7 @@ __all__ = [
     "prefix_rank_length",
     "s2o_prefix_attn_prefill",
     "build_query_permutation",
+    "sample_attention_mask",
     "workspace_size",
     "make_shape",
     "num_blocks",
@@ -321,6 +322,43 @@ def s2o_prefix_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
     if return_error:
         res.append(err)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def sample_attention_mask(q: torch.Tensor, k: torch.Tensor, block_size: int, cia_tau: float, n_trunks: int,
+                          rows_per_trunk: int, force_diag: bool = True, force_first: bool = False,
+                          scale: Optional[float] = None, return_masses: bool = False,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """SampleAttention's block mask: (block_count int32 [Hq][NB], block_idx int32 [Hq][NB(NB+1)/2]
+    [, col fp64 [Hq][N], slash fp64 [Hq][N]]), for block_sparse_attn_prefill with perm = None."""
+    _check_bf16("q", q)
+    _check_bf16("k", k)
+    shape = make_shape(q, k, block_size, 0, scale)
+    Hq, N = q.shape[0], q.shape[1]
+    NB = num_blocks(N, block_size)
+    if out is None:
+        count = torch.empty((Hq, NB), dtype=torch.int32, device=q.device)
+        idx = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device=q.device)
+    else:
+        count, idx = out
+    col = torch.empty((Hq, N), dtype=torch.float64, device=q.device) if return_masses else None
+    slash = torch.empty((Hq, N), dtype=torch.float64, device=q.device) if return_masses else None
+    need = _lib.lib().pbsa_sample_mask_workspace_size(ctypes.byref(shape), int(n_trunks), int(rows_per_trunk))
+    if need == _lib.SIZE_MAX:
+        raise PbsaError(_lib.PBSA_ERR_INVALID_ARG, "pbsa_sample_mask_workspace_size")
+    ws, nbytes = None, 0
+    if need:
+        ws = workspace
+        if ws is None or ws.numel() * ws.element_size() < need + 256:
+            ws = torch.empty(need + 256, dtype=torch.uint8, device=q.device)
+        ws = ws[(-ws.data_ptr()) % 256:]
+        nbytes = ws.numel()
+    flags = (PBSA_FORCE_DIAG if force_diag else 0) | (PBSA_FORCE_FIRST if force_first else 0)
+    st = _lib.lib().pbsa_sample_attention_mask(ctypes.byref(shape), _ptr(q), _ptr(k), float(cia_tau), int(n_trunks),
+                                               int(rows_per_trunk), flags, _ptr(count), _ptr(idx), _ptr(col),
+                                               _ptr(slash), _ptr(ws), nbytes, _stream())
+    _lib.check(st, "pbsa_sample_attention_mask")
+    return (count, idx, col, slash) if return_masses else (count, idx)
 
 
 def tile_max(q: torch.Tensor, k: torch.Tensor, block_size: int, scale: Optional[float] = None) -> torch.Tensor:

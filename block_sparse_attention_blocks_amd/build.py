@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpbsa.so")
-SOURCES = ["api.hip", "estimate.hip", "prefix_rank.hip", "attention.hip"]
+SOURCES = ["api.hip", "estimate.hip", "prefix_rank.hip", "sample_attn.hip", "attention.hip"]
 # per-source extra flags.  attention.hip: no NaN is produced or tested there (masked scores are
 # -inf), so max and compare need no NaN quieting; api.hip validates arguments with comparisons
 # that must keep their NaN meaning and gets no such flag.

@@ -194,6 +194,47 @@ pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, co
                                              static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// Trunk sampling needs every one of the n_trunks chunks (ceil(N / n_trunks) positions each, the
+// last one shorter) to hold rows_per_trunk positions.
+bool trunks_ok(const Geometry& g, int n_trunks, int rpt) {
+  if (n_trunks < 1 || rpt < 1 || g.N < 1) return false;
+  const int64_t C = ((int64_t)g.N + n_trunks - 1) / n_trunks;
+  return (int64_t)(n_trunks - 1) * C + rpt <= g.N;
+}
+}  // namespace
+
+size_t pbsa_sample_mask_workspace_size(const pbsa_shape* shape, int32_t n_trunks, int32_t rows_per_trunk) {
+  Geometry g;
+  if (make_geometry(shape, &g) != PBSA_OK) return SIZE_MAX;
+  if (g.N == 0) return 0;
+  if (!trunks_ok(g, n_trunks, rows_per_trunk)) return SIZE_MAX;
+  return pbsa::sample_mask_workspace_bytes(g, n_trunks, rows_per_trunk);
+}
+
+pbsa_status pbsa_sample_attention_mask(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, double cia_tau,
+                                       int32_t n_trunks, int32_t rows_per_trunk, uint32_t flags,
+                                       int32_t* block_count, int32_t* block_idx, double* col_mass,
+                                       double* slash_mass, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pbsa_status st = make_geometry(shape, &g);
+  if (st != PBSA_OK) return st;
+  if (!q || !k || !block_count || !block_idx || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
+  if (!(cia_tau > 0.0 && cia_tau <= 1.0)) return PBSA_ERR_INVALID_ARG;
+  if (flags & ~(uint32_t)(PBSA_FORCE_DIAG | PBSA_FORCE_FIRST)) return PBSA_ERR_INVALID_ARG;
+  if ((col_mass && (reinterpret_cast<uintptr_t>(col_mass) & 7u)) ||
+      (slash_mass && (reinterpret_cast<uintptr_t>(slash_mass) & 7u)))
+    return PBSA_ERR_INVALID_ARG;
+  if (g.N == 0) return PBSA_OK;
+  if (!trunks_ok(g, n_trunks, rows_per_trunk)) return PBSA_ERR_INVALID_ARG;
+  if ((st = check_workspace(pbsa::sample_mask_workspace_bytes(g, n_trunks, rows_per_trunk), workspace,
+                            workspace_bytes)) != PBSA_OK)
+    return st;
+  return from_hip(pbsa::launch_sample_mask(g, q, k, cia_tau, n_trunks, rows_per_trunk, flags, block_count,
+                                           block_idx, col_mass, slash_mass, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 pbsa_status pbsa_build_query_permutation(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
                                          int32_t* qperm, void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;

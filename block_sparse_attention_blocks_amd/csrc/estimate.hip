@@ -79,12 +79,22 @@ struct ImpArgs {
   int N, G, d, R1, R;
   int64_t qsh, qst, kvsh, kvst;
   double scale;
+  int trunk_c;    // 0: proxy rows are the last R1 positions; > 0: trunk-sampled rows (chunk length)
+  int rpt;        // trunk sampling: rows per trunk
+  int first_row;  // smallest proxy position (every key j <= first_row is visible to every proxy row)
 };
 
-// Proxy row r of KV head g -> (query head, token position).
+// Proxy row r of KV head g -> (query head, token position): the last R1 positions, or with trunk
+// sampling the last rpt positions of every trunk of trunk_c positions.
 __device__ __forceinline__ void imp_row(const ImpArgs& a, int g, int r, int* h, int* i) {
   *h = g * a.G + r / a.R1;
-  *i = a.N - a.R1 + r % a.R1;
+  const int r1 = r % a.R1;
+  if (a.trunk_c > 0) {
+    const int t = r1 / a.rpt;
+    *i = min((t + 1) * a.trunk_c, a.N) - a.rpt + r1 % a.rpt;
+  } else {
+    *i = a.N - a.R1 + r1;
+  }
 }
 
 // DPP row rotation of a double (16-lane rows): all-reduce helpers for the 16 lanes of one row.
@@ -191,7 +201,7 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
     imp_row(a, g, r, &h, &i);
     qi[rr] = r < a.R ? i : -1;
   }
-  const int first_proxy = a.N - a.R1;  // every key j <= first_proxy is visible to every proxy row
+  const int first_proxy = a.first_row;  // every key j <= first_proxy is visible to every proxy row
 
   auto prefetch = [&](int c, u32x4* pf) {
     const int j0 = c * IMP_CK;
@@ -384,6 +394,9 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
   a.kvsh = g.kvsh;
   a.kvst = g.kvst;
   a.scale = g.scale64;
+  a.trunk_c = 0;
+  a.rpt = 0;
+  a.first_row = g.N - a.R1;
   const int nchunk = imp_chunks(g);
   const dim3 grid((a.R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
   if (g.d == 128) {
@@ -449,6 +462,54 @@ __global__ __launch_bounds__(SORT_THREADS) void segment_sort_kernel(const double
     }
   }
   for (int x = t; x < L; x += SORT_THREADS) perm[(size_t)g * N + a + x] = a + (int)off[x];
+}
+
+// Exact causal softmax rows of trunk-sampled queries (SampleAttention, stage 1): the importance
+// kernels with the trunk row map; per KV head its G * n_trunks * rpt rows, head-major.
+size_t sampled_softmax_workspace_bytes(const Geometry& g, int n_trunks, int rpt) {
+  const size_t R = (size_t)g.G * n_trunks * rpt, C = imp_chunks(g);
+  return align256(sizeof(double) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
+         align256(sizeof(double) * g.Hkv * R);
+}
+
+hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const uint16_t* k, int n_trunks, int rpt,
+                                  void* ws, SampledRows* out, hipStream_t st) {
+  const int R = g.G * n_trunks * rpt, nchunk = imp_chunks(g);
+  char* p = static_cast<char*>(ws);
+  out->e = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * (size_t)R * g.N);
+  out->part_m = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * (size_t)nchunk * R);
+  double* part_l = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * (size_t)nchunk * R);
+  out->lse = reinterpret_cast<double*>(p);
+  out->R = R;
+  out->nchunk = nchunk;
+  ImpArgs a;
+  a.q = q;
+  a.k = k;
+  a.N = g.N;
+  a.G = g.G;
+  a.d = g.d;
+  a.R1 = n_trunks * rpt;
+  a.R = R;
+  a.qsh = g.qsh;
+  a.qst = g.qst;
+  a.kvsh = g.kvsh;
+  a.kvst = g.kvst;
+  a.scale = g.scale64;
+  a.trunk_c = (g.N + n_trunks - 1) / n_trunks;
+  a.rpt = rpt;
+  a.first_row = min(a.trunk_c, g.N) - rpt;
+  const dim3 grid((R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
+  if (g.d == 128) {
+    imp_scores_kernel<128><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
+  } else {
+    imp_scores_kernel<64><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
+  }
+  imp_lse_kernel<<<dim3((R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(out->part_m, part_l, nchunk, R,
+                                                                             out->lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_segment_sort(const Geometry& g, const double* score, int32_t* perm, hipStream_t st) {

@@ -278,6 +278,39 @@ pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * SampleAttention's block mask (SampleAttention, Technical Deep Dive: stage 1 trunk sampling,
+ * stage 2 score-based filtering with decoupled filtering, a block-level mask).
+ *
+ * Stage 1: the sequence is cut into n_trunks chunks of C = ceil(N / n_trunks) positions; the last
+ * rows_per_trunk positions of each are the sampled queries of every query head.  Their exact causal
+ * softmax rows are computed in fp64; col[h][j] is the mean over head h's sampled rows of p_ij and
+ * slash[h][dlt] the mean of p_{i, i-dlt} (each sums to 1).  Stage 2: the columns and the slashes are
+ * cut separately, each keeping the shortest prefix of (mass descending, index ascending) whose sum
+ * reaches cia_tau (every index if cia_tau >= 1 or the sum stays below it).  Tile (I, J), J <= I, is
+ * kept when block J holds a kept column, when a kept slash offset is realised by some pair of the
+ * tile (i in I, j in J, j <= i, i - j = dlt), with PBSA_FORCE_DIAG for J = I and with
+ * PBSA_FORCE_FIRST for J = 0.  Keys stay in natural order (perm = NULL for the attention call).
+ *
+ *   cia_tau        in (0, 1]
+ *   n_trunks, rows_per_trunk  >= 1, and every chunk must hold rows_per_trunk positions
+ *   block_count    out, int32 [Hq][NB]
+ *   block_idx      out, int32 [Hq][NB(NB+1)/2], ascending J per row at I(I+1)/2
+ *   col_mass, slash_mass  out, fp64 [Hq][N] each, or NULL
+ *   workspace      >= pbsa_sample_mask_workspace_size(shape, n_trunks, rows_per_trunk) bytes,
+ *                  256-byte aligned (it holds the sampled rows' exponentials: Hkv * G * n_trunks *
+ *                  rows_per_trunk * N doubles)
+ */
+pbsa_status pbsa_sample_attention_mask(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                       double cia_tau, int32_t n_trunks, int32_t rows_per_trunk,
+                                       uint32_t flags, int32_t* block_count, int32_t* block_idx,
+                                       double* col_mass, double* slash_mass, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of pbsa_sample_attention_mask (0 when N = 0; SIZE_MAX for an invalid shape or
+ * sampling).  Host-only. */
+size_t pbsa_sample_mask_workspace_size(const pbsa_shape* shape, int32_t n_trunks, int32_t rows_per_trunk);
+
+/*
  * Early-stop calibration helper (Block Sparse Flash Attention, Approach: offline thresholds).
  * tile_max[h][I(I+1)/2 + J] = c * max over i in block I, j in block J, j <= i of q_i . k_j for
  * every J <= I, natural order, computed like stage 3's gate (fp32 accumulation).

@@ -19,6 +19,8 @@ from .pbsa_oracle import (  # noqa: F401
     kept_bitmap,
     key_importance,
     key_rows_of_block,
+    mask_from_patterns,
+    mass_cut,
     num_blocks,
     num_segments,
     pool_blocks,

@@ -418,7 +418,7 @@ def sampled_masses(q: np.ndarray, k: np.ndarray, n_trunks: int, rows_per_trunk: 
     return col, slash
 
 
-def _mass_cut(m: np.ndarray, tau: float) -> np.ndarray:
+def mass_cut(m: np.ndarray, tau: float) -> np.ndarray:
     """Shortest prefix of the order (m descending, index ascending) whose running sum reaches tau,
     as a boolean mask; every index when tau >= 1 or the sum stays below tau (the mass rule of
     block_mask, applied to key columns or diagonals)."""
@@ -450,13 +450,23 @@ def sample_attention_mask(q: np.ndarray, k: np.ndarray, block_size: int, cia_tau
     B = block_size
     NB = num_blocks(N, B)
     col, slash = sampled_masses(q, k, n_trunks, rows_per_trunk, scale)
+    col_keep = np.stack([mass_cut(col[h], cia_tau) for h in range(Hq)])
+    slash_keep = np.stack([mass_cut(slash[h], cia_tau) for h in range(Hq)])
+    count, idx = mask_from_patterns(col_keep, slash_keep, B, force_diag, force_first)
+    return count, idx, col_keep, slash_keep, col, slash
+
+
+def mask_from_patterns(col_keep: np.ndarray, slash_keep: np.ndarray, block_size: int, force_diag: bool = True,
+                       force_first: bool = False):
+    """Block mask of kept key columns and slashes ([Hq][N] booleans): tile (I, J), J <= I, kept when
+    block J holds a kept column, when a kept offset lies in the tile's range of i - j, or when
+    forced.  Returns (count, idx) as block_mask does."""
+    Hq, N = col_keep.shape
+    B = block_size
+    NB = num_blocks(N, B)
     count = np.zeros((Hq, NB), dtype=np.int64)
     idx = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
-    col_keep = np.zeros((Hq, N), dtype=bool)
-    slash_keep = np.zeros((Hq, N), dtype=bool)
     for h in range(Hq):
-        col_keep[h] = _mass_cut(col[h], cia_tau)
-        slash_keep[h] = _mass_cut(slash[h], cia_tau)
         for I in range(NB):
             qi = block_range(I, B, N)
             lst = []
@@ -472,7 +482,7 @@ def sample_attention_mask(q: np.ndarray, k: np.ndarray, block_size: int, cia_tau
             o = tri_offset(I)
             count[h, I] = len(lst)
             idx[h, o:o + len(lst)] = lst
-    return count, idx, col_keep, slash_keep, col, slash
+    return count, idx
 
 
 # ----------------------------------------------------------------------------- S2O prefix ranking

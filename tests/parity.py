@@ -13,6 +13,10 @@ Tie rules, used wherever a floating-point comparison decides an integer result:
   * historical ranking (S2O prefix order): the GPU ranks fp32-rounded scores; a rank where GPU and
     oracle list different keys is a recorded tie iff the two keys' oracle scores differ by at most
     1e-6 relative;
+  * SampleAttention mask: the GPU's fp64 column / slash masses must match the oracle's to 1e-10
+    relative; a kept column or slash set may differ from the one the oracle's masses give only by
+    members whose mass is within 1e-6 of the cut mass, or when the cumulative mass at the cut is
+    within 1e-6 of the target; the GPU's mask must equal the tiles of the sets its own masses give;
   * marginal-gain stop: the kernel forms dl_i / l_i from bf16-rounded probabilities (each off by
     at most 2^-9 relative, so the ratio by under 0.4%); a stop or a go-on must agree with the
     oracle's exact ratio wherever that ratio is more than S2O_BAND (relative) from gain_tau.
@@ -173,6 +177,44 @@ def bitmap_to_kept_square(bm: np.ndarray, NB: int):
         for I in range(NB):
             kept[(h, I)] = [J for J in range(NB) if (bm[h, (I * NB + J) // 32] >> np.uint32((I * NB + J) % 32)) & 1]
     return kept
+
+
+def _cut_is_near_tie(m: np.ndarray, tau: float, a: np.ndarray, b: np.ndarray) -> bool:
+    """Whether two kept sets of the mass cut over m may differ by rounding: every differing member
+    has a mass within TIE of the cut mass, or the running sum at the cut is within TIE of tau."""
+    n = len(m)
+    order = np.lexsort((np.arange(n), -m))
+    cs = np.cumsum(m[order])
+    hit = np.nonzero(cs >= tau)[0]
+    kstar = int(hit[0]) + 1 if (tau < 1.0 and hit.size) else n
+    cut_mass = m[order[kstar - 1]]
+    diff = np.nonzero(a != b)[0]
+    near_m = np.all(np.abs(m[diff] - cut_mass) <= TIE)
+    near_c = abs(cs[kstar - 1] - tau) <= TIE or (kstar >= 2 and abs(cs[kstar - 2] - tau) <= TIE)
+    return bool(near_m or near_c)
+
+
+def compare_sample_mask(count_g, idx_g, col_g, slash_g, col_o, slash_o, tau: float, B: int, force_diag: bool,
+                        force_first: bool) -> int:
+    """Assert the GPU SampleAttention mask against the oracle (rules above); return the tie count."""
+    np.testing.assert_allclose(col_g, col_o, rtol=1e-10, atol=1e-300)
+    np.testing.assert_allclose(slash_g, slash_o, rtol=1e-10, atol=1e-300)
+    Hq = col_o.shape[0]
+    ck_g = np.stack([oracle.mass_cut(col_g[h], tau) for h in range(Hq)])
+    sk_g = np.stack([oracle.mass_cut(slash_g[h], tau) for h in range(Hq)])
+    ties = 0
+    for h in range(Hq):
+        for keep_g, m in ((ck_g[h], col_o[h]), (sk_g[h], slash_o[h])):
+            keep_o = oracle.mass_cut(m, tau)
+            if not np.array_equal(keep_g, keep_o):
+                assert _cut_is_near_tie(m, tau, keep_g, keep_o), f"head {h}: kept pattern set differs beyond ties"
+                ties += 1
+    count_w, idx_w = oracle.mask_from_patterns(ck_g, sk_g, B, force_diag, force_first)
+    assert np.array_equal(count_g, count_w), "mask counts differ from the GPU masses' patterns"
+    for h in range(Hq):
+        for I in range(count_w.shape[1]):
+            assert _row(idx_g, count_g, h, I) == _row(idx_w, count_w, h, I), f"mask row ({h},{I})"
+    return ties
 
 
 def compare_out(out_g: np.ndarray, out_o: np.ndarray, what: str = "out"):

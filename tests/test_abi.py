@@ -257,3 +257,30 @@ def test_query_permutation_entry_validates_before_launch():
     assert qp(ctypes.byref(s), None, FAKE, FAKE, ws, big, None) == E
     assert qp(ctypes.byref(s), FAKE, FAKE, FAKE, None, 0, None) == W
     assert qp(ctypes.byref(shape(N=0)), FAKE, FAKE, FAKE, None, 0, None) == 0
+
+
+def test_sample_attention_entry_validates_before_launch():
+    l = _lib.lib()
+    E, W = _lib.PBSA_ERR_INVALID_ARG, _lib.PBSA_ERR_WORKSPACE
+    s = shape(N=1000, S=0)
+    ws = ctypes.c_void_p(0x10000)
+    big = 1 << 40
+    size = l.pbsa_sample_mask_workspace_size
+    assert size(ctypes.byref(s), 4, 8) not in (0, _lib.SIZE_MAX)
+    assert size(ctypes.byref(s), 0, 8) == _lib.SIZE_MAX
+    assert size(ctypes.byref(s), 4, 0) == _lib.SIZE_MAX
+    assert size(ctypes.byref(s), 3, 334) == _lib.SIZE_MAX      # chunks of 334: the last holds 332
+    assert size(ctypes.byref(s), 3, 332) != _lib.SIZE_MAX
+    assert size(ctypes.byref(shape(N=0)), 4, 8) == 0
+    m = l.pbsa_sample_attention_mask
+    args = lambda sh, tau, nt, rpt, fl=1, w=ws: (ctypes.byref(sh), FAKE, FAKE, tau, nt, rpt, fl, FAKE, FAKE, None, None,
+                                                 w, big if w else 0, None)
+    assert m(*args(s, 0.0, 4, 8)) == E
+    assert m(*args(s, 1.5, 4, 8)) == E
+    assert m(*args(s, float("nan"), 4, 8)) == E
+    assert m(*args(s, 0.9, 0, 8)) == E
+    assert m(*args(s, 0.9, 3, 334)) == E
+    assert m(*args(s, 0.9, 4, 8, fl=4)) == E                   # ranked flag not accepted here
+    assert m(*args(s, 0.9, 4, 8, w=None)) == W
+    assert m(*args(shape(N=0), 0.9, 4, 8, w=None)) == 0
+    assert m(ctypes.byref(s), FAKE, FAKE, 0.9, 4, 8, 1, None, FAKE, None, None, ws, big, None) == E

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 from parity import (bitmap_to_kept, bitmap_to_kept_square, compare_lse, compare_mask, compare_out, compare_perm,
-                    compare_prefix_rank, compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
+                    compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask, kept_to_mask,
+                    two_pass_lists)
 from workloads import bf16_bits_to_f32, generate
 
 pytestmark = pytest.mark.gpu
@@ -590,3 +591,43 @@ def test_query_permuted_two_pass_zero_threshold_is_dense_and_flags_bad_entries()
     torch.cuda.synchronize()
     assert int(err.item()) & 8
     assert torch.isfinite(out2[:, :100]).all()
+
+
+# SampleAttention mask: (name, N, Hq, Hkv, d, B, stripes, band, cia_tau, n_trunks, rows_per_trunk, seed)
+SAMPLE_CASES = [
+    ("gqa_b128_d128_2048", 2048, 4, 2, 128, 128, 16, 256, 0.9, 4, 16, 71),
+    ("ragged_b64_d64_1500", 1500, 2, 1, 64, 64, 8, 128, 0.6, 3, 8, 72),
+    ("flat_b128_d64_ragged_3000", 3000, 4, 4, 64, 128, 0, 256, 0.95, 8, 4, 73),
+    ("one_trunk_b64_d128_777", 777, 2, 2, 128, 64, 8, 64, 0.8, 1, 32, 74),
+]
+
+
+@pytest.mark.parametrize("case", SAMPLE_CASES, ids=[c[0] for c in SAMPLE_CASES])
+def test_sample_attention_mask_and_attention(case):
+    pbsa = _need_gpu()
+    name, N, Hq, Hkv, d, B, stripes, band, tau, nt, rpt, seed = case
+    _log(f"[parity] sample {name}: N={N} Hq={Hq} Hkv={Hkv} d={d} B={B} tau={tau} trunks={nt}x{rpt}")
+    dev, host = _inputs(N, Hq, Hkv, d, stripes, band, seed)
+    q, k, v = host["q"], host["k"], host["v"]
+    count_t, idx_t, col_t, sl_t = pbsa.sample_attention_mask(dev["q"], dev["k"], B, tau, nt, rpt, return_masses=True)
+    torch.cuda.synchronize()
+    cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+    _, _, _, _, col_o, sl_o = oracle.sample_attention_mask(q, k, B, tau, nt, rpt)
+    ties = compare_sample_mask(cg, ig, col_t.cpu().numpy(), sl_t.cpu().numpy(), col_o, sl_o, tau, B, True, False)
+    out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], None, count_t, idx_t, B, 0)
+    torch.cuda.synchronize()
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, cg, ig, B, None)
+    mx, mean = compare_out(out_t.cpu().numpy(), out_o, "sample mask attention")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    NB = oracle.num_blocks(N, B)
+    _log(f"[parity] sample {name}: ties {ties}, density {cg.sum() / (Hq * NB * (NB + 1) / 2):.3f}, "
+         f"max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+def test_sample_attention_full_target_is_dense():
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B = 1024, 2, 1, 128, 128
+    dev, host = _inputs(N, Hq, Hkv, d, 8, 128, 75)
+    count, idx = pbsa.sample_attention_mask(dev["q"], dev["k"], B, 1.0, 4, 8, force_diag=False)
+    torch.cuda.synchronize()
+    assert (count.cpu().numpy() == np.arange(1, N // B + 1)[None, :]).all()
