@@ -260,6 +260,8 @@ def suite(args) -> int:
         suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=True)
     if "qperm" in parts:
         suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=True, qperm=True)
+    if "sample" in parts:
+        suite_sample(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
     out_f.close()
     return 0
 
@@ -435,6 +437,39 @@ def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pa
         torch.cuda.empty_cache()
 
 
+def suite_sample(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
+    """SampleAttention's mask (8 trunks of 16 sampled rows per query head) at 32K and 128K for a few
+    CIA targets: estimator time, mask density and attention time on the mask against dense."""
+    nt, rpt = 8, 16
+    for name in ("llama8b_32k", "llama8b_128k"):
+        w = WORKLOADS[name]
+        d = load(w)
+        q, k, v = d["q"], d["k"], d["v"]
+        B, NB, Hq = w.block_size, w.num_blocks, w.num_q_heads
+        causal_tiles = Hq * NB * (NB + 1) // 2
+        ws = torch.empty(pbsa.sample_mask_workspace_size(q, k, B, nt, rpt) + 256, dtype=torch.uint8, device="cuda")
+        count = torch.empty((Hq, NB), dtype=torch.int32, device="cuda")
+        idx = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device="cuda")
+        out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
+        lse = torch.empty((Hq, w.seq_len), dtype=torch.float32, device="cuda")
+        dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, out=out, lse=lse)
+        t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+        for tau in (0.5, 0.8, 0.95):
+            fm = lambda: pbsa.sample_attention_mask(q, k, B, tau, nt, rpt, out=(count, idx), workspace=ws)
+            t_mask = _events(torch, stream, fm, reps)["median_ms"]
+            fm()
+            fa = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, count, idx, B, 0, out=out, lse=lse)
+            ta = _events(torch, stream, fa, reps)["median_ms"]
+            tiles = int(count.sum().item())
+            emit({"workload": w.name, "estimator": f"SampleAttention, {nt} trunks x {rpt} rows", "cia_tau": tau,
+                  "block_density": tiles / causal_tiles, "mask_ms": t_mask, "attention_ms": ta,
+                  "dense_kernel_ms": t_dense, "attention_speedup_vs_dense": t_dense / ta,
+                  "step_speedup_vs_dense": t_dense / (t_mask + ta),
+                  "attention_mfma_frac": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+        del d, q, k, v, out, lse, ws, count, idx
+        torch.cuda.empty_cache()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -454,8 +489,8 @@ def main() -> int:
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
     ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
-    ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o,twopass,qperm",
-                    help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass, qperm")
+    ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o,twopass,qperm,sample",
+                    help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass, qperm, sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "

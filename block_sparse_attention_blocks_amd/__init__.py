@@ -30,6 +30,7 @@ __all__ = [
     "s2o_prefix_attn_prefill",
     "build_query_permutation",
     "sample_attention_mask",
+    "sample_mask_workspace_size",
     "workspace_size",
     "make_shape",
     "num_blocks",
@@ -324,6 +325,16 @@ def s2o_prefix_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
     return res[0] if len(res) == 1 else tuple(res)
 
 
+def sample_mask_workspace_size(q: torch.Tensor, k: torch.Tensor, block_size: int, n_trunks: int,
+                               rows_per_trunk: int) -> int:
+    """Workspace bytes of sample_attention_mask for this shape and sampling."""
+    shape = make_shape(q, k, block_size, 0)
+    need = _lib.lib().pbsa_sample_mask_workspace_size(ctypes.byref(shape), int(n_trunks), int(rows_per_trunk))
+    if need == _lib.SIZE_MAX:
+        raise PbsaError(_lib.PBSA_ERR_INVALID_ARG, "pbsa_sample_mask_workspace_size")
+    return need
+
+
 def sample_attention_mask(q: torch.Tensor, k: torch.Tensor, block_size: int, cia_tau: float, n_trunks: int,
                           rows_per_trunk: int, force_diag: bool = True, force_first: bool = False,
                           scale: Optional[float] = None, return_masses: bool = False,
@@ -343,9 +354,7 @@ def sample_attention_mask(q: torch.Tensor, k: torch.Tensor, block_size: int, cia
         count, idx = out
     col = torch.empty((Hq, N), dtype=torch.float64, device=q.device) if return_masses else None
     slash = torch.empty((Hq, N), dtype=torch.float64, device=q.device) if return_masses else None
-    need = _lib.lib().pbsa_sample_mask_workspace_size(ctypes.byref(shape), int(n_trunks), int(rows_per_trunk))
-    if need == _lib.SIZE_MAX:
-        raise PbsaError(_lib.PBSA_ERR_INVALID_ARG, "pbsa_sample_mask_workspace_size")
+    need = sample_mask_workspace_size(q, k, block_size, n_trunks, rows_per_trunk)
     ws, nbytes = None, 0
     if need:
         ws = workspace

@@ -98,20 +98,6 @@ __global__ __launch_bounds__(SA_THREADS) void sa_slash_kernel(MassArgs a, double
   slash[(size_t)h * a.N + dlt] = s / (double)a.R1;
 }
 
-// Sum over the workgroup, in a fixed order (each wave's lanes by xor-butterfly, then the waves in
-// order), so every probe of the same values gives the same result.
-__device__ __forceinline__ double block_sum_f64(double x, double* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  __syncthreads();
-  if (lane == 0) wsum[wave] = x;
-  __syncthreads();
-  double s = 0.0;
-  for (int v = 0; v < CUT_THREADS / 64; ++v) s += wsum[v];
-  return s;
-}
-
 __device__ __forceinline__ int block_exclusive_count(int x, int* wcnt, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = x;
@@ -134,44 +120,102 @@ __device__ __forceinline__ int block_exclusive_count(int x, int* wcnt, int* tota
 
 // The mass cut of one head and family (blockIdx.y: 0 columns, 1 slashes): the kept set is the
 // shortest prefix of the order (mass descending, index ascending) whose sum reaches tau.  With
-// S(t) = sum of the masses >= t, the cut value t* = max{t : S(t) >= tau} is found by bisection
-// over the bit patterns of non-negative doubles (which order like the values); masses > t* are
-// kept, and of those equal to t* the first k in index order, k the fewest with
-// S(> t*) + k t* >= tau.  Every index is kept when tau >= 1 or when the total stays below tau.
-// Thread t owns the contiguous index range [t*L, t*L + L).
+// S(t) = sum of the masses >= t (a fixed-order workgroup sum), the cut value t* = max{t : S(t) >=
+// tau} is searched over the bit patterns of non-negative doubles (which order like the values),
+// CUT_WAYS-ary: each pass evaluates S at CUT_WAYS evenly spaced patterns inside the current bracket and
+// keeps the sub-bracket where S crosses tau.  Masses > t* are kept, and of those equal to t* the
+// first k in index order, k the fewest with S(> t*) + k t* >= tau.  Every index is kept when
+// tau >= 1 or when the total stays below tau.  The sums read the masses striped over the threads;
+// the final pass, which needs index order among equal masses, gives thread t the range
+// [t*L, t*L + L).
+constexpr int CUT_WAYS = 4;
+constexpr int CUT_BATCH = 8;  // loads in flight per thread in a pass
 __global__ __launch_bounds__(CUT_THREADS) void sa_cut_kernel(const double* col, const double* slash, int N, int Hq,
                                                              double tau, uint8_t* keep) {
-  __shared__ double wsum[CUT_THREADS / 64];
+  __shared__ double wsum[CUT_WAYS][CUT_THREADS / 64];
   __shared__ int wcnt[CUT_THREADS / 64];
   const int h = blockIdx.x, fam = blockIdx.y, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const double* m = (fam == 0 ? col : slash) + (size_t)h * N;
   uint8_t* kp = keep + ((size_t)fam * Hq + h) * N;
   const int L = (N + CUT_THREADS - 1) / CUT_THREADS;
   const int b = min(t * L, N), e = min(b + L, N);
-  auto mass_from = [&](double thr) {
-    double s = 0.0;
-    for (int x = b; x < e; ++x) {
-      const double v = m[x];
-      if (v >= thr) s += v;
+  // One pass: S at the patterns c_w = lo + (w + 1) step, w < CUT_WAYS (a pattern >= hi stands for
+  // +inf, where S = 0).  Returns the last w with S(c_w) >= tau, or -1; the same on every thread.
+  auto search_pass = [&](uint64_t lo, uint64_t step, uint64_t hi) -> int {
+    double thr[CUT_WAYS], part[CUT_WAYS];
+#pragma unroll
+    for (int w = 0; w < CUT_WAYS; ++w) {
+      const uint64_t c = lo + (uint64_t)(w + 1) * step;
+      thr[w] = c < hi ? __longlong_as_double((long long)c) : INFINITY;
+      part[w] = 0.0;
     }
-    return block_sum_f64(s, wsum);
+    // striped (coalesced) and in a fixed order; CUT_BATCH loads are issued before any is used
+    for (int x0 = t; x0 < N; x0 += CUT_BATCH * CUT_THREADS) {
+      double v[CUT_BATCH];
+#pragma unroll
+      for (int u = 0; u < CUT_BATCH; ++u) v[u] = x0 + u * CUT_THREADS < N ? m[x0 + u * CUT_THREADS] : -1.0;
+#pragma unroll
+      for (int u = 0; u < CUT_BATCH; ++u)
+#pragma unroll
+        for (int w = 0; w < CUT_WAYS; ++w) part[w] += v[u] >= thr[w] ? v[u] : 0.0;
+    }
+#pragma unroll
+    for (int w = 0; w < CUT_WAYS; ++w)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) part[w] += __shfl_xor(part[w], o, 64);
+    __syncthreads();  // the previous pass has read wsum
+    if (lane == 0)
+#pragma unroll
+      for (int w = 0; w < CUT_WAYS; ++w) wsum[w][wave] = part[w];
+    __syncthreads();
+    int best = -1;
+#pragma unroll
+    for (int w = 0; w < CUT_WAYS; ++w) {
+      double sw = 0.0;
+      for (int v = 0; v < CUT_THREADS / 64; ++v) sw += wsum[w][v];
+      if (sw >= tau) best = w;
+    }
+    return best;
   };
-  bool all = tau >= 1.0;
-  if (!all) all = !(mass_from(0.0) >= tau);
+  // every index when tau >= 1 or when the total S(+0) stays below tau (the bracket lo = -1 (wrapped),
+  // step 1, hi = 1 evaluates c_0 = +0 alone)
+  const bool all = tau >= 1.0 || search_pass(~0ull, 1, 1) < 0;
   if (all) {
     for (int x = b; x < e; ++x) kp[x] = 1;
     return;
   }
   uint64_t lo = 0, hi = 0x7ff0000000000000ull;  // S(+0) >= tau > S(+inf) = 0
   while (hi - lo > 1) {
-    const uint64_t mid = lo + (hi - lo) / 2;
-    if (mass_from(__longlong_as_double((long long)mid)) >= tau)
-      lo = mid;
-    else
-      hi = mid;
+    const uint64_t step = (hi - lo + CUT_WAYS) / (CUT_WAYS + 1);  // >= 1
+    const int best = search_pass(lo, step, hi);
+    const uint64_t nlo = best < 0 ? lo : lo + (uint64_t)(best + 1) * step;
+    const uint64_t cn = lo + (uint64_t)(best + 2) * step;  // next candidate above the best
+    const uint64_t nhi = (best + 1 < CUT_WAYS && cn < hi) ? cn : hi;
+    lo = nlo;
+    hi = nhi;
   }
   const double ts = __longlong_as_double((long long)lo);
-  const double above = mass_from(__longlong_as_double((long long)hi));  // S(> t*)
+  // S(> t*) = S(hi)
+  double above;
+  {
+    double part = 0.0;
+    const double th = __longlong_as_double((long long)hi);
+    for (int x0 = t; x0 < N; x0 += CUT_BATCH * CUT_THREADS) {
+      double v[CUT_BATCH];
+#pragma unroll
+      for (int u = 0; u < CUT_BATCH; ++u) v[u] = x0 + u * CUT_THREADS < N ? m[x0 + u * CUT_THREADS] : -1.0;
+#pragma unroll
+      for (int u = 0; u < CUT_BATCH; ++u) part += v[u] >= th ? v[u] : 0.0;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+    __syncthreads();
+    if (lane == 0) wsum[0][wave] = part;
+    __syncthreads();
+    above = 0.0;
+    for (int v = 0; v < CUT_THREADS / 64; ++v) above += wsum[0][v];
+  }
   int eq = 0;
   for (int x = b; x < e; ++x) eq += m[x] == ts;
   int total;  // values equal to t*

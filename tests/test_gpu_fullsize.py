@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 from parity import (bitmap_to_kept, bitmap_to_kept_square, compare_lse, compare_mask, compare_out, compare_perm,
-                    compare_prefix_rank, compare_ranked, compare_s2o_stops, kept_to_mask, two_pass_lists)
+                    compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask, kept_to_mask,
+                    two_pass_lists)
 from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
 
 pytestmark = pytest.mark.gpu
@@ -245,3 +246,27 @@ def test_fullsize_32k_query_permuted_two_pass_sampled():
     mx, mean = compare_out(np.where(ok, out_t.cpu().numpy(), np.nan), out_o, "qperm two-pass 32K")
     compare_lse(lse_t.cpu().numpy(), lse_o)
     _log(f"[fullsize] 32K query-permuted two-pass: sampled rows {rows} ({near} in band): max abs {mx:.2e} mean {mean:.2e}")
+
+
+def test_fullsize_32k_sample_attention_mask():
+    """SampleAttention's mask at 32K (8 trunks of 16 sampled rows per query head): masses, kept
+    patterns and every mask row against the oracle, and sampled attention rows on the mask."""
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_32k"]
+    tau, nt, rpt = 0.9, 8, 16
+    _log(f"[fullsize] {w.name} SampleAttention mask, tau {tau}, trunks {nt}x{rpt}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, NB, Hq, N = w.block_size, w.num_blocks, w.num_q_heads, w.seq_len
+    count_t, idx_t, col_t, sl_t = pbsa.sample_attention_mask(dev["q"], dev["k"], B, tau, nt, rpt, return_masses=True)
+    out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], None, count_t, idx_t, B, 0)
+    torch.cuda.synchronize()
+    cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+    col_o, sl_o = oracle.sampled_masses(q, k, nt, rpt)
+    ties = compare_sample_mask(cg, ig, col_t.cpu().numpy(), sl_t.cpu().numpy(), col_o, sl_o, tau, B, True, False)
+    rows = _sample_rows(Hq, NB, 8, 14)
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, cg, ig, B, None, rows=rows)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o, "sample mask 32K")
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    _log(f"[fullsize] 32K SampleAttention: {ties} tie heads, density {cg.sum() / (Hq * NB * (NB + 1) / 2):.3f}, "
+         f"rows {rows}: max abs {mx:.2e} mean {mean:.2e}")
