@@ -487,7 +487,7 @@ def main() -> int:
     ap.add_argument("--summary-out", default=TRAFFIC_SUMMARY)
     ap.add_argument("--summary-command", default="")
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
-    ap.add_argument("--suite-out", default="gpurun_out/suite.jsonl")
+    ap.add_argument("--suite-out", default="bench_suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
     ap.add_argument("--suite-parts", default="128k,sweep,earlystop,s2o,twopass,qperm,sample",
                     help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass, qperm, sample")
