@@ -631,3 +631,26 @@ def test_sample_attention_full_target_is_dense():
     count, idx = pbsa.sample_attention_mask(dev["q"], dev["k"], B, 1.0, 4, 8, force_diag=False)
     torch.cuda.synchronize()
     assert (count.cpu().numpy() == np.arange(1, N // B + 1)[None, :]).all()
+
+
+def test_estimators_are_deterministic():
+    """The historical ranking, the query permutation and SampleAttention's mask give identical results
+    on repeated calls (every sum runs in a fixed order)."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S = 2048, 4, 2, 128, 128, 512
+    dev, _ = _inputs(N, Hq, Hkv, d, 8, 256, 81)
+    res = []
+    for _ in range(2):
+        r = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+        qp = pbsa.build_query_permutation(dev["q"], dev["k"], B, S)
+        c, i, col, sl = pbsa.sample_attention_mask(dev["q"], dev["k"], B, 0.8, 4, 16, return_masses=True)
+        torch.cuda.synchronize()
+        valid = torch.zeros_like(i, dtype=torch.bool)
+        cnt = c.cpu().numpy()
+        for h in range(Hq):
+            for I in range(cnt.shape[1]):
+                o = oracle.tri_offset(I)
+                valid[h, o:o + int(cnt[h, I])] = True
+        res.append([r.clone(), qp.clone(), c.clone(), i[valid].clone(), col.clone(), sl.clone()])
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
