@@ -203,6 +203,35 @@ def _events(torch, stream, fn, reps):
     return {"median_ms": xs[len(xs) // 2], "min_ms": xs[0]}
 
 
+def torch_sdpa_ms(torch, q, k, v, stream, reps):
+    """Dense causal attention through torch's fused SDPA kernels on the same tensors, as context:
+    (median ms, backend) or (None, reason).  Only the flash and memory-efficient backends are
+    allowed (the unfused path is never used); K and V are expanded to the query heads."""
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+    except ImportError as e:
+        return None, f"unavailable: {e}"
+    G = q.shape[0] // k.shape[0]
+    qq = q.unsqueeze(0)
+    kk = k.repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+    vv = v.repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
+    reason = "no fused kernel"
+    try:
+        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            try:
+                with sdpa_kernel([be]):
+                    f = lambda: torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
+                    f()
+                    torch.cuda.synchronize()
+                    return _events(torch, stream, f, reps)["median_ms"], be.name
+            except RuntimeError as e:
+                reason = f"{be.name}: {str(e)[:120]}"
+        return None, reason
+    finally:
+        del qq, kk, vv
+        torch.cuda.empty_cache()
+
+
 def suite(args) -> int:
     """Secondary measurements, one JSON object per line into --suite-out:
     128K (as configured and at a bisected ~10% block density), the 64K density sweep with the
@@ -292,6 +321,7 @@ def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
 
     dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
     t_dense = _events(torch, stream, dense, max(2, reps // 2))
+    sdpa_ms, sdpa_backend = torch_sdpa_ms(torch, q, k, v, stream, 2)
     t_perm = _events(torch, stream, fp, reps)
     for label, tau in (("as_configured", w.mass_tau), ("density_10pct", None)):
         if tau is None:  # bisect the mass target to a ~10% computed-block fraction
@@ -315,6 +345,7 @@ def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
         emit({"workload": w.name, "point": label, "mass_tau": tau, "block_density": dens,
               "permutation_ms": t_perm["median_ms"], "mask_ms": t_mask["median_ms"], "attention_ms": ta,
               "step_ms": step, "dense_kernel_ms": t_dense["median_ms"],
+              "torch_sdpa_dense_ms": sdpa_ms, "torch_sdpa_backend": sdpa_backend,
               "attention_speedup_vs_dense": t_dense["median_ms"] / ta,
               "step_speedup_vs_dense": t_dense["median_ms"] / step,
               "attention_mfma_tflops": tiles * 4.0 * B * B * w.head_dim / (ta * 1e-3) / 1e12,
@@ -588,6 +619,7 @@ def main() -> int:
     ms_dense = timed(dense, max(3, reps // 2))
     stage_attn()  # leave the sparse result in `out`
     torch.cuda.synchronize()
+    sdpa_ms, sdpa_backend = torch_sdpa_ms(torch, q, k, v, stream, 3)
 
     tiles = int(count.sum().item())
     causal_tiles = Hq * NB * (NB + 1) // 2
@@ -623,6 +655,8 @@ def main() -> int:
         "dense_kernel_ms": med(ms_dense),
         "speedup_vs_dense_kernel": med(ms_dense) / (t_attn * 1e3),
         "dense_kernel_tflops": w.dense_causal_flop / (med(ms_dense) * 1e-3) / 1e12,
+        "torch_sdpa_dense": {"ms": sdpa_ms, "backend": sdpa_backend,
+                             "step_speedup": None if sdpa_ms is None else sdpa_ms / (t_step * 1e3)},
     }
     if args.copy_calib:
         src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dv)
