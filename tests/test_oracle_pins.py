@@ -596,3 +596,28 @@ def test_sample_attention_full_target_keeps_every_tile():
     count, _, ck, sk, _, _ = oracle.sample_attention_mask(q, k, B, 1.0, 3, 4)
     assert ck.all() and sk.all()
     assert (count == np.arange(1, N // B + 1)[None, :]).all()
+
+
+def test_pooled_block_logits_are_the_mask_scores():
+    """softmax of each row of pooled_block_logits is block_mask's p; with every query u and keys
+    a_j u the logit of (I, J) is c |u|^2 times the mean a over block J."""
+    N, Hq, Hkv, d, B, S = 96, 4, 2, 8, 8, 32
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=4, band=16, seed=42)
+    perm = oracle.segment_permutation(oracle.key_importance(q, k, B), S)
+    z = oracle.pooled_block_logits(q, k, perm, B, S)
+    _, _, prob = oracle.block_mask(q, k, perm, B, S, 0.9)
+    for h in range(Hq):
+        for I in range(N // B):
+            o = oracle.tri_offset(I)
+            e = np.exp(z[h, o:o + I + 1] - z[h, o:o + I + 1].max())
+            np.testing.assert_allclose(e / e.sum(), prob[h, o:o + I + 1], rtol=1e-12, atol=1e-300)
+    u = np.random.default_rng(3).standard_normal(d)
+    a = np.arange(N, dtype=np.float64) / N
+    q2 = np.broadcast_to(u, (Hq, N, d)).copy()
+    k2 = np.broadcast_to(a[:, None] * u[None, :], (Hkv, N, d)).copy()
+    z2 = oracle.pooled_block_logits(q2, k2, None, B, S)
+    c = 1.0 / np.sqrt(d)
+    for I in (0, 5, N // B - 1):
+        o = oracle.tri_offset(I)
+        want = [c * (u @ u) * a[J * B:(J + 1) * B].mean() for J in range(I + 1)]
+        np.testing.assert_allclose(z2[0, o:o + I + 1], want, rtol=1e-12)
