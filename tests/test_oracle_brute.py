@@ -204,3 +204,33 @@ def test_sample_attention_mask_matches_brute_force(c, trunks, tau):
         for I in range(oracle.num_blocks(N, B)):
             o = oracle.tri_offset(I)
             assert idx[h, o:o + int(count[h, I])].tolist() == masks_b[(h, I)], (h, I)
+
+
+@settings(max_examples=15, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(tiny_case(), st.booleans())
+def test_two_pass_ratios_place_the_brute_force_stop(c, with_qperm):
+    # the two-pass counterpart of test_marginal_gain_ratios_place_the_brute_force_stop: at each
+    # history position whose ratio is a new low, a threshold just above it stops the brute force
+    # there and one just below lets it go on (with and without the query permutation)
+    N, Hq, Hkv, d, B, S = c["N"], c["Hq"], c["Hkv"], c["d"], c["B"], c["S"]
+    q, k, _ = small_inputs(N, Hq, Hkv, d, n_stripes=c["stripes"], band=0, seed=c["seed"])
+    scale = 1.0 / math.sqrt(d)
+    pi, _ = oracle.prefix_kv_ranking(q, k, S)
+    qperm = oracle.query_permutation(q, k, S) if with_qperm else None
+    qorder = None if qperm is None else [qperm[g].tolist() for g in range(Hkv)]
+    ranking = {(g, sigma): pi[g, oracle.prefix_offset(sigma, S):oracle.prefix_offset(sigma, S) + sigma * S].tolist()
+               for g in range(Hkv) for sigma in range(1, oracle.num_segments(N, S))}
+    ratios = oracle.s2o_prefix_gain_ratios(q, k, pi, B, S, qperm=qperm)
+    checks = []
+    for (h, I), r in ratios.items():
+        assert np.all(np.isnan(r) | ((r > 0) & (r <= 1 + 1e-12))), (h, I, r)
+        low = math.inf
+        for p, x in enumerate(r):
+            if not np.isnan(x) and x < low * (1 - 1e-6):
+                checks.append((h, I, p, float(x), len(r)))
+                low = x
+    for h, I, p, x, full in checks[:6]:
+        above = brute.s2o_prefix_processed(q, k, ranking, B, S, x * (1 + 1e-9), scale, qorder=qorder)[(h, I)]
+        assert len(above) == p + 1, (h, I, p, x, above)
+        below = brute.s2o_prefix_processed(q, k, ranking, B, S, x * (1 - 1e-9), scale, qorder=qorder)[(h, I)]
+        assert len(below) > p + 1 or len(below) == full, (h, I, p, x, below)

@@ -621,3 +621,44 @@ def test_pooled_block_logits_are_the_mask_scores():
         o = oracle.tri_offset(I)
         want = [c * (u @ u) * a[J * B:(J + 1) * B].mean() for J in range(I + 1)]
         np.testing.assert_allclose(z2[0, o:o + I + 1], want, rtol=1e-12)
+
+
+def test_mass_cut_hand_example_and_characterisation():
+    """mass_cut keeps the heaviest members (ties by lower index) until their mass reaches tau: a
+    hand-worked vector, then the properties that fix the answer on random vectors — the kept set
+    reaches tau, dropping its lightest member falls below tau, and no unkept member outranks a
+    kept one."""
+    m = np.array([0.1, 0.4, 0.3, 0.2])
+    assert oracle.mass_cut(m, 0.65).tolist() == [False, True, True, False]
+    assert oracle.mass_cut(m, 0.4).tolist() == [False, True, False, False]   # reaching tau exactly is enough
+    assert oracle.mass_cut(m, 0.75).tolist() == [False, True, True, True]
+    assert oracle.mass_cut(m, 1.0).all() and oracle.mass_cut(m, 2.0).all()
+    assert oracle.mass_cut(np.array([0.25, 0.25, 0.25, 0.25]), 0.5).tolist() == [True, True, False, False]
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        n = int(rng.integers(1, 12))
+        w = rng.random(n) ** 3
+        w[rng.random(n) < 0.3] = w[0]          # planted ties
+        w = w / w.sum() if w.sum() > 0 else np.full(n, 1.0 / n)
+        tau = float(rng.choice([0.2, 0.5, 0.9, 0.99]))
+        keep = oracle.mass_cut(w, tau)
+        kept, rest = np.nonzero(keep)[0], np.nonzero(~keep)[0]
+        total = w[keep].sum()
+        if total < tau:                          # only when even every member falls short
+            assert keep.all()
+            continue
+        lightest = max(kept, key=lambda i: (-w[i], i))      # last in the (heavy first, index) order
+        assert total - w[lightest] < tau
+        for i in rest:
+            for j in kept:
+                assert (w[j], -j) > (w[i], -i)
+
+
+def test_kept_bitmap_hand_example():
+    """Bit tri_offset(I) + J of head h's row: for NB = 3 the tiles (0,0), (2,0), (2,2) are bits 0, 3
+    and 5 (rows start at bits 0, 1, 3); a second head and a tile past bit 31 land in their own
+    words."""
+    bm = oracle.kept_bitmap({(0, 0): [0], (0, 2): [0, 2]}, 1, 3)
+    assert bm.dtype == np.uint32 and bm.shape == (1, 1) and int(bm[0, 0]) == 0b101001
+    bm = oracle.kept_bitmap({(1, 7): [4]}, 2, 8)       # tri_offset(7) + 4 = 28 + 4 = 32
+    assert bm.shape == (2, 2) and bm[0].tolist() == [0, 0] and bm[1].tolist() == [0, 1]
