@@ -121,6 +121,44 @@ def test_fullsize_128k_sampled():
     _log(f"[fullsize] 128K attention rows {rows}: max abs {mx:.2e} mean abs {mean:.2e}")
 
 
+def test_fullsize_64k_sweep_sampled():
+    """The 64K density-sweep workload (S = 4096) at both ends of its mass targets, permutation on and
+    off, launched as the sweep launches it: the whole permutation, the mask rows of two heads in
+    full, and sampled attention rows."""
+    pbsa = _need_gpu()
+    w = WORKLOADS["llama8b_64k_sweep"]
+    _log(f"[fullsize] {w.name}")
+    dev, host = _load(w)
+    q, k, v = host["q"], host["k"], host["v"]
+    B, S, NB, Hq, N = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads, w.seq_len
+    G = Hq // w.num_kv_heads
+    perm_t, imp_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
+    torch.cuda.synchronize()
+    imp_o = oracle.key_importance(q, k, B)
+    np.testing.assert_allclose(imp_t.cpu().numpy(), imp_o, rtol=1e-12, atol=1e-300)
+    perm_g = perm_t.cpu().numpy()
+    compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
+    _log("[fullsize] 64K permutation ok")
+    for tau in (w.taus[0], w.taus[-1]):
+        for use_perm in (True, False):
+            pp_t, pp_g = (perm_t, perm_g) if use_perm else (None, None)
+            count_t, idx_t, prob_t = pbsa.estimate_block_mask(dev["q"], dev["k"], pp_t, B, S, tau, return_prob=True)
+            out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], pp_t, count_t, idx_t, B, S)
+            torch.cuda.synchronize()
+            cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+            for h in (0, Hq - 1):
+                g = h // G
+                co, io, po = oracle.block_mask(q[h:h + 1], k[g:g + 1], None if pp_g is None else pp_g[g:g + 1], B, S,
+                                               tau)
+                compare_mask(cg[h:h + 1], ig[h:h + 1], co, io, po, tau)
+            rows = _sample_rows(Hq, NB, 5, 17 + int(use_perm))
+            out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, pp_g, cg, ig, B, S, rows=rows)
+            mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
+            compare_lse(lse_t.cpu().numpy(), lse_o)
+            _log(f"[fullsize] 64K tau {tau} permutation {use_perm}: density "
+                 f"{cg.sum() / (Hq * NB * (NB + 1) / 2):.3f}, rows {rows} max abs {mx:.2e} mean abs {mean:.2e}")
+
+
 def test_fullsize_64k_early_stop_sampled():
     pbsa = _need_gpu()
     w = WORKLOADS["llama8b_64k_earlystop"]
