@@ -159,6 +159,48 @@ def test_fullsize_64k_sweep_sampled():
                  f"{cg.sum() / (Hq * NB * (NB + 1) / 2):.3f}, rows {rows} max abs {mx:.2e} mean abs {mean:.2e}")
 
 
+def test_max_blocks_sampled():
+    """The largest sequence the library accepts: 2048 key blocks (N = 262144 at B = 128) with the
+    largest segment (8192), on two query heads of one KV head: the whole permutation, every mask
+    row, and sampled attention rows including the last block (the longest list) and the dense
+    kernel on them."""
+    pbsa = _need_gpu()
+    from workloads import generate
+    N, Hq, Hkv, d, B, S, tau = 262144, 2, 1, 64, 128, 8192, 0.9
+    NB = N // B
+    _log(f"[fullsize] max blocks: N={N} B={B} S={S} NB={NB}")
+    x = generate(N, Hq, Hkv, d, 16, 512, 21)
+    dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    q, k, v = (bf16_bits_to_f32(x[n]).astype(np.float64) for n in ("q", "k", "v"))
+    perm_t, imp_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
+    count_t, idx_t, prob_t = pbsa.estimate_block_mask(dev["q"], dev["k"], perm_t, B, S, tau, return_prob=True)
+    out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S)
+    dense_t, dense_lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B)
+    torch.cuda.synchronize()
+    imp_o = oracle.key_importance(q, k, B)
+    np.testing.assert_allclose(imp_t.cpu().numpy(), imp_o, rtol=1e-12, atol=1e-300)
+    perm_g = perm_t.cpu().numpy()
+    compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
+    cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
+    co, io, po = oracle.block_mask(q, k, perm_g, B, S, tau)
+    compare_mask(cg, ig, co, io, po, tau)
+    _log(f"[fullsize] max blocks: permutation and every mask row ok (density {cg.sum() / (Hq * NB * (NB + 1) / 2):.3f})")
+    rows = [(0, NB - 1), (1, NB - 1), (0, 0), (1, NB // 2), (0, 1365)]
+    out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, perm_g, cg, ig, B, S, rows=rows)
+    mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
+    compare_lse(lse_t.cpu().numpy(), lse_o)
+    full = {(h, I): list(range(I + 1)) for h, I in rows}
+    fc = np.zeros((Hq, NB), dtype=np.int64)
+    fi = np.full((Hq, NB * (NB + 1) // 2), -1, dtype=np.int64)
+    for (h, I), lst in full.items():
+        fc[h, I] = len(lst)
+        fi[h, oracle.tri_offset(I):oracle.tri_offset(I) + len(lst)] = lst
+    dense_o, dense_lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, fc, fi, B, S, rows=rows)
+    dmx, dmean = compare_out(_rows_slice(dense_t.cpu().numpy(), rows, B, N), dense_o, "dense")
+    compare_lse(dense_lse_t.cpu().numpy(), dense_lse_o)
+    _log(f"[fullsize] max blocks rows {rows}: sparse max abs {mx:.2e} mean {mean:.2e}; dense max abs {dmx:.2e}")
+
+
 def test_fullsize_64k_early_stop_sampled():
     pbsa = _need_gpu()
     w = WORKLOADS["llama8b_64k_earlystop"]

@@ -35,6 +35,8 @@ CASES = [
     ("b128_d64_ragged_1000", 1000, 4, 1, 64, 128, 256, 8, 128, 0.95, 9),
     ("shorter_than_a_block_100", 100, 2, 2, 128, 128, 128, 2, 0, 0.9, 10),
     ("b64_d64_pairs_ragged_777", 777, 4, 2, 64, 64, 128, 8, 64, 0.9, 11),
+    ("single_token_1", 1, 2, 1, 64, 64, 64, 0, 0, 0.9, 12),
+    ("single_token_b128_d128_gqa", 1, 4, 2, 128, 128, 128, 0, 0, 0.5, 13),
 ]
 
 
