@@ -328,6 +328,45 @@ def test_fullsize_32k_query_permuted_two_pass_sampled():
     _log(f"[fullsize] 32K query-permuted two-pass: sampled rows {rows} ({near} in band): max abs {mx:.2e} mean {mean:.2e}")
 
 
+def test_max_segments_two_pass_sampled():
+    """The historical ranking at its limit of 256 segments (N = 16384, S = B = 64): the whole
+    ranking and the whole query order, then the stop and outputs of sampled rows, without and with
+    the query permutation."""
+    pbsa = _need_gpu()
+    from workloads import generate
+    N, Hq, Hkv, d, B, S, gain_tau = 16384, 2, 1, 64, 64, 64, 0.02
+    NB = N // B
+    _log(f"[fullsize] max segments: N={N} B={B} S={S} segments={N // S}")
+    x = generate(N, Hq, Hkv, d, 0, 64, 58)
+    dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    q, k, v = (bf16_bits_to_f32(x[n]).astype(np.float64) for n in ("q", "k", "v"))
+    rank_t = pbsa.build_prefix_kv_ranking(dev["q"], dev["k"], B, S)
+    qperm_t = pbsa.build_query_permutation(dev["q"], dev["k"], B, S)
+    torch.cuda.synchronize()
+    pi_g = rank_t.cpu().numpy().astype(np.int64)
+    pi_o, score_o = oracle.prefix_kv_ranking(q, k, S)
+    ties = compare_prefix_rank(pi_g, pi_o, score_o, S)
+    qp_g = qperm_t.cpu().numpy().astype(np.int64)
+    qties = compare_perm(qp_g, oracle.query_permutation(q, k, S), oracle.query_guide_scores(q, k), S)
+    _log(f"[fullsize] max segments: ranking ({ties} ties) and query order ({qties} ties) ok")
+    rows = _sample_rows(Hq, NB, 8, 58)
+    for permuted in (False, True):
+        out_t, lse_t, kept_t = pbsa.s2o_prefix_attn_prefill(dev["q"], dev["k"], dev["v"], rank_t, B, S, gain_tau,
+                                                            qperm=qperm_t if permuted else None, return_kept=True)
+        torch.cuda.synchronize()
+        qp = qp_g if permuted else None
+        kept = (bitmap_to_kept_square if permuted else bitmap_to_kept)(kept_t.cpu().numpy(), NB)
+        cg, ig = two_pass_lists(Hq, N, B, S, permuted_queries=permuted)
+        ratios = oracle.s2o_prefix_gain_ratios(q, k, pi_g, B, S, rows=rows, qperm=qp)
+        _, near = compare_s2o_stops(kept, cg, ig, ratios, gain_tau, **({"row_stride": NB} if permuted else {}))
+        out_o, lse_o = oracle.two_pass_attention_on(q, k, v, pi_g, {r: kept[r] for r in rows}, B, S, qperm=qp)
+        ok = ~np.isnan(out_o)
+        mx, mean = compare_out(np.where(ok, out_t.cpu().numpy(), np.nan), out_o, "two-pass, 256 segments")
+        compare_lse(lse_t.cpu().numpy(), lse_o)
+        _log(f"[fullsize] max segments, query permutation {permuted}: rows {rows} ({near} in band) "
+             f"max abs {mx:.2e} mean {mean:.2e}")
+
+
 def test_fullsize_32k_sample_attention_mask():
     """SampleAttention's mask at 32K (8 trunks of 16 sampled rows per query head): masses, kept
     patterns and every mask row against the oracle, and sampled attention rows on the mask."""
