@@ -326,14 +326,17 @@ __device__ __forceinline__ void block_softmax_pv(SoftmaxState<D, BLK>& st, const
 }
 
 // One KT-key stage from LDS: for each 32-key block, the V operands of this block and the K
-// operands of the next are read while the scores and softmax of this block are computed.
+// operands of the next are read while the scores and softmax of this block are computed.  kop0
+// holds the K operands of block 0, read by the caller as soon as the stage buffer was ready.
 template <int D, int BLK>
 __device__ __forceinline__ void stage_compute(SoftmaxState<D, BLK>& st, const uint16_t* Kc, const uint16_t* Vc,
-                                              const bf16x8* qf, bool diag, int rel0, float sl2) {
+                                              const bf16x8* qf, const bf16x8* kop0, bool diag, int rel0,
+                                              float sl2) {
   using C = AttnCfg<D, BLK>;
   constexpr int NKB = C::KT / 32;
   bf16x8 kop[C::KSTEPS];
-  load_k_ops<D, BLK>(kop, Kc, 0);
+#pragma unroll
+  for (int kk = 0; kk < C::KSTEPS; ++kk) kop[kk] = kop0[kk];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     bf16x8 vop[2 * C::DB];
@@ -731,6 +734,11 @@ void attn_pipe_kernel(AttnArgs a) {
   auto step = [&](int s, int b) __attribute__((always_inline)) -> bool {  // b = s % NBUF
     const uint16_t* Kc = Kb(b);
     const uint16_t* Vc = Vb(b);
+    // the first K operands of this stage are read right after the barrier that made the stage
+    // ready, so their LDS latency passes while the lookups and gathers below are issued (a stage
+    // this head skips reads them for nothing)
+    bf16x8 kop0[AttnCfg<D, BLK>::KSTEPS];
+    load_k_ops<D, BLK>(kop0, Kc, 0);
     RowLook pr_next;
     if (!DENSE) pr_next = lookup_ahead(s + NBUF + 1);
     __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gathers (vmcnt order)
@@ -749,7 +757,7 @@ void attn_pipe_kernel(AttnArgs a) {
       if (S2O && (s % C::STAGES) == 0) st.lb = st.l;  // a new key block starts
       // causal mask: on the diagonal tile, or on every own-segment tile when queries are permuted
       // (key j is visible to the query at natural position qnat iff j <= qnat)
-      stage_compute<D, BLK>(st, Kc, Vc, qf, qperm_on ? J >= J0 : J == I,
+      stage_compute<D, BLK>(st, Kc, Vc, qf, kop0, qperm_on ? J >= J0 : J == I,
                             (qperm_on ? qnat - J * BLK : qloc) - koff - 4 * h2, a.sl2);
       if (S2O && (s % C::STAGES) == C::STAGES - 1) {
         // this block's share of each query's denominator (both half-waves of the query summed)
