@@ -524,8 +524,9 @@ def main() -> int:
                     help="comma-separated subset of 128k, sweep, earlystop, s2o, twopass, qperm, sample")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus}); "
-              "head-parallel sharding across GPUs needs no exchange and is described in the design notes",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (got --gpus {args.gpus}); "
+              "query heads split across GPUs with no exchange between them, each GPU running this same step "
+              "on its heads",
               file=sys.stderr)
         return 2
 
