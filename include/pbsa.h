@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   PBSA_OK = 0,
   PBSA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, stride, tau, flag combination */
-  PBSA_ERR_UNSUPPORTED = 2,  /* a valid shape this build does not handle (d, B, S, NB limits) */
+  PBSA_ERR_UNSUPPORTED = 2,  /* a valid shape the library does not handle (d, B, S, NB limits) */
   PBSA_ERR_WORKSPACE = 3,    /* workspace null or smaller than pbsa_workspace_size */
   PBSA_ERR_HIP = 4           /* a HIP launch or runtime call failed */
 } pbsa_status;
