@@ -105,7 +105,7 @@ def summarize_stats(stats_csv: str, bench_out: str, out: str, command: str, work
 
     def short(name):
         own = "pbsa::" in name
-        name = name.replace("pbsa::", "")
+        name = name.replace("pbsa::", "").replace("(anonymous namespace)::", "")
         if name.startswith("void "):
             name = name[5:]
         cut = name.find("(")
