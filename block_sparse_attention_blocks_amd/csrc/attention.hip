@@ -819,9 +819,24 @@ void attn_pipe_kernel(AttnArgs a) {
 // Score block kb of a tile (S^T, 32 keys x 32 queries) with K operands read from LDS a quarter of
 // the k-steps at a time (fewer live registers than load_k_ops), causal mask on the diagonal.
 template <int D, int BLK>
-__device__ __forceinline__ f32x16 tile_scores(const uint16_t* Ks, const bf16x8* qf, int kb, bool diag, int rel) {
+constexpr int tile_kq() { return AttnCfg<D, BLK>::KSTEPS >= 4 ? AttnCfg<D, BLK>::KSTEPS / 4 : 1; }
+
+// The first operand batch of score block 0 of a tile (read early by the caller).
+template <int D, int BLK>
+__device__ __forceinline__ void tile_first_ops(const uint16_t* Ks, bf16x8* kop) {
+  const int lane = threadIdx.x & 63;
+  const int krow = lane & 31, h2 = lane >> 5;
+  const uint16_t* kp = Ks + krow * D;
+  const int ksw = kt_swz<D>(krow);
+#pragma unroll
+  for (int kk = 0; kk < tile_kq<D, BLK>(); ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kp + (((kk * 2 + h2) ^ ksw) * 8));
+}
+
+template <int D, int BLK>
+__device__ __forceinline__ f32x16 tile_scores(const uint16_t* Ks, const bf16x8* qf, int kb, bool diag, int rel,
+                                              const bf16x8* first = nullptr) {
   using C = AttnCfg<D, BLK>;
-  constexpr int KQ = C::KSTEPS >= 4 ? C::KSTEPS / 4 : 1;  // k-steps per operand batch
+  constexpr int KQ = tile_kq<D, BLK>();  // k-steps per operand batch
   const int lane = threadIdx.x & 63;
   const int krow = kb * 32 + (lane & 31), h2 = lane >> 5;
   const uint16_t* kp = Ks + krow * D;
@@ -833,7 +848,8 @@ __device__ __forceinline__ f32x16 tile_scores(const uint16_t* Ks, const bf16x8* 
   for (int k0 = 0; k0 < C::KSTEPS; k0 += KQ) {
     bf16x8 kop[KQ];
 #pragma unroll
-    for (int kk = 0; kk < KQ; ++kk) kop[kk] = *reinterpret_cast<const bf16x8*>(kp + ((((k0 + kk) * 2 + h2) ^ ksw) * 8));
+    for (int kk = 0; kk < KQ; ++kk)
+      kop[kk] = (first && k0 == 0) ? first[kk] : *reinterpret_cast<const bf16x8*>(kp + ((((k0 + kk) * 2 + h2) ^ ksw) * 8));
 #pragma unroll
     for (int kk = 0; kk < KQ; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[k0 + kk], s, 0, 0, 0);
   }
@@ -1017,6 +1033,8 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   }
 
   auto step = [&](int u, const uint16_t* Kc, uint16_t* Kn, const uint16_t* Vp, uint16_t* Vc) {
+    bf16x8 first[tile_kq<D, BLK>()];  // read before the lookups and the gather are issued
+    tile_first_ops<D, BLK>(Kc, first);
     const RowLook pr = lookup(u + 2 < nblk ? u + 2 : 0, t & (BLK - 1), u + 2 < nblk && t < BLK);
     __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gather (vmcnt order)
     if (u + 1 < nblk) gather_k(u + 1, Kn);
@@ -1027,7 +1045,8 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     float row_max = -INFINITY;
     if ((e >> (16 + hh)) & 1u) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, qloc - kb * 32 - 4 * h2);
+      for (int kb = 0; kb < KB; ++kb)
+        sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, qloc - kb * 32 - 4 * h2, kb == 0 ? first : nullptr);
       row_max = tile_row_max<KB>(sc);
     }
     const float wm = wave_max_f32(qvalid ? row_max : -INFINITY);
