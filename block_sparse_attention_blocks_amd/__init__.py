@@ -42,13 +42,65 @@ def num_blocks(seq_len: int, block_size: int) -> int:
     return -(-seq_len // block_size)
 
 
-def _check_bf16(name: str, t: torch.Tensor, heads: Optional[int] = None) -> None:
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
-    if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
-        raise ValueError(f"{name} must be bf16 [heads][tokens][d] with a contiguous last dimension")
-    if heads is not None and t.shape[0] != heads:
-        raise ValueError(f"{name} has {t.shape[0]} heads, expected {heads}")
+def _check_tensor(name: str, t: Optional[torch.Tensor], dtype, shape, device, contiguous: bool = True) -> None:
+    """t is None, or a tensor of this dtype and exact shape on `device` (None: any), contiguous if asked."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], block_size: int,
+               require_gpu: bool = True) -> None:
+    """q [Hq][N][d], k and v [Hkv][N][d] bf16 on one device, Hq a multiple of Hkv, v with k's strides."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or (require_gpu and t.device.type != "cuda"):
+            raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be bf16 [heads][tokens][d] with a contiguous last dimension")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on the device of q")
+    if k.shape[1:] != q.shape[1:]:
+        raise ValueError(f"k must match q in tokens and head_dim (q {tuple(q.shape)}, k {tuple(k.shape)})")
+    if k.shape[0] < 1 or q.shape[0] % k.shape[0]:
+        raise ValueError("the number of query heads must be a multiple of the number of KV heads")
+    if v is not None and (v.shape != k.shape or v.stride() != k.stride()):
+        raise ValueError("k and v must share shape and strides")
+    if not isinstance(block_size, int) or block_size <= 0:
+        raise ValueError("block_size must be a positive int")
+
+
+def _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, theta=None, out=None, lse=None,
+                     require_gpu: bool = True) -> None:
+    """Argument check of the attention entry points: int32 perm [Hkv][N], int32 block_count [Hq][NB]
+    and block_idx [Hq][NB(NB+1)/2] (both or neither), fp32 theta [Hq][NB], fp32 out [Hq][N][d] with a
+    contiguous last dimension, fp32 lse [Hq][N], all contiguous and on q's device."""
+    _check_qkv(q, k, v, block_size, require_gpu)
+    Hq, N, d = q.shape
+    Hkv = k.shape[0]
+    NB = num_blocks(N, block_size)
+    dev = q.device
+    _check_tensor("perm", perm, torch.int32, (Hkv, N), dev)
+    if (block_count is None) != (block_idx is None):
+        raise ValueError("block_count and block_idx are given together or not at all")
+    _check_tensor("block_count", block_count, torch.int32, (Hq, NB), dev)
+    _check_tensor("block_idx", block_idx, torch.int32, (Hq, NB * (NB + 1) // 2), dev)
+    _check_tensor("early_stop_theta", theta, torch.float32, (Hq, NB), dev)
+    if out is not None:
+        _check_tensor("out", out, torch.float32, (Hq, N, d), dev, contiguous=False)
+        if out.stride(2) != 1:
+            raise ValueError("out must have a contiguous last dimension")
+    _check_tensor("lse", lse, torch.float32, (Hq, N), dev)
 
 
 def make_shape(q: torch.Tensor, k: torch.Tensor, block_size: int, segment_size: int,
@@ -102,8 +154,8 @@ def build_segment_permutation(q: torch.Tensor, k: torch.Tensor, block_size: int,
                               scale: Optional[float] = None, return_importance: bool = False,
                               perm: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Stage 1: int32 index list perm [Hkv][N] (and fp64 importance [Hkv][N] if asked)."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
+    _check_qkv(q, k, None, block_size)
+    _check_tensor("perm", perm, torch.int32, (k.shape[0], k.shape[1]), q.device)
     shape = make_shape(q, k, block_size, segment_size, scale)
     Hkv, N = k.shape[0], k.shape[1]
     if perm is None:
@@ -125,8 +177,8 @@ def estimate_block_mask(q: torch.Tensor, k: torch.Tensor, perm: Optional[torch.T
 
     ranked: list every J <= I in the order of the marginal-gain early stop instead of applying the
     mass cut (mass_tau and the force flags are then not used, and no probabilities are written)."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
+    _check_qkv(q, k, None, block_size)
+    _check_tensor("perm", perm, torch.int32, (k.shape[0], k.shape[1]), q.device)
     shape = make_shape(q, k, block_size, segment_size, scale)
     Hq, N = q.shape[0], q.shape[1]
     NB = num_blocks(N, block_size)
@@ -135,6 +187,8 @@ def estimate_block_mask(q: torch.Tensor, k: torch.Tensor, perm: Optional[torch.T
         idx = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.int32, device=q.device)
     else:
         count, idx = out
+        _check_tensor("block_count", count, torch.int32, (Hq, NB), q.device)
+        _check_tensor("block_idx", idx, torch.int32, (Hq, NB * (NB + 1) // 2), q.device)
     prob = torch.empty((Hq, NB * (NB + 1) // 2), dtype=torch.float64, device=q.device) if return_prob else None
     flags = (PBSA_FORCE_DIAG if force_diag else 0) | (PBSA_FORCE_FIRST if force_first else 0)
     if ranked:
@@ -159,16 +213,10 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word).
     workspace: optional preallocated device buffer of at least workspace_size(shape, PBSA_OP_ATTENTION)
     bytes (the work deques); one is allocated per call otherwise."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
-    _check_bf16("v", v, heads=k.shape[0])
-    if v.stride() != k.stride():
-        raise ValueError("k and v must share strides")
+    _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, early_stop_theta, out, lse)
     Hq, N, d = q.shape
     if out is None:
         out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
-    if out.dtype != torch.float32 or out.stride(2) != 1:
-        raise ValueError("out must be fp32 with a contiguous last dimension")
     if return_lse and lse is None:
         lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
     NB = num_blocks(N, block_size)
@@ -200,11 +248,9 @@ def s2o_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, perm: Op
                      return_error: bool = False, workspace: Optional[torch.Tensor] = None):
     """Attention with the marginal-gain early stop over a ranked list (estimate_block_mask with
     ranked=True): out fp32 [Hq][N][d] (+ lse, processed-block bitmap, device error word)."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
-    _check_bf16("v", v, heads=k.shape[0])
-    if v.stride() != k.stride():
-        raise ValueError("k and v must share strides")
+    if block_count is None or block_idx is None:
+        raise ValueError("the marginal-gain stop needs the ranked lists block_count and block_idx")
+    _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, None, out, lse)
     Hq, N, d = q.shape
     if out is None:
         out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
@@ -245,8 +291,7 @@ def build_prefix_kv_ranking(q: torch.Tensor, k: torch.Tensor, block_size: int, s
     """S2O historical ranking: int32 [Hkv][prefix_rank_length] holding, for every segment sigma >= 1
     at offset S*sigma*(sigma-1)/2, the keys before the segment by descending score against the
     segment's mean query."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
+    _check_qkv(q, k, None, block_size)
     shape = make_shape(q, k, block_size, segment_size)
     L = prefix_rank_length(q, k, block_size, segment_size)
     if out is None:
@@ -264,8 +309,7 @@ def build_query_permutation(q: torch.Tensor, k: torch.Tensor, block_size: int, s
                             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """S2O query permutation: int32 [Hkv][N], each segment's positions by descending score against the
     KV head's mean key (averaged over its query heads), ties by position."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
+    _check_qkv(q, k, None, block_size)
     shape = make_shape(q, k, block_size, segment_size)
     if out is None:
         out = torch.empty((k.shape[0], q.shape[1]), dtype=torch.int32, device=q.device)
@@ -287,11 +331,7 @@ def s2o_prefix_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k
     build_prefix_kv_ranking: out fp32 [Hq][N][d] (+ lse, processed-entry bitmap, device error word).
     qperm (build_query_permutation) permutes the queries inside segments; rows still come back at
     their natural positions, and the kept bitmap then has NB bits per (h, I) row."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
-    _check_bf16("v", v, heads=k.shape[0])
-    if v.stride() != k.stride():
-        raise ValueError("k and v must share strides")
+    _check_attn_args(q, k, v, None, None, None, block_size, None, out, lse)
     Hq, N, d = q.shape
     L = prefix_rank_length(q, k, block_size, segment_size)
     if kv_rank.dtype != torch.int32 or kv_rank.shape != (k.shape[0], L) or not kv_rank.is_contiguous():
@@ -342,8 +382,7 @@ def sample_attention_mask(q: torch.Tensor, k: torch.Tensor, block_size: int, cia
                           workspace: Optional[torch.Tensor] = None):
     """SampleAttention's block mask: (block_count int32 [Hq][NB], block_idx int32 [Hq][NB(NB+1)/2]
     [, col fp64 [Hq][N], slash fp64 [Hq][N]]), for block_sparse_attn_prefill with perm = None."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
+    _check_qkv(q, k, None, block_size)
     shape = make_shape(q, k, block_size, 0, scale)
     Hq, N = q.shape[0], q.shape[1]
     NB = num_blocks(N, block_size)
@@ -370,14 +409,17 @@ def sample_attention_mask(q: torch.Tensor, k: torch.Tensor, block_size: int, cia
     return (count, idx, col, slash) if return_masses else (count, idx)
 
 
-def tile_max(q: torch.Tensor, k: torch.Tensor, block_size: int, scale: Optional[float] = None) -> torch.Tensor:
-    """Calibration helper: fp32 [Hq][NB(NB+1)/2] exact per-tile max of the scaled causal logits."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
-    shape = make_shape(q, k, block_size, 0, scale)
+def tile_max(q: torch.Tensor, k: torch.Tensor, block_size: int, scale: Optional[float] = None,
+             perm: Optional[torch.Tensor] = None, segment_size: int = 0) -> torch.Tensor:
+    """Calibration helper: fp32 [Hq][NB(NB+1)/2] per-tile max of the scaled causal logits, as the
+    early-stop gate computes it.  perm (with segment_size): tiles of earlier segments are read
+    through the permutation, as the gate reads them on a permuted mask."""
+    _check_qkv(q, k, None, block_size)
+    _check_tensor("perm", perm, torch.int32, (k.shape[0], k.shape[1]), q.device)
+    shape = make_shape(q, k, block_size, segment_size if perm is not None else 0, scale)
     NB = num_blocks(q.shape[1], block_size)
     tm = torch.empty((q.shape[0], NB * (NB + 1) // 2), dtype=torch.float32, device=q.device)
-    st = _lib.lib().pbsa_tile_max(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(tm), _stream())
+    st = _lib.lib().pbsa_tile_max(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(perm), _ptr(tm), _stream())
     _lib.check(st, "pbsa_tile_max")
     return tm
 
@@ -386,8 +428,7 @@ def calibrate_thresholds(tile_max_: torch.Tensor, q: torch.Tensor, k: torch.Tens
                          keep: int) -> torch.Tensor:
     """Early-stop thresholds fp32 [Hq][NB] from calibration tile maxima (as from tile_max on q, k):
     the keep-th largest tile max of each query block's row, -inf for rows of at most keep tiles."""
-    _check_bf16("q", q)
-    _check_bf16("k", k)
+    _check_qkv(q, k, None, block_size)
     shape = make_shape(q, k, block_size, 0)
     NB = num_blocks(q.shape[1], block_size)
     if tile_max_.dtype != torch.float32 or tile_max_.shape != (q.shape[0], NB * (NB + 1) // 2) \

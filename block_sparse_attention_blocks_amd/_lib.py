@@ -75,7 +75,7 @@ _SIG = {
                                                   ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P,
                                                   ctypes.c_size_t, _P]),
     "pbsa_sample_mask_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(PbsaShape), ctypes.c_int32, ctypes.c_int32]),
-    "pbsa_tile_max": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P]),
+    "pbsa_tile_max": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P]),
     "pbsa_calibrate_thresholds": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, ctypes.c_int32, _P, _P]),
     "pbsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pbsa_version": (ctypes.c_int32, []),

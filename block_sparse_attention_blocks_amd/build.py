@@ -11,10 +11,19 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpbsa.so")
 SOURCES = ["api.hip", "estimate.hip", "prefix_rank.hip", "sample_attn.hip", "attention.hip"]
-# per-source extra flags.  attention.hip: no NaN is produced or tested there (masked scores are
-# -inf), so max and compare need no NaN quieting; api.hip validates arguments with comparisons
+# MFMA accumulators stay in VGPRs: the fp64 kernels otherwise move every accumulator between the
+# AGPR and VGPR files around each MFMA.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# Per-source extra flags.  The attention sources: no NaN is produced or tested there (masked scores
+# are -inf), so max and compare need no NaN quieting; api.hip validates arguments with comparisons
 # that must keep their NaN meaning and gets no such flag.
-SOURCE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
+SOURCE_FLAGS = {
+    "api.hip": VGPR_FORM,
+    "estimate.hip": VGPR_FORM,
+    "prefix_rank.hip": VGPR_FORM,
+    "sample_attn.hip": VGPR_FORM,
+    "attention.hip": VGPR_FORM + ["-fno-honor-nans"],
+}
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -23,9 +32,6 @@ HIPCC_FLAGS = [
     "-fPIC",
     # packed fp32 VALU forms are kept out of generated code on purpose
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators stay in VGPRs: the fp64 kernels otherwise move every accumulator between
-    # the AGPR and VGPR files around each MFMA
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

@@ -156,24 +156,35 @@ pbsa_status pbsa_estimate_block_mask(const pbsa_shape* shape, const uint16_t* q,
                                           workspace, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+pbsa_status check_attn_args(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* perm, const int32_t* block_count, const int32_t* block_idx, float* out,
+                            Geometry* g) {
+  pbsa_status st = make_geometry(shape, g);
+  if (st != PBSA_OK) return st;
+  if (!q || !k || !v || !out) return PBSA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PBSA_ERR_INVALID_ARG;
+  if ((block_count == nullptr) != (block_idx == nullptr)) return PBSA_ERR_INVALID_ARG;
+  if (perm && g->S <= 0) return PBSA_ERR_INVALID_ARG;
+  return PBSA_OK;
+}
+}  // namespace
+
 pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
                                            const uint16_t* v, const int32_t* perm, const int32_t* block_count,
                                            const int32_t* block_idx, const float* early_stop_theta, float* out,
                                            float* lse, uint32_t* kept_bitmap, int32_t* device_error,
                                            void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
-  pbsa_status st = make_geometry(shape, &g);
+  pbsa_status st = check_attn_args(shape, q, k, v, perm, block_count, block_idx, out, &g);
   if (st != PBSA_OK) return st;
-  if (!q || !k || !v || !out) return PBSA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PBSA_ERR_INVALID_ARG;
-  if ((block_count == nullptr) != (block_idx == nullptr)) return PBSA_ERR_INVALID_ARG;
-  if (perm && g.S <= 0) return PBSA_ERR_INVALID_ARG;
   if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
     return st;
   if (g.N == 0) return PBSA_OK;
   return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out, lse,
                                          kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream)));
 }
+
 
 pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const int32_t* perm, const int32_t* block_count,
@@ -270,14 +281,14 @@ pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t
                                                     device_error, workspace, static_cast<hipStream_t>(stream)));
 }
 
-pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, float* tile_max,
-                          void* stream) {
+pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, const int32_t* perm,
+                          float* tile_max, void* stream) {
   Geometry g;
   pbsa_status st = make_geometry(shape, &g);
   if (st != PBSA_OK) return st;
   if (!q || !k || !tile_max || !aligned16(q) || !aligned16(k)) return PBSA_ERR_INVALID_ARG;
   if (g.N == 0) return PBSA_OK;
-  return from_hip(pbsa::launch_tile_max(g, q, k, tile_max, static_cast<hipStream_t>(stream)));
+  return from_hip(pbsa::launch_tile_max(g, q, k, perm, tile_max, static_cast<hipStream_t>(stream)));
 }
 
 pbsa_status pbsa_calibrate_thresholds(const pbsa_shape* shape, const float* tile_max, int32_t keep, float* theta,

@@ -117,8 +117,8 @@ hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, con
 size_t query_perm_workspace_bytes(const Geometry& g);
 hipError_t launch_query_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* qperm, void* ws,
                                     hipStream_t st);
-hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, float* tmax,
-                           hipStream_t st);
+hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, const int32_t* perm,
+                           float* tmax, hipStream_t st);
 hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);
 
 }  // namespace pbsa

@@ -35,9 +35,8 @@
  *   - Query head h reads KV head h / (Hq / Hkv).  Block J = tokens [J*B, min((J+1)*B, N));
  *     NB = ceil(N / B).  Segment of block J = (J*B) / S.  N need not be a multiple of B or S.
  *   - Ownership: every pointer is device memory owned by the caller (except pbsa_shape, which is
- *     host memory read during the call).  The library allocates nothing; its only state is a
- *     per-device cache of how many attention workgroups fit on the device at once.  Scratch
- *     memory is the caller's workspace, sized by pbsa_workspace_size.
+ *     host memory read during the call).  The library allocates nothing and keeps no state
+ *     between calls.  Scratch memory is the caller's workspace, sized by pbsa_workspace_size.
  *   - Streams: stream is a hipStream_t (NULL = the default stream).  Every call only enqueues
  *     work on it and returns; outputs are valid once the stream reaches that point.  Inputs,
  *     outputs and workspace must stay alive until then.  Calls that share a workspace must be
@@ -187,6 +186,7 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                            uint32_t* kept_bitmap, int32_t* device_error,
                                            void* workspace, size_t workspace_bytes, void* stream);
 
+
 /*
  * Attention with the marginal-gain early stop (S2O, Early-Stopping Rule; Kernel Implementation).
  * block_count/block_idx must hold the ranked order of pbsa_estimate_block_mask with
@@ -312,11 +312,17 @@ size_t pbsa_sample_mask_workspace_size(const pbsa_shape* shape, int32_t n_trunks
 
 /*
  * Early-stop calibration helper (Block Sparse Flash Attention, Approach: offline thresholds).
- * tile_max[h][I(I+1)/2 + J] = c * max over i in block I, j in block J, j <= i of q_i . k_j for
- * every J <= I, natural order, computed like stage 3's gate (fp32 accumulation).
+ * tile_max[h][I(I+1)/2 + J] = c * max over i in block I, j in the key rows block J stands for when
+ * read by I, j <= i, of q_i . k_j, for every J <= I -- the statistic stage 3's gate compares, on the
+ * same rows and with the same fp32 accumulation.
+ *   perm      nullable, int32 [Hkv][N]: as in pbsa_block_sparse_attn_prefill, a block of a segment
+ *             before I's (shape->segment_size > 0) stands for the keys perm[g][J*B .. J*B+B-1]; NULL
+ *             (or segment_size 0) gives natural order.  Thresholds for a permuted mask are calibrated
+ *             with the calibration inputs' own permutation.
  *   tile_max  out, fp32 [Hq][NB(NB+1)/2]
+ * A perm entry out of [0, N) reads a zero key row (no error word here).
  */
-pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+pbsa_status pbsa_tile_max(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k, const int32_t* perm,
                           float* tile_max, void* stream);
 
 /*

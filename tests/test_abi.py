@@ -87,7 +87,7 @@ def test_shape_validation(kw, expect):
                                       1 << 40, None) == expect
     assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
                                             None, None, None, None, 0, None) == expect
-    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == expect
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == expect
 
 
 def test_null_shape_and_pointers():
@@ -108,7 +108,7 @@ def test_null_shape_and_pointers():
     bad = ctypes.c_void_p(0x10002)
     assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), bad, FAKE, FAKE, None, None, None, None, FAKE,
                                             None, None, None, None, 0, None) == E
-    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, None) == E
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, None, None) == E
     assert l.pbsa_calibrate_thresholds(ctypes.byref(s), None, 64, FAKE, None) == E
     assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 64, None, None) == E
     assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 0, FAKE, None) == E
@@ -182,9 +182,9 @@ def test_stride_validation():
     l = _lib.lib()
     s = shape()
     s.q_stride_head, s.q_stride_token = 1024 * 128, 100  # token stride < d
-    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == _lib.PBSA_ERR_INVALID_ARG
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == _lib.PBSA_ERR_INVALID_ARG
     s.q_stride_token = 132  # not a multiple of 8
-    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == _lib.PBSA_ERR_INVALID_ARG
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == _lib.PBSA_ERR_INVALID_ARG
 
 
 def test_empty_sequence_is_a_no_op():
@@ -195,7 +195,7 @@ def test_empty_sequence_is_a_no_op():
                                       1 << 20, None) == 0
     assert l.pbsa_block_sparse_attn_prefill(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE,
                                             None, None, None, None, 0, None) == 0
-    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, FAKE, None) == 0
+    assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == 0
     assert l.pbsa_calibrate_thresholds(ctypes.byref(s), FAKE, 4, FAKE, None) == 0
 
 
@@ -284,3 +284,4 @@ def test_sample_attention_entry_validates_before_launch():
     assert m(*args(s, 0.9, 4, 8, w=None)) == W
     assert m(*args(shape(N=0), 0.9, 4, 8, w=None)) == 0
     assert m(ctypes.byref(s), FAKE, FAKE, 0.9, 4, 8, 1, None, FAKE, None, None, ws, big, None) == E
+

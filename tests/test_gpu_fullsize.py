@@ -10,9 +10,9 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import (bitmap_to_kept, bitmap_to_kept_square, compare_lse, compare_mask, compare_out, compare_perm,
-                    compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask, kept_to_mask,
-                    two_pass_lists)
+from parity import (F32_U, bitmap_to_kept, bitmap_to_kept_square, compare_gate, compare_lse, compare_mask, compare_out,
+                    compare_perm, compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask,
+                    gate_error_bound, kept_to_mask, two_pass_lists)
 from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
 
 pytestmark = pytest.mark.gpu
@@ -226,9 +226,17 @@ def test_fullsize_64k_early_stop_sampled():
     q, k, v = host["q"], host["k"], host["v"]
     rows = _sample_rows(Hq, NB, 6, 10)
     tm_o = oracle.tile_max(q, k, B, rows=rows)
-    for h, I in rows:
+    bound = gate_error_bound(q, k, None, B, None, rows)
+    exact = {}
+    for h, I in rows:  # GPU tile maxima within the fp32 bound, decisions against the fp64 oracle
         o = oracle.tri_offset(I)
-        assert np.abs(tm_o[h, o:o + I + 1] - tm_g[h, o:o + I + 1]).max() <= 1e-3
+        m = tm_o[h, o:o + I + 1]
+        err = np.abs(tm_g[h, o:o + I + 1] - m)
+        assert (err <= bound[(h, I)] + 4 * F32_U * np.abs(m)).all(), (h, I, err.max())
+        exact[(h, I)] = m
+    n, band = compare_gate(kept, {r: list(range(r[1] + 1)) for r in rows}, exact, bound, theta)
+    _log(f"[fullsize] 64K early stop: {n} sampled gate decisions, {band} inside the fp32 bound")
+    assert band <= max(2, n // 200), (n, band)
     kc, ki = kept_to_mask(kept, Hq, NB)
     out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, kc, ki, B, None, rows=rows)
     mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o)
