@@ -209,10 +209,12 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = True,
                               return_kept: bool = False, return_error: bool = False,
-                              workspace: Optional[torch.Tensor] = None):
+                              workspace: Optional[torch.Tensor] = None, no_alloc: bool = False):
     """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word).
     workspace: optional preallocated device buffer of at least workspace_size(shape, PBSA_OP_ATTENTION)
-    bytes (the work deques); one is allocated per call otherwise."""
+    bytes (the work deques); one is allocated per call otherwise.  no_alloc: call
+    pbsa_block_sparse_attn_prefill_noalloc instead, whose work deques live in the library (no
+    workspace); pass out, and lse or return_lse=False, so that this call allocates nothing either."""
     _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, early_stop_theta, out, lse)
     Hq, N, d = q.shape
     if out is None:
@@ -226,11 +228,17 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         kept = torch.zeros((Hq, words), dtype=torch.int32, device=q.device)
     err = torch.zeros(1, dtype=torch.int32, device=q.device) if return_error else None
     shape = make_shape(q, k, block_size, segment_size, scale, out=out)
-    ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
-    st = _lib.lib().pbsa_block_sparse_attn_prefill(
-        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
-        _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
-    _lib.check(st, "pbsa_block_sparse_attn_prefill")
+    if no_alloc:
+        st = _lib.lib().pbsa_block_sparse_attn_prefill_noalloc(
+            ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
+            _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _stream())
+        _lib.check(st, "pbsa_block_sparse_attn_prefill_noalloc")
+    else:
+        ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
+        st = _lib.lib().pbsa_block_sparse_attn_prefill(
+            ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
+            _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
+        _lib.check(st, "pbsa_block_sparse_attn_prefill")
     res = [out]
     if return_lse:
         res.append(lse)

@@ -64,6 +64,8 @@ _SIG = {
                                                 ctypes.c_uint32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_block_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
                                                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pbsa_block_sparse_attn_prefill_noalloc": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P,
+                                                              _P, _P, _P, _P, _P, _P]),
     "pbsa_s2o_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, ctypes.c_float,
                                              _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_build_prefix_kv_ranking": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, ctypes.c_size_t, _P]),

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "common.h"
 
 using pbsa::Geometry;
@@ -185,6 +187,51 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                          kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream)));
 }
 
+// Device memory of pbsa_block_sparse_attn_prefill_noalloc: the work deques that the pipelined
+// attention kernels otherwise keep in the caller's workspace (one 64-bit word per deque, reset by
+// a kernel on the stream before every launch).  Every GPU the library runs on holds its own copy
+// of this array until the process ends.  On the host, `scratch` is only a stand-in for the symbol:
+// its device address is looked up per device with hipGetSymbolAddress and used everywhere instead.
+constexpr size_t kNoAllocScratchBytes = 256;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];  // device address of `scratch`, per device ordinal
+
+// Address of the current device's copy of `scratch`: looked up on the first call on that device
+// (with the device current) and kept.  Concurrent first calls look up the same address.
+pbsa_status scratch_on_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PBSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PBSA_ERR_UNSUPPORTED;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PBSA_ERR_HIP;
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PBSA_OK;
+}
+}  // namespace
+
+pbsa_status pbsa_block_sparse_attn_prefill_noalloc(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                                   const uint16_t* v, const int32_t* perm,
+                                                   const int32_t* block_count, const int32_t* block_idx,
+                                                   const float* early_stop_theta, float* out, float* lse,
+                                                   uint32_t* kept_bitmap, int32_t* device_error, void* stream) {
+  Geometry g;
+  pbsa_status st = check_attn_args(shape, q, k, v, perm, block_count, block_idx, out, &g);
+  if (st != PBSA_OK) return st;
+  if (g.N == 0) return PBSA_OK;
+  // the deques of this shape (one word per KV group, at most kMaxDeques) must fit the array
+  const size_t need = sizeof(unsigned long long) * (size_t)(g.Hkv < pbsa::kMaxDeques ? g.Hkv : pbsa::kMaxDeques);
+  if (need > kNoAllocScratchBytes) return PBSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != PBSA_OK) return st;
+  return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out, lse,
+                                         kept_bitmap, device_error, ws, static_cast<hipStream_t>(stream)));
+}
 
 pbsa_status pbsa_s2o_attn_prefill(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
                                   const uint16_t* v, const int32_t* perm, const int32_t* block_count,

@@ -35,8 +35,10 @@
  *   - Query head h reads KV head h / (Hq / Hkv).  Block J = tokens [J*B, min((J+1)*B, N));
  *     NB = ceil(N / B).  Segment of block J = (J*B) / S.  N need not be a multiple of B or S.
  *   - Ownership: every pointer is device memory owned by the caller (except pbsa_shape, which is
- *     host memory read during the call).  The library allocates nothing and keeps no state
- *     between calls.  Scratch memory is the caller's workspace, sized by pbsa_workspace_size.
+ *     host memory read during the call).  The library allocates nothing.  Scratch memory is the
+ *     caller's workspace, sized by pbsa_workspace_size; the only exception is
+ *     pbsa_block_sparse_attn_prefill_noalloc, whose 256-byte queue array is a device variable of
+ *     the library (one per GPU, with its address kept per device after the first call).
  *   - Streams: stream is a hipStream_t (NULL = the default stream).  Every call only enqueues
  *     work on it and returns; outputs are valid once the stream reaches that point.  Inputs,
  *     outputs and workspace must stay alive until then.  Calls that share a workspace must be
@@ -186,6 +188,25 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                            uint32_t* kept_bitmap, int32_t* device_error,
                                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pbsa_block_sparse_attn_prefill without a workspace, for callers that cannot allocate device
+ * memory: code recorded under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, layouts, results and errors as pbsa_block_sparse_attn_prefill; the
+ * work queues live in a 256-byte device array of the library instead (each GPU it runs on holds
+ * its own copy until the process ends; its address is looked up on the first call on a device).
+ * The call allocates nothing and calls no allocating routine.  Limit: the queues of one call take
+ * 8 bytes per KV head, at most 64; a shape needing more than the array returns PBSA_ERR_WORKSPACE
+ * (none does today).  Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call resets what it uses on its stream before its kernel): calls that overlap on
+ * one GPU -- on different streams, or from several host threads without ordering -- race.
+ */
+pbsa_status pbsa_block_sparse_attn_prefill_noalloc(const pbsa_shape* shape, const uint16_t* q,
+                                                   const uint16_t* k, const uint16_t* v,
+                                                   const int32_t* perm, const int32_t* block_count,
+                                                   const int32_t* block_idx,
+                                                   const float* early_stop_theta, float* out,
+                                                   float* lse, uint32_t* kept_bitmap,
+                                                   int32_t* device_error, void* stream);
 
 /*
  * Attention with the marginal-gain early stop (S2O, Early-Stopping Rule; Kernel Implementation).

@@ -285,3 +285,19 @@ def test_sample_attention_entry_validates_before_launch():
     assert m(*args(shape(N=0), 0.9, 4, 8, w=None)) == 0
     assert m(ctypes.byref(s), FAKE, FAKE, 0.9, 4, 8, 1, None, FAKE, None, None, ws, big, None) == E
 
+
+def test_noalloc_attention_validates_before_touching_the_device():
+    l = _lib.lib()
+    E = _lib.PBSA_ERR_INVALID_ARG
+    s = shape()
+    f = l.pbsa_block_sparse_attn_prefill_noalloc
+    assert f(None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None) == E
+    assert f(ctypes.byref(s), FAKE, FAKE, None, None, None, None, None, FAKE, None, None, None, None) == E
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None, None, None, None) == E
+    bad = ctypes.c_void_p(0x10002)
+    assert f(ctypes.byref(s), bad, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None) == E
+    s0 = shape(N=0)
+    assert f(ctypes.byref(s0), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None) == 0
+    s.head_dim = 96
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None,
+             None) == _lib.PBSA_ERR_UNSUPPORTED
