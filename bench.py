@@ -11,7 +11,10 @@ attention.  Prints ONE JSON line on stdout (progress goes to stderr):
                 tiles (4 B^2 d per tile) / mean kernel duration (HIP events on its stream)
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample, extrapolated per stage
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_32k]
+  subrecords    the 128K layer (tau 0.9 and tau bisected to ~10% density), the 64K early-stop
+                layer and the 1K single-head case, each against the library's dense kernel
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_32k] [--no-subrecords]
 """
 from __future__ import annotations
 
@@ -60,15 +63,16 @@ def read_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, out: str, command: str) -> int:
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the attention kernel, scaled by what the same
-    counters read for the plain copy of COPY_CALIB_BYTES in the same run."""
+def summarize_pmc(fetch_csv: str, write_csv: str, out: str, command: str, kernel: str = ATTN_KERNEL,
+                  workload: str = "llama8b_32k") -> int:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of one kernel, scaled by what the same counters
+    read for the plain copy of COPY_CALIB_BYTES in the same run."""
     import csv
     import statistics
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        attn = [float(r["Counter_Value"]) for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
+        attn = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"].replace("pbsa::", "")]
         copy = [float(r["Counter_Value"]) for r in rows
                 if "copy" in r["Kernel_Name"].lower() and float(r["Counter_Value"]) > COPY_CALIB_BYTES / 1024 / 4]
         return statistics.median(attn), statistics.median(copy), len(attn)
@@ -79,7 +83,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out: str, command: str) -> int
     sw = (COPY_CALIB_BYTES / 1024) / wc   # same for writes
     traffic = (fa * sf + wa * sw) * 1024
     with open(out, "w") as f:
-        f.write(f"# {ATTN_KERNEL}, llama8b_32k workload: HBM traffic per launch from rocprofv3 byte counters\n")
+        f.write(f"# {kernel}, {workload} workload: HBM traffic per launch from rocprofv3 byte counters\n")
         f.write(f"# command: {command}\n")
         f.write(f"# FETCH_SIZE / WRITE_SIZE are KiB per dispatch (median of {n_f} / {n_w} dispatches); each is scaled\n")
         f.write(f"# by the ratio true/counted bytes of a plain {COPY_CALIB_BYTES} B device copy in the same run.\n")
@@ -119,7 +123,7 @@ def summarize_stats(stats_csv: str, bench_out: str, out: str, command: str, work
 
     total = sum(float(r["TotalDurationNs"]) for r in rows)
     with open(out, "w") as f:
-        f.write(f"# rocprofv3 kernel-trace statistics, {workload} workload\n")
+        f.write(f"# rocprofv3 kernel-trace statistics, {workload}\n")
         f.write(f"# command (from the repository root, TMPDIR=/tmp):\n#   {command}\n")
         f.write("# calls include warm-up, timed steps and bench.py's own dense-kernel timing; times in microseconds.\n")
         if kernel_ms is not None:
@@ -150,11 +154,20 @@ def cpu_baseline(w, x, count, budget_s, np):
     (head, query block) rows extrapolated by computed-tile count."""
     import oracle
     from workloads import bf16_bits_to_f32
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=cores, user_api="blas")
+    except ImportError:  # pragma: no cover
+        limit = None
+    try:
+        return _cpu_baseline(w, x, count, budget_s, np, oracle, bf16_bits_to_f32, cores)
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
+
+
+def _cpu_baseline(w, x, count, budget_s, np, oracle, bf16_bits_to_f32, cores):
     q = bf16_bits_to_f32(x["q"]).astype(np.float64)
     k = bf16_bits_to_f32(x["k"]).astype(np.float64)
     v = bf16_bits_to_f32(x["v"]).astype(np.float64)
@@ -186,7 +199,8 @@ def cpu_baseline(w, x, count, budget_s, np):
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"permutation and mask stages in full ({t1 - t0:.2f} s, {t2 - t1:.2f} s); attention on "
+        "sample": (f"{cores} cores (the process's affinity mask), BLAS threads set to {cores}; "
+                   f"permutation and mask stages in full ({t1 - t0:.2f} s, {t2 - t1:.2f} s); attention on "
                    f"{len(rows)} seeded (head, query-block) rows = {tiles} of {total_tiles} computed tiles "
                    f"({t_att:.2f} s), extrapolated by tile count to {t_att_full:.1f} s; step {t_step:.1f} s"),
         "step_s": t_step,
@@ -293,14 +307,32 @@ def suite(args) -> int:
     if "sample" in parts:
         suite_sample(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps)
     out_f.close()
+    if args.copy_calib:
+        copy_calibration(torch)
     return 0
 
 
+def copy_calibration(torch):
+    """A plain device copy of COPY_CALIB_BYTES, whose byte counters scale the kernels' counters."""
+    src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
+    for rec in measure_128k(torch, np, pbsa, WORKLOADS, load, stream, reps):
+        emit(rec)
+
+
+def measure_128k(torch, np, pbsa, WORKLOADS, load, stream, reps, sdpa=True):
+    """The 128K layer as configured (tau 0.9) and at tau bisected to ~10% block density: stage times,
+    the library's dense causal kernel and the speedups, MFMA fraction on computed tiles."""
     w = WORKLOADS["llama8b_128k"]
     t0 = time.perf_counter()
     d = load(w)
-    log(f"[suite] {w.name} inputs in {time.perf_counter() - t0:.1f} s")
+    log(f"[bench] {w.name} inputs in {time.perf_counter() - t0:.1f} s")
     q, k, v = d["q"], d["k"], d["v"]
     B, S, NB, Hq = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads
     causal_tiles = Hq * NB * (NB + 1) // 2
@@ -322,8 +354,9 @@ def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
 
     dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
     t_dense = _events(torch, stream, dense, max(2, reps // 2))
-    sdpa_ms, sdpa_backend = torch_sdpa_ms(torch, q, k, v, stream, 2)
+    sdpa_ms, sdpa_backend = torch_sdpa_ms(torch, q, k, v, stream, 2) if sdpa else (None, "not run")
     t_perm = _events(torch, stream, fp, reps)
+    recs = []
     for label, tau in (("as_configured", w.mass_tau), ("density_10pct", None)):
         if tau is None:  # bisect the mass target to a ~10% computed-block fraction
             lo, hi = 0.0, 1.0
@@ -343,7 +376,7 @@ def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
         tiles = int(count.sum().item())
         ta = t_attn["median_ms"]
         step = t_perm["median_ms"] + t_mask["median_ms"] + ta
-        emit({"workload": w.name, "point": label, "mass_tau": tau, "block_density": dens,
+        recs.append({"workload": w.name, "point": label, "mass_tau": tau, "block_density": dens,
               "permutation_ms": t_perm["median_ms"], "mask_ms": t_mask["median_ms"], "attention_ms": ta,
               "step_ms": step, "dense_kernel_ms": t_dense["median_ms"],
               "torch_sdpa_dense_ms": sdpa_ms, "torch_sdpa_backend": sdpa_backend,
@@ -354,6 +387,7 @@ def suite_128k(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
               "dense_equiv_tflops_step": w.dense_causal_flop / (step * 1e-3) / 1e12})
     del d, q, k, v, out, lse, ws_p, ws_m, perm, count, idx
     torch.cuda.empty_cache()
+    return recs
 
 
 def suite_sweep(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
@@ -381,6 +415,12 @@ def suite_sweep(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
 
 
 def suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
+    emit(measure_earlystop(torch, np, pbsa, WORKLOADS, load, stream, reps))
+
+
+def measure_earlystop(torch, np, pbsa, WORKLOADS, load, stream, reps):
+    """64K tile-max early stop with thresholds calibrated on a second draw (top 64 tiles per query
+    block): kept-tile and V-gather fractions, time against the library's dense causal kernel."""
     w = WORKLOADS["llama8b_64k_earlystop"]
     d = load(w)
     cal = load(w, seed=w.calib_seed)
@@ -398,15 +438,46 @@ def suite_earlystop(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     t_gate = _events(torch, stream, gated, reps)["median_ms"]
     _, kept = pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, early_stop_theta=theta_t,
                                              return_lse=False, return_kept=True)
-    kept_tiles = int(np.unpackbits(kept.cpu().numpy().view(np.uint8)).sum())
+    bits = np.unpackbits(kept.cpu().numpy().view(np.uint8), bitorder="little").reshape(Hq, -1)
+    kept_tiles = int(bits.sum())
     causal_tiles = Hq * NB * (NB + 1) // 2
+    # the head-pair kernel gathers a V tile when either head of the pair keeps it
+    pairs = bits[0::2] | bits[1::2] if Hq % 2 == 0 and (Hq // w.num_kv_heads) % 2 == 0 else bits
+    v_gather = int(pairs.sum()) * (2 if pairs is not bits else 1)
     flop = causal_tiles * 2.0 * B * B * w.head_dim + kept_tiles * 2.0 * B * B * w.head_dim
-    emit({"workload": w.name, "calibration": f"seed {w.calib_seed}, keep top {w.calib_keep} tiles per query block",
-          "kept_tile_fraction": kept_tiles / causal_tiles, "attention_ms": t_gate, "dense_kernel_ms": t_dense,
-          "attention_speedup_vs_dense": t_dense / t_gate,
-          "mfma_frac": flop / (t_gate * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+    rec = {"workload": w.name, "calibration": f"seed {w.calib_seed}, keep top {w.calib_keep} tiles per query block",
+           "kept_tile_fraction": kept_tiles / causal_tiles, "v_gather_fraction": v_gather / causal_tiles,
+           "attention_ms": t_gate, "dense_kernel_ms": t_dense, "attention_speedup_vs_dense": t_dense / t_gate,
+           "mfma_frac": flop / (t_gate * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     del d, q, k, v, out
     torch.cuda.empty_cache()
+    return rec
+
+
+def measure_1k(torch, np, pbsa, WORKLOADS, load, stream, reps):
+    """The single-head 1K case: the three stages and the library's dense causal kernel."""
+    w = WORKLOADS["single_head_1k"]
+    d = load(w)
+    q, k, v = d["q"], d["k"], d["v"]
+    B, S, NB, Hq = w.block_size, w.segment_size, w.num_blocks, w.num_q_heads
+    perm = pbsa.build_segment_permutation(q, k, B, S)
+    count, idx = pbsa.estimate_block_mask(q, k, perm, B, S, w.mass_tau, w.force_diag, w.force_first)
+    out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((Hq, w.seq_len), dtype=torch.float32, device="cuda")
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    fp = lambda: pbsa.build_segment_permutation(q, k, B, S, perm=perm)
+    fm = lambda: pbsa.estimate_block_mask(q, k, perm, B, S, w.mass_tau, w.force_diag, w.force_first,
+                                          out=(count, idx))
+    fa = lambda: pbsa.block_sparse_attn_prefill(q, k, v, perm, count, idx, B, S, out=out, lse=lse, workspace=ws)
+    fd = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse, workspace=ws)
+    t = {n: _events(torch, stream, f, reps)["median_ms"] for n, f in
+         (("permutation", fp), ("mask", fm), ("attention", fa), ("dense", fd))}
+    tiles = int(count.sum().item())
+    step = t["permutation"] + t["mask"] + t["attention"]
+    return {"workload": w.name, "block_density": tiles / (Hq * NB * (NB + 1) // 2), "mass_tau": w.mass_tau,
+            "stages_ms": {k_: t[k_] for k_ in ("permutation", "mask", "attention")}, "step_ms": step,
+            "dense_kernel_ms": t["dense"], "attention_speedup_vs_dense": t["dense"] / t["attention"],
+            "step_speedup_vs_dense": t["dense"] / step}
 
 
 def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pass=False, qperm=False):
@@ -508,6 +579,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--mass-tau", type=float, default=None, help="override the workload's mass target")
+    ap.add_argument("--no-subrecords", action="store_true",
+                    help="time only the main workload (no 128K, 64K early-stop and 1K sub-records)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle attention sampling")
     ap.add_argument("--copy-calib", action="store_true",
@@ -518,6 +592,8 @@ def main() -> int:
                     help="write a kernel table from a rocprofv3 kernel_stats.csv and the bench line of that run")
     ap.add_argument("--summary-out", default=TRAFFIC_SUMMARY)
     ap.add_argument("--summary-command", default="")
+    ap.add_argument("--summary-kernel", default=ATTN_KERNEL, help="kernel whose counters --summarize-pmc reads")
+    ap.add_argument("--summary-label", default="", help="workload description in a --summarize-stats header")
     ap.add_argument("--suite", action="store_true", help="run the secondary measurements instead")
     ap.add_argument("--suite-out", default="bench_suite.jsonl")
     ap.add_argument("--suite-reps", type=int, default=5)
@@ -532,10 +608,11 @@ def main() -> int:
         return 2
 
     if args.summarize_pmc:
-        return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_out, args.summary_command)
+        return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_out, args.summary_command,
+                             args.summary_kernel, args.workload)
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.summary_out,
-                               args.summary_command, args.workload)
+                               args.summary_command, args.summary_label or f"{args.workload} workload")
     if args.suite:
         os.makedirs(os.path.dirname(os.path.abspath(args.suite_out)), exist_ok=True)
         return suite(args)
@@ -547,6 +624,9 @@ def main() -> int:
     from workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.mass_tau is not None:
+        import dataclasses
+        w = dataclasses.replace(w, mass_tau=args.mass_tau)
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     torch.cuda.set_device(0)
@@ -661,12 +741,30 @@ def main() -> int:
                              "step_speedup": None if sdpa_ms is None else sdpa_ms / (t_step * 1e3)},
     }
     if args.copy_calib:
-        src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device=dv)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    res["roofline"]["traffic"] = read_traffic()
+        copy_calibration(torch)
+    res["roofline"]["traffic"] = read_traffic() if w.name == "llama8b_32k" and args.mass_tau is None else None
+    if not args.no_subrecords:
+        # the other workloads, timed after the main one (their inputs are generated here)
+        del dev, q, k, v, out, lse, ws_p, ws_m, ws_a, perm, idx
+        torch.cuda.empty_cache()
+        from workloads import generate_for
+
+        def load(wl, seed=None):
+            xx = generate_for(wl, seed=seed)
+            return {n: torch.from_numpy(xx[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+
+        sub = {}
+        t_sub = time.perf_counter()
+        recs = measure_128k(torch, np, pbsa, WORKLOADS, load, stream, 5, sdpa=False)
+        sub["llama8b_128k"] = {r["point"]: {kk: vv for kk, vv in r.items() if kk not in ("workload", "point")}
+                               for r in recs}
+        log(f"[bench] llama8b_128k: {json.dumps(sub['llama8b_128k'])}")
+        sub["llama8b_64k_earlystop"] = measure_earlystop(torch, np, pbsa, WORKLOADS, load, stream, 5)
+        log(f"[bench] llama8b_64k_earlystop: {json.dumps(sub['llama8b_64k_earlystop'])}")
+        sub["single_head_1k"] = measure_1k(torch, np, pbsa, WORKLOADS, load, stream, 20)
+        log(f"[bench] single_head_1k: {json.dumps(sub['single_head_1k'])}")
+        log(f"[bench] sub-records in {time.perf_counter() - t_sub:.1f} s")
+        res["subrecords"] = sub
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (bounded sample)")
         cb = cpu_baseline(w, x, count.cpu().numpy(), args.cpu_budget, np)
