@@ -461,12 +461,12 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   auto gather_k = [&](int u, uint16_t* dst) {
     const uint32_t* ids = rowid[u & 3];
     auto rf = [&](int j) { return ids[j]; };
-    dma_tile<D, BLK, false, decltype(rf), BLK, C::WAVES>(dst, kr, rf);
+    dma_tile<D, BLK, false, decltype(rf), BLK, C::WAVES>(dst, kr, rf, opaque(lane));
   };
   auto gather_v = [&](int u, uint16_t* dst) {
     const uint32_t* ids = rowid[u & 3];
     auto rf = [&](int j) { return ids[j]; };
-    dma_tile<D, BLK, true, decltype(rf), BLK, C::WAVES>(dst, vr, rf);
+    dma_tile<D, BLK, true, decltype(rf), BLK, C::WAVES>(dst, vr, rf, opaque(lane));
   };
 
   SoftmaxState<D, BLK> st;
@@ -495,14 +495,15 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     f32x16 sc[KB];
     float row_max = -INFINITY;
     if ((e >> (16 + hh)) & 1u) {
+      const int rel = opaque(qloc - 4 * h2);  // causal offset, computed per tile (see opaque)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, qloc - kb * 32 - 4 * h2, kb == 0 ? first : nullptr);
+        sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, rel - kb * 32, kb == 0 ? first : nullptr);
       row_max = tile_row_max<KB>(sc);
     }
     const float wm = wave_max_f32(qvalid ? row_max : -INFINITY);
-    if (lane == 0) red[u & 1][wave] = wm;
-    if (u + 2 < nblk && t < BLK) rowid[(u + 2) & 3][t] = row_off(pr);
+    if (lane == 0) red[u & 1][opaque(wave)] = wm;
+    if (u + 2 < nblk && t < BLK) rowid[(u + 2) & 3][opaque(t)] = row_off(pr);
     wait_vmcnt<0>();  // V of block u-1 and K of block u+1 have landed (this wave's share)
     __syncthreads();
     if (keep_prev) tile_pv<D, BLK>(st, pb, Vp);

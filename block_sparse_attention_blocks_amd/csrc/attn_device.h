@@ -148,14 +148,16 @@ __device__ __forceinline__ void lds_dma_b32(rsrc_t r, uint32_t lds, uint32_t off
 
 // One gathered tile: the rows at byte offsets row_off(j) of the head's slab into LDS [ROWS][D]
 // with the chunk swizzle.  An offset of kOutOfRange leaves a zero row.
+// lane: this lane's index, passed in when the caller wants the per-lane swizzle offsets computed
+// at each gather rather than hoisted out of its loop (see opaque_lane); -1 reads threadIdx.x.
 template <int D, int BLK, bool IS_V, typename RowFn, int ROWS = AttnCfg<D, BLK>::KT,
           int WAVES = AttnCfg<D, BLK>::WAVES, bool ASM = false>
-__device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, RowFn row_off) {
+__device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, RowFn row_off, int lane_in = -1) {
   constexpr int RPI = 512 / D;  // rows per 1 KiB wave instruction
   constexpr int LPR = D / 8;    // lanes per row
   constexpr int NI = ROWS / (RPI * WAVES);
   static_assert(NI * RPI * WAVES == ROWS, "tile rows must split evenly over the waves");
-  const int lane = threadIdx.x & 63;
+  const int lane = lane_in >= 0 ? lane_in : (int)(threadIdx.x & 63);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -172,6 +174,15 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, RowFn row_off)
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A copy of x that the compiler cannot see through.  Values derived from it inside a loop body are
+// computed there instead of being hoisted out of the loop and kept in registers for its whole
+// length: where registers run short, the hoisted per-lane constants were spilled, and reloading a
+// spilled value waits (vmcnt) for every load in flight, gathers included.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 // Online-softmax state of one lane's query column (S2O section 3: m, l, acc).  m is kept in log2
 // units and only moved when a block of scores exceeds it by more than kLazy: the probabilities
