@@ -209,13 +209,20 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = True,
                               return_kept: bool = False, return_error: bool = False,
-                              workspace: Optional[torch.Tensor] = None, no_alloc: bool = False):
+                              workspace: Optional[torch.Tensor] = None, no_alloc: bool = False,
+                              max_workgroups: int = 0, claim_back: bool = False):
     """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word).
     workspace: optional preallocated device buffer of at least workspace_size(shape, PBSA_OP_ATTENTION)
     bytes (the work deques); one is allocated per call otherwise.  no_alloc: call
     pbsa_block_sparse_attn_prefill_noalloc instead, whose work deques live in the library (no
-    workspace); pass out, and lse or return_lse=False, so that this call allocates nothing either."""
+    workspace); pass out, and lse or return_lse=False, so that this call allocates nothing either.
+    max_workgroups / claim_back: launch options of pbsa_block_sparse_attn_prefill_ex (a cap on the
+    persistent grid, and the order workgroups take rows in); results do not depend on them."""
     _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, early_stop_theta, out, lse)
+    if int(max_workgroups) < 0:
+        raise ValueError("max_workgroups must be >= 0")
+    if no_alloc and (max_workgroups or claim_back):
+        raise ValueError("launch options are not available with no_alloc")
     Hq, N, d = q.shape
     if out is None:
         out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
@@ -233,6 +240,14 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
             _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _stream())
         _lib.check(st, "pbsa_block_sparse_attn_prefill_noalloc")
+    elif max_workgroups or claim_back:
+        ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
+        opt = _lib.PbsaLaunchOptions(int(max_workgroups), _lib.PBSA_LAUNCH_CLAIM_BACK if claim_back else 0)
+        st = _lib.lib().pbsa_block_sparse_attn_prefill_ex(
+            ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
+            _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes,
+            ctypes.byref(opt), _stream())
+        _lib.check(st, "pbsa_block_sparse_attn_prefill_ex")
     else:
         ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
         st = _lib.lib().pbsa_block_sparse_attn_prefill(

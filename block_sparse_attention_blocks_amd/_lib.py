@@ -47,6 +47,16 @@ class PbsaShape(ctypes.Structure):
     ]
 
 
+PBSA_LAUNCH_CLAIM_BACK = 1
+
+
+class PbsaLaunchOptions(ctypes.Structure):
+    _fields_ = [
+        ("max_workgroups", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
 class PbsaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -64,6 +74,9 @@ _SIG = {
                                                 ctypes.c_uint32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_block_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
                                                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pbsa_block_sparse_attn_prefill_ex": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
+                                                         _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                                         ctypes.POINTER(PbsaLaunchOptions), _P]),
     "pbsa_block_sparse_attn_prefill_noalloc": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P,
                                                               _P, _P, _P, _P, _P, _P]),
     "pbsa_s2o_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, ctypes.c_float,

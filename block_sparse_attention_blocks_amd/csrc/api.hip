@@ -187,6 +187,29 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                          kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream)));
 }
 
+pbsa_status pbsa_block_sparse_attn_prefill_ex(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                              const uint16_t* v, const int32_t* perm, const int32_t* block_count,
+                                              const int32_t* block_idx, const float* early_stop_theta, float* out,
+                                              float* lse, uint32_t* kept_bitmap, int32_t* device_error,
+                                              void* workspace, size_t workspace_bytes,
+                                              const pbsa_launch_options* options, void* stream) {
+  pbsa::LaunchOpts opt;
+  if (options) {
+    if (options->max_workgroups < 0 || (options->flags & ~PBSA_LAUNCH_CLAIM_BACK) != 0) return PBSA_ERR_INVALID_ARG;
+    opt.max_wg = options->max_workgroups;
+    opt.claim_back = (options->flags & PBSA_LAUNCH_CLAIM_BACK) != 0;
+  }
+  Geometry g;
+  pbsa_status st = check_attn_args(shape, q, k, v, perm, block_count, block_idx, out, &g);
+  if (st != PBSA_OK) return st;
+  if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
+    return st;
+  if (g.N == 0) return PBSA_OK;
+  return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out, lse,
+                                         kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream),
+                                         opt));
+}
+
 // Device memory of pbsa_block_sparse_attn_prefill_noalloc: the work deques that the pipelined
 // attention kernels otherwise keep in the caller's workspace (one 64-bit word per deque, reset by
 // a kernel on the stream before every launch).  Every GPU the library runs on holds its own copy

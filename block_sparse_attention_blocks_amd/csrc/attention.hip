@@ -659,7 +659,7 @@ void attn_gated_kernel(AttnArgs a) {
 // The number of resident workgroups is queried on every call (the runtime answers from the kernel's
 // metadata without touching the device), so the library keeps no state between calls.
 template <int D, int BLK, bool DENSE, int HPW, bool S2O = false>
-static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st) {
+static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st, int max_wg = 0) {
   constexpr int THREADS = PipeCfg<D, BLK, HPW>::THREADS;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -668,7 +668,8 @@ static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_pipe_kernel<D, BLK, DENSE, HPW, S2O>, THREADS,
                                                         0)) != hipSuccess)
     return e;
-  const int resident = cus * (per_cu > 0 ? per_cu : 1);
+  int resident = cus * (per_cu > 0 ? per_cu : 1);
+  if (max_wg > 0 && max_wg < resident) resident = max_wg;
   if ((long long)a.NB * (a.Hq / HPW) >= (1ll << 24)) return hipErrorInvalidValue;  // item index field
   deque_init_kernel<<<1, 64, 0, st>>>(a, a.G / HPW);
   const int grid = items < resident ? items : resident;
@@ -677,13 +678,13 @@ static hipError_t launch_persistent(const AttnArgs& a, int items, hipStream_t st
 }
 
 template <int D, int BLK, int MODE>
-static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st) {
+static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st, int max_wg) {
   if constexpr (MODE == MODE_ATTN || MODE == MODE_DENSE) {
     constexpr bool DENSE = MODE == MODE_DENSE;
     if ((a.G & 1) == 0) {
-      return launch_persistent<D, BLK, DENSE, 2>(a, nwg / 2, st);
+      return launch_persistent<D, BLK, DENSE, 2>(a, nwg / 2, st, max_wg);
     } else {
-      return launch_persistent<D, BLK, DENSE, 1>(a, nwg, st);
+      return launch_persistent<D, BLK, DENSE, 1>(a, nwg, st, max_wg);
     }
   } else if (MODE == MODE_ATTN_GATED && (a.G & 1) == 0) {
     if (a.count == nullptr) {
@@ -698,12 +699,12 @@ static hipError_t launch_mode(const AttnArgs& a, int nwg, hipStream_t st) {
 }
 
 template <int MODE>
-static hipError_t dispatch(const Geometry& g, const AttnArgs& a, hipStream_t st) {
+static hipError_t dispatch(const Geometry& g, const AttnArgs& a, hipStream_t st, int max_wg = 0) {
   const int nwg = g.Hq * g.NB;
-  if (g.d == 128 && g.B == 128) return launch_mode<128, 128, MODE>(a, nwg, st);
-  if (g.d == 128 && g.B == 64) return launch_mode<128, 64, MODE>(a, nwg, st);
-  if (g.d == 64 && g.B == 128) return launch_mode<64, 128, MODE>(a, nwg, st);
-  return launch_mode<64, 64, MODE>(a, nwg, st);
+  if (g.d == 128 && g.B == 128) return launch_mode<128, 128, MODE>(a, nwg, st, max_wg);
+  if (g.d == 128 && g.B == 64) return launch_mode<128, 64, MODE>(a, nwg, st, max_wg);
+  if (g.d == 64 && g.B == 128) return launch_mode<64, 128, MODE>(a, nwg, st, max_wg);
+  return launch_mode<64, 64, MODE>(a, nwg, st, max_wg);
 }
 
 static AttnArgs make_args(const Geometry& g) {
@@ -731,9 +732,10 @@ static AttnArgs make_args(const Geometry& g) {
 hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* perm, const int32_t* count, const int32_t* idx,
                             const float* theta, float* out, float* lse, uint32_t* kept, int32_t* err,
-                            void* ws, hipStream_t st) {
+                            void* ws, hipStream_t st, const LaunchOpts& opt) {
   AttnArgs a = make_args(g);
   a.queue = static_cast<unsigned long long*>(ws);
+  a.claim_back = opt.claim_back ? 1 : 0;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -746,8 +748,8 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
   a.kept = kept;
   a.err = err;
   if (theta) return dispatch<MODE_ATTN_GATED>(g, a, st);
-  if (count == nullptr) return dispatch<MODE_DENSE>(g, a, st);
-  return dispatch<MODE_ATTN>(g, a, st);
+  if (count == nullptr) return dispatch<MODE_DENSE>(g, a, st, opt.max_wg);
+  return dispatch<MODE_ATTN>(g, a, st, opt.max_wg);
 }
 
 // Early-stop thresholds from calibration tile maxima (Block Sparse Flash Attention, Approach:

@@ -53,6 +53,7 @@ struct AttnArgs {
   float gain_tau;             // marginal-gain early stop threshold (S2O kernels)
   unsigned long long* queue;  // work deques of the pipelined kernels (workspace)
   int nq;                     // number of deques: one per KV group, at most one per XCD
+  int claim_back;             // take items from the back of the home deque (and the front of the others)
   int Hkv;
   int two_pass;               // S2O kernels: two-pass lists over the per-segment prefix order kvr
   const int32_t* kvr;         // per-segment prefix key order (NULL when no segment has a prefix)
@@ -561,8 +562,23 @@ static __global__ __launch_bounds__(64) void deque_init_kernel(AttnArgs a, int u
   if (q < a.nq) a.queue[q] = (unsigned long long)deque_items(a, q, units_per_group) << 32;
 }
 
-// item code (q << 24 | index) or -1 when every deque is empty
+// item code (q << 24 | index) or -1 when every deque is empty.  With a.claim_back the two ends swap
+// roles (the home deque's shortest rows first, the others' longest stolen); the results do not
+// depend on which workgroup computes an item or when, which that order lets a caller check.
 __device__ __forceinline__ int claim_item(const AttnArgs& a, int home) {
+  if (a.claim_back) {
+    unsigned long long old = atomicAdd(&a.queue[home], 0xFFFFFFFF00000000ull);
+    int f = (int)(uint32_t)old, b = (int)(uint32_t)(old >> 32);
+    if (b >= 1 && b - 1 >= f) return (home << 24) | (b - 1);
+    for (int k = 1; k < a.nq; ++k) {
+      const int q = home + k < a.nq ? home + k : home + k - a.nq;
+      old = atomicAdd(&a.queue[q], 1ull);
+      f = (int)(uint32_t)old;
+      b = (int)(uint32_t)(old >> 32);
+      if (f < b) return (q << 24) | f;
+    }
+    return -1;
+  }
   unsigned long long old = atomicAdd(&a.queue[home], 1ull);
   int f = (int)(uint32_t)old, b = (int)(uint32_t)(old >> 32);
   if (f < b) return (home << 24) | f;

@@ -96,10 +96,16 @@ hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_
 // Attention workspace: the work deques of the pipelined kernels, one 64-bit word per deque.
 constexpr int kMaxDeques = 8;
 constexpr size_t kAttnWorkspaceBytes = 256;
+// Launch options of the persistent attention kernels: at most max_wg workgroups (0 = as many as
+// fit on the device), and the order in which they take work items.
+struct LaunchOpts {
+  int max_wg = 0;
+  bool claim_back = false;
+};
 hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* perm, const int32_t* count, const int32_t* idx,
                             const float* theta, float* out, float* lse, uint32_t* kept, int32_t* err,
-                            void* ws, hipStream_t st);
+                            void* ws, hipStream_t st, const LaunchOpts& opt = LaunchOpts());
 hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* perm, const int32_t* count, const int32_t* idx, float gain_tau,
                                 float* out, float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st);

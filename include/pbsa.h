@@ -188,6 +188,35 @@ pbsa_status pbsa_block_sparse_attn_prefill(const pbsa_shape* shape, const uint16
                                            uint32_t* kept_bitmap, int32_t* device_error,
                                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Launch options of pbsa_block_sparse_attn_prefill_ex. */
+typedef struct pbsa_launch_options {
+  int32_t max_workgroups; /* >= 0: cap on the workgroups of the persistent kernel (0: as many as
+                             fit on the device), e.g. to leave compute units to concurrent work */
+  uint32_t flags;         /* PBSA_LAUNCH_* bits */
+} pbsa_launch_options;
+
+/* Workgroups take work items from the back of their home queue and steal from the front of the
+ * others (the default order is the reverse: longest query rows first). */
+#define PBSA_LAUNCH_CLAIM_BACK 1u
+
+/*
+ * pbsa_block_sparse_attn_prefill with launch options: the same operation, arguments, layouts,
+ * results and errors.  The options change only how the persistent kernel of the mask and dense
+ * paths spreads query rows over workgroups (the early-stop path starts one workgroup per row and
+ * ignores them); each row is computed by one workgroup in a fixed order, so out, lse and
+ * kept_bitmap are bitwise the same under every option.
+ *   options   NULL (defaults) or a pbsa_launch_options; max_workgroups < 0 or an unknown flag bit
+ *             returns PBSA_ERR_INVALID_ARG
+ */
+pbsa_status pbsa_block_sparse_attn_prefill_ex(const pbsa_shape* shape, const uint16_t* q,
+                                              const uint16_t* k, const uint16_t* v,
+                                              const int32_t* perm, const int32_t* block_count,
+                                              const int32_t* block_idx,
+                                              const float* early_stop_theta, float* out, float* lse,
+                                              uint32_t* kept_bitmap, int32_t* device_error,
+                                              void* workspace, size_t workspace_bytes,
+                                              const pbsa_launch_options* options, void* stream);
+
 /*
  * pbsa_block_sparse_attn_prefill without a workspace, for callers that cannot allocate device
  * memory: code recorded under HIP graph capture, tight serving loops, harnesses that forbid

@@ -301,3 +301,26 @@ def test_noalloc_attention_validates_before_touching_the_device():
     s.head_dim = 96
     assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None,
              None) == _lib.PBSA_ERR_UNSUPPORTED
+
+
+def test_launch_options_entry_validates_before_launch():
+    l = _lib.lib()
+    E = _lib.PBSA_ERR_INVALID_ARG
+    s = shape()
+    f = l.pbsa_block_sparse_attn_prefill_ex
+    ws = ctypes.c_void_p(0x100000)
+    assert ctypes.sizeof(_lib.PbsaLaunchOptions) == 8
+    for bad in (_lib.PbsaLaunchOptions(-1, 0), _lib.PbsaLaunchOptions(0, 2), _lib.PbsaLaunchOptions(4, 0x80000000)):
+        assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, ws, 256,
+                 ctypes.byref(bad), None) == E
+    ok = _lib.PbsaLaunchOptions(16, _lib.PBSA_LAUNCH_CLAIM_BACK)
+    # the other arguments are checked as in pbsa_block_sparse_attn_prefill
+    assert f(ctypes.byref(s), FAKE, FAKE, None, None, None, None, None, FAKE, None, None, None, ws, 256,
+             ctypes.byref(ok), None) == E
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, ws, 8,
+             ctypes.byref(ok), None) == _lib.PBSA_ERR_WORKSPACE
+    s0 = shape(N=0)
+    assert f(ctypes.byref(s0), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None, 0,
+             None, None) == 0
+    assert f(ctypes.byref(s0), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None, 0,
+             ctypes.byref(ok), None) == 0
