@@ -50,9 +50,25 @@ pbsa_status make_geometry(const pbsa_shape* s, Geometry* g) {
   if (!strides(s->q_stride_head, s->q_stride_token, &g->qsh, &g->qst)) return PBSA_ERR_INVALID_ARG;
   if (!strides(s->kv_stride_head, s->kv_stride_token, &g->kvsh, &g->kvst)) return PBSA_ERR_INVALID_ARG;
   if (!strides(s->o_stride_head, s->o_stride_token, &g->osh, &g->ost)) return PBSA_ERR_INVALID_ARG;
-  // kernels address one head's rows with 32-bit byte offsets
-  const int64_t lim = (int64_t)1 << 31;
-  if ((int64_t)s->seq_len * g->qst * 2 >= lim || (int64_t)s->seq_len * g->kvst * 2 >= lim) return PBSA_ERR_UNSUPPORTED;
+  // kernels address one head's rows with 32-bit byte offsets, and a whole tensor with 64-bit ones:
+  // the byte extent of one head of q, k, v must stay below 2^31, and that of every tensor (all its
+  // heads) below 2^48, more than any device address space holds; computed without overflow
+  const int64_t N = s->seq_len;
+  auto head_bytes_ok = [&](int64_t st) {
+    int64_t b = 0;
+    return !__builtin_mul_overflow(N, st, &b) && !__builtin_mul_overflow(b, (int64_t)2, &b) && b < ((int64_t)1 << 31);
+  };
+  auto extent_ok = [&](int64_t heads, int64_t sh, int64_t st, int64_t elem_bytes) {
+    if (N == 0) return true;
+    int64_t a = 0, b = 0, e = 0;
+    if (__builtin_mul_overflow(heads - 1, sh, &a) || __builtin_mul_overflow(N - 1, st, &b)) return false;
+    if (__builtin_add_overflow(a, b, &e) || __builtin_add_overflow(e, (int64_t)d, &e)) return false;
+    return !__builtin_mul_overflow(e, elem_bytes, &e) && e < ((int64_t)1 << 48);
+  };
+  if (!head_bytes_ok(g->qst) || !head_bytes_ok(g->kvst)) return PBSA_ERR_UNSUPPORTED;
+  if (!extent_ok(s->num_q_heads, g->qsh, g->qst, 2) || !extent_ok(s->num_kv_heads, g->kvsh, g->kvst, 2) ||
+      !extent_ok(s->num_q_heads, g->osh, g->ost, 4))
+    return PBSA_ERR_UNSUPPORTED;
   g->N = s->seq_len;
   g->Hq = s->num_q_heads;
   g->Hkv = s->num_kv_heads;

@@ -48,6 +48,9 @@
  *     crosses the ABI.  Calls are reentrant.
  *   - Supported: d in {64, 128}; B in {64, 128}; S a positive multiple of B up to 8192 (or 0 for
  *     "no permutation"); Hq a positive multiple of Hkv; N >= 0 (N = 0 is a no-op); NB <= 2048.
+ *     One head of q, k or v spans less than 2^31 bytes (N * token stride * 2), and each of q, k,
+ *     v and out, all heads included, less than 2^48 bytes; larger strides return
+ *     PBSA_ERR_UNSUPPORTED.
  */
 #ifndef PBSA_H
 #define PBSA_H

@@ -324,3 +324,16 @@ def test_launch_options_entry_validates_before_launch():
              None, None) == 0
     assert f(ctypes.byref(s0), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None, 0,
              ctypes.byref(ok), None) == 0
+
+
+def test_stride_extents_are_bounded_without_overflow():
+    l = _lib.lib()
+    U = _lib.PBSA_ERR_UNSUPPORTED
+    big8 = (1 << 63) - 8
+    for sh, st in ((big8, big8), (big8, 128), (1 << 62, 128), (1024 * 128, big8), (1024 * 128, 1 << 21),
+                   (1 << 47, 128)):
+        for which in ("q", "kv"):
+            s = shape()
+            setattr(s, f"{which}_stride_head", sh)
+            setattr(s, f"{which}_stride_token", st)
+            assert l.pbsa_tile_max(ctypes.byref(s), FAKE, FAKE, None, FAKE, None) == U, (which, sh, st)
