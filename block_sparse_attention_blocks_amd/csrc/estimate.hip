@@ -1,9 +1,12 @@
 // Stage 1 (key importance, segment sort) and stage 2 (pooling, block selection) on gfx950.
 //
-// Everything here is fp64: bf16 x bf16 products are exact in fp64, block means of bf16 rows are
-// exact sums divided by a power of two, and the ranks and cumulative-mass cuts these kernels
+// The arithmetic here is fp64: bf16 x bf16 products are exact in fp64, block means of bf16 rows
+// are exact sums divided by a power of two, and the ranks and cumulative-mass cuts these kernels
 // decide must agree with an fp64 evaluation of the same definitions bit for bit except at
 // genuine near-ties.  fp32 accumulation would swap ranks whose gaps are far above the tie band.
+// The one fp32 value is storage: the importance pass keeps its chunk-normalised exponentials
+// (numbers in (0, 1]) rounded to fp32 between its two halves, which moves each importance by at
+// most 2^-24 relative (every term is positive) and halves the pass's largest memory stream.
 #include "common.h"
 
 #include <math.h>
@@ -17,8 +20,8 @@ namespace pbsa {
 // h = g*G + r / R1, i = N - R1 + r % R1.  imp_j = (1/R) sum_r exp(s_rj - lse_r), s_rj = c q_r.k_j
 // over causal j <= i.  Three launches:
 //   imp_scores : per (64-key chunk c, g), the fp64 logits of all R rows on the fp64 matrix cores
-//                (v_mfma_f64_16x16x4_f64); per row the chunk max m_cr and l_cr = sum exp(s - m_cr),
-//                and e_rj = exp(s_rj - m_cr) stored to the workspace
+//                (v_mfma_f64_16x16x4_f64); per row the chunk max m_cr and l_cr = sum exp(s - m_cr)
+//                (fp64), and e_rj = exp(s_rj - m_cr) stored to the workspace rounded to fp32
 //   imp_lse    : per (row, g), lse_r = M + log sum_c l_cr exp(m_cr - M)
 //   imp_colsum : per key, imp_j = (1/R) sum_r e_rj exp(m_c(j)r - lse_r) in row order
 // so every logit is computed once and exponentiated once.
@@ -35,7 +38,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 struct ImpWs {
-  double* e;       // [Hkv][R][N] chunk-normalised exponentials
+  float* e;        // [Hkv][R][N] chunk-normalised exponentials, rounded to fp32
   double* part_m;  // [Hkv][nchunk][R]
   double* part_l;  // [Hkv][nchunk][R]
   double* lse;     // [Hkv][R]
@@ -55,8 +58,8 @@ static ImpWs carve_imp_ws(const Geometry& g, void* ws) {
   const size_t R = imp_rows(g), C = imp_chunks(g);
   char* p = static_cast<char*>(ws);
   ImpWs w;
-  w.e = reinterpret_cast<double*>(p);
-  p += align256(sizeof(double) * g.Hkv * R * (size_t)g.N);
+  w.e = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * g.Hkv * R * (size_t)g.N);
   w.part_m = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * C * R);
   w.part_l = reinterpret_cast<double*>(p);
@@ -69,7 +72,7 @@ static ImpWs carve_imp_ws(const Geometry& g, void* ws) {
 
 size_t importance_workspace_bytes(const Geometry& g) {
   const size_t R = imp_rows(g), C = imp_chunks(g);
-  return align256(sizeof(double) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
+  return align256(sizeof(float) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
          align256(sizeof(double) * g.Hkv * R) + align256(sizeof(double) * g.Hkv * (size_t)g.N);
 }
 
@@ -151,9 +154,10 @@ __device__ __forceinline__ double exp_nonpos(double x) {
 // registers as doubles; every key chunk is widened to doubles once, by the staging threads, into
 // LDS rows padded to D + 4 doubles, so a B operand is one 8-byte read at a fixed offset from the
 // lane's base address and the 64 lanes of a read fall on distinct bank pairs two at a time.  The
-// next chunk's bf16 rows are loaded into registers while the current one is multiplied.
-template <int D>
-__global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, double* E, double* part_m,
+// next chunk's bf16 rows are loaded into registers while the current one is multiplied.  ET is
+// the stored type of the exponentials: fp32 for the importance pass, fp64 for sampled rows.
+template <int D, typename ET>
+__global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* E, double* part_m,
                                                                  double* part_l) {
   constexpr int KS = D / 4;         // MFMA k-steps
   constexpr int PITCH = D + 4;      // doubles per staged key row
@@ -276,11 +280,11 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, doub
       l = row_sum_f64(l);
       const int r = r0 + 16 * w + lg + 4 * rr;
       if (r < a.R) {
-        double* er = E + ((size_t)g * a.R + r) * a.N;
+        ET* er = E + ((size_t)g * a.R + r) * a.N;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int j = j0 + 16 * tt + l16;
-          if (j < a.N) er[j] = sv[tt];
+          if (j < a.N) er[j] = (ET)sv[tt];
         }
         if (l16 == 0) {
           const size_t o = ((size_t)g * nchunk + c) * a.R + r;
@@ -346,8 +350,8 @@ __global__ __launch_bounds__(256) void imp_lse_kernel(const double* part_m, cons
   }
 }
 
-// imp_j = (1/R) sum_r e_rj * exp(m_c(j)r - lse_r), rows summed in order.
-__global__ __launch_bounds__(COL_KEYS) void imp_colsum_kernel(const double* E, const double* part_m,
+// imp_j = (1/R) sum_r e_rj * exp(m_c(j)r - lse_r), rows summed in order in fp64.
+__global__ __launch_bounds__(COL_KEYS) void imp_colsum_kernel(const float* E, const double* part_m,
                                                               const double* lse, int N, int R, int nchunk,
                                                               double* imp) {
   constexpr int CPB = COL_KEYS / IMP_CK;  // chunks per workgroup
@@ -369,10 +373,10 @@ __global__ __launch_bounds__(COL_KEYS) void imp_colsum_kernel(const double* E, c
     }
     __syncthreads();
     if (j < N) {
-      const double* col = E + ((size_t)g * R + rb) * N + j;
+      const float* col = E + ((size_t)g * R + rb) * N + j;
       const int nr = min(COL_ROWS, R - rb);
       const double* wc = wsh[t / IMP_CK];
-      for (int rr = 0; rr < nr; ++rr) sum = fma(col[(size_t)rr * N], wc[rr], sum);
+      for (int rr = 0; rr < nr; ++rr) sum = fma((double)col[(size_t)rr * N], wc[rr], sum);
     }
   }
   if (j < N) imp[(size_t)g * N + j] = sum / (double)R;
@@ -400,9 +404,9 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
   const int nchunk = imp_chunks(g);
   const dim3 grid((a.R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
   if (g.d == 128) {
-    imp_scores_kernel<128><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
+    imp_scores_kernel<128, float><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
   } else {
-    imp_scores_kernel<64><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
+    imp_scores_kernel<64, float><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
   }
   imp_lse_kernel<<<dim3((a.R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(w.part_m, w.part_l, nchunk, a.R,
                                                                                  w.lse);
@@ -503,9 +507,9 @@ hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const ui
   a.first_row = min(a.trunk_c, g.N) - rpt;
   const dim3 grid((R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
   if (g.d == 128) {
-    imp_scores_kernel<128><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
+    imp_scores_kernel<128, double><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
   } else {
-    imp_scores_kernel<64><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
+    imp_scores_kernel<64, double><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
   }
   imp_lse_kernel<<<dim3((R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(out->part_m, part_l, nchunk, R,
                                                                              out->lse);

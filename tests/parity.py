@@ -1,8 +1,14 @@
 """Comparison helpers for GPU-vs-oracle parity (imported by the gpu tests, smoke and bench).
 
+Importance values: the GPU computes every logit, exponential and sum in fp64 and keeps only the
+chunk-normalised exponentials e (in (0, 1]) rounded to fp32 between its two launches; each term
+of the (positive) mean is then off by at most 2^-24 relative (or 2^-150 absolute in the fp32
+subnormal range), so imp_gpu must lie within IMP_RTOL = 2^-24 + 1e-12 relative (the 1e-12 for
+the fp64 steps) plus IMP_ATOL = 2^-149 of the oracle's (compare_importance).
+
 Tie rules, used wherever a floating-point comparison decides an integer result:
   * permutation: a rank where GPU and oracle list different keys is a recorded tie iff the two
-    keys' oracle importances differ by at most 1e-6 relative;
+    keys' oracle importances differ by at most 1e-6 relative (above twice IMP_RTOL);
   * block mask: a differing row is a recorded tie iff every differing block has
     |p_J - p_(k*)| <= 1e-6, or is the cut block or the next one in the oracle's order while the
     oracle's running mass C_{k*-1} or C_{k*} is within 1e-6 of tau; at most 1% of rows may tie;
@@ -39,6 +45,19 @@ O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
 S2O_BAND = 1e-2
 F32_U = 2.0 ** -24
+IMP_RTOL = 2.0 ** -24 + 1e-12
+IMP_ATOL = 2.0 ** -149
+
+
+def compare_importance(imp_g: np.ndarray, imp_o: np.ndarray) -> float:
+    """Assert the GPU importance is within IMP_RTOL relative (+ IMP_ATOL) of the oracle's; return the
+    largest relative error seen."""
+    err = np.abs(imp_g - imp_o)
+    lim = IMP_RTOL * np.abs(imp_o) + IMP_ATOL
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, f"importance off at {bad[:5].tolist()}: gpu {imp_g[tuple(bad[0])]!r} oracle {imp_o[tuple(bad[0])]!r}"
+    nz = imp_o != 0
+    return float((err[nz] / np.abs(imp_o[nz])).max()) if nz.any() else 0.0
 
 
 def fp32_sum_gamma(n: int) -> float:

@@ -127,3 +127,38 @@ def test_compare_gate_catches_a_wrong_decision():
         compare_gate({(0, 3): [0, 3]}, sel, exact, bound, theta)
     with pytest.raises(AssertionError):  # the diagonal dropped
         compare_gate({(0, 3): [0, 1]}, sel, exact, bound, theta)
+
+
+def test_importance_bound_covers_fp32_exponentials(make_inputs):
+    """The importance pass keeps exp(s - chunk max) rounded to fp32 between its launches: evaluate
+    the mean that way (64-key chunks, as the kernel does) and check it against the oracle within
+    IMP_RTOL, and that the rounding is actually visible (the bound is not vacuous)."""
+    from parity import IMP_ATOL, IMP_RTOL, compare_importance
+    N, Hq, Hkv, d, B = 700, 4, 2, 64, 64
+    q, k, _ = make_inputs(N, Hq, Hkv, d, n_stripes=6, band=64, seed=21)
+    G, c = Hq // Hkv, 1.0 / math.sqrt(d)
+    rows = np.arange(N - B, N)
+    ok = np.arange(N)[None, :] <= rows[:, None]
+    sim = np.zeros((Hkv, N))
+    for g in range(Hkv):
+        for h in range(g * G, (g + 1) * G):
+            s = np.where(ok, c * (q[h, rows] @ k[g].T), -np.inf)
+            lse = np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)) + s.max(1)
+            for c0 in range(0, N, 64):
+                blk = s[:, c0:c0 + 64]
+                m = blk.max(1, keepdims=True)
+                mm = np.where(np.isfinite(m), m, 0.0)
+                e32 = np.exp(blk - mm).astype(np.float32).astype(np.float64)
+                w = np.where(np.isfinite(m), np.exp(m - lse[:, None]), 0.0)
+                sim[g, c0:c0 + 64] += (e32 * w).sum(0)
+        sim[g] /= G * len(rows)
+    imp_o = oracle.key_importance(q, k, B)
+    worst = compare_importance(sim, imp_o)
+    assert 1e-9 < worst <= IMP_RTOL
+    # an error just outside the bound is caught
+    planted = imp_o.copy()
+    j = int(np.argmax(imp_o[0]))
+    planted[0, j] *= 1 + 2 * IMP_RTOL
+    with pytest.raises(AssertionError):
+        compare_importance(planted, imp_o)
+    assert IMP_ATOL < 1e-40
