@@ -23,14 +23,18 @@ namespace pbsa {
 // group usually keep nearly the same blocks).  While stage s is computed, stages s+1 .. s+NBUF-1
 // are in flight, and the physical row ids of stage s+NBUF are fetched from perm.
 //
-// S2O = true (one head per workgroup): the list is the head's ranked list, taken in its order, and
-// after every earlier-segment block the workgroup stops the row when each query's share of that
-// block in its softmax denominator is below a.gain_tau (S2O, Early-Stopping Rule).
+// S2O = true: after every earlier-segment block, a head stops its row when each query's share of
+// that block in its softmax denominator is below a.gain_tau (S2O, Early-Stopping Rule), and the
+// workgroup stops when all its heads have.  With ranked lists (HPW = 1) the list is the head's own
+// ranked list, taken in its order.  With the two-pass lists (a.two_pass) every query head of a KV
+// group walks the same blocks in the same order -- its own segment, then the KV head's prefix
+// order -- so HPW = 2 heads share each gathered tile until they stop; a head that has stopped
+// leaves its later tiles to the other.
 template <int D, int BLK, bool DENSE, int HPW, bool S2O = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PipeCfg<D, BLK, HPW>::THREADS, PipeCfg<D, BLK, HPW>::THREADS),
                           amdgpu_waves_per_eu(2)))
 void attn_pipe_kernel(AttnArgs a) {
-  static_assert(!S2O || (HPW == 1 && !DENSE), "the marginal-gain stop runs one head per workgroup");
+  static_assert(!S2O || !DENSE, "the marginal-gain stop walks lists");
   using C = PipeCfg<D, BLK, HPW>;
   constexpr int KT = C::KT;
   constexpr int NBUF = C::NBUF;
@@ -121,8 +125,8 @@ void attn_pipe_kernel(AttnArgs a) {
   // merged key-block list: ascending J kept by any of the workgroup's heads
   const int Jend = qperm_on ? min((min((sI + 1) * a.S, a.N) + BLK - 1) / BLK, a.NB) - 1 : I;
   const int nblk = DENSE     ? I + 1
-                   : two_pass ? two_pass_list<C::THREADS>(Jend, J0, mlist)
-                   : S2O      ? ranked_list<C::THREADS>(a, h0, I, ntri, mlist, &mcount)
+                   : two_pass ? two_pass_list<C::THREADS>(Jend, J0, mlist, HPW)
+                   : S2O      ? (HPW == 1 ? ranked_list<C::THREADS>(a, h0, I, ntri, mlist, &mcount) : 0)
                               : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
   const int nst = nblk * C::STAGES;
   const uint32_t all_heads = ((1u << HPW) - 1u) << 16;
@@ -164,6 +168,7 @@ void attn_pipe_kernel(AttnArgs a) {
 
   SoftmaxState<D, BLK> st;
   st.init();
+  uint32_t done = 0;  // heads of the workgroup whose row has stopped (marginal-gain stop)
 
   RowLook pr_prev = RowLook{kPastEnd, 0};  // lookup of stage s + NBUF, issued in step s - 1
   if (nst > 0) {
@@ -196,7 +201,7 @@ void attn_pipe_kernel(AttnArgs a) {
     const bool issue = s + NBUF - 1 < nst;
     if (issue) gather(s + NBUF - 1, (b + NBUF - 1) % NBUF);
     const uint32_t e = s < nst ? entry_of(s) : 0u;
-    if ((e >> (16 + hh)) & 1u) {
+    if (((e & ~(done << 16)) >> (16 + hh)) & 1u) {
       const int J = (int)(e & 0xffffu);
       const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
       if (a.kept && lane == 0 && wq == 0 && (s % C::STAGES) == 0) {
@@ -230,14 +235,21 @@ void attn_pipe_kernel(AttnArgs a) {
     }
     lds_barrier();
     if (S2O && s < nst && (s % C::STAGES) == C::STAGES - 1) {
-      // after an earlier-segment block: stop when every wave found its share below the threshold
+      // after an earlier-segment block: a head that processed it stops when every one of its waves
+      // found its share below the threshold; the workgroup stops when every head has
       const uint32_t e2 = entry_of(s);
       const int J = (int)(e2 & 0xffffu);
-      if (((e2 >> 16) & 1u) && a.S > 0 && (J * BLK) / a.S < sI) {
-        bool all = true;
+      if (a.S > 0 && (J * BLK) / a.S < sI) {
 #pragma unroll
-        for (int x = 0; x < C::WAVES; ++x) all = all && stop_flag[(s / C::STAGES) & 1][x];
-        return all;
+        for (int x = 0; x < HPW; ++x) {
+          if ((((e2 & ~(done << 16)) >> (16 + x)) & 1u) == 0) continue;
+          bool all = true;
+#pragma unroll
+          for (int y = 0; y < C::WAVES_PER_HEAD; ++y)
+            all = all && stop_flag[(s / C::STAGES) & 1][x * C::WAVES_PER_HEAD + y];
+          if (all) done |= 1u << x;
+        }
+        return done == (1u << HPW) - 1u;
       }
     }
     return false;
@@ -799,14 +811,21 @@ hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* 
   return hipGetLastError();
 }
 
-// One head per workgroup with the marginal-gain stop, over ranked lists (a.count / a.idx) or over
-// the two-pass lists of the per-segment prefix order (a.kvr).
+// The marginal-gain stop: one head per workgroup over ranked lists (a.count / a.idx), whose order
+// differs from head to head; over the two-pass lists of the per-segment prefix order (a.kvr), which
+// every head of a KV group shares, two heads per workgroup when the group size is even.
+template <int HPW>
+static hipError_t launch_s2o_hpw(const Geometry& g, const AttnArgs& a, hipStream_t st) {
+  const int items = g.Hq * g.NB / HPW;
+  if (g.d == 128 && g.B == 128) return launch_persistent<128, 128, false, HPW, true>(a, items, st);
+  if (g.d == 128 && g.B == 64) return launch_persistent<128, 64, false, HPW, true>(a, items, st);
+  if (g.d == 64 && g.B == 128) return launch_persistent<64, 128, false, HPW, true>(a, items, st);
+  return launch_persistent<64, 64, false, HPW, true>(a, items, st);
+}
+
 static hipError_t launch_s2o_kernel(const Geometry& g, const AttnArgs& a, hipStream_t st) {
-  const int items = g.Hq * g.NB;
-  if (g.d == 128 && g.B == 128) return launch_persistent<128, 128, false, 1, true>(a, items, st);
-  if (g.d == 128 && g.B == 64) return launch_persistent<128, 64, false, 1, true>(a, items, st);
-  if (g.d == 64 && g.B == 128) return launch_persistent<64, 128, false, 1, true>(a, items, st);
-  return launch_persistent<64, 64, false, 1, true>(a, items, st);
+  if (a.two_pass && (g.G & 1) == 0) return launch_s2o_hpw<2>(g, a, st);
+  return launch_s2o_hpw<1>(g, a, st);
 }
 
 hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -529,10 +529,11 @@ __device__ __forceinline__ int ranked_list(const AttnArgs& a, int h, int I, size
 // the segment's last block when queries are permuted); pass 2, blocks 0 .. J0-1 of the segment's
 // prefix key order (block J = ranked keys J*B .. J*B+B-1).  Returns the list length, Jend + 1.
 template <int THREADS>
-__device__ __forceinline__ int two_pass_list(int Jend, int J0, uint32_t* mlist) {
+__device__ __forceinline__ int two_pass_list(int Jend, int J0, uint32_t* mlist, int hpw) {
   const int nin = Jend + 1 - J0;
+  const uint32_t heads = ((1u << hpw) - 1u) << 16;  // every head of the workgroup walks the list
   for (int x = threadIdx.x; x <= Jend; x += THREADS)
-    mlist[x] = (uint32_t)(x < nin ? J0 + x : x - nin) | (1u << 16);
+    mlist[x] = (uint32_t)(x < nin ? J0 + x : x - nin) | heads;
   __syncthreads();
   return Jend + 1;
 }
