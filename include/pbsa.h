@@ -116,7 +116,9 @@ size_t pbsa_workspace_size(const pbsa_shape* shape, int op);
  * Sparser Block-Sparse Attention via Token Permutation, sections 2 and 3.  For KV head g the proxy
  * rows are the last B query positions [max(0, N-B), N) of each of its Hq/Hkv query heads.  Each row
  * i takes the causal softmax of c * q_i . k_j over j <= i; importance[g][j] is the mean of these
- * probabilities over all proxy rows (masked entries count 0), computed in fp64.  Inside every
+ * probabilities over all proxy rows (masked entries count 0), computed in fp64 except that the
+ * per-chunk exponentials are stored as fp32 between the two halves of the pass, so each value is
+ * within 2^-24 relative of the exact fp64 mean (plus fp64 rounding).  Inside every
  * segment [s*S, min((s+1)*S, N)) the positions are sorted by importance descending, ties by
  * position ascending: perm[g][s*S + r] = position of the r-th key.  perm is a bijection on each
  * segment; K and V are never moved.
