@@ -100,12 +100,13 @@ __device__ __forceinline__ void imp_row(const ImpArgs& a, int g, int r, int* h, 
   }
 }
 
-// DPP row rotation of a double (16-lane rows): all-reduce helpers for the 16 lanes of one row.
+// DPP row rotation of a double (16-lane rows): all-reduce helpers for the 16 lanes of one row.  A
+// rotation reads a lane of the same row for every lane, so no fill value is needed (mov_dpp).
 template <int N>
 __device__ __forceinline__ double row_ror_f64(double x) {
   const uint64_t b = (uint64_t)__double_as_longlong(x);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x120 + N, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x120 + N, 0xf, 0xf, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0x120 + N, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0x120 + N, 0xf, 0xf, false);
   return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 __device__ __forceinline__ double row_max_f64(double x) {
@@ -127,20 +128,19 @@ __device__ __forceinline__ double row_sum_f64(double x) {  // exact on lane 0 of
 // so n * head is exact, and the rounded remainder), exp(r) by its Taylor series to degree 11
 // (truncation below 1e-14 relative on that interval; 8.8e-15 worst case measured against the math
 // library on [-60, 0]), then the exact scaling by 2^n.  Below -745 the result is 0.
+// Taylor coefficients 1/11! .. 1/3!, read from constant memory so that they reach the FMAs as scalar
+// operands (as literals they were copied into vector registers before every accumulating FMA).
+__constant__ double kExpTaylor[9] = {2.505210838544172e-08, 2.755731922398589e-07, 2.7557319223985893e-06,
+                                     2.48015873015873e-05, 0.0001984126984126984, 0.001388888888888889,
+                                     0.008333333333333333, 0.041666666666666664, 0.16666666666666666};
 __device__ __forceinline__ double exp_nonpos(double x) {
   constexpr double kLog2e = 1.4426950408889634, kLn2Hi = 0.6931471803691238, kLn2Lo = 1.9082149292705877e-10;
   const double n = rint(x * kLog2e);
   double r = fma(-n, kLn2Hi, x);
   r = fma(-n, kLn2Lo, r);
-  double q = 2.505210838544172e-08;  // 1/11!
-  q = fma(q, r, 2.755731922398589e-07);
-  q = fma(q, r, 2.7557319223985893e-06);
-  q = fma(q, r, 2.48015873015873e-05);
-  q = fma(q, r, 0.0001984126984126984);
-  q = fma(q, r, 0.001388888888888889);
-  q = fma(q, r, 0.008333333333333333);
-  q = fma(q, r, 0.041666666666666664);
-  q = fma(q, r, 0.16666666666666666);
+  double q = kExpTaylor[0];  // 1/11!
+#pragma unroll
+  for (int i = 1; i < 9; ++i) q = fma(q, r, kExpTaylor[i]);
   q = fma(q, r, 0.5);
   q = fma(q, r, 1.0);
   q = fma(q, r, 1.0);
