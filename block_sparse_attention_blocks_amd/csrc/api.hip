@@ -7,7 +7,7 @@
 
 #include <atomic>
 
-#include "common.h"
+#include "estimate.h"
 
 using pbsa::Geometry;
 

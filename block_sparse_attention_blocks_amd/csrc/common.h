@@ -59,39 +59,6 @@ __device__ __forceinline__ double wave_max_f64(double x) {
 
 // ---------------------------------------------------------------- launchers (internal C++ API)
 
-// Stage 1 workspace layout and launches.
-size_t importance_workspace_bytes(const Geometry& g);
-// Importance (into imp, or into the workspace when imp is NULL) followed by the segment sort.
-hipError_t launch_build_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* perm,
-                                    double* imp, void* ws, hipStream_t st);
-
-// Sort of fp64 scores [Hkv][N] inside segments of g.S: descending, ties by position, into perm.
-hipError_t launch_segment_sort(const Geometry& g, const double* score, int32_t* perm, hipStream_t st);
-
-// SampleAttention stage 1: exact causal softmax rows of trunk-sampled queries, stored as in the
-// importance pass (p[r][j] = e[g][r][j] * exp(part_m[g][j / 64][r] - lse[g][r])).
-struct SampledRows {
-  double* e;       // [Hkv][R][N] chunk-normalised exponentials (0 where j > i)
-  double* part_m;  // [Hkv][nchunk][R] chunk maxima (-inf for a chunk wholly past the row)
-  double* lse;     // [Hkv][R]
-  int R;           // rows per KV head: G * n_trunks * rpt, head-major
-  int nchunk;      // key chunks of 64
-};
-size_t sampled_softmax_workspace_bytes(const Geometry& g, int n_trunks, int rpt);
-hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const uint16_t* k, int n_trunks, int rpt,
-                                  void* ws, SampledRows* out, hipStream_t st);
-size_t sample_mask_workspace_bytes(const Geometry& g, int n_trunks, int rpt);
-hipError_t launch_sample_mask(const Geometry& g, const uint16_t* q, const uint16_t* k, double cia_tau, int n_trunks,
-                              int rpt, uint32_t flags, int32_t* count, int32_t* idx, double* col, double* slash,
-                              void* ws, hipStream_t st);
-
-// Stage 2.
-size_t mask_workspace_bytes(const Geometry& g);
-constexpr uint32_t kMaskRanked = 4u;  // PBSA_MASK_RANKED
-hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_t* k, const int32_t* perm,
-                             double tau, uint32_t flags, int32_t* count, int32_t* idx, double* prob,
-                             void* ws, hipStream_t st);
-
 // Stage 3 and calibration.
 // Attention workspace: the work deques of the pipelined kernels, one 64-bit word per deque.
 constexpr int kMaxDeques = 8;
@@ -109,20 +76,10 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
 hipError_t launch_s2o_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                 const int32_t* perm, const int32_t* count, const int32_t* idx, float gain_tau,
                                 float* out, float* lse, uint32_t* kept, int32_t* err, void* ws, hipStream_t st);
-// Historical KV ranking of S2O: workspace, entries per KV head, and the launch (kv_rank int32
-// [Hkv][rank_len]).
-size_t prefix_rank_workspace_bytes(const Geometry& g);
-int64_t prefix_rank_length(const Geometry& g);
-hipError_t launch_prefix_rank(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* kv_rank, void* ws,
-                              hipStream_t st);
 hipError_t launch_s2o_prefix_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                        const int32_t* kv_rank, int64_t rank_len, const int32_t* qperm,
                                        float gain_tau, float* out, float* lse, uint32_t* kept, int32_t* err,
                                        void* ws, hipStream_t st);
-// S2O query permutation: workspace and launch (qperm int32 [Hkv][N]).
-size_t query_perm_workspace_bytes(const Geometry& g);
-hipError_t launch_query_permutation(const Geometry& g, const uint16_t* q, const uint16_t* k, int32_t* qperm, void* ws,
-                                    hipStream_t st);
 hipError_t launch_tile_max(const Geometry& g, const uint16_t* q, const uint16_t* k, const int32_t* perm,
                            float* tmax, hipStream_t st);
 hipError_t launch_calibrate(int Hq, int NB, const float* tmax, int keep, float* theta, hipStream_t st);

@@ -7,7 +7,7 @@
 // The one fp32 value is storage: the importance pass keeps its chunk-normalised exponentials
 // (numbers in (0, 1]) rounded to fp32 between its two halves, which moves each importance by at
 // most 2^-24 relative (every term is positive) and halves the pass's largest memory stream.
-#include "common.h"
+#include "estimate.h"
 
 #include <math.h>
 
@@ -155,7 +155,7 @@ __device__ __forceinline__ double exp_nonpos(double x) {
 // LDS rows padded to D + 4 doubles, so a B operand is one 8-byte read at a fixed offset from the
 // lane's base address and the 64 lanes of a read fall on distinct bank pairs two at a time.  The
 // next chunk's bf16 rows are loaded into registers while the current one is multiplied.  ET is
-// the stored type of the exponentials: fp32 for the importance pass, fp64 for sampled rows.
+// the stored type of the exponentials (fp32 for both users of the kernel).
 template <int D, typename ET>
 __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* E, double* part_m,
                                                                  double* part_l) {
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(SORT_THREADS) void segment_sort_kernel(const double
 // kernels with the trunk row map; per KV head its G * n_trunks * rpt rows, head-major.
 size_t sampled_softmax_workspace_bytes(const Geometry& g, int n_trunks, int rpt) {
   const size_t R = (size_t)g.G * n_trunks * rpt, C = imp_chunks(g);
-  return align256(sizeof(double) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
+  return align256(sizeof(float) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
          align256(sizeof(double) * g.Hkv * R);
 }
 
@@ -480,8 +480,8 @@ hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const ui
                                   void* ws, SampledRows* out, hipStream_t st) {
   const int R = g.G * n_trunks * rpt, nchunk = imp_chunks(g);
   char* p = static_cast<char*>(ws);
-  out->e = reinterpret_cast<double*>(p);
-  p += align256(sizeof(double) * g.Hkv * (size_t)R * g.N);
+  out->e = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * g.Hkv * (size_t)R * g.N);
   out->part_m = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * (size_t)nchunk * R);
   double* part_l = reinterpret_cast<double*>(p);
@@ -507,9 +507,9 @@ hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const ui
   a.first_row = min(a.trunk_c, g.N) - rpt;
   const dim3 grid((R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
   if (g.d == 128) {
-    imp_scores_kernel<128, double><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
+    imp_scores_kernel<128, float><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
   } else {
-    imp_scores_kernel<64, double><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
+    imp_scores_kernel<64, float><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
   }
   imp_lse_kernel<<<dim3((R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(out->part_m, part_l, nchunk, R,
                                                                              out->lse);

@@ -8,7 +8,7 @@
 //                        8-bit digits, four passes
 // Output layout: kv_rank[g][S*sigma*(sigma-1)/2 + r] = key of rank r for segment sigma.
 // Also S2O's query permutation (query_guide_kernel + the segment sort of stage 1).
-#include "common.h"
+#include "estimate.h"
 
 namespace pbsa {
 namespace {

@@ -8,7 +8,7 @@
 //   sa_cut_kernel            per head and family: the shortest heaviest set reaching the target
 //   sa_block_kernel          per head: kept columns per key block, prefix counts of kept slashes
 //   sa_mask_kernel           per (h, I): tiles with a kept column, crossed by a kept slash, or forced
-#include "common.h"
+#include "estimate.h"
 
 namespace pbsa {
 namespace {
@@ -65,7 +65,7 @@ __device__ __forceinline__ int trunk_pos(int u, int rpt, int C, int N) {
 }
 
 struct MassArgs {
-  const double* e;
+  const float* e;  // exponentials stored in fp32 (each within 2^-24 relative)
   const double* w;
   int N, G, R, R1, nchunk, rpt, C;
 };
@@ -75,10 +75,10 @@ __global__ __launch_bounds__(SA_THREADS) void sa_col_kernel(MassArgs a, double* 
   const int j = blockIdx.x * SA_THREADS + threadIdx.x, h = blockIdx.y;
   if (j >= a.N) return;
   const int g = h / a.G, r0 = (h % a.G) * a.R1;
-  const double* e = a.e + ((size_t)g * a.R + r0) * a.N + j;
+  const float* e = a.e + ((size_t)g * a.R + r0) * a.N + j;
   const double* w = a.w + ((size_t)g * a.nchunk + j / SA_CK) * a.R + r0;
   double s = 0.0;
-  for (int u = 0; u < a.R1; ++u) s = fma(e[(size_t)u * a.N], w[u], s);
+  for (int u = 0; u < a.R1; ++u) s = fma((double)e[(size_t)u * a.N], w[u], s);
   col[(size_t)h * a.N + j] = s / (double)a.R1;
 }
 
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(SA_THREADS) void sa_slash_kernel(MassArgs a, double
     if (i < dlt) continue;
     const int j = i - dlt;
     const size_t r = (size_t)g * a.R + r0 + u;
-    s = fma(a.e[r * a.N + j], a.w[((size_t)g * a.nchunk + j / SA_CK) * a.R + r0 + u], s);
+    s = fma((double)a.e[r * a.N + j], a.w[((size_t)g * a.nchunk + j / SA_CK) * a.R + r0 + u], s);
   }
   slash[(size_t)h * a.N + dlt] = s / (double)a.R1;
 }

@@ -338,7 +338,8 @@ pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t
  *
  * Stage 1: the sequence is cut into n_trunks chunks of C = ceil(N / n_trunks) positions; the last
  * rows_per_trunk positions of each are the sampled queries of every query head.  Their exact causal
- * softmax rows are computed in fp64; col[h][j] is the mean over head h's sampled rows of p_ij and
+ * softmax rows are computed in fp64 (the per-chunk exponentials stored as fp32, so each mass is
+ * within 2^-24 relative of the exact one); col[h][j] is the mean over head h's sampled rows of p_ij and
  * slash[h][dlt] the mean of p_{i, i-dlt} (each sums to 1).  Stage 2: the columns and the slashes are
  * cut separately, each keeping the shortest prefix of (mass descending, index ascending) whose sum
  * reaches cia_tau (every index if cia_tau >= 1 or the sum stays below it).  Tile (I, J), J <= I, is
@@ -353,7 +354,7 @@ pbsa_status pbsa_s2o_prefix_attn_prefill(const pbsa_shape* shape, const uint16_t
  *   col_mass, slash_mass  out, fp64 [Hq][N] each, or NULL
  *   workspace      >= pbsa_sample_mask_workspace_size(shape, n_trunks, rows_per_trunk) bytes,
  *                  256-byte aligned (it holds the sampled rows' exponentials: Hkv * G * n_trunks *
- *                  rows_per_trunk * N doubles)
+ *                  rows_per_trunk * N floats)
  */
 pbsa_status pbsa_sample_attention_mask(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
                                        double cia_tau, int32_t n_trunks, int32_t rows_per_trunk,
