@@ -30,7 +30,7 @@ namespace pbsa {
 constexpr int IMP_CK = 64;        // keys per chunk (4 MFMA column tiles of 16)
 constexpr int IMP_RT = 64;        // proxy rows per workgroup (4 waves x 16 rows)
 constexpr int IMP_THREADS = 256;
-constexpr int IMP_KR = 16;        // chunks per workgroup
+constexpr int IMP_KR = 16;        // chunks per workgroup, at most (fewer when the grid would be small)
 constexpr int COL_KEYS = 256;     // keys per workgroup of imp_colsum
 constexpr int COL_ROWS = 256;     // rows staged per pass of imp_colsum
 
@@ -85,7 +85,16 @@ struct ImpArgs {
   int trunk_c;    // 0: proxy rows are the last R1 positions; > 0: trunk-sampled rows (chunk length)
   int rpt;        // trunk sampling: rows per trunk
   int first_row;  // smallest proxy position (every key j <= first_row is visible to every proxy row)
+  int kr;         // key chunks per workgroup
 };
+
+// Chunks per workgroup: IMP_KR, or fewer so that short sequences still spread over at least ~512
+// workgroups (a chunk's results do not depend on which workgroup computes it).
+static inline int imp_chunks_per_wg(int row_blocks, int nchunk, int hkv) {
+  const long long wg_at_one = (long long)row_blocks * nchunk * hkv;
+  const long long kr = wg_at_one / 512;
+  return (int)(kr < 1 ? 1 : kr > IMP_KR ? IMP_KR : kr);
+}
 
 // Proxy row r of KV head g -> (query head, token position): the last R1 positions, or with trunk
 // sampling the last rpt positions of every trunk of trunk_c positions.
@@ -168,7 +177,7 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
   const int l16 = lane & 15, lg = lane >> 4;
   const int r0 = blockIdx.x * IMP_RT, g = blockIdx.z;
   const int nchunk = (a.N + IMP_CK - 1) / IMP_CK;
-  const int c0 = blockIdx.y * IMP_KR, c1 = min(c0 + IMP_KR, nchunk);
+  const int c0 = blockIdx.y * a.kr, c1 = min(c0 + a.kr, nchunk);
   const uint16_t* kbase = a.k + (int64_t)g * a.kvsh;
 
   // A operand: proxy row r0 + 16 w + l16, slots k = 4 ks + lg
@@ -402,7 +411,8 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
   a.rpt = 0;
   a.first_row = g.N - a.R1;
   const int nchunk = imp_chunks(g);
-  const dim3 grid((a.R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
+  a.kr = imp_chunks_per_wg((a.R + IMP_RT - 1) / IMP_RT, nchunk, g.Hkv);
+  const dim3 grid((a.R + IMP_RT - 1) / IMP_RT, (nchunk + a.kr - 1) / a.kr, g.Hkv);
   if (g.d == 128) {
     imp_scores_kernel<128, float><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
   } else {
@@ -505,7 +515,8 @@ hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const ui
   a.trunk_c = (g.N + n_trunks - 1) / n_trunks;
   a.rpt = rpt;
   a.first_row = min(a.trunk_c, g.N) - rpt;
-  const dim3 grid((R + IMP_RT - 1) / IMP_RT, (nchunk + IMP_KR - 1) / IMP_KR, g.Hkv);
+  a.kr = imp_chunks_per_wg((R + IMP_RT - 1) / IMP_RT, nchunk, g.Hkv);
+  const dim3 grid((R + IMP_RT - 1) / IMP_RT, (nchunk + a.kr - 1) / a.kr, g.Hkv);
   if (g.d == 128) {
     imp_scores_kernel<128, float><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
   } else {
