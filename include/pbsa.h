@@ -207,9 +207,9 @@ typedef struct pbsa_launch_options {
 /*
  * pbsa_block_sparse_attn_prefill with launch options: the same operation, arguments, layouts,
  * results and errors.  The options change only how the persistent kernel of the mask and dense
- * paths spreads query rows over workgroups (the early-stop path starts one workgroup per row and
- * ignores them); each row is computed by one workgroup in a fixed order, so out, lse and
- * kept_bitmap are bitwise the same under every option.
+ * paths spreads query rows over workgroups (the early-stop path launches one workgroup per query
+ * block and head unit and ignores them); each row is computed by one workgroup in a fixed order,
+ * so out, lse and kept_bitmap are bitwise the same under every option.
  *   options   NULL (defaults) or a pbsa_launch_options; max_workgroups < 0 or an unknown flag bit
  *             returns PBSA_ERR_INVALID_ARG
  */
