@@ -38,12 +38,22 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t byte_off) {
 
 __device__ __forceinline__ int tri_offset(int I) { return (I * (I + 1)) >> 1; }
 
-// Wave64 reductions through cross-lane swizzles.
+// Max over the 64 lanes, in every lane, with no LDS round trip: four DPP row rotations leave each
+// 16-lane row's max in all its lanes, then the partners l ^ 16 (permlane16 swap) and l ^ 32
+// (permlane32 swap) are folded in.  A max is exact in any order, so the result is the same value
+// the butterfly through ds_bpermute gives, at a fraction of its latency.
 __device__ __forceinline__ float wave_max_f32(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x121, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x122, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xf, 0xf, false)));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
+
+// Wave64 sums and maxima of doubles through cross-lane swizzles.
 
 __device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll
