@@ -30,12 +30,18 @@ namespace pbsa {
 // group walks the same blocks in the same order -- its own segment, then the KV head's prefix
 // order -- so HPW = 2 heads share each gathered tile until they stop; a head that has stopped
 // leaves its later tiles to the other.
+// Keys per LDS stage: the mask path of head pairs takes whole 128-key blocks (two buffers), which
+// pays each stage's fixed part (row ids, gather issue, wait, barrier) once per block; the dense
+// and marginal-gain paths keep 64-key stages.
+template <int BLK, bool DENSE, int HPW, bool S2O>
+constexpr int pipe_kt() { return (!DENSE && !S2O && HPW == 2 && BLK == 128) ? 128 : 64; }
+
 template <int D, int BLK, bool DENSE, int HPW, bool S2O = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(PipeCfg<D, BLK, HPW>::THREADS, PipeCfg<D, BLK, HPW>::THREADS),
                           amdgpu_waves_per_eu(2)))
 void attn_pipe_kernel(AttnArgs a) {
   static_assert(!S2O || !DENSE, "the marginal-gain stop walks lists");
-  using C = PipeCfg<D, BLK, HPW>;
+  using C = PipeCfg<D, BLK, HPW, pipe_kt<BLK, DENSE, HPW, S2O>()>;
   constexpr int KT = C::KT;
   constexpr int NBUF = C::NBUF;
   // stage buffers as distinct LDS objects, so reads of one are not ordered behind the gathers still
@@ -213,7 +219,7 @@ void attn_pipe_kernel(AttnArgs a) {
       if (S2O && (s % C::STAGES) == 0) st.lb = st.l;  // a new key block starts
       // causal mask: on the diagonal tile, or on every own-segment tile when queries are permuted
       // (key j is visible to the query at natural position qnat iff j <= qnat)
-      stage_compute<D, BLK>(st, Kc, Vc, qf, kop0, qperm_on ? J >= J0 : J == I,
+      stage_compute<D, BLK, KT>(st, Kc, Vc, qf, kop0, qperm_on ? J >= J0 : J == I,
                             (qperm_on ? qnat - J * BLK : qloc) - koff - 4 * h2, a.sl2);
       if (S2O && (s % C::STAGES) == C::STAGES - 1) {
         // this block's share of each query's denominator (both half-waves of the query summed)

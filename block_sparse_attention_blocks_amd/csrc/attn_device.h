@@ -27,7 +27,7 @@ struct AttnCfg {
   static constexpr int DB = D / 32;                    // 32-row d sub-blocks of O^T
   static constexpr int KLOADS = BLK * KCH / THREADS;   // K chunks per thread
   static constexpr int VBLOCKS = (BLK / 8) * (D / 8);  // 8 x 8 blocks of the V transpose
-  static constexpr int KT = 64;                        // keys per pipelined LDS stage
+  static constexpr int KT = 64;                        // keys per pipelined LDS stage (default)
   static constexpr int STAGES = BLK / KT;              // stages per key block
 };
 
@@ -354,12 +354,12 @@ __device__ __forceinline__ void block_softmax_pv(SoftmaxState<D, BLK>& st, const
 // One KT-key stage from LDS: for each 32-key block, the V operands of this block and the K
 // operands of the next are read while the scores and softmax of this block are computed.  kop0
 // holds the K operands of block 0, read by the caller as soon as the stage buffer was ready.
-template <int D, int BLK>
+template <int D, int BLK, int KT = AttnCfg<D, BLK>::KT>
 __device__ __forceinline__ void stage_compute(SoftmaxState<D, BLK>& st, const uint16_t* Kc, const uint16_t* Vc,
                                               const bf16x8* qf, const bf16x8* kop0, bool diag, int rel0,
                                               float sl2) {
   using C = AttnCfg<D, BLK>;
-  constexpr int NKB = C::KT / 32;
+  constexpr int NKB = KT / 32;
   bf16x8 kop[C::KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < C::KSTEPS; ++kk) kop[kk] = kop0[kk];
@@ -399,14 +399,15 @@ __device__ __forceinline__ void write_output(const AttnArgs& a, const SoftmaxSta
 
 // Pipelined kernel configuration: HPW query heads of one KV group per workgroup (WAVES_PER_HEAD
 // waves of 32 query rows each), KT-key LDS stages, NBUF stage buffers.
-template <int D, int BLK, int HPW>
+template <int D, int BLK, int HPW, int KT_ = AttnCfg<D, BLK>::KT>
 struct PipeCfg {
   static constexpr int WAVES_PER_HEAD = BLK / 32;
   static constexpr int WAVES = HPW * WAVES_PER_HEAD;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int KT = AttnCfg<D, BLK>::KT;
+  static constexpr int KT = KT_;
   static constexpr int STAGES = BLK / KT;
-  static constexpr int NBUF = HPW == 1 ? 2 : 3;  // one workgroup per CU has room for three
+  // one workgroup per CU has room for three 64-key stages (two of 128 keys)
+  static constexpr int NBUF = (HPW == 1 || KT == 128) ? 2 : 3;
   static constexpr int RING = NBUF;              // row-id slots: stage y uses slot y % NBUF
   static constexpr int NDMA = 2 * KT / ((512 / D) * WAVES);  // gather instructions per wave per stage
   static constexpr int MAXNB = 2048;
