@@ -208,6 +208,10 @@ def _cpu_baseline(w, x, count, budget_s, np, oracle, bf16_bits_to_f32, cores):
 
 
 def _events(torch, stream, fn, reps):
+    """Median and minimum of reps timed calls of fn on the stream, after one untimed warm-up call (a
+    first call on freshly written inputs runs cold and is never part of a figure)."""
+    fn()
+    torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
         a.record(stream)
@@ -353,7 +357,7 @@ def measure_128k(torch, np, pbsa, WORKLOADS, load, stream, reps, sdpa=True):
         return int(count.sum().item()) / causal_tiles
 
     dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
-    t_dense = _events(torch, stream, dense, max(2, reps // 2))
+    t_dense = _events(torch, stream, dense, max(3, reps))
     sdpa_ms, sdpa_backend = torch_sdpa_ms(torch, q, k, v, stream, 2) if sdpa else (None, "not run")
     t_perm = _events(torch, stream, fp, reps)
     recs = []
@@ -399,7 +403,7 @@ def suite_sweep(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
     perm = pbsa.build_segment_permutation(q, k, B, S)
     out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
     dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, return_lse=False)
-    t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+    t_dense = _events(torch, stream, dense, max(3, reps))["median_ms"]
     for tau in w.taus:
         for use_perm in (True, False):
             pp = perm if use_perm else None
@@ -434,7 +438,7 @@ def measure_earlystop(torch, np, pbsa, WORKLOADS, load, stream, reps):
     dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, out=out, return_lse=False)
     gated = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, early_stop_theta=theta_t,
                                                    out=out, return_lse=False)
-    t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+    t_dense = _events(torch, stream, dense, max(3, reps))["median_ms"]
     t_gate = _events(torch, stream, gated, reps)["median_ms"]
     _, kept = pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, early_stop_theta=theta_t,
                                              return_lse=False, return_kept=True)
@@ -518,7 +522,7 @@ def suite_s2o(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps, two_pa
             fr = lambda: pbsa.estimate_block_mask(q, k, perm, B, S, 1.0, ranked=True, out=(count, idx))
         t_rank = _events(torch, stream, fr, reps)["median_ms"]
         dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, S, out=out, lse=lse)
-        t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+        t_dense = _events(torch, stream, dense, max(3, reps))["median_ms"]
         for gain_tau in (0.001, 0.01, 0.05):
             if two_pass:
                 fa = lambda: pbsa.s2o_prefix_attn_prefill(q, k, v, rank, B, S, gain_tau, out=out, lse=lse, qperm=qp)
@@ -556,7 +560,7 @@ def suite_sample(args, torch, np, pbsa, WORKLOADS, load, emit, stream, reps):
         out = torch.empty((Hq, w.seq_len, w.head_dim), dtype=torch.float32, device="cuda")
         lse = torch.empty((Hq, w.seq_len), dtype=torch.float32, device="cuda")
         dense = lambda: pbsa.block_sparse_attn_prefill(q, k, v, None, None, None, B, 0, out=out, lse=lse)
-        t_dense = _events(torch, stream, dense, max(2, reps // 2))["median_ms"]
+        t_dense = _events(torch, stream, dense, max(3, reps))["median_ms"]
         for tau in (0.5, 0.8, 0.95):
             fm = lambda: pbsa.sample_attention_mask(q, k, B, tau, nt, rpt, out=(count, idx), workspace=ws)
             t_mask = _events(torch, stream, fm, reps)["median_ms"]
