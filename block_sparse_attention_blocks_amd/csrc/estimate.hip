@@ -563,14 +563,30 @@ __global__ __launch_bounds__(POOL_THREADS) void pool_kernel(const uint16_t* src,
   const int cnt = min(B, N - r0);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t* base = src + (int64_t)h * sh;
-  for (int r = rs; r < cnt; r += rp) {
-    const int pos = rowmap ? rowmap[(size_t)h * N + r0 + r] : r0 + r;
-    if (pos < 0 || pos >= N) continue;  // a corrupt index list contributes nothing
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(base + (int64_t)pos * st_ + c * 8);
+  // four rows per trip: their loads are all issued before the first is added, and the rows are
+  // added in ascending order as before
+  constexpr int U = 4;
+  for (int rb = rs; rb < cnt; rb += U * rp) {
+    int pos[U];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += (double)bf16_bits_to_f32(raw[e] & 0xffffu);
-      acc[2 * e + 1] += (double)bf16_bits_to_f32(raw[e] >> 16);
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * rp;
+      pos[u] = r < cnt ? (rowmap ? rowmap[(size_t)h * N + r0 + r] : r0 + r) : -1;
+    }
+    u32x4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = pos[u] >= 0 && pos[u] < N;  // a corrupt index list contributes nothing
+      raw[u] = ok ? *reinterpret_cast<const u32x4*>(base + (int64_t)pos[u] * st_ + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (pos[u] < 0 || pos[u] >= N) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_bits_to_f32(raw[u][e] & 0xffffu);
+        acc[2 * e + 1] += (double)bf16_bits_to_f32(raw[u][e] >> 16);
+      }
     }
   }
 #pragma unroll
@@ -758,7 +774,35 @@ __global__ __launch_bounds__(SEL_WAVES * 64) void block_select_kernel(SelArgs a)
   int ntie_keep = 0;      // J with p == t* that are kept, smallest J first
   if (a.tau < 1.0 && mass_ge(0) >= a.tau) {
     all = false;
+    // Invariant: mass_ge(tstar) >= tau > mass_ge(tstar + 2^(bit+1)), so t* lies in that window.
+    // Once the window holds a single value of the row, that value is t*: the remaining probes
+    // could only confirm it, so the search stops there (checked from the mantissa bits on).
     for (int bit = 62; bit >= 0; --bit) {
+      if (bit < 52) {
+        const uint64_t hi = tstar + (2ull << bit);  // window [tstar, hi); bit <= 51, no overflow
+        int cnt = 0;
+        int src = -1, slot = 0;
+#pragma unroll
+        for (int i = 0; i < SEL_PL; ++i) {
+          if (i < npl) {
+            const uint64_t key = (uint64_t)__double_as_longlong(v[i]);
+            const unsigned long long bw = __ballot(lane + 64 * i < nJ && key >= tstar && key < hi);
+            if (bw && src < 0) {
+              src = __ffsll((long long)bw) - 1;
+              slot = i;
+            }
+            cnt += __popcll(bw);
+          }
+        }
+        if (cnt == 1) {
+          double only = 0.0;
+#pragma unroll
+          for (int i = 0; i < SEL_PL; ++i)
+            if (i == slot) only = __shfl(v[i], src, 64);
+          tstar = (uint64_t)__double_as_longlong(only);
+          break;
+        }
+      }
       const uint64_t cand = tstar | (1ull << bit);
       if (mass_ge(cand) >= a.tau) tstar = cand;
     }

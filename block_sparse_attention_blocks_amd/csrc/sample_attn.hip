@@ -134,6 +134,8 @@ __global__ __launch_bounds__(CUT_THREADS) void sa_cut_kernel(const double* col, 
                                                              double tau, uint8_t* keep) {
   __shared__ double wsum[CUT_WAYS][CUT_THREADS / 64];
   __shared__ int wcnt[CUT_THREADS / 64];
+  __shared__ double wmax[CUT_THREADS / 64];
+  __shared__ int wnum[CUT_THREADS / 64];
   const int h = blockIdx.x, fam = blockIdx.y, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const double* m = (fam == 0 ? col : slash) + (size_t)h * N;
@@ -142,8 +144,14 @@ __global__ __launch_bounds__(CUT_THREADS) void sa_cut_kernel(const double* col, 
   const int b = min(t * L, N), e = min(b + L, N);
   // One pass: S at the patterns c_w = lo + (w + 1) step, w < CUT_WAYS (a pattern >= hi stands for
   // +inf, where S = 0).  Returns the last w with S(c_w) >= tau, or -1; the same on every thread.
-  auto search_pass = [&](uint64_t lo, uint64_t step, uint64_t hi) -> int {
+  // Also counts the values whose pattern lies in [lo, hi) (*nwin) and returns the largest (*vwin).
+  auto search_pass = [&](uint64_t lo, uint64_t step, uint64_t hi, int* nwin, double* vwin) -> int {
     double thr[CUT_WAYS], part[CUT_WAYS];
+    // non-negative values order as their patterns; lo = ~0 (the all-test) matches no value
+    const double wlo = lo < 0x7ff0000000000000ull ? __longlong_as_double((long long)lo) : INFINITY;
+    const double whi = hi < 0x7ff0000000000000ull ? __longlong_as_double((long long)hi) : INFINITY;
+    int cw = 0;
+    double mw = -1.0;
 #pragma unroll
     for (int w = 0; w < CUT_WAYS; ++w) {
       const uint64_t c = lo + (uint64_t)(w + 1) * step;
@@ -156,19 +164,41 @@ __global__ __launch_bounds__(CUT_THREADS) void sa_cut_kernel(const double* col, 
 #pragma unroll
       for (int u = 0; u < CUT_BATCH; ++u) v[u] = x0 + u * CUT_THREADS < N ? m[x0 + u * CUT_THREADS] : -1.0;
 #pragma unroll
-      for (int u = 0; u < CUT_BATCH; ++u)
+      for (int u = 0; u < CUT_BATCH; ++u) {
 #pragma unroll
         for (int w = 0; w < CUT_WAYS; ++w) part[w] += v[u] >= thr[w] ? v[u] : 0.0;
+        const bool in = v[u] >= wlo && v[u] < whi;
+        cw += in ? 1 : 0;
+        mw = in ? fmax(mw, v[u]) : mw;
+      }
     }
 #pragma unroll
     for (int w = 0; w < CUT_WAYS; ++w)
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) part[w] += __shfl_xor(part[w], o, 64);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      cw += __shfl_xor(cw, o, 64);
+      mw = fmax(mw, __shfl_xor(mw, o, 64));
+    }
     __syncthreads();  // the previous pass has read wsum
-    if (lane == 0)
+    if (lane == 0) {
 #pragma unroll
       for (int w = 0; w < CUT_WAYS; ++w) wsum[w][wave] = part[w];
+      wnum[wave] = cw;
+      wmax[wave] = mw;
+    }
     __syncthreads();
+    {
+      int n = 0;
+      double mx = -1.0;
+      for (int v = 0; v < CUT_THREADS / 64; ++v) {
+        n += wnum[v];
+        mx = fmax(mx, wmax[v]);
+      }
+      *nwin = n;
+      *vwin = mx;
+    }
     int best = -1;
 #pragma unroll
     for (int w = 0; w < CUT_WAYS; ++w) {
@@ -180,15 +210,24 @@ __global__ __launch_bounds__(CUT_THREADS) void sa_cut_kernel(const double* col, 
   };
   // every index when tau >= 1 or when the total S(+0) stays below tau (the bracket lo = -1 (wrapped),
   // step 1, hi = 1 evaluates c_0 = +0 alone)
-  const bool all = tau >= 1.0 || search_pass(~0ull, 1, 1) < 0;
+  int nwin = 0;
+  double vwin = 0.0;
+  const bool all = tau >= 1.0 || search_pass(~0ull, 1, 1, &nwin, &vwin) < 0;
   if (all) {
     for (int x = b; x < e; ++x) kp[x] = 1;
     return;
   }
   uint64_t lo = 0, hi = 0x7ff0000000000000ull;  // S(+0) >= tau > S(+inf) = 0
+  // S(lo) >= tau > S(hi) throughout, so t* lies in [lo, hi): once a single value is left there, it
+  // is t* and the search stops (the later passes could only confirm it)
   while (hi - lo > 1) {
     const uint64_t step = (hi - lo + CUT_WAYS) / (CUT_WAYS + 1);  // >= 1
-    const int best = search_pass(lo, step, hi);
+    const int best = search_pass(lo, step, hi, &nwin, &vwin);
+    if (nwin == 1) {
+      lo = (uint64_t)__double_as_longlong(vwin);
+      hi = lo + 1;
+      break;
+    }
     const uint64_t nlo = best < 0 ? lo : lo + (uint64_t)(best + 1) * step;
     const uint64_t cn = lo + (uint64_t)(best + 2) * step;  // next candidate above the best
     const uint64_t nhi = (best + 1 < CUT_WAYS && cn < hi) ? cn : hi;
