@@ -14,7 +14,7 @@ from parity import (F32_U, bitmap_to_kept, bitmap_to_kept_square, compare_gate, 
                     compare_mask, compare_out,
                     compare_perm, compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask,
                     gate_error_bound, kept_to_mask, two_pass_lists)
-from workloads import bf16_bits_to_f32, generate
+from workloads import bf16_bits_to_f32, bf16_round_bits, generate
 
 pytestmark = pytest.mark.gpu
 
@@ -137,6 +137,43 @@ def test_mask_without_permutation(Hq, Hkv):
     out_o, lse_o, _, _ = oracle.block_sparse_attention(host["q"], host["k"], host["v"], None, cg, ig, B, S)
     compare_out(out.cpu().numpy(), out_o, "mask without permutation")
     compare_lse(lse.cpu().numpy(), lse_o)
+
+
+@pytest.mark.parametrize("groups", [1, 3])
+def test_mask_with_exact_ties(groups):
+    """Key rows equal inside each block and across block groups, so the pooled logits of a row take
+    one value (groups = 1) or three (block 0 alone, the even and the odd blocks): the cut falls
+    inside runs of exactly equal p.  Equal p are taken smallest J first, and tau = 0.61803 leaves
+    every cut at least 0.0026 of mass from tau, so the lists must equal the oracle's exactly."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, S, tau = 2048, 2, 1, 128, 128, 512, 0.61803
+    x = generate(N, Hq, Hkv, d, 0, 0, 81)
+    rng = np.random.default_rng(82)
+    rows = [bf16_round_bits(rng.standard_normal(d).astype(np.float32)) for _ in range(3)]
+    kbits = x["k"].copy()
+    for J in range(N // B):
+        grp = 0 if groups == 1 else (2 if J == 0 else J % 2)
+        kbits[:, J * B:(J + 1) * B, :] = rows[grp]
+    qd = torch.from_numpy(x["q"].view(np.int16)).view(torch.bfloat16).cuda()
+    kd = torch.from_numpy(kbits.view(np.int16)).view(torch.bfloat16).cuda()
+    qh = bf16_bits_to_f32(x["q"]).astype(np.float64)
+    kh = bf16_bits_to_f32(kbits).astype(np.float64)
+    _log(f"[exact ties] groups={groups} N={N} Hq={Hq} tau={tau}")
+    count, idx, prob = pbsa.estimate_block_mask(qd, kd, None, B, S, tau, return_prob=True)
+    torch.cuda.synchronize()
+    cg, ig, pg = count.cpu().numpy(), idx.cpu().numpy(), prob.cpu().numpy()
+    co, io, po = oracle.block_mask(qh, kh, None, B, S, tau)
+    NB = N // B
+    tied = sum(I + 1 - len(np.unique(pg[h, oracle.tri_offset(I):oracle.tri_offset(I) + I + 1]))
+               for h in range(Hq) for I in range(NB))
+    _log(f"[exact ties] {tied} probabilities equal to another of their row on the GPU")
+    assert tied > 0  # the selection really meets exact ties
+    assert compare_mask(cg, ig, co, io, po, tau) == 0
+    for h in range(Hq):
+        for I in range(NB):
+            o = oracle.tri_offset(I)
+            assert cg[h, I] == co[h, I], (h, I)
+            assert np.array_equal(ig[h, o:o + cg[h, I]], io[h, o:o + co[h, I]]), (h, I)
 
 
 # query heads paired per workgroup (even G) and not, every supported (d, B), one ragged N
@@ -645,6 +682,32 @@ def test_sample_attention_mask_and_attention(case):
     NB = oracle.num_blocks(N, B)
     _log(f"[parity] sample {name}: ties {ties}, density {cg.sum() / (Hq * NB * (NB + 1) / 2):.3f}, "
          f"max abs {mx:.2e} mean abs {mean:.2e}")
+
+
+def test_sample_attention_mask_with_exact_ties():
+    """Every key row equal: each sampled row weights its visible keys uniformly, so the column and
+    slash masses are piecewise constant (exactly equal between consecutive sampled rows) and the
+    cut falls inside runs of equal masses.  The kernel's kept patterns must be the oracle's cut of
+    the GPU's own masses exactly (equal masses taken in index order)."""
+    pbsa = _need_gpu()
+    N, Hq, Hkv, d, B, tau, nt, rpt = 2048, 2, 1, 128, 128, 0.61803, 4, 8
+    x = generate(N, Hq, Hkv, d, 0, 0, 83)
+    row = bf16_round_bits(np.random.default_rng(84).standard_normal(d).astype(np.float32))
+    kbits = x["k"].copy()
+    kbits[:, :, :] = row
+    qd = torch.from_numpy(x["q"].view(np.int16)).view(torch.bfloat16).cuda()
+    kd = torch.from_numpy(kbits.view(np.int16)).view(torch.bfloat16).cuda()
+    qh = bf16_bits_to_f32(x["q"]).astype(np.float64)
+    kh = bf16_bits_to_f32(kbits).astype(np.float64)
+    _log(f"[exact ties] sample mask N={N} Hq={Hq} tau={tau} trunks={nt}x{rpt}")
+    count_t, idx_t, col_t, sl_t = pbsa.sample_attention_mask(qd, kd, B, tau, nt, rpt, return_masses=True)
+    torch.cuda.synchronize()
+    col_g, sl_g = col_t.cpu().numpy(), sl_t.cpu().numpy()
+    tied = sum(N - len(np.unique(m[h])) for m in (col_g, sl_g) for h in range(Hq))
+    _log(f"[exact ties] {tied} masses equal to another of their head and family on the GPU")
+    assert tied > 0
+    _, _, _, _, col_o, sl_o = oracle.sample_attention_mask(qh, kh, B, tau, nt, rpt)
+    compare_sample_mask(count_t.cpu().numpy(), idx_t.cpu().numpy(), col_g, sl_g, col_o, sl_o, tau, B, True, False)
 
 
 def test_sample_attention_full_target_is_dense():
