@@ -290,10 +290,16 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
       const int r = r0 + 16 * w + lg + 4 * rr;
       if (r < a.R) {
         ET* er = E + ((size_t)g * a.R + r) * a.N;
+        if (j0 + IMP_CK <= a.N) {  // the chunk lies inside the sequence: one address, no key checks
+          ET* ej = er + j0 + l16;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const int j = j0 + 16 * tt + l16;
-          if (j < a.N) er[j] = (ET)sv[tt];
+          for (int tt = 0; tt < 4; ++tt) ej[16 * tt] = (ET)sv[tt];
+        } else {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int j = j0 + 16 * tt + l16;
+            if (j < a.N) er[j] = (ET)sv[tt];
+          }
         }
         if (l16 == 0) {
           const size_t o = ((size_t)g * nchunk + c) * a.R + r;
