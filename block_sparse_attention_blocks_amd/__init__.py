@@ -81,10 +81,10 @@ def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], bloc
 
 
 def _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, theta=None, out=None, lse=None,
-                     require_gpu: bool = True) -> None:
+                     require_gpu: bool = True, out_dtype=torch.float32) -> None:
     """Argument check of the attention entry points: int32 perm [Hkv][N], int32 block_count [Hq][NB]
-    and block_idx [Hq][NB(NB+1)/2] (both or neither), fp32 theta [Hq][NB], fp32 out [Hq][N][d] with a
-    contiguous last dimension, fp32 lse [Hq][N], all contiguous and on q's device."""
+    and block_idx [Hq][NB(NB+1)/2] (both or neither), fp32 theta [Hq][NB], out [Hq][N][d] of
+    out_dtype with a contiguous last dimension, fp32 lse [Hq][N], all contiguous and on q's device."""
     _check_qkv(q, k, v, block_size, require_gpu)
     Hq, N, d = q.shape
     Hkv = k.shape[0]
@@ -97,7 +97,7 @@ def _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, theta=No
     _check_tensor("block_idx", block_idx, torch.int32, (Hq, NB * (NB + 1) // 2), dev)
     _check_tensor("early_stop_theta", theta, torch.float32, (Hq, NB), dev)
     if out is not None:
-        _check_tensor("out", out, torch.float32, (Hq, N, d), dev, contiguous=False)
+        _check_tensor("out", out, out_dtype, (Hq, N, d), dev, contiguous=False)
         if out.stride(2) != 1:
             raise ValueError("out must have a contiguous last dimension")
     _check_tensor("lse", lse, torch.float32, (Hq, N), dev)
@@ -210,22 +210,33 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               lse: Optional[torch.Tensor] = None, return_lse: bool = True,
                               return_kept: bool = False, return_error: bool = False,
                               workspace: Optional[torch.Tensor] = None, no_alloc: bool = False,
-                              max_workgroups: int = 0, claim_back: bool = False):
+                              max_workgroups: int = 0, claim_back: bool = False,
+                              out_dtype: Optional[torch.dtype] = None):
     """Stage 3: out fp32 [Hq][N][d] (+ lse fp32 [Hq][N], kept-tile bitmap, device error word).
+    out_dtype torch.bfloat16 (or a bf16 out): pbsa_block_sparse_attn_prefill_bf16out, the fp32
+    result rounded to bf16 as it is stored (not with no_alloc or launch options).
     workspace: optional preallocated device buffer of at least workspace_size(shape, PBSA_OP_ATTENTION)
     bytes (the work deques); one is allocated per call otherwise.  no_alloc: call
     pbsa_block_sparse_attn_prefill_noalloc instead, whose work deques live in the library (no
     workspace); pass out, and lse or return_lse=False, so that this call allocates nothing either.
     max_workgroups / claim_back: launch options of pbsa_block_sparse_attn_prefill_ex (a cap on the
     persistent grid, and the order workgroups take rows in); results do not depend on them."""
-    _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, early_stop_theta, out, lse)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    bf16_out = out_dtype == torch.bfloat16
+    _check_attn_args(q, k, v, perm, block_count, block_idx, block_size, early_stop_theta, out, lse,
+                     out_dtype=out_dtype)
     if int(max_workgroups) < 0:
         raise ValueError("max_workgroups must be >= 0")
     if no_alloc and (max_workgroups or claim_back):
         raise ValueError("launch options are not available with no_alloc")
+    if bf16_out and (no_alloc or max_workgroups or claim_back):
+        raise ValueError("the bf16 output is not available with no_alloc or launch options")
     Hq, N, d = q.shape
     if out is None:
-        out = torch.empty((Hq, N, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((Hq, N, d), dtype=out_dtype, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
     NB = num_blocks(N, block_size)
@@ -240,6 +251,12 @@ def block_sparse_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
             _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _stream())
         _lib.check(st, "pbsa_block_sparse_attn_prefill_noalloc")
+    elif bf16_out:
+        ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
+        st = _lib.lib().pbsa_block_sparse_attn_prefill_bf16out(
+            ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(perm), _ptr(block_count), _ptr(block_idx),
+            _ptr(early_stop_theta), _ptr(out), _ptr(lse), _ptr(kept), _ptr(err), _ptr(ws), nbytes, _stream())
+        _lib.check(st, "pbsa_block_sparse_attn_prefill_bf16out")
     elif max_workgroups or claim_back:
         ws, nbytes = _workspace(shape, PBSA_OP_ATTENTION, q.device, workspace)
         opt = _lib.PbsaLaunchOptions(int(max_workgroups), _lib.PBSA_LAUNCH_CLAIM_BACK if claim_back else 0)

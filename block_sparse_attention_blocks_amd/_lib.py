@@ -74,6 +74,8 @@ _SIG = {
                                                 ctypes.c_uint32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_block_sparse_attn_prefill": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
                                                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pbsa_block_sparse_attn_prefill_bf16out": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P,
+                                                              _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pbsa_block_sparse_attn_prefill_ex": (ctypes.c_int, [ctypes.POINTER(PbsaShape), _P, _P, _P, _P, _P, _P, _P,
                                                          _P, _P, _P, _P, _P, ctypes.c_size_t,
                                                          ctypes.POINTER(PbsaLaunchOptions), _P]),

@@ -226,6 +226,27 @@ pbsa_status pbsa_block_sparse_attn_prefill_ex(const pbsa_shape* shape, const uin
                                          opt));
 }
 
+pbsa_status pbsa_block_sparse_attn_prefill_bf16out(const pbsa_shape* shape, const uint16_t* q, const uint16_t* k,
+                                                   const uint16_t* v, const int32_t* perm,
+                                                   const int32_t* block_count, const int32_t* block_idx,
+                                                   const float* early_stop_theta, uint16_t* out, float* lse,
+                                                   uint32_t* kept_bitmap, int32_t* device_error, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  // the kernels take the output as an fp32 pointer and store bf16 through it when out_bf16 is set
+  float* out_any = reinterpret_cast<float*>(out);
+  Geometry g;
+  pbsa_status st = check_attn_args(shape, q, k, v, perm, block_count, block_idx, out_any, &g);
+  if (st != PBSA_OK) return st;
+  if ((st = check_workspace(g.N > 0 ? pbsa::kAttnWorkspaceBytes : 0, workspace, workspace_bytes)) != PBSA_OK)
+    return st;
+  if (g.N == 0) return PBSA_OK;
+  pbsa::LaunchOpts opt;
+  opt.out_bf16 = true;
+  return from_hip(pbsa::launch_attention(g, q, k, v, perm, block_count, block_idx, early_stop_theta, out_any, lse,
+                                         kept_bitmap, device_error, workspace, static_cast<hipStream_t>(stream),
+                                         opt));
+}
+
 // Device memory of pbsa_block_sparse_attn_prefill_noalloc: the work deques that the pipelined
 // attention kernels otherwise keep in the caller's workspace (one 64-bit word per deque, reset by
 // a kernel on the stream before every launch).  Every GPU the library runs on holds its own copy

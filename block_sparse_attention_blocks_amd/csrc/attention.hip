@@ -754,6 +754,7 @@ hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t
   AttnArgs a = make_args(g);
   a.queue = static_cast<unsigned long long*>(ws);
   a.claim_back = opt.claim_back ? 1 : 0;
+  a.out_bf16 = opt.out_bf16 ? 1 : 0;
   a.q = q;
   a.k = k;
   a.v = v;

@@ -59,6 +59,7 @@ struct AttnArgs {
   const int32_t* kvr;         // per-segment prefix key order (NULL when no segment has a prefix)
   int64_t kvr_L;              // entries of kvr per KV head
   const int32_t* qperm;       // two-pass lists: query order inside segments [Hkv][N], or NULL
+  int out_bf16;               // out holds bf16 values (same element strides) instead of fp32
 };
 
 enum { MODE_ATTN = 0, MODE_ATTN_GATED = 1, MODE_TILE_MAX = 2, MODE_DENSE = 3 };
@@ -383,16 +384,30 @@ __device__ __forceinline__ void write_output(const AttnArgs& a, const SoftmaxSta
   const float l_tot = la + lb;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (!qvalid) return;
-  float* orow = a.out + (int64_t)h * a.osh + (int64_t)qpos * a.ost;
+  if (a.out_bf16) {  // the same fp32 values, rounded to bf16 (nearest even) as they are stored
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (int64_t)h * a.osh + (int64_t)qpos * a.ost;
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      f32x4 val;
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 val;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) val[e] = st.o[db][rq * 4 + e] * inv;
-      *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * rq + 4 * h2) = val;
-    }
+        for (int e = 0; e < 4; ++e) val[e] = (__bf16)(st.o[db][rq * 4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + db * 32 + 8 * rq + 4 * h2) = val;
+      }
+  } else {
+    float* orow = a.out + (int64_t)h * a.osh + (int64_t)qpos * a.ost;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        f32x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) val[e] = st.o[db][rq * 4 + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * rq + 4 * h2) = val;
+      }
+  }
   if (a.lse && h2 == 0)
     a.lse[(size_t)h * a.N + qpos] = l_tot > 0.f ? st.m * 0.69314718055994531f + logf(l_tot) : -INFINITY;
 }

@@ -78,6 +78,7 @@ constexpr size_t kAttnWorkspaceBytes = 256;
 struct LaunchOpts {
   int max_wg = 0;
   bool claim_back = false;
+  bool out_bf16 = false;  // out is bf16 storage (same element strides), rounded to nearest even
 };
 hipError_t launch_attention(const Geometry& g, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const int32_t* perm, const int32_t* count, const int32_t* idx,

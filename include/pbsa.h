@@ -223,6 +223,22 @@ pbsa_status pbsa_block_sparse_attn_prefill_ex(const pbsa_shape* shape, const uin
                                               const pbsa_launch_options* options, void* stream);
 
 /*
+ * pbsa_block_sparse_attn_prefill with a bf16 output: the same operation, arguments, layouts and
+ * errors, except that out points to bf16 values (uint16_t bit patterns, [Hq][N][d] by the shape's
+ * o strides in elements).  Each output element is the fp32 value pbsa_block_sparse_attn_prefill
+ * writes, rounded to the nearest bf16 (ties to even), so callers whose next layer reads bf16 need
+ * no separate conversion pass, and the output write is half as large.  lse stays fp32.
+ */
+pbsa_status pbsa_block_sparse_attn_prefill_bf16out(const pbsa_shape* shape, const uint16_t* q,
+                                                   const uint16_t* k, const uint16_t* v,
+                                                   const int32_t* perm, const int32_t* block_count,
+                                                   const int32_t* block_idx,
+                                                   const float* early_stop_theta, uint16_t* out,
+                                                   float* lse, uint32_t* kept_bitmap,
+                                                   int32_t* device_error, void* workspace,
+                                                   size_t workspace_bytes, void* stream);
+
+/*
  * pbsa_block_sparse_attn_prefill without a workspace, for callers that cannot allocate device
  * memory: code recorded under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  Same arguments, layouts, results and errors as pbsa_block_sparse_attn_prefill; the

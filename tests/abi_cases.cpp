@@ -358,6 +358,36 @@ void launch_options_entry() {
             PBSA_OK);
 }
 
+void bf16_output_entry() {
+  const pbsa_status E = PBSA_ERR_INVALID_ARG;
+  pbsa_shape s = shape();
+  uint16_t* FO = reinterpret_cast<uint16_t*>(FF);
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(nullptr, FQ, FQ, FQ, nullptr, nullptr, nullptr, nullptr, FO,
+                                                   nullptr, nullptr, nullptr, FW, 256, nullptr),
+            E);
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(&s, FQ, FQ, FQ, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                   nullptr, nullptr, nullptr, FW, 256, nullptr),
+            E);
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(&s, FQ, FQ, FQ, nullptr, FI, nullptr, nullptr, FO, nullptr,
+                                                   nullptr, nullptr, FW, 256, nullptr),
+            E);
+  uint16_t* bad = reinterpret_cast<uint16_t*>(0x10002);
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(&s, FQ, FQ, FQ, nullptr, nullptr, nullptr, nullptr, bad, nullptr,
+                                                   nullptr, nullptr, FW, 256, nullptr),
+            E);
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(&s, FQ, FQ, FQ, nullptr, nullptr, nullptr, nullptr, FO, nullptr,
+                                                   nullptr, nullptr, FW, 8, nullptr),
+            PBSA_ERR_WORKSPACE);
+  pbsa_shape s0 = shape(0);
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(&s0, FQ, FQ, FQ, nullptr, nullptr, nullptr, nullptr, FO, nullptr,
+                                                   nullptr, nullptr, nullptr, 0, nullptr),
+            PBSA_OK);
+  s.head_dim = 96;
+  EXPECT_EQ(pbsa_block_sparse_attn_prefill_bf16out(&s, FQ, FQ, FQ, nullptr, nullptr, nullptr, nullptr, FO, nullptr,
+                                                   nullptr, nullptr, FW, 256, nullptr),
+            PBSA_ERR_UNSUPPORTED);
+}
+
 // Extreme shape fields: validation must reject them without overflowing its own arithmetic (a
 // signed overflow here is what UndefinedBehaviorSanitizer reports).
 void extreme_shapes() {
@@ -433,6 +463,7 @@ int main() {
   sample_attention_entry();
   noalloc_attention();
   launch_options_entry();
+  bf16_output_entry();
   extreme_shapes();
   printf("abi_cases: %d checks, %d failures\n", g_checks, g_failures);
   return g_failures == 0 ? 0 : 1;

@@ -326,6 +326,28 @@ def test_launch_options_entry_validates_before_launch():
              ctypes.byref(ok), None) == 0
 
 
+def test_bf16_output_entry_validates_before_launch():
+    """pbsa_block_sparse_attn_prefill_bf16out checks its arguments as pbsa_block_sparse_attn_prefill
+    does (the output pointer included), before any launch."""
+    l = _lib.lib()
+    E = _lib.PBSA_ERR_INVALID_ARG
+    s = shape()
+    f = l.pbsa_block_sparse_attn_prefill_bf16out
+    ws = ctypes.c_void_p(0x100000)
+    assert f(None, FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, ws, 256, None) == E
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, None, None, None, None, ws, 256, None) == E
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None, None, None, ws, 256, None) == E
+    bad = ctypes.c_void_p(0x10002)  # misaligned output
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, bad, None, None, None, ws, 256, None) == E
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, ws, 8,
+             None) == _lib.PBSA_ERR_WORKSPACE
+    s0 = shape(N=0)
+    assert f(ctypes.byref(s0), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, None, 0, None) == 0
+    s.head_dim = 96
+    assert f(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, None, None, FAKE, None, None, None, ws, 256,
+             None) == _lib.PBSA_ERR_UNSUPPORTED
+
+
 def test_stride_extents_are_bounded_without_overflow():
     l = _lib.lib()
     U = _lib.PBSA_ERR_UNSUPPORTED

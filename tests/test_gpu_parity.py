@@ -320,6 +320,40 @@ def test_early_stop_with_permutation():
     compare_lse(lse_t.cpu().numpy(), lse_o)
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,B,N,mode", [(4, 2, 128, 128, 2125, "mask"), (3, 1, 128, 128, 1500, "mask"),
+                                               (4, 2, 64, 64, 1900, "dense"), (4, 2, 128, 128, 2048, "gate")])
+def test_bf16_output(Hq, Hkv, d, B, N, mode):
+    """pbsa_block_sparse_attn_prefill_bf16out: every output element is the fp32 result rounded to the
+    nearest bf16 (ties to even), bit for bit, on the paired and one-head mask paths, the dense path
+    and the early-stop path; the lse is the same; and the bf16 output stays within the attention
+    tolerances of the oracle."""
+    pbsa = _need_gpu()
+    S = 512
+    _log(f"[bf16 out] {mode}: N={N} Hq={Hq} Hkv={Hkv} d={d} B={B}")
+    dev, host = _inputs(N, Hq, Hkv, d, 16, 256, 91)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    perm = count = idx = theta = None
+    if mode == "mask":
+        perm = pbsa.build_segment_permutation(q, k, B, S)
+        count, idx = pbsa.estimate_block_mask(q, k, perm, B, S, 0.9)
+    elif mode == "gate":
+        theta = pbsa.calibrate_thresholds(pbsa.tile_max(q, k, B), q, k, B, 6)
+    out32, lse32 = pbsa.block_sparse_attn_prefill(q, k, v, perm, count, idx, B, S, early_stop_theta=theta)
+    out16, lse16 = pbsa.block_sparse_attn_prefill(q, k, v, perm, count, idx, B, S, early_stop_theta=theta,
+                                                  out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert out16.dtype == torch.bfloat16
+    got = out16.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, bf16_round_bits(out32.cpu().numpy()))
+    assert torch.equal(lse16, lse32)
+    if mode != "gate":  # the early-stop path's fp32 output is checked against the oracle elsewhere
+        cg = count.cpu().numpy() if count is not None else None
+        ig = idx.cpu().numpy() if idx is not None else None
+        pg = perm.cpu().numpy() if perm is not None else None
+        out_o, _, _, _ = oracle.block_sparse_attention(host["q"], host["k"], host["v"], pg, cg, ig, B, S)
+        compare_out(bf16_bits_to_f32(got).astype(np.float64), out_o, f"bf16 output ({mode})")
+
+
 def test_deterministic():
     pbsa = _need_gpu()
     N, Hq, Hkv, d, B, S = 2048, 4, 2, 128, 128, 512
