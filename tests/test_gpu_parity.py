@@ -428,9 +428,17 @@ def test_strided_layout_matches_contiguous():
     cs, is_ = pbsa.estimate_block_mask(qs, ks, perm_s, B, S, 0.9)
     o = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm, c, i, B, S, return_lse=False)
     os_ = pbsa.block_sparse_attn_prefill(qs, ks, vs, perm_s, cs, is_, B, S, return_lse=False)
+    # outputs written through strides too (token-major views), fp32 and bf16
+    ov = torch.empty((N, Hq, d), dtype=torch.float32, device="cuda").transpose(0, 1)
+    ob = torch.empty((N, Hq, d), dtype=torch.bfloat16, device="cuda").transpose(0, 1)
+    pbsa.block_sparse_attn_prefill(qs, ks, vs, perm_s, cs, is_, B, S, out=ov, return_lse=False)
+    pbsa.block_sparse_attn_prefill(qs, ks, vs, perm_s, cs, is_, B, S, out=ob, return_lse=False)
     torch.cuda.synchronize()
     assert torch.equal(perm, perm_s) and torch.equal(c, cs)
     assert torch.equal(o, os_)
+    assert torch.equal(ov, o)
+    bits = ob.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, bf16_round_bits(o.cpu().numpy()))
 
 
 @pytest.mark.parametrize("N,B,keep", [(4096, 128, 5), (2100, 64, 1), (1024, 64, 16), (8192, 128, 64)])
