@@ -557,11 +557,10 @@ hipError_t launch_build_permutation(const Geometry& g, const uint16_t* q, const 
 
 constexpr int POOL_THREADS = 256;
 
-__global__ __launch_bounds__(POOL_THREADS) void pool_kernel(const uint16_t* src, int64_t sh, int64_t st_,
-                                                            int N, int B, int d, const int32_t* rowmap,
-                                                            double* dst, int NB) {
+__device__ __forceinline__ void pool_body(const uint16_t* src, int64_t sh, int64_t st_, int N, int B, int d,
+                                          const int32_t* rowmap, double* dst, int NB, int h) {
   __shared__ double part[32][128];
-  const int J = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int J = blockIdx.x, t = threadIdx.x;
   const int lanes = d / 8;                 // threads per row
   const int rp = POOL_THREADS / lanes;     // rows in flight
   const int c = t % lanes, rs = t / lanes;
@@ -603,6 +602,26 @@ __global__ __launch_bounds__(POOL_THREADS) void pool_kernel(const uint16_t* src,
     for (int x = 0; x < rp; ++x) s += part[x][t];
     dst[((size_t)h * NB + J) * d + t] = s / (double)cnt;
   }
+}
+
+// The three poolings of the mask stage in one launch (fewer launches on short sequences): grid rows
+// [0, Hq) pool Q, the next Hkv the natural K, the last Hkv (when perm is given) the permuted K.
+struct PoolJobs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t qsh, qst, ksh, kst;
+  const int32_t* perm;
+  double *qbar, *knat, *kperm;
+  int Hq, Hkv;
+};
+__global__ __launch_bounds__(POOL_THREADS) void pool_kernel(PoolJobs p, int N, int B, int d, int NB) {
+  const int y = blockIdx.y;
+  if (y < p.Hq)
+    pool_body(p.q, p.qsh, p.qst, N, B, d, nullptr, p.qbar, NB, y);
+  else if (y < p.Hq + p.Hkv)
+    pool_body(p.k, p.ksh, p.kst, N, B, d, nullptr, p.knat, NB, y - p.Hq);
+  else
+    pool_body(p.k, p.ksh, p.kst, N, B, d, p.perm, p.kperm, NB, y - p.Hq - p.Hkv);
 }
 
 // =====================================================================================
@@ -931,10 +950,10 @@ hipError_t launch_block_mask(const Geometry& g, const uint16_t* q, const uint16_
   double* kperm = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * (size_t)g.NB * g.d);
   double* z = reinterpret_cast<double*>(p);
-  pool_kernel<<<dim3(g.NB, g.Hq), POOL_THREADS, 0, st>>>(q, g.qsh, g.qst, g.N, g.B, g.d, nullptr, qbar, g.NB);
-  pool_kernel<<<dim3(g.NB, g.Hkv), POOL_THREADS, 0, st>>>(k, g.kvsh, g.kvst, g.N, g.B, g.d, nullptr, knat, g.NB);
-  if (perm)
-    pool_kernel<<<dim3(g.NB, g.Hkv), POOL_THREADS, 0, st>>>(k, g.kvsh, g.kvst, g.N, g.B, g.d, perm, kperm, g.NB);
+  {
+    PoolJobs pj = {q, k, g.qsh, g.qst, g.kvsh, g.kvst, perm, qbar, knat, kperm, g.Hq, g.Hkv};
+    pool_kernel<<<dim3(g.NB, g.Hq + (perm ? 2 : 1) * g.Hkv), POOL_THREADS, 0, st>>>(pj, g.N, g.B, g.d, g.NB);
+  }
   ZArgs za;
   za.qbar = qbar;
   za.knat = knat;
