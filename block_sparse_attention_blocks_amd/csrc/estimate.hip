@@ -1,9 +1,15 @@
 // Stage 1 (key importance, segment sort) and stage 2 (pooling, block selection) on gfx950.
 //
-// The arithmetic here is fp64: bf16 x bf16 products are exact in fp64, block means of bf16 rows
-// are exact sums divided by a power of two, and the ranks and cumulative-mass cuts these kernels
-// decide must agree with an fp64 evaluation of the same definitions bit for bit except at
-// genuine near-ties.  fp32 accumulation would swap ranks whose gaps are far above the tie band.
+// Ranks and cumulative-mass cuts decided here must agree with an fp64 evaluation of the same
+// definitions bit for bit except at genuine near-ties, so nothing is summed in fp32:
+//   * the importance logits q.k are exact integer sums on the int8 matrix cores: each bf16 row is
+//     written as a 42-bit fixed-point integer at its own largest exponent (exact for every element
+//     within 2^34 of the row's largest) and split into six 7-bit digits; the digit products whose
+//     weight is at least 2^-42 of the leading one are summed in int32 and combined in fp64, so a
+//     logit is off by at most 6 d 2^-40 max|q| max|k| (the dropped products and truncated
+//     elements), far below fp32 rounding;
+//   * block means of bf16 rows are exact sums divided by a power of two, taken in fp64, and
+//     everything after the logits (exponentials, sums, softmax) is fp64.
 // The one fp32 value is storage: the importance pass keeps its chunk-normalised exponentials
 // (numbers in (0, 1]) rounded to fp32 between its two halves, which moves each importance by at
 // most 2^-24 relative (every term is positive) and halves the pass's largest memory stream.
@@ -18,24 +24,48 @@ namespace pbsa {
 // "Proxy Scoring").  The proxy rows of KV head g are (h, i) with h in g's query-head group and
 // i in [N - R1, N), R1 = min(B, N); there are R = G * R1 of them.  Row r maps to
 // h = g*G + r / R1, i = N - R1 + r % R1.  imp_j = (1/R) sum_r exp(s_rj - lse_r), s_rj = c q_r.k_j
-// over causal j <= i.  Three launches:
-//   imp_scores : per (64-key chunk c, g), the fp64 logits of all R rows on the fp64 matrix cores
-//                (v_mfma_f64_16x16x4_f64); per row the chunk max m_cr and l_cr = sum exp(s - m_cr)
-//                (fp64), and e_rj = exp(s_rj - m_cr) stored to the workspace rounded to fp32
+// over causal j <= i.  Four launches:
+//   imp_kdigits: per key row, its fixed-point digits (below) and exponent, once per key
+//   imp_scores : per (64-key chunk c, g), the logits of all R rows from digit products on the
+//                int8 matrix cores (v_mfma_i32_16x16x64_i8); per row the chunk max m_cr and
+//                l_cr = sum exp(s - m_cr) (fp64), and e_rj = exp(s_rj - m_cr) stored to the
+//                workspace rounded to fp32
 //   imp_lse    : per (row, g), lse_r = M + log sum_c l_cr exp(m_cr - M)
 //   imp_colsum : per key, imp_j = (1/R) sum_r e_rj exp(m_c(j)r - lse_r) in row order
 // so every logit is computed once and exponentiated once.
+//
+// Fixed-point digits.  A bf16 value is x = M 2^(e' - 134): M its significand with the implicit bit
+// (0..255), e' = max(e, 1) for the exponent field e.  With E the largest e' of x's row,
+// V = trunc(M 2^(e' - E + 34)) is an integer below 2^42 (exact whenever E - e' <= 34) and
+// x = (+-V) 2^(E - 168) up to that truncation.  In two's complement, +-V = sum_a D_a 2^(35 - 7a)
+// (a = 0..5) with D_0 = (+-V) >> 35 in [-128, 127] and D_a (a >= 1) the 7-bit fields below it, in
+// [0, 127]; every digit fits an int8.  For a query row and a key row,
+//   q.k = 2^(Eq + Ek - 336) sum_{a,b} (sum_t Dq_a,t Dk_b,t) 2^(70 - 7(a + b)),
+// and the level sums A_L = sum_{a+b=L} sum_t Dq_a Dk_b are exact in int32 (|A_L| <= (L+1) d 2^14).
+// Levels L <= 5 are kept (21 digit products per 64-wide contraction step); levels 6..10 weigh at
+// most 2^-42 of level 0 each.  A_L 2^7 + A_{L+1} still fits an int32 for the pairs (0,1), (2,3),
+// (4,5), so a logit is  ((C01 2^14 + C23) 2^14 + C45) 2^(Eq + Ek - 301)  with two fp64 FMAs.
 // =====================================================================================
 
 constexpr int IMP_CK = 64;        // keys per chunk (4 MFMA column tiles of 16)
-constexpr int IMP_RT = 64;        // proxy rows per workgroup (4 waves x 16 rows)
-constexpr int IMP_THREADS = 256;
+constexpr int IMP_RT = 128;       // proxy rows per workgroup (8 waves x 16 rows)
+constexpr int IMP_THREADS = 512;
 constexpr int IMP_KR = 16;        // chunks per workgroup, at most (fewer when the grid would be small)
 constexpr int COL_KEYS = 256;     // keys per workgroup of imp_colsum
 constexpr int COL_ROWS = 256;     // rows staged per pass of imp_colsum
 
+constexpr int IMP_NDIG = 6;       // fixed-point digits per bf16 value
+
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Digits of the key rows, chunk-major: [Hkv][nchunk][IMP_NDIG][IMP_CK][d] bytes, then the row
+// exponents E [Hkv][nchunk * IMP_CK] (int32).  Keys past N are zero rows (digits 0, E = 1).
+static inline size_t kdig_bytes(const Geometry& g, size_t nchunk) {
+  return (size_t)g.Hkv * nchunk * IMP_NDIG * IMP_CK * g.d;
+}
+static inline size_t kexp_bytes(const Geometry& g, size_t nchunk) { return sizeof(int) * g.Hkv * nchunk * IMP_CK; }
 
 struct ImpWs {
   float* e;        // [Hkv][R][N] chunk-normalised exponentials, rounded to fp32
@@ -43,6 +73,8 @@ struct ImpWs {
   double* part_l;  // [Hkv][nchunk][R]
   double* lse;     // [Hkv][R]
   double* imp;     // [Hkv][N] (used when the caller passes no importance output)
+  int8_t* kdig;    // key digits (layout above)
+  int* kexp;       // key row exponents
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -67,19 +99,24 @@ static ImpWs carve_imp_ws(const Geometry& g, void* ws) {
   w.lse = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * R);
   w.imp = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * (size_t)g.N);
+  w.kdig = reinterpret_cast<int8_t*>(p);
+  p += align256(kdig_bytes(g, C));
+  w.kexp = reinterpret_cast<int*>(p);
   return w;
 }
 
 size_t importance_workspace_bytes(const Geometry& g) {
   const size_t R = imp_rows(g), C = imp_chunks(g);
   return align256(sizeof(float) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
-         align256(sizeof(double) * g.Hkv * R) + align256(sizeof(double) * g.Hkv * (size_t)g.N);
+         align256(sizeof(double) * g.Hkv * R) + align256(sizeof(double) * g.Hkv * (size_t)g.N) +
+         align256(kdig_bytes(g, C)) + align256(kexp_bytes(g, C));
 }
 
 struct ImpArgs {
   const uint16_t* q;
   const uint16_t* k;
-  int N, G, d, R1, R;
+  int N, G, d, R1, R, Hkv;
   int64_t qsh, qst, kvsh, kvst;
   double scale;
   int trunk_c;    // 0: proxy rows are the last R1 positions; > 0: trunk-sampled rows (chunk length)
@@ -157,32 +194,112 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   return x < -745.0 ? 0.0 : y;
 }
 
-// v_mfma_f64_16x16x4_f64 (lane l): A holds row l%16 and B column l%16 at contraction slot l/16; D
-// holds column l%16, rows l/16 + 4 r in its four doubles r = 0..3.  The contraction index of lane
-// group lg at MFMA step ks is k = 4 ks + lg.  Each wave keeps its 16 proxy rows (all of d) in
-// registers as doubles; every key chunk is widened to doubles once, by the staging threads, into
-// LDS rows padded to D + 4 doubles, so a B operand is one 8-byte read at a fixed offset from the
-// lane's base address and the 64 lanes of a read fall on distinct bank pairs two at a time.  The
-// next chunk's bf16 rows are loaded into registers while the current one is multiplied.  ET is
-// the stored type of the exponentials (fp32 for both users of the kernel).
+// Largest exponent field (at least 1) of the bf16 values packed two to a word.
+__device__ __forceinline__ int bf16_pair_emax(uint32_t w) {
+  return max(max((int)((w >> 7) & 0xffu), (int)((w >> 23) & 0xffu)), 1);
+}
+
+// The fixed-point integer +-V of bf16 bits h in a row whose largest exponent is emax (the digit
+// representation above): two's complement, |V| < 2^42.
+__device__ __forceinline__ uint64_t bf16_fixed(uint32_t h, int emax) {
+  const int e = (int)((h >> 7) & 0xffu);
+  const uint32_t m = (h & 0x7fu) | (e ? 0x80u : 0u);
+  const int sh = 34 - (emax - max(e, 1));
+  const uint64_t v = sh >= 0 ? ((uint64_t)m << sh) : (uint64_t)(m >> min(-sh, 31));
+  return (h & 0x8000u) ? (uint64_t)(-(int64_t)v) : v;
+}
+
+// Digit a (0 = leading, signed) of a fixed-point integer, as the byte the int8 operand holds.
+template <int A>
+__device__ __forceinline__ uint32_t fixed_digit(uint64_t v) {
+  return A == 0 ? (uint32_t)(v >> 35) & 0xffu : (uint32_t)(v >> (35 - 7 * A)) & 0x7fu;
+}
+
+// Digits of four fixed-point integers as one word (byte i from v[i]).
+template <int A>
+__device__ __forceinline__ uint32_t pack_digits(const uint64_t* v) {
+  return fixed_digit<A>(v[0]) | (fixed_digit<A>(v[1]) << 8) | (fixed_digit<A>(v[2]) << 16) |
+         (fixed_digit<A>(v[3]) << 24);
+}
+
+// Largest value over the n lanes of an aligned group of n = 8 or 16 lanes (DPP, within a row).
+template <int NL>
+__device__ __forceinline__ int group_max_i32(int x) {
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  if (NL == 16) x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false));  // row_mirror
+  return x;
+}
+
+// Key digits, once per key: one workgroup per (64-key chunk, KV head); a thread takes 8 values
+// (16 bytes) of a row, the D/8 threads of a row are consecutive lanes and share its exponent.
+template <int D>
+__global__ __launch_bounds__(256) void imp_kdigits_kernel(const uint16_t* k, int N, int64_t kvsh, int64_t kvst,
+                                                          int8_t* kdig, int* kexp) {
+  constexpr int cpr = D / 8;
+  constexpr int NLD = IMP_CK * cpr / 256;
+  const int c = blockIdx.x, g = blockIdx.y, t = threadIdx.x, nchunk = gridDim.x;
+  const uint16_t* kbase = k + (int64_t)g * kvsh;
+  int8_t* out = kdig + ((size_t)g * nchunk + c) * IMP_NDIG * IMP_CK * D;
+#pragma unroll
+  for (int x = 0; x < NLD; ++x) {
+    const int idx = t + x * 256, row = idx / cpr, ch = idx % cpr, j = c * IMP_CK + row;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (j < N) w = *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * kvst + ch * 8);
+    int em = max(max(bf16_pair_emax(w[0]), bf16_pair_emax(w[1])), max(bf16_pair_emax(w[2]), bf16_pair_emax(w[3])));
+    em = group_max_i32<cpr>(em);
+    uint64_t v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_fixed(w[e] & 0xffffu, em);
+      v[2 * e + 1] = bf16_fixed(w[e] >> 16, em);
+    }
+    int8_t* o = out + row * D + ch * 8;
+    *reinterpret_cast<uint2*>(o + 0 * IMP_CK * D) = make_uint2(pack_digits<0>(v), pack_digits<0>(v + 4));
+    *reinterpret_cast<uint2*>(o + 1 * IMP_CK * D) = make_uint2(pack_digits<1>(v), pack_digits<1>(v + 4));
+    *reinterpret_cast<uint2*>(o + 2 * IMP_CK * D) = make_uint2(pack_digits<2>(v), pack_digits<2>(v + 4));
+    *reinterpret_cast<uint2*>(o + 3 * IMP_CK * D) = make_uint2(pack_digits<3>(v), pack_digits<3>(v + 4));
+    *reinterpret_cast<uint2*>(o + 4 * IMP_CK * D) = make_uint2(pack_digits<4>(v), pack_digits<4>(v + 4));
+    *reinterpret_cast<uint2*>(o + 5 * IMP_CK * D) = make_uint2(pack_digits<5>(v), pack_digits<5>(v + 4));
+    if (ch == 0) kexp[(size_t)g * nchunk * IMP_CK + c * IMP_CK + row] = em;
+  }
+}
+
+// v_mfma_i32_16x16x64_i8 (lane l): A holds row l%16 and B column l%16, each 16 int8 of the
+// contraction from lane group l/16 (the same 16 indices on both sides); D holds column l%16, rows
+// 4 (l/16) + i in its four int32 i = 0..3.  Each wave keeps the digits of its 16 proxy rows in
+// registers (A), lane group lg holding elements 64 h + 16 lg .. + 15 of each 64-wide step h; the key
+// digits of a chunk are copied to LDS, one row of each digit plane per key padded to D + 16 bytes
+// (the 16 lanes of a B read then cover all 64 banks once), while the next chunk's digits are loaded
+// into registers.  Workgroups are numbered so that the row blocks of one chunk range are dispatched
+// to the same XCD (consecutive workgroup ids go to consecutive XCDs) and read its key digits
+// through one L2.  ET is the stored type of the exponentials (fp32 for both users of the kernel).
 template <int D, typename ET>
-__global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* E, double* part_m,
-                                                                 double* part_l) {
-  constexpr int KS = D / 4;         // MFMA k-steps
-  constexpr int PITCH = D + 4;      // doubles per staged key row
-  constexpr int cpr = D / 8;        // 16-byte bf16 chunks per key row
-  constexpr int NLD = IMP_CK * cpr / IMP_THREADS;  // chunks per thread per stage
-  __shared__ __align__(16) double Kf[IMP_CK * PITCH];
+__global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))) void imp_scores_kernel(
+    ImpArgs a, const int8_t* kdig, const int* kexp,
+                                                                 ET* E, double* part_m, double* part_l) {
+  constexpr int NH = D / 64;                       // 64-wide contraction steps
+  constexpr int PITCH = D + 16;                    // bytes per key row of a staged digit plane
+  constexpr int U16 = D / 16;                      // 16-byte pieces per key row of a plane
+  constexpr int NST = IMP_NDIG * IMP_CK * U16 / IMP_THREADS;  // pieces per thread per chunk
+  __shared__ __align__(16) int8_t Ks[IMP_NDIG * IMP_CK * PITCH];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int r0 = blockIdx.x * IMP_RT, g = blockIdx.z;
   const int nchunk = (a.N + IMP_CK - 1) / IMP_CK;
-  const int c0 = blockIdx.y * a.kr, c1 = min(c0 + a.kr, nchunk);
-  const uint16_t* kbase = a.k + (int64_t)g * a.kvsh;
 
-  // A operand: proxy row r0 + 16 w + l16, slots k = 4 ks + lg
+  // work item: XCD x = blockIdx.x % 8 takes items x * per + blockIdx.x / 8 (row block fastest)
+  const int nrb = (a.R + IMP_RT - 1) / IMP_RT, ncg = (nchunk + a.kr - 1) / a.kr;
+  const int items = nrb * ncg * a.Hkv, per = (items + 7) / 8;
+  const int item = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (item >= items) return;
+  const int r0 = (item % nrb) * IMP_RT, g = item / (nrb * ncg);
+  const int c0 = ((item / nrb) % ncg) * a.kr, c1 = min(c0 + a.kr, nchunk);
+
+  // A operand: digits of proxy row r0 + 16 w + l16, elements 64 h + 16 lg + i
   const int ra = r0 + 16 * w + l16;
-  double av[KS];
+  i32x4 av[IMP_NDIG][NH];
+  int emq;
   {
     const uint16_t* src = nullptr;
     if (ra < a.R) {
@@ -190,74 +307,108 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
       imp_row(a, g, ra, &h, &i);
       src = a.q + (int64_t)h * a.qsh + (int64_t)i * a.qst;
     }
+    u32x4 raw[NH][2];
 #pragma unroll
-    for (int p = 0; p < D / 32; ++p) {  // 32 elements (8 k-steps) at a time
-      u32x4 raw[4] = {};
-      if (src)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) raw[c] = *reinterpret_cast<const u32x4*>(src + 32 * p + 8 * c);
+      for (int c = 0; c < 2; ++c)
+        raw[h][c] = src ? *reinterpret_cast<const u32x4*>(src + 64 * h + 16 * lg + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    emq = 1;
 #pragma unroll
-      for (int kl = 0; kl < 8; ++kl) {
-        // element 4 kl + lg of these 32: 16-byte chunk kl / 2, word 2 (kl % 2) + lg / 2, half lg % 2
-        const u32x4 v = raw[kl >> 1];
-        const uint32_t wd = (lg >> 1) ? v[2 * (kl & 1) + 1] : v[2 * (kl & 1)];
-        av[8 * p + kl] = (double)bf16_bits_to_f32((lg & 1) ? (wd >> 16) : (wd & 0xffffu));
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) emq = max(emq, bf16_pair_emax(raw[h][c][e]));
+    emq = max(emq, __shfl_xor(emq, 16));
+    emq = max(emq, __shfl_xor(emq, 32));
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {  // elements 4 q4 .. 4 q4 + 3 of the lane's 16
+        const u32x4& r = raw[h][q4 >> 1];
+        uint64_t v[4];
+        v[0] = bf16_fixed(r[2 * (q4 & 1)] & 0xffffu, emq);
+        v[1] = bf16_fixed(r[2 * (q4 & 1)] >> 16, emq);
+        v[2] = bf16_fixed(r[2 * (q4 & 1) + 1] & 0xffffu, emq);
+        v[3] = bf16_fixed(r[2 * (q4 & 1) + 1] >> 16, emq);
+        av[0][h][q4] = (int)pack_digits<0>(v);
+        av[1][h][q4] = (int)pack_digits<1>(v);
+        av[2][h][q4] = (int)pack_digits<2>(v);
+        av[3][h][q4] = (int)pack_digits<3>(v);
+        av[4][h][q4] = (int)pack_digits<4>(v);
+        av[5][h][q4] = (int)pack_digits<5>(v);
       }
-    }
   }
-  // this lane's D rows (proxy rows r0 + 16 w + lg + 4 rr) and their query positions
+  // this lane's D rows (proxy rows r0 + 16 w + 4 lg + rr): query positions and the factor
+  // c 2^(Eq - 150) of the logit
   int qi[4];
+  double fq[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int r = r0 + 16 * w + lg + 4 * rr;
+    const int r = r0 + 16 * w + 4 * lg + rr;
     int h, i;
     imp_row(a, g, r, &h, &i);
     qi[rr] = r < a.R ? i : -1;
+    fq[rr] = ldexp(a.scale, __shfl(emq, 4 * lg + rr) - 150);
   }
   const int first_proxy = a.first_row;  // every key j <= first_proxy is visible to every proxy row
 
-  auto prefetch = [&](int c, u32x4* pf) {
-    const int j0 = c * IMP_CK;
+  const int8_t* kd = kdig + (size_t)g * nchunk * IMP_NDIG * IMP_CK * D;
+  const int* ke = kexp + (size_t)g * nchunk * IMP_CK;
+  auto prefetch = [&](int c, u32x4* pf, int* pe) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(kd + (size_t)c * IMP_NDIG * IMP_CK * D);
 #pragma unroll
-    for (int x = 0; x < NLD; ++x) {
-      const int idx = t + x * IMP_THREADS;
-      const int row = idx / cpr, ch = idx % cpr;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j0 + row < a.N) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(j0 + row) * a.kvst + ch * 8);
-      pf[x] = v;
-    }
+    for (int x = 0; x < NST; ++x) pf[x] = src[t + x * IMP_THREADS];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) pe[tt] = ke[c * IMP_CK + 16 * tt + l16];
   };
-  // widen the prefetched bf16 rows to doubles into the padded LDS rows
+  // piece u = t + x * IMP_THREADS of the chunk: plane u / (IMP_CK U16), key (u / U16) % IMP_CK,
+  // bytes 16 (u % U16) of the row
   auto stage = [&](const u32x4* pf) {
 #pragma unroll
-    for (int x = 0; x < NLD; ++x) {
-      const int idx = t + x * IMP_THREADS;
-      const int row = idx / cpr, ch = idx % cpr;
-      double* dst = Kf + row * PITCH + ch * 8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t wd = pf[x][e];
-        const f64x2 two = {(double)bf16_bits_to_f32(wd & 0xffffu), (double)bf16_bits_to_f32(wd >> 16)};
-        *reinterpret_cast<f64x2*>(dst + 2 * e) = two;
-      }
+    for (int x = 0; x < NST; ++x) {
+      const int u = t + x * IMP_THREADS;
+      const int pl = u / (IMP_CK * U16), key = (u / U16) % IMP_CK, pc = u % U16;
+      *reinterpret_cast<u32x4*>(Ks + (pl * IMP_CK + key) * PITCH + 16 * pc) = pf[x];
     }
   };
-  const double* bbase = Kf + l16 * PITCH + lg;  // B operand of column tile tt, step ks: bbase[16 tt PITCH + 4 ks]
+  const int8_t* bbase = Ks + l16 * PITCH + 16 * lg;  // B of plane b, column tile tt, step h
 
-  u32x4 pf[NLD];
-  prefetch(c0, pf);
+  u32x4 pf[NST];
+  int pe[4];
+  prefetch(c0, pf, pe);
   for (int c = c0; c < c1; ++c) {
     stage(pf);
+    double fk[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) fk[tt] = ldexp(1.0, pe[tt] - 151);
     __syncthreads();
-    if (c + 1 < c1) prefetch(c + 1, pf);
-    f64x4 acc[4];
+    if (c + 1 < c1) prefetch(c + 1, pf, pe);
+    double x[4][4];  // logit of row 4 lg + rr, key 16 tt + l16
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[tt] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int tt = 0; tt < 4; ++tt) {
+      i32x4 lv[IMP_NDIG];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int L = 0; L < IMP_NDIG; ++L) lv[L] = i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        acc[tt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bbase[16 * tt * PITCH + 4 * ks], acc[tt], 0, 0, 0);
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int b = 0; b < IMP_NDIG; ++b) {
+          const i32x4 bv = *reinterpret_cast<const i32x4*>(bbase + (b * IMP_CK + 16 * tt) * PITCH + 64 * h);
+#pragma unroll
+          for (int aa = 0; aa + b < IMP_NDIG; ++aa)
+            lv[aa + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[aa][h], bv, lv[aa + b], 0, 0, 0);
+        }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int c01 = lv[0][rr] * 128 + lv[1][rr];
+        const int c23 = lv[2][rr] * 128 + lv[3][rr];
+        const int c45 = lv[4][rr] * 128 + lv[5][rr];
+        const double tv = fma(fma((double)c01, 16384.0, (double)c23), 16384.0, (double)c45);
+        x[tt][rr] = tv * fq[rr] * fk[tt];
+      }
+    }
     // per proxy row: chunk max, sum of exponentials, and the exponentials themselves
     const int j0 = c * IMP_CK;
     const bool open = j0 + IMP_CK - 1 <= first_proxy && j0 + IMP_CK <= a.N;  // no key of the chunk is masked
@@ -266,10 +417,9 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
       double sv[4];
       double m;
       if (open) {
-        double mx = fmax(fmax(acc[0][rr], acc[1][rr]), fmax(acc[2][rr], acc[3][rr]));
-        m = a.scale * row_max_f64(mx);  // scale > 0 keeps the max
+        m = row_max_f64(fmax(fmax(x[0][rr], x[1][rr]), fmax(x[2][rr], x[3][rr])));
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_nonpos(fma(a.scale, acc[tt][rr], -m));
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_nonpos(x[tt][rr] - m);
       } else {
         const int i = qi[rr];
         m = -INFINITY;
@@ -277,7 +427,7 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
         for (int tt = 0; tt < 4; ++tt) {
           const int j = j0 + 16 * tt + l16;
           const bool ok = (i >= 0) && (j < a.N) && (j <= i);
-          sv[tt] = ok ? a.scale * acc[tt][rr] : -INFINITY;
+          sv[tt] = ok ? x[tt][rr] : -INFINITY;
           m = fmax(m, sv[tt]);
         }
         m = row_max_f64(m);
@@ -287,7 +437,7 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
       }
       double l = (sv[0] + sv[1]) + (sv[2] + sv[3]);
       l = row_sum_f64(l);
-      const int r = r0 + 16 * w + lg + 4 * rr;
+      const int r = r0 + 16 * w + 4 * lg + rr;
       if (r < a.R) {
         ET* er = E + ((size_t)g * a.R + r) * a.N;
         if (j0 + IMP_CK <= a.N) {  // the chunk lies inside the sequence: one address, no key checks
@@ -308,7 +458,7 @@ __global__ __launch_bounds__(IMP_THREADS) void imp_scores_kernel(ImpArgs a, ET* 
         }
       }
     }
-    __syncthreads();  // every wave is done with this chunk's rows before they are replaced
+    __syncthreads();  // every wave is done with this chunk's digits before they are replaced
   }
 }
 
@@ -397,6 +547,21 @@ __global__ __launch_bounds__(COL_KEYS) void imp_colsum_kernel(const float* E, co
   if (j < N) imp[(size_t)g * N + j] = sum / (double)R;
 }
 
+// Key digits, then the logits and chunk exponentials of the R proxy rows (a fully set up).
+static void launch_scores(const Geometry& g, const ImpArgs& a, int8_t* kdig, int* kexp, float* e, double* part_m,
+                          double* part_l, hipStream_t st) {
+  const int nchunk = imp_chunks(g);
+  const int items = ((a.R + IMP_RT - 1) / IMP_RT) * ((nchunk + a.kr - 1) / a.kr) * g.Hkv;
+  const int nwg = (items + 7) / 8 * 8;
+  if (g.d == 128) {
+    imp_kdigits_kernel<128><<<dim3(nchunk, g.Hkv), 256, 0, st>>>(a.k, g.N, g.kvsh, g.kvst, kdig, kexp);
+    imp_scores_kernel<128, float><<<nwg, IMP_THREADS, 0, st>>>(a, kdig, kexp, e, part_m, part_l);
+  } else {
+    imp_kdigits_kernel<64><<<dim3(nchunk, g.Hkv), 256, 0, st>>>(a.k, g.N, g.kvsh, g.kvst, kdig, kexp);
+    imp_scores_kernel<64, float><<<nwg, IMP_THREADS, 0, st>>>(a, kdig, kexp, e, part_m, part_l);
+  }
+}
+
 static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, const uint16_t* k, double* out,
                                         void* ws, hipStream_t st) {
   ImpWs w = carve_imp_ws(g, ws);
@@ -417,13 +582,9 @@ static hipError_t launch_key_importance(const Geometry& g, const uint16_t* q, co
   a.rpt = 0;
   a.first_row = g.N - a.R1;
   const int nchunk = imp_chunks(g);
+  a.Hkv = g.Hkv;
   a.kr = imp_chunks_per_wg((a.R + IMP_RT - 1) / IMP_RT, nchunk, g.Hkv);
-  const dim3 grid((a.R + IMP_RT - 1) / IMP_RT, (nchunk + a.kr - 1) / a.kr, g.Hkv);
-  if (g.d == 128) {
-    imp_scores_kernel<128, float><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
-  } else {
-    imp_scores_kernel<64, float><<<grid, IMP_THREADS, 0, st>>>(a, w.e, w.part_m, w.part_l);
-  }
+  launch_scores(g, a, w.kdig, w.kexp, w.e, w.part_m, w.part_l, st);
   imp_lse_kernel<<<dim3((a.R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(w.part_m, w.part_l, nchunk, a.R,
                                                                                  w.lse);
   imp_colsum_kernel<<<dim3((g.N + COL_KEYS - 1) / COL_KEYS, g.Hkv), COL_KEYS, 0, st>>>(w.e, w.part_m, w.lse, g.N,
@@ -489,7 +650,7 @@ __global__ __launch_bounds__(SORT_THREADS) void segment_sort_kernel(const double
 size_t sampled_softmax_workspace_bytes(const Geometry& g, int n_trunks, int rpt) {
   const size_t R = (size_t)g.G * n_trunks * rpt, C = imp_chunks(g);
   return align256(sizeof(float) * g.Hkv * R * (size_t)g.N) + 2 * align256(sizeof(double) * g.Hkv * C * R) +
-         align256(sizeof(double) * g.Hkv * R);
+         align256(sizeof(double) * g.Hkv * R) + align256(kdig_bytes(g, C)) + align256(kexp_bytes(g, C));
 }
 
 hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const uint16_t* k, int n_trunks, int rpt,
@@ -503,6 +664,10 @@ hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const ui
   double* part_l = reinterpret_cast<double*>(p);
   p += align256(sizeof(double) * g.Hkv * (size_t)nchunk * R);
   out->lse = reinterpret_cast<double*>(p);
+  p += align256(sizeof(double) * g.Hkv * (size_t)R);
+  int8_t* kdig = reinterpret_cast<int8_t*>(p);
+  p += align256(kdig_bytes(g, nchunk));
+  int* kexp = reinterpret_cast<int*>(p);
   out->R = R;
   out->nchunk = nchunk;
   ImpArgs a;
@@ -521,13 +686,9 @@ hipError_t launch_sampled_softmax(const Geometry& g, const uint16_t* q, const ui
   a.trunk_c = (g.N + n_trunks - 1) / n_trunks;
   a.rpt = rpt;
   a.first_row = min(a.trunk_c, g.N) - rpt;
+  a.Hkv = g.Hkv;
   a.kr = imp_chunks_per_wg((R + IMP_RT - 1) / IMP_RT, nchunk, g.Hkv);
-  const dim3 grid((R + IMP_RT - 1) / IMP_RT, (nchunk + a.kr - 1) / a.kr, g.Hkv);
-  if (g.d == 128) {
-    imp_scores_kernel<128, float><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
-  } else {
-    imp_scores_kernel<64, float><<<grid, IMP_THREADS, 0, st>>>(a, out->e, out->part_m, part_l);
-  }
+  launch_scores(g, a, kdig, kexp, out->e, out->part_m, part_l, st);
   imp_lse_kernel<<<dim3((R + LSE_ROWS - 1) / LSE_ROWS, g.Hkv), 256, 0, st>>>(out->part_m, part_l, nchunk, R,
                                                                              out->lse);
   return hipGetLastError();

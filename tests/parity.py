@@ -1,14 +1,20 @@
 """Comparison helpers for GPU-vs-oracle parity (imported by the gpu tests, smoke and bench).
 
-Importance values: the GPU computes every logit, exponential and sum in fp64 and keeps only the
-chunk-normalised exponentials e (in (0, 1]) rounded to fp32 between its two launches; each term
-of the (positive) mean is then off by at most 2^-24 relative (or 2^-150 absolute in the fp32
-subnormal range), so imp_gpu must lie within IMP_RTOL = 2^-24 + 1e-12 relative (the 1e-12 for
-the fp64 steps) plus IMP_ATOL = 2^-149 of the oracle's (compare_importance).
+Importance values: the GPU forms each logit c q.k from fixed-point digits of the bf16 rows (six
+7-bit digits of a 42-bit integer at the row's largest exponent E, digit products of weight at
+least 2^-42 of the leading one summed exactly in int32), so a logit is off by at most
+  delta = c (u_q sum|k| + u_k sum|q| + d u_q u_k (1 + IMP_DROP)),  u = 2^(E - 168),
+(the truncated elements and the dropped digit products; imp_logit_error takes the largest over the
+rows and keys of each KV group, a few 1e-10 on the workloads); every exponential, sum and
+log-sum-exp after that is fp64, and only the chunk-normalised exponentials e (in (0, 1]) are kept
+rounded to fp32 between launches.  A term exp(s - lse) of the (positive) mean then moves by at
+most exp(2 delta) - 1 from the logit error and 2^-24 from the storage, so imp_gpu must lie within
+imp_rtol = 2^-24 + 2.001 delta + 1e-12 relative (the 1e-12 for the fp64 steps) plus
+IMP_ATOL = 2^-149 of the oracle's (compare_importance).
 
 Tie rules, used wherever a floating-point comparison decides an integer result:
   * permutation: a rank where GPU and oracle list different keys is a recorded tie iff the two
-    keys' oracle importances differ by at most 1e-6 relative (above twice IMP_RTOL);
+    keys' oracle importances differ by at most 1e-6 relative (above twice imp_rtol);
   * block mask: a differing row is a recorded tie iff every differing block has
     |p_J - p_(k*)| <= 1e-6, or is the cut block or the next one in the oracle's order while the
     oracle's running mass C_{k*-1} or C_{k*} is within 1e-6 of tau; at most 1% of rows may tie;
@@ -27,7 +33,7 @@ Tie rules, used wherever a floating-point comparison decides an integer result:
     oracle list different keys is a recorded tie iff the two keys' oracle scores differ by at most
     1e-6 relative;
   * SampleAttention mask: the GPU's column / slash masses (fp64 sums of exponentials stored in
-    fp32, as for the importance) must match the oracle's within IMP_RTOL relative (+ IMP_ATOL); a kept column or slash set may differ from the one the oracle's masses give only by
+    fp32, as for the importance) must match the oracle's within imp_rtol relative (+ IMP_ATOL); a kept column or slash set may differ from the one the oracle's masses give only by
     members whose mass is within 1e-6 of the cut mass, or when the cumulative mass at the cut is
     within 1e-6 of the target; the GPU's mask must equal the tiles of the sets its own masses give;
   * marginal-gain stop: the kernel forms dl_i / l_i from bf16-rounded probabilities (each off by
@@ -45,15 +51,49 @@ O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
 S2O_BAND = 1e-2
 F32_U = 2.0 ** -24
-IMP_RTOL = 2.0 ** -24 + 1e-12
 IMP_ATOL = 2.0 ** -149
 
 
-def compare_importance(imp_g: np.ndarray, imp_o: np.ndarray) -> float:
-    """Assert the GPU importance is within IMP_RTOL relative (+ IMP_ATOL) of the oracle's; return the
+# Weight of the digit products the logits leave out, per element and in units of u_q u_k: levels
+# a + b = 6..10 of two six-digit numbers (11 - L pairs at level L, |digit products| <= 2^14).
+IMP_DROP = 2 ** 14 * (5 * 2 ** 28 + 4 * 2 ** 21 + 3 * 2 ** 14 + 2 * 2 ** 7 + 1)
+
+
+def _row_unit(x: np.ndarray) -> np.ndarray:
+    """2^(E - 168) per row of bf16 values held in fp64, E the row's largest exponent field (at
+    least 1): the unit of the row's 42-bit fixed-point form."""
+    amax = np.abs(x).max(axis=-1)
+    _, ex = np.frexp(amax)  # amax = f 2^ex, f in [0.5, 1): exponent field ex + 126 for a normal
+    e = np.where(amax > 0, ex + 126, 0)
+    return np.ldexp(1.0, np.maximum(e, 1) - 168)
+
+
+def imp_logit_error(q: np.ndarray, k: np.ndarray, scale: float | None = None) -> float:
+    """Upper bound of |GPU logit - c q.k| over every query row of each KV group's heads and every
+    key of that group (the rule in the module docstring; sums of maxima bound the max of sums)."""
+    Hq, _, d = q.shape
+    Hkv = k.shape[0]
+    G = Hq // Hkv
+    c = 1.0 / np.sqrt(d) if scale is None else scale
+    worst = 0.0
+    for g in range(Hkv):
+        qg = q[g * G:(g + 1) * G].reshape(-1, d)
+        uq, sq = _row_unit(qg).max(), np.abs(qg).sum(axis=-1).max()
+        uk, sk = _row_unit(k[g]).max(), np.abs(k[g]).sum(axis=-1).max()
+        worst = max(worst, c * (uq * sk + uk * sq + d * uq * uk * (1 + IMP_DROP)))
+    return float(worst)
+
+
+def imp_rtol(q: np.ndarray, k: np.ndarray, scale: float | None = None) -> float:
+    """Relative tolerance of GPU importances (and SampleAttention masses) for these inputs."""
+    return F32_U + 2.001 * imp_logit_error(q, k, scale) + 1e-12
+
+
+def compare_importance(imp_g: np.ndarray, imp_o: np.ndarray, rtol: float) -> float:
+    """Assert the GPU importance is within rtol relative (+ IMP_ATOL) of the oracle's; return the
     largest relative error seen."""
     err = np.abs(imp_g - imp_o)
-    lim = IMP_RTOL * np.abs(imp_o) + IMP_ATOL
+    lim = rtol * np.abs(imp_o) + IMP_ATOL
     bad = np.argwhere(err > lim)
     assert bad.size == 0, f"importance off at {bad[:5].tolist()}: gpu {imp_g[tuple(bad[0])]!r} oracle {imp_o[tuple(bad[0])]!r}"
     nz = imp_o != 0
@@ -283,10 +323,11 @@ def _cut_is_near_tie(m: np.ndarray, tau: float, a: np.ndarray, b: np.ndarray) ->
 
 
 def compare_sample_mask(count_g, idx_g, col_g, slash_g, col_o, slash_o, tau: float, B: int, force_diag: bool,
-                        force_first: bool) -> int:
-    """Assert the GPU SampleAttention mask against the oracle (rules above); return the tie count."""
-    compare_importance(col_g, col_o)
-    compare_importance(slash_g, slash_o)
+                        force_first: bool, rtol: float) -> int:
+    """Assert the GPU SampleAttention mask against the oracle (rules above; rtol = imp_rtol of the
+    inputs); return the tie count."""
+    compare_importance(col_g, col_o, rtol)
+    compare_importance(slash_g, slash_o, rtol)
     Hq = col_o.shape[0]
     ck_g = np.stack([oracle.mass_cut(col_g[h], tau) for h in range(Hq)])
     sk_g = np.stack([oracle.mass_cut(slash_g[h], tau) for h in range(Hq)])

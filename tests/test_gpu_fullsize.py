@@ -13,7 +13,7 @@ import oracle
 from parity import (F32_U, bitmap_to_kept, bitmap_to_kept_square, compare_gate, compare_importance, compare_lse,
                     compare_mask, compare_out,
                     compare_perm, compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask,
-                    gate_error_bound, kept_to_mask, two_pass_lists)
+                    gate_error_bound, imp_rtol, kept_to_mask, two_pass_lists)
 from workloads import WORKLOADS, bf16_bits_to_f32, generate_for
 
 pytestmark = pytest.mark.gpu
@@ -70,7 +70,7 @@ def test_fullsize_32k_pipeline():
     out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S)
     torch.cuda.synchronize()
     imp_o = oracle.key_importance(q, k, B)
-    compare_importance(imp_t.cpu().numpy(), imp_o)
+    compare_importance(imp_t.cpu().numpy(), imp_o, imp_rtol(q, k))
     perm_g = perm_t.cpu().numpy()
     ties = compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
     _log(f"[fullsize] permutation ok ({ties} recorded ties)")
@@ -103,7 +103,7 @@ def test_fullsize_128k_sampled():
     out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], perm_t, count_t, idx_t, B, S)
     torch.cuda.synchronize()
     imp_o = oracle.key_importance(q, k, B)
-    compare_importance(imp_t.cpu().numpy(), imp_o)
+    compare_importance(imp_t.cpu().numpy(), imp_o, imp_rtol(q, k))
     perm_g = perm_t.cpu().numpy()
     compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
     _log("[fullsize] 128K permutation ok")
@@ -136,7 +136,7 @@ def test_fullsize_64k_sweep_sampled():
     perm_t, imp_t = pbsa.build_segment_permutation(dev["q"], dev["k"], B, S, return_importance=True)
     torch.cuda.synchronize()
     imp_o = oracle.key_importance(q, k, B)
-    compare_importance(imp_t.cpu().numpy(), imp_o)
+    compare_importance(imp_t.cpu().numpy(), imp_o, imp_rtol(q, k))
     perm_g = perm_t.cpu().numpy()
     compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
     _log("[fullsize] 64K permutation ok")
@@ -179,7 +179,7 @@ def test_max_blocks_sampled():
     dense_t, dense_lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], block_size=B)
     torch.cuda.synchronize()
     imp_o = oracle.key_importance(q, k, B)
-    compare_importance(imp_t.cpu().numpy(), imp_o)
+    compare_importance(imp_t.cpu().numpy(), imp_o, imp_rtol(q, k))
     perm_g = perm_t.cpu().numpy()
     compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
     cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
@@ -391,7 +391,8 @@ def test_fullsize_32k_sample_attention_mask():
     torch.cuda.synchronize()
     cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
     col_o, sl_o = oracle.sampled_masses(q, k, nt, rpt)
-    ties = compare_sample_mask(cg, ig, col_t.cpu().numpy(), sl_t.cpu().numpy(), col_o, sl_o, tau, B, True, False)
+    ties = compare_sample_mask(cg, ig, col_t.cpu().numpy(), sl_t.cpu().numpy(), col_o, sl_o, tau, B, True, False,
+                               imp_rtol(q, k))
     rows = _sample_rows(Hq, NB, 8, 14)
     out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, cg, ig, B, None, rows=rows)
     mx, mean = compare_out(_rows_slice(out_t.cpu().numpy(), rows, B, N), out_o, "sample mask 32K")

@@ -13,7 +13,7 @@ import oracle
 from parity import (F32_U, bitmap_to_kept, bitmap_to_kept_square, compare_gate, compare_importance, compare_lse,
                     compare_mask, compare_out,
                     compare_perm, compare_prefix_rank, compare_ranked, compare_s2o_stops, compare_sample_mask,
-                    gate_error_bound, kept_to_mask, two_pass_lists)
+                    gate_error_bound, imp_rtol, kept_to_mask, two_pass_lists)
 from workloads import bf16_bits_to_f32, bf16_round_bits, generate
 
 pytestmark = pytest.mark.gpu
@@ -67,7 +67,7 @@ def test_pipeline_stagewise(case):
     torch.cuda.synchronize()
     imp_g, perm_g = imp_t.cpu().numpy(), perm_t.cpu().numpy()
     imp_o = oracle.key_importance(q, k, B)
-    compare_importance(imp_g, imp_o)
+    compare_importance(imp_g, imp_o, imp_rtol(q, k))
     compare_perm(perm_g, oracle.segment_permutation(imp_o, S), imp_o, S)
 
     # stage 2, on the GPU's permutation
@@ -715,7 +715,8 @@ def test_sample_attention_mask_and_attention(case):
     torch.cuda.synchronize()
     cg, ig = count_t.cpu().numpy(), idx_t.cpu().numpy()
     _, _, _, _, col_o, sl_o = oracle.sample_attention_mask(q, k, B, tau, nt, rpt)
-    ties = compare_sample_mask(cg, ig, col_t.cpu().numpy(), sl_t.cpu().numpy(), col_o, sl_o, tau, B, True, False)
+    ties = compare_sample_mask(cg, ig, col_t.cpu().numpy(), sl_t.cpu().numpy(), col_o, sl_o, tau, B, True, False,
+                               imp_rtol(q, k))
     out_t, lse_t = pbsa.block_sparse_attn_prefill(dev["q"], dev["k"], dev["v"], None, count_t, idx_t, B, 0)
     torch.cuda.synchronize()
     out_o, lse_o, _, _ = oracle.block_sparse_attention(q, k, v, None, cg, ig, B, None)
@@ -749,7 +750,8 @@ def test_sample_attention_mask_with_exact_ties():
     _log(f"[exact ties] {tied} masses equal to another of their head and family on the GPU")
     assert tied > 0
     _, _, _, _, col_o, sl_o = oracle.sample_attention_mask(qh, kh, B, tau, nt, rpt)
-    compare_sample_mask(count_t.cpu().numpy(), idx_t.cpu().numpy(), col_g, sl_g, col_o, sl_o, tau, B, True, False)
+    compare_sample_mask(count_t.cpu().numpy(), idx_t.cpu().numpy(), col_g, sl_g, col_o, sl_o, tau, B, True, False,
+                        imp_rtol(qh, kh))
 
 
 def test_sample_attention_full_target_is_dense():

@@ -132,8 +132,8 @@ def test_compare_gate_catches_a_wrong_decision():
 def test_importance_bound_covers_fp32_exponentials(make_inputs):
     """The importance pass keeps exp(s - chunk max) rounded to fp32 between its launches: evaluate
     the mean that way (64-key chunks, as the kernel does) and check it against the oracle within
-    IMP_RTOL, and that the rounding is actually visible (the bound is not vacuous)."""
-    from parity import IMP_ATOL, IMP_RTOL, compare_importance
+    imp_rtol, and that the rounding is actually visible (the bound is not vacuous)."""
+    from parity import IMP_ATOL, compare_importance, imp_rtol
     N, Hq, Hkv, d, B = 700, 4, 2, 64, 64
     q, k, _ = make_inputs(N, Hq, Hkv, d, n_stripes=6, band=64, seed=21)
     G, c = Hq // Hkv, 1.0 / math.sqrt(d)
@@ -153,12 +153,95 @@ def test_importance_bound_covers_fp32_exponentials(make_inputs):
                 sim[g, c0:c0 + 64] += (e32 * w).sum(0)
         sim[g] /= G * len(rows)
     imp_o = oracle.key_importance(q, k, B)
-    worst = compare_importance(sim, imp_o)
-    assert 1e-9 < worst <= IMP_RTOL
+    rtol = imp_rtol(q, k)
+    assert 2.0 ** -24 < rtol < 2.0 ** -24 * 1.1  # the logit term is small beside the storage rounding
+    worst = compare_importance(sim, imp_o, rtol)
+    assert 1e-9 < worst <= rtol
     # an error just outside the bound is caught
     planted = imp_o.copy()
     j = int(np.argmax(imp_o[0]))
-    planted[0, j] *= 1 + 2 * IMP_RTOL
+    planted[0, j] *= 1 + 2 * rtol
     with pytest.raises(AssertionError):
-        compare_importance(planted, imp_o)
+        compare_importance(planted, imp_o, rtol)
     assert IMP_ATOL < 1e-40
+
+
+def _bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest even), returned in fp64."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _fixed_digits(row: np.ndarray):
+    """The 42-bit fixed-point form of a bf16 row and its six digits, written from the description
+    of the importance logits: x = M 2^(e' - 134), V = trunc(M 2^(e' - E + 34)), +-V in two's
+    complement = D_0 2^35 + sum_a D_a 2^(35 - 7a).  Returns (E, digits [d][6])."""
+    f, ex = np.frexp(np.abs(row))
+    e = np.where(row == 0, 0, np.maximum(ex + 126, 0))
+    ep = np.maximum(e, 1)
+    M = np.abs(row) / np.ldexp(1.0, ep - 134)
+    assert np.all(M == np.round(M)) and np.all(M <= 255)  # the row really is bf16
+    E = int(ep.max())
+    digs = []
+    for m, p, x in zip(M.astype(np.int64), ep, row):
+        sh = 34 - (E - int(p))
+        v = (int(m) << sh) if sh >= 0 else (int(m) >> -sh)
+        v = -v if x < 0 else v
+        dg = [v >> 35] + [(v >> (35 - 7 * a)) & 127 for a in range(1, 6)]
+        assert -128 <= dg[0] <= 127 and sum(x_ << (35 - 7 * a) for a, x_ in enumerate(dg)) == v
+        digs.append(dg)
+    return E, np.array(digs, dtype=np.int64)
+
+
+def test_importance_logit_digits_within_bound():
+    """The importance logits are exact integer sums of digit products (levels a + b <= 5) scaled by
+    2^(Eq + Ek - 301): model that on the CPU with exact integers and check every logit against the
+    correctly rounded c q.k within the bound the parity tests use (parity.imp_logit_error), on rows
+    with narrow and very wide exponent spreads, zeros, subnormals and large values; the level sums
+    stay inside int32 as the kernel needs.  Planted slips (a dropped level, a wrong digit weight)
+    break the bound."""
+    import math
+    from parity import imp_logit_error
+    rng = np.random.default_rng(7)
+
+    def model(qr, kr, c, drop_level=None, shift=7):
+        Eq, Dq = _fixed_digits(qr)
+        Ek, Dk = _fixed_digits(kr)
+        A = [sum(int(Dq[:, a] @ Dk[:, L - a]) for a in range(L + 1)) if L != drop_level else 0 for L in range(6)]
+        assert all(abs(x) < 2 ** 31 for x in A)
+        c01, c23, c45 = A[0] * 2 ** shift + A[1], A[2] * 2 ** shift + A[3], A[4] * 2 ** shift + A[5]
+        assert all(abs(x) < 2 ** 31 for x in (c01, c23, c45))
+        t = (float(c01) * 16384.0 + float(c23)) * 16384.0 + float(c45)
+        return t * math.ldexp(c, Eq - 150) * math.ldexp(1.0, Ek - 151)
+
+    worst, caught5 = 0.0, 0
+    for trial in range(160):
+        d = (64, 128)[trial % 2]
+        q, k = rng.standard_normal(d), rng.standard_normal(d)
+        kind = trial % 5
+        if kind == 1:  # exponents spread over 2^-60 .. 2^10: truncated elements on both sides
+            q *= np.exp2(rng.integers(-60, 10, d))
+            k *= np.exp2(rng.integers(-60, 10, d))
+        elif kind == 2:  # zeros, bf16 subnormals, a large leading element
+            q[rng.integers(0, d, 8)] = 0.0
+            k[:4] = 3e-39
+            q[0] = 1e20
+        elif kind == 3:
+            q, k = q * 40, k * 0.01
+        elif kind == 4:  # every element at the row's top exponent
+            q, k = np.sign(q) * (1 + np.abs(q) % 1), np.sign(k) * (1 + np.abs(k) % 1)
+        q, k = _bf16_round(q), _bf16_round(k)
+        c = 1.0 / math.sqrt(d)
+        exact = c * math.fsum(q * k)
+        bound = imp_logit_error(q[None, None], k[None, None], c) + 4 * 2.0 ** -53 * abs(exact)
+        err = abs(model(q, k, c) - exact)
+        assert err <= bound, (trial, err, bound)
+        worst = max(worst, err / bound)
+        if kind == 0:
+            assert abs(model(q, k, c, drop_level=1) - exact) > bound  # a dropped level is caught
+            assert abs(model(q, k, c, shift=6) - exact) > bound       # a wrong digit weight is caught
+        elif kind == 1:  # the low levels matter once elements sit far below the row's largest
+            caught5 += abs(model(q, k, c, drop_level=5) - exact) > bound
+    assert worst > 1e-3  # the bound is not vacuous: the truncation shows in some rows
+    assert caught5 >= 16  # of the 32 wide-spread pairs
