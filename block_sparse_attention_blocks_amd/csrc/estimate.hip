@@ -35,7 +35,8 @@ namespace pbsa {
 // so every logit is computed once and exponentiated once.
 //
 // Fixed-point digits.  A bf16 value is x = M 2^(e' - 134): M its significand with the implicit bit
-// (0..255), e' = max(e, 1) for the exponent field e.  With E the largest e' of x's row,
+// (0..255), e' = max(e, 1) for the exponent field e.  With E the largest e' of x's row (for keys:
+// of the 64-key chunk),
 // V = trunc(M 2^(e' - E + 34)) is an integer below 2^42 (exact whenever E - e' <= 34) and
 // x = (+-V) 2^(E - 168) up to that truncation.  In two's complement, +-V = sum_a D_a 2^(35 - 7a)
 // (a = 0..5) with D_0 = (+-V) >> 35 in [-128, 127] and D_a (a >= 1) the 7-bit fields below it, in
@@ -60,12 +61,12 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Digits of the key rows, chunk-major: [Hkv][nchunk][IMP_NDIG][IMP_CK][d] bytes, then the row
-// exponents E [Hkv][nchunk * IMP_CK] (int32).  Keys past N are zero rows (digits 0, E = 1).
+// Digits of the key rows, chunk-major: [Hkv][nchunk][IMP_NDIG][IMP_CK][d] bytes, then the chunk
+// exponents E [Hkv][nchunk] (int32).  Keys past N are zero rows (digits 0).
 static inline size_t kdig_bytes(const Geometry& g, size_t nchunk) {
   return (size_t)g.Hkv * nchunk * IMP_NDIG * IMP_CK * g.d;
 }
-static inline size_t kexp_bytes(const Geometry& g, size_t nchunk) { return sizeof(int) * g.Hkv * nchunk * IMP_CK; }
+static inline size_t kexp_bytes(const Geometry& g, size_t nchunk) { return sizeof(int) * g.Hkv * nchunk; }
 
 struct ImpWs {
   float* e;        // [Hkv][R][N] chunk-normalised exponentials, rounded to fp32
@@ -74,7 +75,7 @@ struct ImpWs {
   double* lse;     // [Hkv][R]
   double* imp;     // [Hkv][N] (used when the caller passes no importance output)
   int8_t* kdig;    // key digits (layout above)
-  int* kexp;       // key row exponents
+  int* kexp;       // key chunk exponents
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -169,29 +170,23 @@ __device__ __forceinline__ double row_sum_f64(double x) {  // exact on lane 0 of
 }
 
 
-// exp(x) for the logits of the importance pass (x <= 0, -inf allowed), written out in fp64:
-// Cody-Waite reduction x = n ln2 + r with |r| <= ln2/2 (ln2 split into a 32-significant-bit head,
-// so n * head is exact, and the rounded remainder), exp(r) by its Taylor series to degree 11
-// (truncation below 1e-14 relative on that interval; 8.8e-15 worst case measured against the math
-// library on [-60, 0]), then the exact scaling by 2^n.  Below -745 the result is 0.
-// Taylor coefficients 1/11! .. 1/3!, read from constant memory so that they reach the FMAs as scalar
-// operands (as literals they were copied into vector registers before every accumulating FMA).
-__constant__ double kExpTaylor[9] = {2.505210838544172e-08, 2.755731922398589e-07, 2.7557319223985893e-06,
-                                     2.48015873015873e-05, 0.0001984126984126984, 0.001388888888888889,
-                                     0.008333333333333333, 0.041666666666666664, 0.16666666666666666};
-__device__ __forceinline__ double exp_nonpos(double x) {
-  constexpr double kLog2e = 1.4426950408889634, kLn2Hi = 0.6931471803691238, kLn2Lo = 1.9082149292705877e-10;
-  const double n = rint(x * kLog2e);
-  double r = fma(-n, kLn2Hi, x);
-  r = fma(-n, kLn2Lo, r);
-  double q = kExpTaylor[0];  // 1/11!
-#pragma unroll
-  for (int i = 1; i < 9; ++i) q = fma(q, r, kExpTaylor[i]);
-  q = fma(q, r, 0.5);
-  q = fma(q, r, 1.0);
-  q = fma(q, r, 1.0);
-  const double y = ldexp(q, (int)n);
-  return x < -745.0 ? 0.0 : y;
+// exp(dT F) for the logits of the importance pass: dT = T - Tmax <= 0 (-inf allowed) in the integer
+// units of the logit, F > 0 the unit.  With t = dT G (G = F 64 / ln2, clamped at -70000) and
+// n = rint(t), the remainder r = (dT - n K) F, K = ln2 / (64 F), has |r| <= ln2/128 up to rounding
+// (n K F = n ln2/64 to 2^-53 relative, |n| <= 70000: below 1e-13 absolute), and
+// exp = 2^(n >> 6) tab[n & 63] p(r) with tab[j] = 2^(j/64) and p the Taylor polynomial of e^r to
+// degree 4 (truncation below 4e-14 relative).  Below t = -68800 (dT F < -745.2) the result is 0.
+__device__ __forceinline__ double exp_chunk(double dT, double F, double G, double K, const double* tab) {
+  const double t = fmax(dT * G, -70000.0);
+  const double n = rint(t);
+  const double r = fma(-n, K, dT) * F;
+  double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ni = (int)n;
+  const double y = ldexp(tab[ni & 63] * p, ni >> 6);
+  return t < -68800.0 ? 0.0 : y;
 }
 
 // Largest exponent field (at least 1) of the bf16 values packed two to a word.
@@ -222,38 +217,41 @@ __device__ __forceinline__ uint32_t pack_digits(const uint64_t* v) {
          (fixed_digit<A>(v[3]) << 24);
 }
 
-// Largest value over the n lanes of an aligned group of n = 8 or 16 lanes (DPP, within a row).
-template <int NL>
-__device__ __forceinline__ int group_max_i32(int x) {
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
-  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false));  // row_half_mirror
-  if (NL == 16) x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false));  // row_mirror
-  return x;
-}
-
 // Key digits, once per key: one workgroup per (64-key chunk, KV head); a thread takes 8 values
-// (16 bytes) of a row, the D/8 threads of a row are consecutive lanes and share its exponent.
+// (16 bytes) of a row.  All keys of a chunk share one exponent E (the largest over the chunk), so
+// a logit's unit is the same along a row of the chunk.
 template <int D>
 __global__ __launch_bounds__(256) void imp_kdigits_kernel(const uint16_t* k, int N, int64_t kvsh, int64_t kvst,
                                                           int8_t* kdig, int* kexp) {
   constexpr int cpr = D / 8;
   constexpr int NLD = IMP_CK * cpr / 256;
+  __shared__ int wmax[4];
   const int c = blockIdx.x, g = blockIdx.y, t = threadIdx.x, nchunk = gridDim.x;
   const uint16_t* kbase = k + (int64_t)g * kvsh;
   int8_t* out = kdig + ((size_t)g * nchunk + c) * IMP_NDIG * IMP_CK * D;
+  u32x4 w[NLD];
+  int em = 1;
 #pragma unroll
   for (int x = 0; x < NLD; ++x) {
     const int idx = t + x * 256, row = idx / cpr, ch = idx % cpr, j = c * IMP_CK + row;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (j < N) w = *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * kvst + ch * 8);
-    int em = max(max(bf16_pair_emax(w[0]), bf16_pair_emax(w[1])), max(bf16_pair_emax(w[2]), bf16_pair_emax(w[3])));
-    em = group_max_i32<cpr>(em);
+    w[x] = u32x4{0u, 0u, 0u, 0u};
+    if (j < N) w[x] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)j * kvst + ch * 8);
+    em = max(em, max(max(bf16_pair_emax(w[x][0]), bf16_pair_emax(w[x][1])),
+                     max(bf16_pair_emax(w[x][2]), bf16_pair_emax(w[x][3]))));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) em = max(em, __shfl_xor(em, o));
+  if ((t & 63) == 0) wmax[t >> 6] = em;
+  __syncthreads();
+  em = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+#pragma unroll
+  for (int x = 0; x < NLD; ++x) {
+    const int idx = t + x * 256, row = idx / cpr, ch = idx % cpr;
     uint64_t v[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      v[2 * e] = bf16_fixed(w[e] & 0xffffu, em);
-      v[2 * e + 1] = bf16_fixed(w[e] >> 16, em);
+      v[2 * e] = bf16_fixed(w[x][e] & 0xffffu, em);
+      v[2 * e + 1] = bf16_fixed(w[x][e] >> 16, em);
     }
     int8_t* o = out + row * D + ch * 8;
     *reinterpret_cast<uint2*>(o + 0 * IMP_CK * D) = make_uint2(pack_digits<0>(v), pack_digits<0>(v + 4));
@@ -262,8 +260,8 @@ __global__ __launch_bounds__(256) void imp_kdigits_kernel(const uint16_t* k, int
     *reinterpret_cast<uint2*>(o + 3 * IMP_CK * D) = make_uint2(pack_digits<3>(v), pack_digits<3>(v + 4));
     *reinterpret_cast<uint2*>(o + 4 * IMP_CK * D) = make_uint2(pack_digits<4>(v), pack_digits<4>(v + 4));
     *reinterpret_cast<uint2*>(o + 5 * IMP_CK * D) = make_uint2(pack_digits<5>(v), pack_digits<5>(v + 4));
-    if (ch == 0) kexp[(size_t)g * nchunk * IMP_CK + c * IMP_CK + row] = em;
   }
+  if (t == 0) kexp[(size_t)g * nchunk + c] = em;
 }
 
 // v_mfma_i32_16x16x64_i8 (lane l): A holds row l%16 and B column l%16, each 16 int8 of the
@@ -340,28 +338,28 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
         av[5][h][q4] = (int)pack_digits<5>(v);
       }
   }
-  // this lane's D rows (proxy rows r0 + 16 w + 4 lg + rr): query positions and the factor
-  // c 2^(Eq - 150) of the logit
-  int qi[4];
-  double fq[4];
+  // this lane's D rows (proxy rows r0 + 16 w + 4 lg + rr): query positions and exponents; the unit
+  // of a logit is c 2^(Eq + Ek - 301)
+  int qi[4], eq[4];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int r = r0 + 16 * w + 4 * lg + rr;
     int h, i;
     imp_row(a, g, r, &h, &i);
     qi[rr] = r < a.R ? i : -1;
-    fq[rr] = ldexp(a.scale, __shfl(emq, 4 * lg + rr) - 150);
+    eq[rr] = __shfl(emq, 4 * lg + rr) - 301;
   }
+  const double cG = a.scale * (64.0 / 0.69314718055994530942), cK = 0.69314718055994530942 / (64.0 * a.scale);
+  __shared__ double tab[64];  // 2^(j/64)
+  if (t < 64) tab[t] = exp2((double)t * (1.0 / 64.0));
   const int first_proxy = a.first_row;  // every key j <= first_proxy is visible to every proxy row
 
   const int8_t* kd = kdig + (size_t)g * nchunk * IMP_NDIG * IMP_CK * D;
-  const int* ke = kexp + (size_t)g * nchunk * IMP_CK;
-  auto prefetch = [&](int c, u32x4* pf, int* pe) {
+  const int* ke = kexp + (size_t)g * nchunk;
+  auto prefetch = [&](int c, u32x4* pf) {
     const u32x4* src = reinterpret_cast<const u32x4*>(kd + (size_t)c * IMP_NDIG * IMP_CK * D);
 #pragma unroll
     for (int x = 0; x < NST; ++x) pf[x] = src[t + x * IMP_THREADS];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) pe[tt] = ke[c * IMP_CK + 16 * tt + l16];
   };
   // piece u = t + x * IMP_THREADS of the chunk: plane u / (IMP_CK U16), key (u / U16) % IMP_CK,
   // bytes 16 (u % U16) of the row
@@ -376,16 +374,13 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
   const int8_t* bbase = Ks + l16 * PITCH + 16 * lg;  // B of plane b, column tile tt, step h
 
   u32x4 pf[NST];
-  int pe[4];
-  prefetch(c0, pf, pe);
+  prefetch(c0, pf);
   for (int c = c0; c < c1; ++c) {
     stage(pf);
-    double fk[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) fk[tt] = ldexp(1.0, pe[tt] - 151);
+    const int ek = ke[c];
     __syncthreads();
-    if (c + 1 < c1) prefetch(c + 1, pf, pe);
-    double x[4][4];  // logit of row 4 lg + rr, key 16 tt + l16
+    if (c + 1 < c1) prefetch(c + 1, pf);
+    double x[4][4];  // logit of row 4 lg + rr, key 16 tt + l16, in units of c 2^(Eq + Ek - 301)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
       i32x4 lv[IMP_NDIG];
@@ -405,8 +400,7 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
         const int c01 = lv[0][rr] * 128 + lv[1][rr];
         const int c23 = lv[2][rr] * 128 + lv[3][rr];
         const int c45 = lv[4][rr] * 128 + lv[5][rr];
-        const double tv = fma(fma((double)c01, 16384.0, (double)c23), 16384.0, (double)c45);
-        x[tt][rr] = tv * fq[rr] * fk[tt];
+        x[tt][rr] = fma(fma((double)c01, 16384.0, (double)c23), 16384.0, (double)c45);
       }
     }
     // per proxy row: chunk max, sum of exponentials, and the exponentials themselves
@@ -414,26 +408,29 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
     const bool open = j0 + IMP_CK - 1 <= first_proxy && j0 + IMP_CK <= a.N;  // no key of the chunk is masked
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
+      const double F = ldexp(a.scale, eq[rr] + ek), G = ldexp(cG, eq[rr] + ek), K = ldexp(cK, -eq[rr] - ek);
       double sv[4];
       double m;
       if (open) {
-        m = row_max_f64(fmax(fmax(x[0][rr], x[1][rr]), fmax(x[2][rr], x[3][rr])));
+        const double tm = row_max_f64(fmax(fmax(x[0][rr], x[1][rr]), fmax(x[2][rr], x[3][rr])));
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_nonpos(x[tt][rr] - m);
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_chunk(x[tt][rr] - tm, F, G, K, tab);
+        m = tm * F;
       } else {
         const int i = qi[rr];
-        m = -INFINITY;
+        double tm = -INFINITY;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
           const int j = j0 + 16 * tt + l16;
           const bool ok = (i >= 0) && (j < a.N) && (j <= i);
           sv[tt] = ok ? x[tt][rr] : -INFINITY;
-          m = fmax(m, sv[tt]);
+          tm = fmax(tm, sv[tt]);
         }
-        m = row_max_f64(m);
-        const double mm = m > -INFINITY ? m : 0.0;
+        tm = row_max_f64(tm);
+        const double tmm = tm > -INFINITY ? tm : 0.0;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_nonpos(sv[tt] - mm);
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_chunk(sv[tt] - tmm, F, G, K, tab);
+        m = tm * F;  // -inf for a row with no key in the chunk
       }
       double l = (sv[0] + sv[1]) + (sv[2] + sv[3]);
       l = row_sum_f64(l);

@@ -4,8 +4,9 @@ Importance values: the GPU forms each logit c q.k from fixed-point digits of the
 7-bit digits of a 42-bit integer at the row's largest exponent E, digit products of weight at
 least 2^-42 of the leading one summed exactly in int32), so a logit is off by at most
   delta = c (u_q sum|k| + u_k sum|q| + d u_q u_k (1 + IMP_DROP)),  u = 2^(E - 168),
-(the truncated elements and the dropped digit products; imp_logit_error takes the largest over the
-rows and keys of each KV group, a few 1e-10 on the workloads); every exponential, sum and
+(the truncated elements and the dropped digit products; E of a key is the largest over its 64-key
+chunk, never above the largest over all keys, so imp_logit_error takes the largest u over the rows
+and keys of each KV group: a few 1e-10 on the workloads); every exponential, sum and
 log-sum-exp after that is fp64, and only the chunk-normalised exponentials e (in (0, 1]) are kept
 rounded to fp32 between launches.  A term exp(s - lse) of the (positive) mean then moves by at
 most exp(2 delta) - 1 from the logit error and 2^-24 from the storage, so imp_gpu must lie within

@@ -173,16 +173,18 @@ def _bf16_round(x: np.ndarray) -> np.ndarray:
     return b.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def _fixed_digits(row: np.ndarray):
+def _fixed_digits(row: np.ndarray, E: int | None = None):
     """The 42-bit fixed-point form of a bf16 row and its six digits, written from the description
     of the importance logits: x = M 2^(e' - 134), V = trunc(M 2^(e' - E + 34)), +-V in two's
-    complement = D_0 2^35 + sum_a D_a 2^(35 - 7a).  Returns (E, digits [d][6])."""
+    complement = D_0 2^35 + sum_a D_a 2^(35 - 7a), E the row's largest e' or a larger exponent
+    shared with other rows (a key chunk's).  Returns (E, digits [d][6])."""
     f, ex = np.frexp(np.abs(row))
     e = np.where(row == 0, 0, np.maximum(ex + 126, 0))
     ep = np.maximum(e, 1)
     M = np.abs(row) / np.ldexp(1.0, ep - 134)
     assert np.all(M == np.round(M)) and np.all(M <= 255)  # the row really is bf16
-    E = int(ep.max())
+    E = int(ep.max()) if E is None else E
+    assert E >= ep.max()
     digs = []
     for m, p, x in zip(M.astype(np.int64), ep, row):
         sh = 34 - (E - int(p))
@@ -205,9 +207,9 @@ def test_importance_logit_digits_within_bound():
     from parity import imp_logit_error
     rng = np.random.default_rng(7)
 
-    def model(qr, kr, c, drop_level=None, shift=7):
+    def model(qr, kr, c, drop_level=None, shift=7, ek=None):
         Eq, Dq = _fixed_digits(qr)
-        Ek, Dk = _fixed_digits(kr)
+        Ek, Dk = _fixed_digits(kr, ek)
         A = [sum(int(Dq[:, a] @ Dk[:, L - a]) for a in range(L + 1)) if L != drop_level else 0 for L in range(6)]
         assert all(abs(x) < 2 ** 31 for x in A)
         c01, c23, c45 = A[0] * 2 ** shift + A[1], A[2] * 2 ** shift + A[3], A[4] * 2 ** shift + A[5]
@@ -237,6 +239,13 @@ def test_importance_logit_digits_within_bound():
         bound = imp_logit_error(q[None, None], k[None, None], c) + 4 * 2.0 ** -53 * abs(exact)
         err = abs(model(q, k, c) - exact)
         assert err <= bound, (trial, err, bound)
+        # the key row inside a chunk whose largest exponent is up to 2^12 above its own: the bound
+        # over a key set holding that larger row still covers it
+        ek = _fixed_digits(k)[0] + int(rng.integers(1, 13))
+        big = np.zeros((2, d))
+        big[0], big[1, 0] = k, np.ldexp(1.0, ek - 127)
+        bound_c = imp_logit_error(q[None, None], big[None], c) + 4 * 2.0 ** -53 * abs(exact)
+        assert abs(model(q, k, c, ek=ek) - exact) <= bound_c, (trial, ek)
         worst = max(worst, err / bound)
         if kind == 0:
             assert abs(model(q, k, c, drop_level=1) - exact) > bound  # a dropped level is caught
