@@ -165,10 +165,13 @@ void attn_pipe_kernel(AttnArgs a) {
       dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES, true>(Kd, kr, rf);
       dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES, true>(Vd, vr, rf);
     } else {
-      const uint32_t* ids = rowid[b];
-      auto rf = [&](int j) { return ids[j]; };
-      dma_tile<D, BLK, false, decltype(rf), KT, C::WAVES, true>(Kd, kr, rf);
-      dma_tile<D, BLK, true, decltype(rf), KT, C::WAVES, true>(Vd, vr, rf);
+      // the lane's row offsets, read once for both tiles and all before the first DMA
+      using L = GatherLane<D, KT, C::WAVES>;
+      uint32_t ro[L::NI];
+#pragma unroll
+      for (int i = 0; i < L::NI; ++i) ro[i] = rowid[b][L::row(i)];
+      dma_tile_ro<D, false, KT, C::WAVES>(Kd, kr, ro);
+      dma_tile_ro<D, true, KT, C::WAVES>(Vd, vr, ro);
     }
   };
 
@@ -196,6 +199,9 @@ void attn_pipe_kernel(AttnArgs a) {
   auto step = [&](int s, int b) __attribute__((always_inline)) -> bool {  // b = s % NBUF
     const uint16_t* Kc = Kb(b);
     const uint16_t* Vc = Vb(b);
+    // this stage's list entry is read ahead of the gathers below, whose asm statements would
+    // otherwise hold the LDS read back until they are issued
+    const uint32_t e = s < nst ? entry_of(s) : 0u;
     // the first K operands of this stage are read right after the barrier that made the stage
     // ready, so their LDS latency passes while the lookups and gathers below are issued (a stage
     // this head skips reads them for nothing)
@@ -206,7 +212,6 @@ void attn_pipe_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gathers (vmcnt order)
     const bool issue = s + NBUF - 1 < nst;
     if (issue) gather(s + NBUF - 1, (b + NBUF - 1) % NBUF);
-    const uint32_t e = s < nst ? entry_of(s) : 0u;
     if (((e & ~(done << 16)) >> (16 + hh)) & 1u) {
       const int J = (int)(e & 0xffffu);
       const int koff = (s % C::STAGES) * KT;  // first key of this stage inside block J
@@ -325,6 +330,52 @@ __device__ __forceinline__ f32x16 tile_scores(const uint16_t* Ks, const bf16x8* 
   if (diag) causal_mask(s, rel);
   return s;
 }
+
+// Scores of every score block of a tile, with the K operands streamed through a ring of PF + 1
+// registers in block-major, k-step-minor order: the read of operand i + PF is issued before the
+// product that takes operand i, so PF reads are in flight under the products instead of one batch
+// read and waited for at a time.  first holds operands 0 .. PF - 1 (tile_first_ring, read early by
+// the caller).  The products of each block run in k-step order, as in tile_scores.
+template <int D, int BLK>
+__device__ __forceinline__ bf16x8 tile_k_operand(const uint16_t* Ks, int i) {
+  constexpr int KS = AttnCfg<D, BLK>::KSTEPS;
+  const int lane = threadIdx.x & 63, h2 = lane >> 5;
+  const int kb = i / KS, kk = i % KS;
+  const int krow = kb * 32 + (lane & 31);
+  return *reinterpret_cast<const bf16x8*>(Ks + krow * D + (((kk * 2 + h2) ^ kt_swz<D>(krow)) * 8));
+}
+template <int D, int BLK, int PF>
+__device__ __forceinline__ void tile_first_ring(const uint16_t* Ks, bf16x8* first) {
+#pragma unroll
+  for (int i = 0; i < PF; ++i) first[i] = tile_k_operand<D, BLK>(Ks, i);
+}
+template <int D, int BLK, int PF>
+__device__ __forceinline__ void tile_scores_ring(const uint16_t* Ks, const bf16x8* qf, f32x16* sc, bool diag, int rel,
+                                                 const bf16x8* first) {
+  using C = AttnCfg<D, BLK>;
+  constexpr int KS = C::KSTEPS, NT = C::KB * KS;
+  bf16x8 ring[PF + 1];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) ring[i] = first[i];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    if (i + PF < NT) ring[(i + PF) % (PF + 1)] = tile_k_operand<D, BLK>(Ks, i + PF);
+    const int kb = i / KS, kk = i % KS;
+    if (kk == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.f;
+    }
+    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (PF + 1)], qf[kk], sc[kb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (diag) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) causal_mask(sc[kb], rel - kb * 32);
+  }
+}
+#ifndef PBSA_GATE_PF
+#define PBSA_GATE_PF 2
+#endif
 
 // Row max over a whole key tile (KB score blocks) of this lane's query, both half-waves, unscaled.
 template <int KB>
@@ -502,8 +553,8 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   }
 
   auto step = [&](int u, const uint16_t* Kc, uint16_t* Kn, const uint16_t* Vp, uint16_t* Vc) {
-    bf16x8 first[tile_kq<D, BLK>()];  // read before the lookups and the gather are issued
-    tile_first_ops<D, BLK>(Kc, first);
+    bf16x8 first[PBSA_GATE_PF];  // read before the lookups and the gather are issued
+    tile_first_ring<D, BLK, PBSA_GATE_PF>(Kc, first);
     const RowLook pr = lookup(u + 2 < nblk ? u + 2 : 0, t & (BLK - 1), u + 2 < nblk && t < BLK);
     __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gather (vmcnt order)
     if (u + 1 < nblk) gather_k(u + 1, Kn);
@@ -514,9 +565,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     float row_max = -INFINITY;
     if ((e >> (16 + hh)) & 1u) {
       const int rel = opaque(qloc - 4 * h2);  // causal offset, computed per tile (see opaque)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        sc[kb] = tile_scores<D, BLK>(Kc, qf, kb, diag, rel - kb * 32, kb == 0 ? first : nullptr);
+      tile_scores_ring<D, BLK, PBSA_GATE_PF>(Kc, qf, sc, diag, rel, first);
       row_max = tile_row_max<KB>(sc);
     }
     const float wm = wave_max_f32(qvalid ? row_max : -INFINITY);

@@ -175,6 +175,37 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, rsrc_t r, RowFn row_off,
   }
 }
 
+// The rows of a gather that one lane issues: row (wave * NI + i) * RPI + lane / LPR for i < NI, the
+// same rows in the K and the V tile of a stage.
+template <int D, int ROWS, int WAVES>
+struct GatherLane {
+  static constexpr int RPI = 512 / D;
+  static constexpr int LPR = D / 8;
+  static constexpr int NI = ROWS / (RPI * WAVES);
+  __device__ static __forceinline__ int row0(int i) {  // first row of the wave's i-th DMA (uniform)
+    return (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * NI + i) * RPI;
+  }
+  __device__ static __forceinline__ int row(int i) { return row0(i) + (int)(threadIdx.x & 63) / LPR; }
+};
+
+// dma_tile (inline-assembly form) from row offsets already in registers, ro[i] for the lane's row
+// GatherLane::row(i).  The offsets of a stage are read from LDS together before the first DMA: the
+// DMA's asm statement orders memory, so an LDS read placed after one DMA waits for its own round
+// trip before the next DMA can issue.
+template <int D, bool IS_V, int ROWS, int WAVES>
+__device__ __forceinline__ void dma_tile_ro(uint16_t* dst, rsrc_t r, const uint32_t* ro) {
+  using L = GatherLane<D, ROWS, WAVES>;
+  static_assert(L::NI * L::RPI * WAVES == ROWS, "tile rows must split evenly over the waves");
+  const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+  for (int i = 0; i < L::NI; ++i) {
+    const int row0 = L::row0(i);
+    const int rw = row0 + lane / L::LPR;
+    const uint32_t c = (lane % L::LPR) ^ (IS_V ? vt_swz<D>(rw) : kt_swz<D>(rw));
+    lds_dma_b128(r, lds_addr(dst) + row0 * D * 2, ro[i] + c * 16);  // kOutOfRange + c*16 stays out of range
+  }
+}
+
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // A copy of x that the compiler cannot see through.  Values derived from it inside a loop body are
