@@ -400,18 +400,24 @@ __device__ __forceinline__ void tile_softmax(SoftmaxState<D, BLK>& st, const f32
   lazy_rescale<D, BLK>(st, row_max, sl2);
   const float m_use = st.muse;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
+    // two probabilities per packed conversion; each pair is added to the row sum as it is and placed
+    // as one dword of the PV operand
+    u32x4_t pw[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pb[2 * kb + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][r], sl2, -m_use));
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pair = {pb[2 * kb + hf][2 * e], pb[2 * kb + hf][2 * e + 1]};
-        st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
-      }
+    for (int j = 0; j < 8; ++j) {
+      const f32x2 x = {__builtin_amdgcn_exp2f(fmaf(s[kb][2 * j], sl2, -m_use)),
+                       __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j + 1], sl2, -m_use))};
+      const bf16x2 pair = __builtin_convertvector(x, bf16x2);
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
+      pw[j >> 2][j & 3] = __builtin_bit_cast(unsigned int, pair);
+    }
+    pb[2 * kb] = __builtin_bit_cast(bf16x8, pw[0]);
+    pb[2 * kb + 1] = __builtin_bit_cast(bf16x8, pw[1]);
   }
 }
 

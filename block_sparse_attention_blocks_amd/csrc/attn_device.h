@@ -357,17 +357,23 @@ __device__ __forceinline__ void block_softmax_pv_ops(SoftmaxState<D, BLK>& st, c
   using C = AttnCfg<D, BLK>;
   lazy_rescale<D, BLK>(st, block_row_max(s), sl2);
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // probabilities converted two at a time (one packed conversion per pair), each pair added to the
+  // row sum as it is and placed as one dword of the PV operand
+  u32x4_t pw[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x2 x = {__builtin_amdgcn_exp2f(fmaf(s[2 * j], sl2, -st.muse)),
+                     __builtin_amdgcn_exp2f(fmaf(s[2 * j + 1], sl2, -st.muse))};
+    const bf16x2 pair = __builtin_convertvector(x, bf16x2);
+    st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
+    pw[j >> 2][j & 3] = __builtin_bit_cast(unsigned int, pair);
+  }
   bf16x8 pb[2];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) pb[r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[r], sl2, -st.muse));
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2 pair = {pb[hf][2 * e], pb[hf][2 * e + 1]};
-      st.l = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, st.l, false);
-    }
+  pb[0] = __builtin_bit_cast(bf16x8, pw[0]);
+  pb[1] = __builtin_bit_cast(bf16x8, pw[1]);
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
