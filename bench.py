@@ -96,6 +96,51 @@ def summarize_pmc(fetch_csv: str, write_csv: str, out: str, command: str, kernel
     return 0
 
 
+SQ_COUNTERS = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVE_CYCLES")
+
+
+def summarize_sq(sections, out: str, commands) -> int:
+    """Per-kernel SQ counter table from rocprofv3 --pmc counter_collection.csv files: counters summed
+    over every dispatch of a kernel; sections = [(title, csv path)].  SQ_INSTS_VALU counts the MFMA
+    instructions too, so VALU/MFMA is that count over SQ_INSTS_MFMA."""
+    import csv
+
+    def short(name):
+        name = name.replace("pbsa::", "").replace("(anonymous namespace)::", "")
+        if name.startswith("void "):
+            name = name[5:]
+        cut = name.find("(")
+        return name[:cut] if cut > 0 else name
+
+    with open(out, "w") as f:
+        f.write("# rocprofv3 SQ counters per kernel (summed over every dispatch of the kernel in the run)\n")
+        f.write("# commands (from the repository root, TMPDIR=/tmp; one --pmc pass each):\n")
+        for c in commands:
+            f.write(f"#   {c}\n")
+        f.write("# ratios: VALU/MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA, LDS/MFMA = SQ_INSTS_LDS / SQ_INSTS_MFMA,\n")
+        f.write("# waiting = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave cycles spent waiting on s_waitcnt or "
+                "a barrier)\n")
+        for title, path in sections:
+            tot, disp = {}, {}
+            for r in csv.DictReader(open(path)):
+                k = short(r["Kernel_Name"])
+                d = tot.setdefault(k, {})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                disp.setdefault(k, set()).add(r.get("Dispatch_Id", r.get("Correlation_Id", len(disp.get(k, ())))))
+            f.write(f"\n## {title}\n")
+            f.write(f"{'kernel':60s} {'dispatches':>11s} {'SQ_INSTS_MFMA':>14s} {'SQ_INSTS_VALU':>14s} "
+                    f"{'SQ_INSTS_LDS':>13s} VALU/MFMA LDS/MFMA waiting\n")
+            rows = [(k, d) for k, d in tot.items() if d.get("SQ_INSTS_MFMA", 0.0) > 0]
+            for k, d in sorted(rows, key=lambda kd: -kd[1]["SQ_INSTS_MFMA"]):
+                mf, va, ld = d["SQ_INSTS_MFMA"], d.get("SQ_INSTS_VALU", 0.0), d.get("SQ_INSTS_LDS", 0.0)
+                wt = d.get("SQ_WAIT_INST_ANY", 0.0) / max(d.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+                f.write(f"{k[:60]:60s} {len(disp[k]):11d} {mf:14.4g} {va:14.4g} {ld:13.4g} {va / mf:9.2f} "
+                        f"{ld / mf:8.2f} {100 * wt:6.1f}%\n")
+    print(open(out).read())
+    return 0
+
+
 def summarize_stats(stats_csv: str, bench_out: str, out: str, command: str, workload: str) -> int:
     """Per-kernel table from a rocprofv3 --kernel-trace --stats kernel_stats.csv, with the HIP-event
     kernel time that the bench line of the same run reported beside it."""
@@ -594,6 +639,8 @@ def main() -> int:
                     help="write the traffic summary from two rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "BENCH_OUT"),
                     help="write a kernel table from a rocprofv3 kernel_stats.csv and the bench line of that run")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="TITLE=CSV",
+                    help="write the SQ counter table from rocprofv3 --pmc counter_collection.csv files")
     ap.add_argument("--summary-out", default=TRAFFIC_SUMMARY)
     ap.add_argument("--summary-command", default="")
     ap.add_argument("--summary-kernel", default=ATTN_KERNEL, help="kernel whose counters --summarize-pmc reads")
@@ -614,6 +661,9 @@ def main() -> int:
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.summary_out, args.summary_command,
                              args.summary_kernel, args.workload)
+    if args.summarize_sq:
+        secs = [tuple(x.split("=", 1)) for x in args.summarize_sq]
+        return summarize_sq(secs, args.summary_out, [c for c in args.summary_command.split(" ;; ") if c])
     if args.summarize_stats:
         return summarize_stats(args.summarize_stats[0], args.summarize_stats[1], args.summary_out,
                                args.summary_command, args.summary_label or f"{args.workload} workload")

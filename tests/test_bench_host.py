@@ -55,3 +55,23 @@ def test_committed_traffic_summary_matches_the_kernel_sources():
     """The committed counter summary was taken on the attention source as it stands (else bench.py
     reports traffic as null)."""
     assert bench.read_traffic() is not None
+
+
+def test_sq_summary_sums_counters_per_kernel(tmp_path):
+    """Counters of two dispatches of one kernel are summed; the ratios are those sums' quotients."""
+    path = tmp_path / "sq.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for disp in (1, 2):
+            for name, val in (("SQ_INSTS_MFMA", 100.0), ("SQ_INSTS_VALU", 550.0), ("SQ_INSTS_LDS", 150.0),
+                              ("SQ_WAIT_INST_ANY", 40.0), ("SQ_WAVE_CYCLES", 100.0)):
+                w.writerow({"Dispatch_Id": disp, "Kernel_Name": "void pbsa::k<1>(pbsa::AttnArgs)",
+                            "Counter_Name": name, "Counter_Value": val})
+    out = tmp_path / "sq.txt"
+    assert bench.summarize_sq([("one run", str(path))], str(out), ["cmd a", "cmd b"]) == 0
+    text = out.read_text()
+    assert "#   cmd a" in text and "## one run" in text
+    line = [l for l in text.splitlines() if l.startswith("k<1>")][0].split()
+    assert line[1] == "2" and float(line[2]) == 200.0 and float(line[3]) == 1100.0
+    assert line[5] == "5.50" and line[6] == "1.50" and line[7] == "40.0%"
