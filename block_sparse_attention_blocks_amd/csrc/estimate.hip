@@ -170,23 +170,26 @@ __device__ __forceinline__ double row_sum_f64(double x) {  // exact on lane 0 of
 }
 
 
-// exp(dT F) for the logits of the importance pass: dT = T - Tmax <= 0 (-inf allowed) in the integer
-// units of the logit, F > 0 the unit.  With t = dT G (G = F 64 / ln2, clamped at -70000) and
-// n = rint(t), the remainder r = (dT - n K) F, K = ln2 / (64 F), has |r| <= ln2/128 up to rounding
-// (n K F = n ln2/64 to 2^-53 relative, |n| <= 70000: below 1e-13 absolute), and
-// exp = 2^(n >> 6) tab[n & 63] p(r) with tab[j] = 2^(j/64) and p the Taylor polynomial of e^r to
-// degree 4 (truncation below 4e-14 relative).  Below t = -68800 (dT F < -745.2) the result is 0.
+// exp(dT F) for the logits of the importance pass: dT = T - Tmax <= 0 in the integer units of the
+// logit (-inf allowed when MASKED), F > 0 the unit.  With t = dT G (G = F 256 / ln2, clamped at
+// -280000) and n = rint(t), the remainder r = (dT - n K) F, K = ln2 / (256 F), has |r| <= ln2/512
+// up to rounding (n K F = n ln2/256 to 2^-53 relative, |n| <= 280000: below 1e-13 absolute), and
+// exp = 2^(n >> 8) tab[n & 255] p(r) with tab[j] = 2^(j/256) and p the Taylor polynomial of e^r to
+// degree 3 (truncation below 1.5e-13 relative).  MASKED: below t = -275200 (dT F < -745.2, which
+// covers dT = -inf) the result is 0.  Without MASKED (every dT finite) that test is left out: there
+// the ldexp alone gives 0 or a subnormal below 2^-1022, and the values are stored as fp32, whose
+// range ends at 2^-149 anyway.
+template <bool MASKED>
 __device__ __forceinline__ double exp_chunk(double dT, double F, double G, double K, const double* tab) {
-  const double t = fmax(dT * G, -70000.0);
+  const double t = fmax(dT * G, -280000.0);
   const double n = rint(t);
   const double r = fma(-n, K, dT) * F;
-  double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-  p = fma(p, r, 0.5);
+  double p = fma(r, 1.0 / 6.0, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
   const int ni = (int)n;
-  const double y = ldexp(tab[ni & 63] * p, ni >> 6);
-  return t < -68800.0 ? 0.0 : y;
+  const double y = ldexp(tab[ni & 255] * p, ni >> 8);
+  return (MASKED && t < -275200.0) ? 0.0 : y;
 }
 
 // Largest exponent field (at least 1) of the bf16 values packed two to a word.
@@ -349,9 +352,10 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
     qi[rr] = r < a.R ? i : -1;
     eq[rr] = __shfl(emq, 4 * lg + rr) - 301;
   }
-  const double cG = a.scale * (64.0 / 0.69314718055994530942), cK = 0.69314718055994530942 / (64.0 * a.scale);
-  __shared__ double tab[64];  // 2^(j/64)
-  if (t < 64) tab[t] = exp2((double)t * (1.0 / 64.0));
+  const double cG = a.scale * (256.0 / 0.69314718055994530942), cK = 0.69314718055994530942 / (256.0 * a.scale);
+  __shared__ double tab[256];  // 2^(j/256)
+  static_assert(IMP_THREADS >= 256, "one table entry per thread");
+  if (t < 256) tab[t] = exp2((double)t * (1.0 / 256.0));
   const int first_proxy = a.first_row;  // every key j <= first_proxy is visible to every proxy row
 
   const int8_t* kd = kdig + (size_t)g * nchunk * IMP_NDIG * IMP_CK * D;
@@ -414,7 +418,7 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
       if (open) {
         const double tm = row_max_f64(fmax(fmax(x[0][rr], x[1][rr]), fmax(x[2][rr], x[3][rr])));
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_chunk(x[tt][rr] - tm, F, G, K, tab);
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_chunk<false>(x[tt][rr] - tm, F, G, K, tab);
         m = tm * F;
       } else {
         const int i = qi[rr];
@@ -429,7 +433,7 @@ __global__ __launch_bounds__(IMP_THREADS) __attribute__((amdgpu_waves_per_eu(2))
         tm = row_max_f64(tm);
         const double tmm = tm > -INFINITY ? tm : 0.0;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_chunk(sv[tt] - tmm, F, G, K, tab);
+        for (int tt = 0; tt < 4; ++tt) sv[tt] = exp_chunk<true>(sv[tt] - tmm, F, G, K, tab);
         m = tm * F;  // -inf for a row with no key in the chunk
       }
       double l = (sv[0] + sv[1]) + (sv[2] + sv[3]);
