@@ -14,12 +14,13 @@ SOURCES = ["api.hip", "estimate.hip", "prefix_rank.hip", "sample_attn.hip", "att
 # MFMA accumulators stay in VGPRs: the fp64 kernels otherwise move every accumulator between the
 # AGPR and VGPR files around each MFMA.
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-# Per-source extra flags.  The attention sources: no NaN is produced or tested there (masked scores
-# are -inf), so max and compare need no NaN quieting; api.hip validates arguments with comparisons
-# that must keep their NaN meaning and gets no such flag.
+# Per-source extra flags.  The attention and estimation sources: no NaN is produced or tested there
+# (masked scores and logits are -inf, and every -inf path is selected away before it could meet an
+# opposite infinity), so max and compare need no NaN quieting; api.hip validates arguments with
+# comparisons that must keep their NaN meaning and gets no such flag.
 SOURCE_FLAGS = {
     "api.hip": VGPR_FORM,
-    "estimate.hip": VGPR_FORM,
+    "estimate.hip": VGPR_FORM + ["-fno-honor-nans"],
     "prefix_rank.hip": VGPR_FORM,
     "sample_attn.hip": VGPR_FORM,
     "attention.hip": VGPR_FORM + ["-fno-honor-nans"],
