@@ -482,7 +482,7 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   __shared__ int mcount;
   __shared__ float red[2][C::WAVES];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int l32 = lane & 31, h2 = lane >> 5;
   const int hh = wave / WPH;  // this wave's head within the workgroup
   const int wq = wave % WPH;  // this wave's 32-row slice of the query block
@@ -518,6 +518,13 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   float th[HPW];
 #pragma unroll
   for (int x = 0; x < HPW; ++x) th[x] = a.theta[(size_t)(h0 + x) * a.NB + I];
+  // Q operands and thresholds complete here, before the loop: the compiler cannot see the gathers'
+  // waits (inline assembly), and waits left to it inside the loop would count the gathers in
+  // flight as well
+#pragma unroll
+  for (int kk = 0; kk < AC::KSTEPS; ++kk) asm volatile("" ::"v"(qf[kk]));
+#pragma unroll
+  for (int x = 0; x < HPW; ++x) asm volatile("" ::"v"(th[x]));
 
   const int nblk = DENSE ? I + 1 : union_list<HPW, C::THREADS>(a, h0, I, ntri, selb, mlist, &mcount);
   const int sI = a.S > 0 ? I0 / a.S : 0;
@@ -533,15 +540,23 @@ void attn_gate_pipe_kernel(AttnArgs a) {
     return row_lookup(permr, p, a.N, want, a.perm != nullptr && a.S > 0 && (J * BLK) / a.S < sI);
   };
   auto row_off = [&](const RowLook& r) { return row_lookup_offset(r, a.N, a.N, a.kv_row_bytes, a.err); };
+  // Gathers as inline-assembly DMAs, which the compiler's wait-count pass does not track: issued
+  // through the builtin, a V gather still in flight made the compiler wait for it (vmcnt(0)) before
+  // the first LDS read of the next step, so the V load of a kept tile was not hidden behind the next
+  // tile's QK^T.  The kernel waits for its gathers itself (wait_vmcnt before each barrier).  A lane's
+  // row offsets are read together before its first DMA.
+  using GL = GatherLane<D, BLK, C::WAVES>;
   auto gather_k = [&](int u, uint16_t* dst) {
-    const uint32_t* ids = rowid[u & 3];
-    auto rf = [&](int j) { return ids[j]; };
-    dma_tile<D, BLK, false, decltype(rf), BLK, C::WAVES>(dst, kr, rf, opaque(lane));
+    uint32_t ro[GL::NI];
+#pragma unroll
+    for (int i = 0; i < GL::NI; ++i) ro[i] = rowid[u & 3][GL::row(i)];
+    dma_tile_ro<D, false, BLK, C::WAVES>(dst, kr, ro);
   };
   auto gather_v = [&](int u, uint16_t* dst) {
-    const uint32_t* ids = rowid[u & 3];
-    auto rf = [&](int j) { return ids[j]; };
-    dma_tile<D, BLK, true, decltype(rf), BLK, C::WAVES>(dst, vr, rf, opaque(lane));
+    uint32_t ro[GL::NI];
+#pragma unroll
+    for (int i = 0; i < GL::NI; ++i) ro[i] = rowid[u & 3][GL::row(i)];
+    dma_tile_ro<D, true, BLK, C::WAVES>(dst, vr, ro);
   };
 
   SoftmaxState<D, BLK> st;
@@ -559,11 +574,11 @@ void attn_gate_pipe_kernel(AttnArgs a) {
   }
 
   auto step = [&](int u, const uint16_t* Kc, uint16_t* Kn, const uint16_t* Vp, uint16_t* Vc) {
-    bf16x8 first[PBSA_GATE_PF];  // read before the lookups and the gather are issued
-    tile_first_ring<D, BLK, PBSA_GATE_PF>(Kc, first);
     const RowLook pr = lookup(u + 2 < nblk ? u + 2 : 0, t & (BLK - 1), u + 2 < nblk && t < BLK);
     __builtin_amdgcn_sched_barrier(0);  // the lookup is issued before the gather (vmcnt order)
     if (u + 1 < nblk) gather_k(u + 1, Kn);
+    bf16x8 first[PBSA_GATE_PF];
+    tile_first_ring<D, BLK, PBSA_GATE_PF>(Kc, first);
     const uint32_t e = entry_of(u);
     const int J = (int)(e & 0xffffu);
     const bool diag = J == I;
